@@ -1,0 +1,244 @@
+"""Seeded synthetic inputs for decode-time Sevren Sparse Attention.
+
+This module only draws random numbers and lays them out: it holds none of the
+attention arithmetic, and both the HIP path's tests/benchmark and the CPU
+oracle consume what it produces.
+
+Recipes (the model's trained query/key projections are not available, so
+these stand in for them; "The Architecture of Embla 1", section "Sevren Sparse
+Attention learns to be sparse", reports ~50% zero weights at initialisation
+and ~95% after training):
+
+* ``iid``: q and K drawn N(0, 1) per element, keys scaled to RMS 1 (Euclidean
+  norm sqrt(D)); about half of all scores are negative.
+* ``planted``: per (sequence, KV head) a random unit direction u; each query
+  head of the group is q = u + 0.5 * N(0, I/D); each key is
+  k = +-2u + N(0, I/D) with the + sign drawn with probability p, then scaled
+  to RMS 1. A key's score is then positive for every head of the group
+  exactly when its sign is +, so about 1 - p of the V rows can be skipped.
+  The noise is read as N(0, I/D) (isotropic, unit expected norm, the scale
+  of u); N(0, I) would drown u and give about 60% zeros instead of ~95%.
+* V rows are N(0, 1) per element.
+
+Stored keys/values are bf16 (round to nearest even, kept as uint16 bit
+patterns) or float32. Cache slots at or beyond a sequence's context length
+hold NaN so that any read past the live keys shows up in the output.
+Queries are float32 and are NOT normalised (the attention path does that).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 (round half to even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    out = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Exact bf16 -> float32 (for building float32 copies of stored data)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(seed: int, *tag: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *tag])))
+
+
+def _unit(rng: np.random.Generator, d: int) -> np.ndarray:
+    u = rng.standard_normal(d)
+    return u / np.linalg.norm(u)
+
+
+def _rows_to_rms1(x: np.ndarray) -> np.ndarray:
+    """Scale each row to Euclidean norm sqrt(D) (the stored-key recipe)."""
+    nrm = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
+    return (x * (np.sqrt(x.shape[-1]) / nrm)).astype(np.float32)
+
+
+@dataclass
+class Workload:
+    """One batch of decode inputs: a full layer's cache plus queries."""
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    kv_capacity: int
+    kv_dtype: str                 # "bf16" or "f32"
+    ctx_lens: np.ndarray          # [B] int32
+    q: np.ndarray                 # [B, Hq, D] float32 (raw)
+    k: np.ndarray                 # [B, Hkv, Nmax, D] uint16 (bf16 bits) or float32
+    v: np.ndarray                 # same layout as k
+    q_sparse: np.ndarray          # [L, B, Hq, D] float32 (raw), one set per sparse layer
+    planted_p: float | None = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_ctx_len(self) -> int:
+        return int(self.ctx_lens.max()) if self.batch else 0
+
+
+def _store(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    return to_bf16_bits(x) if kv_dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_heads: int,
+                  head_dim: int = 128, ctx_lens, kv_capacity: int | None = None,
+                  kv_dtype: str = "bf16", recipe: str = "planted", p: float = 0.05,
+                  n_sparse_layers: int = 1, poison_tail: bool = True) -> Workload:
+    """Draw one workload. ``recipe`` is "planted" (with positive fraction p) or "iid"."""
+    ctx = np.asarray(ctx_lens, dtype=np.int32).reshape(batch)
+    nmax = int(kv_capacity if kv_capacity is not None else (ctx.max() if batch else 0))
+    if batch and int(ctx.max()) > nmax:
+        raise ValueError("context longer than the cache capacity")
+    B, Hq, Hkv, D = batch, n_q_heads, n_kv_heads, head_dim
+    g = Hq // Hkv
+    sdt = np.uint16 if kv_dtype == "bf16" else np.float32
+    fill = BF16_NAN if kv_dtype == "bf16" else np.float32(np.nan)
+    k = np.empty((B, Hkv, nmax, D), dtype=sdt)
+    v = np.empty((B, Hkv, nmax, D), dtype=sdt)
+    q = np.empty((B, Hq, D), dtype=np.float32)
+    L = n_sparse_layers
+    qs = np.empty((L, B, Hq, D), dtype=np.float32)
+    sigma = 1.0 / np.sqrt(D)
+    for b in range(B):
+        n = int(ctx[b])
+        for kvh in range(Hkv):
+            r = _rng(seed, 1, b, kvh)
+            heads = slice(kvh * g, (kvh + 1) * g)
+            if recipe == "planted":
+                u = _unit(r, D)
+                q[b, heads] = u + 0.5 * sigma * r.standard_normal((g, D))
+                for l in range(L):
+                    qs[l, b, heads] = u + 0.5 * sigma * r.standard_normal((g, D))
+                sign = np.where(r.random(n) < p, 2.0, -2.0).astype(np.float32)
+                keys = r.standard_normal((n, D), dtype=np.float32) * np.float32(sigma)
+                keys += sign[:, None] * u.astype(np.float32)[None, :]
+            elif recipe == "iid":
+                q[b, heads] = r.standard_normal((g, D))
+                for l in range(L):
+                    qs[l, b, heads] = r.standard_normal((g, D))
+                keys = r.standard_normal((n, D), dtype=np.float32)
+            else:
+                raise ValueError(recipe)
+            k[b, kvh, :n] = _store(_rows_to_rms1(keys), kv_dtype)
+            v[b, kvh, :n] = _store(r.standard_normal((n, D), dtype=np.float32), kv_dtype)
+            if poison_tail:
+                k[b, kvh, n:] = fill
+                v[b, kvh, n:] = fill
+            else:
+                k[b, kvh, n:] = 0
+                v[b, kvh, n:] = 0
+    return Workload(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                    kv_capacity=nmax, kv_dtype=kv_dtype, ctx_lens=ctx, q=q, k=k, v=v,
+                    q_sparse=qs, planted_p=p if recipe == "planted" else None,
+                    meta={"seed": seed, "recipe": recipe})
+
+
+# --------------------------------------------------------------------------
+# the five workloads, at full size by default (sizes can be shrunk for tests)
+# --------------------------------------------------------------------------
+
+def tiny_decode(seed: int = 1, n: int = 4096) -> Workload:
+    """1 sequence, 1 query head / 1 KV head, D=128, fp32, i.i.d. (about 50% zero weights)."""
+    return make_workload("tiny_decode_fp32_4k", seed=seed, batch=1, n_q_heads=1, n_kv_heads=1,
+                         ctx_lens=[n], kv_dtype="f32", recipe="iid")
+
+
+def single_decode(seed: int = 2, n: int = 32768, p: float = 0.05) -> Workload:
+    """1 sequence, 16 q / 2 KV heads, D=128, bf16, planted 95% sparsity."""
+    return make_workload(f"single_decode_bf16_{n}", seed=seed, batch=1, n_q_heads=16,
+                         n_kv_heads=2, ctx_lens=[n], p=p)
+
+
+def batched_ctx_lens(seed: int = 3, batch: int = 8, lo: int = 65536, hi: int = 131072) -> np.ndarray:
+    """Context lengths drawn uniformly from the integers lo..hi inclusive."""
+    return _rng(seed, 0).integers(lo, hi + 1, size=batch).astype(np.int32)
+
+
+def batched_decode(seed: int = 3, batch: int = 8, lo: int = 65536, hi: int = 131072,
+                   kv_capacity: int = 131072, p: float = 0.05, fixed_len: int | None = None,
+                   n_sparse_layers: int = 1) -> Workload:
+    """Batch 8, contexts uniform in [64K, 128K], 16 q / 2 KV heads, bf16, planted 95%."""
+    if fixed_len is not None:
+        ctx = np.full(batch, fixed_len, dtype=np.int32)
+    else:
+        ctx = batched_ctx_lens(seed, batch, lo, hi)
+    return make_workload("batched_decode_b8_64k_128k" if fixed_len is None else
+                         f"batched_decode_b{batch}_fixed{fixed_len}",
+                         seed=seed, batch=batch, n_q_heads=16, n_kv_heads=2, ctx_lens=ctx,
+                         kv_capacity=kv_capacity, p=p, n_sparse_layers=n_sparse_layers)
+
+
+SWEEP_FRACTIONS = (0.5, 0.2, 0.05, 0.01, 0.002)
+
+
+def sweep_decode(p: float, seed: int = 4, batch: int = 4, n: int = 65536) -> Workload:
+    """Batch 4, context 65536, planted positive-key fraction p."""
+    return make_workload(f"sweep_decode_p{p}", seed=seed, batch=batch, n_q_heads=16,
+                         n_kv_heads=2, ctx_lens=[n] * batch, p=p)
+
+
+def block_ctx_lens(seed: int = 5, batch: int = 32, lo: int = 1024, hi: int = 262144) -> np.ndarray:
+    """Context lengths log-uniform in [lo, hi]: round(exp(U(ln lo, ln hi)))."""
+    x = _rng(seed, 0).uniform(np.log(lo), np.log(hi), size=batch)
+    return np.clip(np.rint(np.exp(x)), lo, hi).astype(np.int32)
+
+
+def block_step(seed: int = 5, batch: int = 32, lo: int = 1024, hi: int = 262144,
+               kv_capacity: int = 262144) -> Workload:
+    """Batch 32, contexts log-uniform in [1K, 256K], one full + three sparse layers."""
+    return make_workload("block_step_b32_1k_256k", seed=seed, batch=batch, n_q_heads=16,
+                         n_kv_heads=2, ctx_lens=block_ctx_lens(seed, batch, lo, hi),
+                         kv_capacity=kv_capacity, p=0.05, n_sparse_layers=3)
+
+
+@dataclass
+class PrefillWorkload:
+    """A chunk of prompt queries against a full layer's cache."""
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_query: int
+    kv_capacity: int
+    q_pos0: np.ndarray            # [B] int32
+    q: np.ndarray                 # [B, Hq, Tq, D] uint16 (bf16 bits, raw)
+    k: np.ndarray                 # [B, Hkv, Nmax, D] uint16
+    v: np.ndarray
+
+
+def prefill_chunk(seed: int = 5, batch: int = 1, n_query: int = 2048, n_keys: int = 65536,
+                  p: float = 0.05, recipe: str = "planted") -> PrefillWorkload:
+    """2048 prompt queries at the end of a 64K cache (q_pos0 = n_keys - n_query)."""
+    Hq, Hkv, D = 16, 2, 128
+    g = Hq // Hkv
+    wl = make_workload("prefill", seed=seed, batch=batch, n_q_heads=Hq, n_kv_heads=Hkv,
+                       ctx_lens=[n_keys] * batch, p=p, recipe=recipe)
+    q = np.empty((batch, Hq, n_query, D), dtype=np.float32)
+    sigma = 1.0 / np.sqrt(D)
+    for b in range(batch):
+        for kvh in range(Hkv):
+            r = _rng(seed, 2, b, kvh)
+            if recipe == "planted":
+                u = _unit(_rng(seed, 1, b, kvh), D)
+                q[b, kvh * g:(kvh + 1) * g] = u + 0.5 * sigma * r.standard_normal((g, n_query, D))
+            else:
+                q[b, kvh * g:(kvh + 1) * g] = r.standard_normal((g, n_query, D))
+    return PrefillWorkload(name=f"prefill_{n_query}x{n_keys}", batch=batch, n_q_heads=Hq,
+                           n_kv_heads=Hkv, head_dim=D, n_query=n_query, kv_capacity=n_keys,
+                           q_pos0=np.full(batch, n_keys - n_query, dtype=np.int32),
+                           q=to_bf16_bits(q), k=wl.k, v=wl.v)

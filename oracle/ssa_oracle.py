@@ -1,0 +1,268 @@
+"""Plain CPU oracle for decode-time Sevren Sparse Attention (SSA).
+
+TEST INFRASTRUCTURE. This module is the reference that the HIP path is checked
+against. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg may import it; the product path never does. It shares no code with the
+HIP library or its Python binding and imports nothing from them.
+
+Everything is computed in float64 with NumPy, one obvious loop per
+(sequence, head). Stored bf16 values arrive as raw uint16 bit patterns and are
+decoded exactly; float32 inputs are widened exactly. Nothing here is blocked,
+fused or reordered beyond the definitions it follows.
+
+Source: the web page "The Architecture of Embla 1" (sevren.ai blog):
+  * "Three kinds of attention" -- full layers read every token and use no
+    position encoding; sparse layers reuse the full layer's cache restricted
+    to the 1,024 keys that layer scored highest plus the 128 most recent,
+    choose by raw score (keys just below zero included), and apply their own
+    softmax over the selection.
+  * "Sevren Sparse Attention learns to be sparse" -- each key's weight is
+    ReLU(score)^2 of the RMS-normalised query and key; the output is the
+    weighted sum of values divided by (a constant + the sum of the weights);
+    a score of zero or below gives exactly zero weight.
+  * "Skipping V" -- a value row is needed only if some query head sharing the
+    KV head gives the key a nonzero weight.
+  * "KV bridge, KV reuse, and prefill" -- the prompt is pushed through the
+    full layer to fill its cache (causal prefill).
+
+The displayed SSA formula itself did not survive on the page: the constant in
+the denominator and the hat symbols are missing from the text. Readings taken
+where the page is silent or garbled (each is listed with its reason in the
+design notes of the repository):
+  * the constant ``c`` is a parameter (default 1.0); its value is not on the
+    page, so parity of the default value is unpinned -- tests sweep c;
+  * the score is ``scale * (q_hat . k_hat)`` with ``scale`` a parameter
+    (default 1.0); only ``c / scale**2`` matters;
+  * RMS normalisation has unit gain and ``x / sqrt(mean(x^2) + eps)``;
+    the query is normalised here (flag SSA_NORM_Q), keys are stored already
+    normalised unless SSA_NORM_K asks for it on the fly;
+  * ``c + sum(w) == 0`` gives an output of exactly 0;
+  * selection is per query head, top-k by score with ties broken towards the
+    lower key index, united (deduplicated) with the most recent window, which
+    includes the current token; SSA_SELECT_DISJOINT instead takes the window
+    plus the top-k of the keys outside it;
+  * the sparse layer's softmax scale is a parameter (default 1/sqrt(D)) and an
+    empty selection gives an output of 0;
+  * prefill query t of a chunk sits at position q_pos0 + t and attends keys
+    0 .. q_pos0 + t inclusive.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+SSA_NORM_Q = 1
+SSA_NORM_K = 2
+SSA_SELECT_DISJOINT = 4
+
+
+# --------------------------------------------------------------------------
+# exact widening of stored values
+# --------------------------------------------------------------------------
+
+def widen(x) -> np.ndarray:
+    """Return the stored values of ``x`` exactly as float64.
+
+    uint16 arrays are bf16 bit patterns: the 16 bits are the upper half of an
+    IEEE binary32, so shifting them up and reinterpreting is exact.
+    """
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float16, np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported stored dtype {a.dtype}")
+
+
+# --------------------------------------------------------------------------
+# full layer: ReLU^2 attention with V-skip
+# --------------------------------------------------------------------------
+
+def rms_normalize(x, eps: float) -> np.ndarray:
+    """RMS normalisation with unit gain over the last axis.
+
+    "Sevren Sparse Attention learns to be sparse": query and key enter the
+    score RMS-normalised. No trained gain exists here, so the gain is 1.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def relu2_weights(s: np.ndarray) -> np.ndarray:
+    """w = ReLU(s)^2, exactly zero for s <= 0 ("zero or below gets exactly zero")."""
+    s = np.asarray(s, dtype=np.float64)
+    return np.where(s > 0.0, s * s, 0.0)
+
+
+def relu2_attend(q_hat, k_hat, vals, scale: float, c: float):
+    """One query against one key/value stream.
+
+    Returns (out, s, w): s = scale * (q_hat . k_hat_i) for every key, the
+    weights w, and out = sum_i w_i v_i / (c + sum_i w_i). Only value rows with
+    w_i > 0 are touched ("Skipping V"). A zero denominator gives out = 0.
+    ``vals`` is indexable by key and yields float64 rows.
+    """
+    s = scale * (k_hat @ q_hat)
+    w = relu2_weights(s)
+    live = np.flatnonzero(s > 0.0)
+    den = float(np.sum(w[live]))
+    d = q_hat.shape[-1]
+    if live.size:
+        num = w[live] @ widen(vals[live])
+    else:
+        num = np.zeros(d)
+    if c + den == 0.0:
+        return np.zeros(d), s, w
+    return num / (c + den), s, w
+
+
+def decode_full(q, k, v, ctx_lens, scale: float = 1.0, c: float = 1.0,
+                eps: float = 1e-6, flags: int = SSA_NORM_Q):
+    """Full-layer decode for one query token per sequence.
+
+    q: [B, Hq, D] float; k, v: [B, Hkv, Nmax, D] stored (uint16 bf16 bits or
+    float32); ctx_lens: [B] ints, keys 0..n_b-1 are live.
+
+    Returns a dict with
+      out    [B, Hq, D]  float64
+      scores list over b of [Hq, n_b] float64 raw (pre-ReLU) scores
+      nnz    [B, Hq]     keys with nonzero weight per query head
+      vrows  [B, Hkv]    keys whose V row some head of the group needs
+    """
+    q = widen(q)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    nnz = np.zeros((B, Hq), dtype=np.int64)
+    vrows = np.zeros((B, Hkv), dtype=np.int64)
+    scores = []
+    for b in range(B):
+        n = int(ctx_lens[b])
+        sb = np.zeros((Hq, n))
+        for kvh in range(Hkv):
+            keys = widen(k[b, kvh, :n])
+            if flags & SSA_NORM_K:
+                keys = rms_normalize(keys, eps)
+            needed = np.zeros(n, dtype=bool)
+            for j in range(g):
+                h = kvh * g + j
+                qh = rms_normalize(q[b, h], eps) if flags & SSA_NORM_Q else q[b, h]
+                o, s, w = relu2_attend(qh, keys, v[b, kvh], scale, c)
+                out[b, h] = o
+                sb[h] = s
+                nnz[b, h] = int(np.count_nonzero(s > 0.0))
+                needed |= s > 0.0
+            vrows[b, kvh] = int(np.count_nonzero(needed))
+        scores.append(sb)
+    return {"out": out, "scores": scores, "nnz": nnz, "vrows": vrows}
+
+
+# --------------------------------------------------------------------------
+# selection for the sparse layers
+# --------------------------------------------------------------------------
+
+def select_topk_recent(s, n: int, k_top: int = 1024, n_recent: int = 128,
+                       disjoint: bool = False) -> np.ndarray:
+    """Key indices a sparse layer reads, ascending.
+
+    "Three kinds of attention": the keys the full layer scored highest (by raw
+    score, so keys scored just below zero still count) plus the most recent
+    keys. Ties at the cut go to the lower index. The recent window is the
+    last ``n_recent`` cache positions, current token included.
+    """
+    s = np.asarray(s, dtype=np.float64)[:n]
+    idx = np.arange(n)
+    order = np.lexsort((idx, -s))  # score descending, then index ascending
+    recent = idx[max(0, n - n_recent):]
+    if disjoint:
+        in_recent = order >= max(0, n - n_recent)
+        top = order[~in_recent][:k_top]
+    else:
+        top = order[:min(k_top, n)]
+    return np.union1d(top, recent).astype(np.int64)
+
+
+def select_all(scores, ctx_lens, k_top: int = 1024, n_recent: int = 128,
+               flags: int = 0):
+    """Per (b, query head) selections: returns a list over b of lists over h."""
+    disjoint = bool(flags & SSA_SELECT_DISJOINT)
+    res = []
+    for b, sb in enumerate(scores):
+        n = int(ctx_lens[b])
+        res.append([select_topk_recent(sb[h], n, k_top, n_recent, disjoint)
+                    for h in range(sb.shape[0])])
+    return res
+
+
+# --------------------------------------------------------------------------
+# sparse layer: softmax over the selection
+# --------------------------------------------------------------------------
+
+def softmax_attend(q_vec, k_rows, v_rows, scale: float) -> np.ndarray:
+    """p = softmax(scale * q . k_j) over the given rows; returns sum_j p_j v_j."""
+    if k_rows.shape[0] == 0:
+        return np.zeros(q_vec.shape[-1])
+    t = scale * (k_rows @ q_vec)
+    e = np.exp(t - np.max(t))
+    p = e / np.sum(e)
+    return p @ v_rows
+
+
+def decode_sparse(q, k, v, selections, scale: float | None = None,
+                  eps: float = 1e-6, flags: int = SSA_NORM_Q) -> np.ndarray:
+    """Sparse-layer decode over the full layer's cache.
+
+    q: [B, Hq, D] (this sparse layer's own queries); selections[b][h]: key
+    indices for query head h. No position encoding; no cache of its own.
+    """
+    q = widen(q)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // g
+            sel = np.asarray(selections[b][h], dtype=np.int64)
+            keys = widen(k[b, kvh][sel])
+            if flags & SSA_NORM_K:
+                keys = rms_normalize(keys, eps)
+            qh = rms_normalize(q[b, h], eps) if flags & SSA_NORM_Q else q[b, h]
+            out[b, h] = softmax_attend(qh, keys, widen(v[b, kvh][sel]), scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# chunked causal prefill of the full layer
+# --------------------------------------------------------------------------
+
+def prefill_full(q, k, v, q_pos0, scale: float = 1.0, c: float = 1.0,
+                 eps: float = 1e-6, flags: int = SSA_NORM_Q, rows=None) -> np.ndarray:
+    """ReLU^2 attention for a chunk of prompt queries.
+
+    q: [B, Hq, Tq, D]; query t of sequence b sits at position q_pos0[b] + t and
+    attends keys 0 .. q_pos0[b] + t (causal, no position encoding).
+    ``rows`` optionally restricts the work to a list of (b, h, t); other
+    output rows are left at zero.
+    """
+    q = widen(q)
+    B, Hq, Tq, D = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    if rows is None:
+        rows = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(Tq)]
+    out = np.zeros((B, Hq, Tq, D))
+    for b, h, t in rows:
+        kvh = h // g
+        last = int(q_pos0[b]) + t + 1
+        keys = widen(k[b, kvh, :last])
+        if flags & SSA_NORM_K:
+            keys = rms_normalize(keys, eps)
+        qt = rms_normalize(q[b, h, t], eps) if flags & SSA_NORM_Q else q[b, h, t]
+        out[b, h, t] = relu2_attend(qt, keys, v[b, kvh, :last], scale, c)[0]
+    return out

@@ -1,0 +1,425 @@
+"""Pins that tie the CPU oracle to what the page and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+an independent fact: a hand-worked example (tests/golden/worked_d4.json), a
+closed form of a special case, an invariant of the definition, a library
+routine that the special case reduces to, or a brute-force count on tiny
+inputs. ``test_oracle_pins.py`` runs them against the oracle as written;
+``test_oracle_mutants.py`` plants plausible mistakes in the oracle and checks
+that some pin fails for each.
+
+Source page: "The Architecture of Embla 1" (sevren.ai blog), sections
+"Three kinds of attention", "Sevren Sparse Attention learns to be sparse",
+"Skipping V" and "KV bridge, KV reuse, and prefill".
+"""
+
+from __future__ import annotations
+
+import heapq
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import ssa_oracle as O
+from long_context_decode_relu_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_d4.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _num(s):
+    if isinstance(s, (int, float)):
+        return float(s)
+    if s == "nan":
+        return float("nan")
+    if "e" in s:  # closed form in Euler's number
+        return float(eval(s, {"__builtins__": {}}, {"e": math.e}))
+    return float(Fraction(s))
+
+
+def _arr(x):
+    return np.array([[_num(a) for a in row] for row in x]) if isinstance(x[0], list) \
+        else np.array([_num(a) for a in x])
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.allclose(a, b, rtol=rtol, atol=atol), f"{what}: {a} vs {b}"
+
+
+# --------------------------------------------------------------------------
+# hand-worked example (golden fixture)
+# --------------------------------------------------------------------------
+
+def pin_golden_full():
+    g = _golden()
+    K = np.array(g["keys"], dtype=np.float32)[None, None]
+    V = np.array([[_num(a) for a in r] for r in g["values"]], dtype=np.float32)[None, None]
+    for case in g["full_layer"]:
+        q = np.array(case["q"], dtype=np.float32)[None]
+        r = O.decode_full(q, K, V, [K.shape[2]], scale=case["scale"], c=case["c"],
+                          eps=g["eps"], flags=O.SSA_NORM_Q)
+        _close(r["out"][0], _arr(case["out"]), what=case["name"] + " out")
+        _close(r["scores"][0], _arr(case["scores"]), what=case["name"] + " scores")
+        assert list(r["nnz"][0]) == case["nnz"], case["name"]
+        assert int(r["vrows"][0, 0]) == case["vrows"], case["name"]
+
+
+def pin_golden_select():
+    g = _golden()["select"]
+    s = np.array(g["scores"], dtype=np.float64)
+    for case in g["cases"]:
+        sel = O.select_topk_recent(s, len(s), case["k_top"], case["n_recent"], case["disjoint"])
+        assert list(sel) == case["sel"], (case, list(sel))
+
+
+def pin_golden_sparse():
+    g = _golden()
+    sp = g["sparse_layer"]
+    K = np.array(g["keys"], dtype=np.float32)[None, None]
+    V = np.array([[_num(a) for a in r] for r in g["values"]], dtype=np.float32)[None, None]
+    q = np.array(sp["q"], dtype=np.float32)[None, None]
+    out = O.decode_sparse(q, K, V, [[sp["sel"]]], scale=sp["scale"], eps=g["eps"])
+    _close(out[0, 0], _arr(sp["out"]), what="sparse golden")
+
+
+def pin_golden_prefill():
+    g = _golden()
+    pf = g["prefill"]
+    K = synth.to_bf16_bits(np.array(g["keys"], dtype=np.float32))[None, None]
+    V = synth.to_bf16_bits(np.array([[_num(a) for a in r] for r in g["values"]],
+                                    dtype=np.float32))[None, None]
+    q = synth.to_bf16_bits(np.array(pf["q"], dtype=np.float32))[None, None]
+    out = O.prefill_full(q, K, V, [pf["q_pos0"]], scale=pf["scale"], c=pf["c"], eps=g["eps"])
+    _close(out[0, 0], _arr(pf["out"]), what="prefill golden")
+
+
+# --------------------------------------------------------------------------
+# exact zero rule, closed forms, invariants
+# --------------------------------------------------------------------------
+
+def pin_widen_bf16():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x8000, 0x7F80], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0078125, 2.0 ** -133, -0.0, math.inf]
+    got = O.widen(bits)
+    assert list(got) == want, got
+    assert math.copysign(1.0, got[4]) == -1.0
+
+
+def pin_zero_rule():
+    """Scores of exactly zero or below give weight exactly zero; such V rows are never read."""
+    w = O.relu2_weights(np.array([-3.0, -0.0, 0.0, -1e-300, 1e-150, 2.0]))
+    assert w[0] == 0.0 and w[1] == 0.0 and w[2] == 0.0 and w[3] == 0.0
+    assert w[4] > 0.0 and w[5] == 4.0
+    D, n = 16, 40
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    qhat = q[0, 0] / np.linalg.norm(q[0, 0])
+    K = np.empty((1, 1, n, D), dtype=np.float32)
+    for i in range(n):
+        x = rng.standard_normal(D)
+        x -= (x @ qhat) * qhat            # orthogonal to q: score 0 up to rounding
+        if i % 2:
+            x -= (1.0 + rng.random()) * qhat * np.linalg.norm(x)   # strictly negative score
+        K[0, 0, i] = x
+    V = np.full((1, 1, n, D), np.nan, dtype=np.float32)
+    sc = O.decode_full(q, K, V, [n], flags=O.SSA_NORM_Q)["scores"][0][0]
+    keep = np.flatnonzero(sc <= 0.0)
+    K2 = K[:, :, keep].copy()
+    V2 = V[:, :, keep].copy()
+    r = O.decode_full(q, K2, V2, [keep.size], c=1.0)
+    assert keep.size >= n // 2
+    assert np.all(r["out"] == 0.0) and r["nnz"][0, 0] == 0 and r["vrows"][0, 0] == 0
+
+
+def _onehot_case(D=128, n=64, j=5, alpha=3.0, seed=11):
+    rng = np.random.default_rng(seed)
+    q = np.zeros((1, 1, D), dtype=np.float32)
+    q[0, 0, j] = alpha                     # RMS-normalised: sqrt(D) * e_j
+    K = rng.standard_normal((1, 1, n, D)).astype(np.float32)
+    K[0, 0, :, j] = -np.abs(K[0, 0, :, j]) - 0.1
+    V = rng.standard_normal((1, 1, n, D)).astype(np.float32)
+    return q, K, V, rng
+
+
+def pin_one_survivor_closed_form():
+    """One key with positive score: out = w/(c + w) * v with w = (scale*sqrt(D)*K[i,j])^2."""
+    D, j = 128, 5
+    q, K, V, rng = _onehot_case(D=D, j=j)
+    i = 17
+    K[0, 0, i, j] = 0.75
+    for scale, c in [(1.0, 1.0), (0.25, 3.0), (2.0, 0.5)]:
+        r = O.decode_full(q, K, V, [K.shape[2]], scale=scale, c=c, eps=0.0)
+        w = (scale * math.sqrt(D) * float(K[0, 0, i, j])) ** 2
+        _close(r["out"][0, 0], w / (c + w) * V[0, 0, i].astype(np.float64), rtol=1e-12,
+               what="one survivor")
+        assert r["nnz"][0, 0] == 1 and r["vrows"][0, 0] == 1
+
+
+def pin_two_survivors_closed_form():
+    D, j = 128, 9
+    q, K, V, rng = _onehot_case(D=D, j=j, seed=12)
+    K[0, 0, 3, j] = 0.5
+    K[0, 0, 40, j] = 1.25
+    c = 2.0
+    r = O.decode_full(q, K, V, [K.shape[2]], scale=1.0, c=c, eps=0.0)
+    w3 = (math.sqrt(D) * 0.5) ** 2
+    w40 = (math.sqrt(D) * 1.25) ** 2
+    want = (w3 * V[0, 0, 3].astype(np.float64) + w40 * V[0, 0, 40].astype(np.float64)) / (c + w3 + w40)
+    _close(r["out"][0, 0], want, rtol=1e-12, what="two survivors")
+
+
+def _iid(seed=3, B=2, Hq=4, Hkv=2, n=300, D=128):
+    return synth.make_workload("iid", seed=seed, batch=B, n_q_heads=Hq, n_kv_heads=Hkv,
+                               head_dim=D, ctx_lens=[n] * B, kv_dtype="f32", recipe="iid")
+
+
+def pin_constant_values():
+    """All V rows equal v0: c = 0 gives exactly v0 (a weighted mean), c > 0 shrinks it by W/(c+W) < 1."""
+    wl = _iid()
+    V = np.broadcast_to(wl.v[:, :, :1], wl.v.shape).copy()
+    r0 = O.decode_full(wl.q, wl.k, V, wl.ctx_lens, c=0.0)
+    for b in range(wl.batch):
+        for h in range(wl.n_q_heads):
+            _close(r0["out"][b, h], V[b, h // 2, 0], rtol=1e-12, what="c=0 mean")
+    r1 = O.decode_full(wl.q, wl.k, V, wl.ctx_lens, c=50.0)
+    ratio = r1["out"] / np.asarray(V[:, [0, 0, 1, 1], 0], dtype=np.float64)
+    assert np.all(ratio > 0.0) and np.all(ratio < 1.0)
+    assert np.allclose(ratio, ratio[..., :1], rtol=1e-12)
+
+
+def pin_homogeneity():
+    """w is homogeneous of degree 2 in the score: o(a*scale, c) == o(scale, c / a^2)."""
+    wl = _iid(seed=4)
+    for a in (0.5, 3.0):
+        r1 = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens, scale=a, c=5.0)
+        r2 = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens, scale=1.0, c=5.0 / a ** 2)
+        _close(r1["out"], r2["out"], rtol=1e-10, atol=1e-13, what="homogeneity")
+
+
+def pin_query_scale_invariance():
+    """The query is RMS-normalised: scaling it by b > 0 changes nothing (eps = 0)."""
+    wl = _iid(seed=5)
+    c = 2.0e4   # comparable to the weight sum, so a change of score scale shows
+    r1 = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens, c=c, eps=0.0)
+    r2 = O.decode_full(wl.q * np.float32(8.0), wl.k, wl.v, wl.ctx_lens, c=c, eps=0.0)
+    _close(r1["out"], r2["out"], rtol=1e-12, atol=1e-14, what="q scale")
+    r3 = O.decode_full(wl.q * np.float32(8.0), wl.k, wl.v, wl.ctx_lens, c=c, eps=0.0, flags=0)
+    assert not np.allclose(r1["out"], r3["out"], rtol=1e-3)
+
+
+def pin_norm_k_flag():
+    """SSA_NORM_K on keys scaled per row by any positive factor equals the stored-normalised keys."""
+    wl = _iid(seed=6)
+    rng = np.random.default_rng(1)
+    scaled = (wl.k * rng.uniform(0.2, 5.0, size=wl.k.shape[:3] + (1,))).astype(np.float32)
+    r1 = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens, eps=0.0)
+    r2 = O.decode_full(wl.q, scaled, wl.v, wl.ctx_lens, eps=0.0, flags=O.SSA_NORM_Q | O.SSA_NORM_K)
+    _close(r1["out"], r2["out"], rtol=1e-6, atol=1e-6, what="norm k")
+
+
+def pin_permutation_invariance():
+    """No position encoding: permuting keys together with their values leaves the output unchanged."""
+    wl = _iid(seed=8, B=1, n=200)
+    perm = np.random.default_rng(2).permutation(200)
+    r1 = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    r2 = O.decode_full(wl.q, wl.k[:, :, perm], wl.v[:, :, perm], wl.ctx_lens)
+    _close(r1["out"], r2["out"], rtol=1e-10, atol=1e-13, what="perm")
+    sel = [[np.arange(0, 200, 3)] * wl.n_q_heads]
+    inv = np.argsort(perm)
+    sel_p = [[inv[np.arange(0, 200, 3)]] * wl.n_q_heads]
+    o1 = O.decode_sparse(wl.q, wl.k, wl.v, sel)
+    o2 = O.decode_sparse(wl.q, wl.k[:, :, perm], wl.v[:, :, perm], sel_p)
+    _close(o1, o2, rtol=1e-10, atol=1e-13, what="perm sparse")
+
+
+def pin_random_init_half_zero():
+    """Random normalised q and k: a score is as likely negative as positive (page: 50.8% at init).
+
+    n i.i.d. keys against one query: zero-weight fraction within 4 sigma of 1/2.
+    """
+    n = 65536
+    wl = synth.make_workload("iid", seed=21, batch=1, n_q_heads=1, n_kv_heads=1,
+                             ctx_lens=[n], kv_dtype="f32", recipe="iid")
+    r = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    frac = 1.0 - r["nnz"][0, 0] / n
+    assert abs(frac - 0.5) < 4 * 0.5 / math.sqrt(n), frac
+
+
+def pin_group_skip_independent_heads():
+    """g = 8 independent query heads: a V row is skippable only if all 8 weights are zero.
+
+    For independent isotropic queries the 8 signs are independent, so the skip
+    probability is 2^-8 and each head alone is zero with probability 1/2.
+    """
+    n = 32768
+    wl = synth.make_workload("iid", seed=22, batch=1, n_q_heads=8, n_kv_heads=1,
+                             ctx_lens=[n], kv_dtype="f32", recipe="iid")
+    r = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    p_skip = 2.0 ** -8
+    skipped = n - r["vrows"][0, 0]
+    sd = math.sqrt(n * p_skip * (1 - p_skip))
+    assert abs(skipped - n * p_skip) < 5 * sd + 2, skipped
+    assert r["vrows"][0, 0] >= r["nnz"][0].max()
+
+
+def pin_planted_sparsity():
+    """Planted keys: positive for every head of the group exactly when the key's sign is +."""
+    n, p = 20000, 0.05
+    wl = synth.make_workload("planted", seed=23, batch=1, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[n], kv_dtype="f32", recipe="planted", p=p)
+    r = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    sd = math.sqrt(n * p * (1 - p))
+    for kvh in range(2):
+        assert abs(r["vrows"][0, kvh] - n * p) < 5 * sd
+    assert np.all(np.abs(r["nnz"][0] - n * p) < 5 * sd)
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+
+def _better(s, a, b):
+    """Key a ranks before key b: higher score, ties to the lower index."""
+    return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+
+def _check_selection(s, n, k, r, sel):
+    sel = list(sel)
+    assert sel == sorted(set(sel)), "ascending and unique"
+    recent = set(range(max(0, n - r), n))
+    assert recent <= set(sel), "recent window included"
+    S = set(sel)
+    # a key outside the recent window is selected iff fewer than k keys rank before it
+    for i in range(n):
+        if i in recent:
+            continue
+        rank = sum(1 for j in range(n) if _better(s, j, i))
+        assert (i in S) == (rank < k), (i, rank)
+    lo, hi = min(n, k), min(n, k + r)
+    assert lo <= len(sel) <= hi
+
+
+def pin_select_bruteforce():
+    """Brute-force rank counts on tiny inputs with many ties, at the boundary sizes."""
+    rng = np.random.default_rng(31)
+    for n in (0, 1, 2, 7, 8, 9, 15, 16, 17, 23, 24, 25, 40):
+        for k, r in ((8, 4), (16, 0), (1, 1), (3, 16)):
+            s = rng.integers(-3, 4, size=n).astype(np.float64)
+            s[rng.random(n) < 0.2] = -0.0
+            sel = O.select_topk_recent(s, n, k, r)
+            _check_selection(s, n, k, r, sel)
+
+
+def pin_select_heap():
+    """Against the standard library's heap selection on random distinct scores."""
+    rng = np.random.default_rng(32)
+    for n in (1, 127, 128, 129, 1023, 1024, 1025, 1151, 1152, 1153, 3000):
+        s = rng.standard_normal(n)
+        sel = O.select_topk_recent(s, n, 1024, 128)
+        top = heapq.nlargest(1024, range(n), key=lambda i: (s[i], -i))
+        want = sorted(set(top) | set(range(max(0, n - 128), n)))
+        assert list(sel) == want, n
+        if n <= 1024:
+            assert list(sel) == list(range(n))
+
+
+def pin_select_below_zero():
+    """Fewer than k positive scores: the rest are the keys scored just below zero."""
+    rng = np.random.default_rng(33)
+    n, k = 500, 32
+    s = -rng.random(n) - 0.01
+    pos = rng.choice(n - 10, size=10, replace=False)
+    s[pos] = rng.random(10) + 0.1
+    sel = set(O.select_topk_recent(s, n, k, 0))
+    neg_order = [i for i in np.argsort(-s, kind="stable") if s[i] < 0]
+    assert set(pos) <= sel and set(neg_order[:k - 10]) <= sel and len(sel) == k
+
+
+def pin_select_disjoint():
+    rng = np.random.default_rng(34)
+    for n in (5, 50, 300):
+        s = rng.standard_normal(n)
+        sel = O.select_topk_recent(s, n, 16, 8, disjoint=True)
+        outside = [i for i in range(n) if i < n - 8]
+        top = heapq.nlargest(16, outside, key=lambda i: (s[i], -i))
+        assert list(sel) == sorted(set(top) | set(range(max(0, n - 8), n)))
+
+
+# --------------------------------------------------------------------------
+# sparse layer
+# --------------------------------------------------------------------------
+
+def pin_sparse_equals_sdpa():
+    """With n <= k_top the selection is every key, so the layer is textbook softmax attention.
+
+    Checked against PyTorch's scaled_dot_product_attention on the CPU in float64.
+    """
+    import torch
+    import torch.nn.functional as F
+    wl = synth.make_workload("sp", seed=41, batch=2, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                             ctx_lens=[300, 300], kv_dtype="f32", recipe="iid")
+    sel = O.select_all([np.zeros((4, 300))] * 2, wl.ctx_lens, 1024, 128)
+    out = O.decode_sparse(wl.q, wl.k, wl.v, sel, flags=0)
+    q = torch.from_numpy(wl.q.astype(np.float64))[:, :, None, :]
+    k = torch.from_numpy(wl.k.astype(np.float64)).repeat_interleave(2, dim=1)
+    v = torch.from_numpy(wl.v.astype(np.float64)).repeat_interleave(2, dim=1)
+    want = F.scaled_dot_product_attention(q, k, v)[:, :, 0, :].numpy()
+    _close(out, want, rtol=1e-10, atol=1e-12, what="sdpa")
+
+
+def pin_sparse_single_key():
+    """A selection of one key returns that key's value row exactly (softmax of one entry is 1)."""
+    wl = _iid(seed=42)
+    sel = [[np.array([7])] * wl.n_q_heads for _ in range(wl.batch)]
+    out = O.decode_sparse(wl.q, wl.k, wl.v, sel)
+    for b in range(wl.batch):
+        for h in range(wl.n_q_heads):
+            _close(out[b, h], wl.v[b, h // 2, 7], rtol=1e-15, what="single key")
+
+
+# --------------------------------------------------------------------------
+# prefill
+# --------------------------------------------------------------------------
+
+def pin_prefill_first_position():
+    """A query at position 0 sees only key 0: out = w/(c + w) * v0."""
+    D, j = 128, 3
+    rng = np.random.default_rng(51)
+    q = np.zeros((1, 1, 2, D), dtype=np.float32)
+    q[0, 0, :, j] = 2.0
+    K = rng.standard_normal((1, 1, 2, D)).astype(np.float32)
+    K[0, 0, 0, j] = 0.5
+    V = rng.standard_normal((1, 1, 2, D)).astype(np.float32)
+    out = O.prefill_full(synth.to_bf16_bits(q), synth.to_bf16_bits(K), synth.to_bf16_bits(V),
+                         [0], c=1.0, eps=0.0)
+    w = (math.sqrt(D) * 0.5) ** 2
+    v0 = O.widen(synth.to_bf16_bits(V[0, 0, 0]))
+    _close(out[0, 0, 0], w / (1 + w) * v0, rtol=1e-12, what="prefill pos 0")
+
+
+def pin_prefill_causal():
+    """Row t ignores keys after position q_pos0 + t, and equals decode at that context length."""
+    pw = synth.prefill_chunk(seed=52, n_query=6, n_keys=40, recipe="iid")
+    out = O.prefill_full(pw.q, pw.k, pw.v, pw.q_pos0)
+    k2, v2 = pw.k.copy(), pw.v.copy()
+    k2[:, :, 36:] = synth.to_bf16_bits(np.ones(1, np.float32))[0]
+    v2[:, :, 36:] = 0
+    out2 = O.prefill_full(pw.q, k2, v2, pw.q_pos0)
+    _close(out[:, :, :2], out2[:, :, :2], rtol=0, atol=0, what="causal")
+    assert not np.allclose(out[:, :, 2:], out2[:, :, 2:])
+    for t in range(6):
+        r = O.decode_full(pw.q[:, :, t], pw.k, pw.v, [34 + t + 1])
+        _close(out[:, :, t], r["out"], rtol=1e-12, atol=1e-14, what=f"prefill vs decode t={t}")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,157 @@
+"""Plant plausible mistakes in the CPU oracle and check that some pin catches each one.
+
+Every mutant replaces one oracle helper (through monkeypatch, on the CPU only)
+with a variant carrying a typical slip: a dropped square, a sign error, a
+missing constant, a transposed operand, an off-by-one window or tie rule.
+The pins in ``oracle_pins.py`` must fail for every mutant; otherwise the pins
+are too weak to trust the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import ssa_oracle as O
+
+_orig_attend = O.relu2_attend
+_orig_select = O.select_topk_recent
+_orig_softmax = O.softmax_attend
+_orig_prefill = O.prefill_full
+_orig_decode = O.decode_full
+_orig_widen = O.widen
+
+
+def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
+    def attend(q_hat, k_hat, vals, scale, c):
+        s = scale * (k_hat @ q_hat)
+        w = (weights or O.relu2_weights)(s)
+        live = np.flatnonzero(w != 0.0)
+        den = float(np.sum(w[live])) if den_fn is None else den_fn(s, w)
+        cc = c if c_override is None else c_override
+        src = k_hat if values_from_keys else O.widen(vals[live]) if live.size else None
+        if live.size:
+            num = w[live] @ (src[live] if values_from_keys else src)
+        else:
+            num = np.zeros(q_hat.shape[-1])
+        if cc + den == 0.0:
+            return np.zeros(q_hat.shape[-1]), s, w
+        return num / (cc + den), s, w
+    return attend
+
+
+def _select_variant(kind):
+    def sel(s, n, k_top=1024, n_recent=128, disjoint=False):
+        s = np.asarray(s, dtype=np.float64)[:n]
+        idx = np.arange(n)
+        if kind == "ties_high":
+            order = np.lexsort((-idx, -s))
+        elif kind == "by_abs":
+            order = np.lexsort((idx, -np.abs(s)))
+        else:
+            order = np.lexsort((idx, -s))
+        if kind == "survivors_only":
+            order = order[s[order] > 0]
+        lo = max(0, n - n_recent)
+        recent = idx[lo:]
+        if kind == "no_recent":
+            recent = idx[:0]
+        if kind == "recent_excludes_current":
+            recent = idx[max(0, n - n_recent - 1):max(0, n - 1)]
+        if disjoint and kind != "disjoint_as_union":
+            top = order[~(order >= lo)][:k_top]
+        else:
+            top = order[:min(k_top, n)]
+        return np.union1d(top, recent).astype(np.int64)
+    return sel
+
+
+def _softmax_variant(kind):
+    def attend(q_vec, k_rows, v_rows, scale):
+        if k_rows.shape[0] == 0:
+            return np.zeros(q_vec.shape[-1])
+        t = (k_rows @ q_vec) * (1.0 if kind == "no_scale" else scale)
+        if kind == "relu2":
+            p = np.where(t > 0, t * t, 0.0)
+            p = p / max(np.sum(p), 1e-300)
+        else:
+            e = np.exp(t - np.max(t))
+            p = e / np.sum(e)
+        if kind == "keys_as_values":
+            return p @ k_rows
+        return p @ v_rows
+    return attend
+
+
+def _prefill_variant(kind):
+    def prefill(q, k, v, q_pos0, scale=1.0, c=1.0, eps=1e-6, flags=O.SSA_NORM_Q, rows=None):
+        q = O.widen(q)
+        B, Hq, Tq, D = q.shape
+        g = Hq // k.shape[1]
+        out = np.zeros((B, Hq, Tq, D))
+        for b in range(B):
+            for h in range(Hq):
+                for t in range(Tq):
+                    last = int(q_pos0[b]) + t + 1
+                    if kind == "excludes_self":
+                        last -= 1
+                    if kind == "ignores_pos0":
+                        last = t + 1
+                    keys = O.widen(k[b, h // g, :last])
+                    qt = O.rms_normalize(q[b, h, t], eps)
+                    out[b, h, t] = O.relu2_attend(qt, keys, v[b, h // g, :last], scale, c)[0]
+        return out
+    return prefill
+
+
+def _decode_vrows_all_heads(*a, **kw):
+    r = _orig_decode(*a, **kw)
+    r["vrows"] = r["nnz"].reshape(r["vrows"].shape[0], r["vrows"].shape[1], -1).min(axis=2)
+    return r
+
+
+MUTANTS = {
+    "weight_not_squared": ("relu2_attend", _attend_with(weights=lambda s: np.where(s > 0, s, 0.0))),
+    "no_relu": ("relu2_attend", _attend_with(weights=lambda s: s * s)),
+    "relu_sign_flipped": ("relu2_attend", _attend_with(weights=lambda s: np.where(s < 0, s * s, 0.0))),
+    "softmax_weights": ("relu2_attend", _attend_with(weights=lambda s: np.exp(s - s.max()))),
+    "c_dropped": ("relu2_attend", _attend_with(c_override=0.0)),
+    "den_without_weights": ("relu2_attend", _attend_with(den_fn=lambda s, w: 0.0)),
+    "den_sum_of_scores": ("relu2_attend", _attend_with(den_fn=lambda s, w: float(np.sum(np.maximum(s, 0))))),
+    "values_from_keys": ("relu2_attend", _attend_with(values_from_keys=True)),
+    "no_rms_norm": ("rms_normalize", lambda x, eps: np.asarray(x, dtype=np.float64)),
+    "l2_norm_not_rms": ("rms_normalize",
+                        lambda x, eps: np.asarray(x, np.float64)
+                        / np.linalg.norm(np.asarray(x, np.float64), axis=-1, keepdims=True)),
+    "rms_without_mean": ("rms_normalize",
+                         lambda x, eps: np.asarray(x, np.float64)
+                         / np.sqrt(np.sum(np.asarray(x, np.float64) ** 2, axis=-1, keepdims=True) + eps)),
+    "select_ties_high": ("select_topk_recent", _select_variant("ties_high")),
+    "select_by_abs": ("select_topk_recent", _select_variant("by_abs")),
+    "select_survivors_only": ("select_topk_recent", _select_variant("survivors_only")),
+    "select_no_recent": ("select_topk_recent", _select_variant("no_recent")),
+    "select_recent_excludes_current": ("select_topk_recent", _select_variant("recent_excludes_current")),
+    "select_disjoint_ignored": ("select_topk_recent", _select_variant("disjoint_as_union")),
+    "softmax_no_scale": ("softmax_attend", _softmax_variant("no_scale")),
+    "softmax_relu2": ("softmax_attend", _softmax_variant("relu2")),
+    "softmax_keys_as_values": ("softmax_attend", _softmax_variant("keys_as_values")),
+    "prefill_excludes_self": ("prefill_full", _prefill_variant("excludes_self")),
+    "prefill_ignores_pos0": ("prefill_full", _prefill_variant("ignores_pos0")),
+    "vrows_all_heads": ("decode_full", _decode_vrows_all_heads),
+    "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
+                                          if np.asarray(x).dtype != np.uint16
+                                          else np.asarray(x).astype(np.float64) / 256.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+            break
+    assert failed, f"mutant {name} passes every pin"
