@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of decode-time Sevren Sparse Attention on one MI355X.
+
+Workload: batched long-context decode -- batch 8, 16 query heads / 2 KV heads,
+head dim 128, bf16 KV cache, context lengths drawn uniformly from
+[65536, 131072], planted 95% sparsity (seeded synthetic data). One step is
+the whole decode hot path for one query token per sequence:
+
+  full layer   ssa_decode_full         ReLU^2 attention with V-skip + raw scores
+  selection    ssa_select_topk_recent  top-1024 by score + 128 most recent
+  sparse layer ssa_decode_sparse       softmax over the selected rows
+
+The inputs are resident in HBM before timing starts. Three copies of the
+cache (over 1.5 GB together) are used in rotation so that reads come from
+HBM, not from the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import functools
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "batched_decode_b8_ctx64k-128k_bf16_p0.05"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--copies", type=int, default=3, help="cache copies used in rotation")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fixed-len", type=int, default=None,
+                   help="use this context length for every sequence instead of U[64K,128K]")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def alg_bytes_full(wl, vrows: np.ndarray, with_scores: bool = True) -> dict:
+    """Algorithmic bytes of one ssa_decode_full call.
+
+    K: every live key of every (sequence, KV head); V: only the rows fetched
+    (keys some head of the group weighted above zero); q in and out (fp32);
+    raw scores written (fp32, one per query head and key).
+    """
+    D = wl.head_dim
+    kvb = 2 if wl.kv_dtype == "bf16" else 4
+    n = wl.ctx_lens.astype(np.int64)
+    k_bytes = int(wl.n_kv_heads * D * kvb * n.sum())
+    v_bytes = int(D * kvb * int(vrows.sum()))
+    qo = 2 * wl.batch * wl.n_q_heads * D * 4
+    sc = 4 * wl.n_q_heads * int(n.sum()) if with_scores else 0
+    return {"k": k_bytes, "v": v_bytes, "q_out": qo, "scores": sc,
+            "v_dense": int(wl.n_kv_heads * D * kvb * n.sum())}
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
+
+
+def cpu_baseline(wl) -> dict:
+    """The CPU oracle, as it stands, on the whole batch (about 10-30 s on a server CPU)."""
+    from oracle import ssa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    t0 = time.perf_counter()
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    sel = O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
+    O.decode_sparse(wl.q_sparse[0], wl.k, wl.v, sel)
+    dt = time.perf_counter() - t0
+    kv = alg_bytes_full(wl, ref["vrows"], with_scores=False)
+    sparse_rows = sum(len(functools.reduce(np.union1d, sel[b][kvh * 8:(kvh + 1) * 8]))
+                      for b in range(wl.batch) for kvh in range(wl.n_kv_heads))
+    kvb = 2
+    kv_total = kv["k"] + kv["v"] + 2 * wl.head_dim * kvb * sparse_rows
+    return {"value": round(kv_total / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "query_tok_per_s": round(wl.batch / dt, 3), "seconds": round(dt, 2),
+            "sample": f"the whole batch ({wl.batch} sequences, {int(wl.ctx_lens.sum())} keys per KV "
+                      "head): full layer, selection and one sparse layer, float64 NumPy, one pass"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is built and "
+              "measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+    from long_context_decode_relu_amd import ssa, synth
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    wl = synth.batched_decode(fixed_len=args.fixed_len, kv_capacity=131072)
+    log(f"[bench] generated workload in {time.perf_counter() - t0:.1f}s: ctx_lens={wl.ctx_lens.tolist()}")
+
+    caches = [ssa.cache_from_workload(wl, dev) for _ in range(max(1, args.copies))]
+    q = torch.from_numpy(wl.q).to(dev)
+    B, Hq, D = q.shape
+    Nmax = wl.kv_capacity
+    scores = torch.empty((B, Hq, Nmax), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws_full = ssa.workspace(ssa.SSA_OP_DECODE_FULL, caches[0].shape(Hq), 0, dev)
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        if ev is not None:
+            ev[0].record()
+        ssa.ssa_decode_full(q, c, out=out, scores=scores, ws=ws_full, want_scores=True)
+        if ev is not None:
+            ev[1].record()
+
+    # stats once (not timed): rows fetched, for the algorithmic byte count
+    _, _, nnz, vrows = ssa.ssa_decode_full(q, caches[0], want_scores=True, want_stats=True)
+    torch.cuda.synchronize()
+    vrows_np = vrows.cpu().numpy()
+    nnz_np = nnz.cpu().numpy()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    full_ms = [a.elapsed_time(b) for a, b in evs]
+    log(f"[bench] timed {args.steps} steps in {wall:.3f}s")
+
+    ms_step = wall * 1e3 / args.steps
+    ab = alg_bytes_full(wl, vrows_np)
+    kv_read = ab["k"] + ab["v"]
+    full_alg = ab["k"] + ab["v"] + ab["q_out"] + ab["scores"]
+    full_avg_ms = float(np.mean(full_ms))
+    achieved = full_alg / (full_avg_ms * 1e-3) / 1e9
+    value = kv_read / (ms_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "KV GB/s (% of HBM peak) + query-tok/s, ReLU² decode, 128K ctx, batch 8",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 KV, f32 accumulate",
+        "data": "synthetic (seeded planted-direction keys, 95% sparsity)",
+        "config": {"workload": WORKLOAD if args.fixed_len is None else f"batched_decode_b8_fixed{args.fixed_len}",
+                   "batch": B, "n_q_heads": Hq, "n_kv_heads": wl.n_kv_heads, "head_dim": D,
+                   "ctx_lens": wl.ctx_lens.tolist(), "kv_capacity": Nmax,
+                   "step": "ssa_decode_full"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "query_tok_per_s": round(B / (ms_step * 1e-3), 1),
+        "kv_bytes_read_per_step": kv_read,
+        "vskip": {"v_rows_fetched": int(vrows_np.sum()),
+                  "v_rows_dense": int(wl.n_kv_heads * wl.ctx_lens.astype(np.int64).sum()),
+                  "v_traffic_saved": round(1 - ab["v"] / ab["v_dense"], 4),
+                  "measured_zero_weight_fraction": round(
+                      1 - float(nnz_np.sum()) / (Hq * float(wl.ctx_lens.astype(np.int64).sum())), 4)},
+        "roofline": {"kernel": "ssa_decode_full (decode_full_kernel + decode_full_combine)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

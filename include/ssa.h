@@ -1,0 +1,174 @@
+/*
+ * ssa.h -- C ABI of libssa: decode-time Sevren Sparse Attention on MI355X (gfx950).
+ *
+ * The operations follow the web page "The Architecture of Embla 1"
+ * (sevren.ai blog):
+ *   - "Sevren Sparse Attention learns to be sparse": a full layer weights each
+ *     key by w = ReLU(score)^2, the score taken between the RMS-normalised
+ *     query and key; the output is sum(w * v) / (c + sum(w)). A score of zero
+ *     or below gives a weight of exactly zero. The constant c did not survive
+ *     in the page's text, so it is a parameter here.
+ *   - "Skipping V": a decode kernel reads every key but fetches a value row
+ *     only when some query head sharing that KV head gives the key a nonzero
+ *     weight.
+ *   - "Three kinds of attention": a sparse layer owns no cache; it reads its
+ *     block's full-layer cache restricted to the 1,024 keys the full layer
+ *     scored highest (by raw score, so keys just below zero count) plus the
+ *     128 most recent, and applies its own softmax over them. Neither layer
+ *     type encodes positions.
+ *   - "KV bridge, KV reuse, and prefill": prompt tokens run through the full
+ *     layer to fill its cache (here: a causal chunk of queries).
+ *
+ * Conventions shared by every entry point
+ *   Layout   All tensors are dense and row-major.
+ *            queries  q   [B, Hq, D]        float32 (decode), bf16 (prefill: [B, Hq, Tq, D])
+ *            cache    k,v [B, Hkv, Nmax, D] kv_dtype (SSA_F32 or SSA_BF16), Nmax = kv_capacity
+ *            outputs  out [B, Hq, D] / [B, Hq, Tq, D] float32
+ *            Query head h uses KV head h / (Hq / Hkv) (grouped-query attention).
+ *            D must be 128. Hq / Hkv must be 1, 2, 4 or 8.
+ *   Memory   Every pointer except `shape` is a DEVICE pointer owned by the
+ *            caller. The library allocates nothing, frees nothing and keeps
+ *            no state between calls. Scratch space is passed in `ws`
+ *            (ws_bytes >= ssa_workspace_bytes(op, ...)); its contents on
+ *            entry do not matter.
+ *   Context  ctx_lens[b] (device int32) is the number of live keys of
+ *            sequence b: cache rows 0 .. ctx_lens[b]-1. It must not exceed
+ *            shape->max_ctx_len, a host-side upper bound used to size the
+ *            launch so that no call waits on the device. Rows at or past
+ *            ctx_lens[b] are never read.
+ *   Streams  Work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *            stream) and the call returns without synchronising.
+ *   Errors   Arguments are checked before anything is launched; on a
+ *            failed check nothing is written and the status says why.
+ *            SSA_ERR_HIP reports a launch error from the HIP runtime.
+ *            Faults inside a kernel surface at the caller's next
+ *            synchronisation. Calls are thread-safe.
+ */
+#ifndef SSA_H
+#define SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSA_ABI_VERSION 1
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  SSA_ERR_DTYPE = 3,       /* unknown kv_dtype */
+  SSA_ERR_UNSUPPORTED = 4, /* valid but not built: D != 128, Hq/Hkv not in {1,2,4,8}, ... */
+  SSA_ERR_WORKSPACE = 5,   /* ws missing or smaller than ssa_workspace_bytes() */
+  SSA_ERR_HIP = 6          /* the HIP runtime reported an error */
+} ssa_status;
+
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+
+enum {
+  SSA_NORM_Q = 1,          /* RMS-normalise each query row in the kernel */
+  SSA_NORM_K = 2,          /* RMS-normalise each key row on the fly (else keys are stored normalised) */
+  SSA_SELECT_DISJOINT = 4  /* selection = recent window + top-k of the keys outside it */
+};
+
+typedef struct {
+  int32_t batch;        /* B  >= 0 */
+  int32_t n_q_heads;    /* Hq >= 1 */
+  int32_t n_kv_heads;   /* Hkv >= 1, divides Hq */
+  int32_t head_dim;     /* D  == 128 */
+  int32_t kv_capacity;  /* Nmax >= max_ctx_len, rows per (b, kv head) in the cache */
+  int32_t max_ctx_len;  /* host upper bound on every ctx_lens[b], 0 <= max_ctx_len <= 2^28 */
+  ssa_dtype kv_dtype;   /* storage type of k and v */
+} ssa_shape;
+
+enum {
+  SSA_OP_DECODE_FULL = 0,
+  SSA_OP_SELECT = 1,
+  SSA_OP_DECODE_SPARSE = 2,
+  SSA_OP_PREFILL_FULL = 3
+};
+
+/* Bytes of scratch the operation needs for this shape. `aux` is the query
+ * count Tq for SSA_OP_PREFILL_FULL, the selection row stride for
+ * SSA_OP_DECODE_SPARSE and SSA_OP_SELECT (k_top + n_recent), 0 otherwise.
+ * Returns 0 for an invalid shape. */
+size_t ssa_workspace_bytes(int32_t op, const ssa_shape* shape, int32_t aux);
+
+/* Full-layer decode, one query token per sequence ("Sevren Sparse Attention
+ * learns to be sparse", "Skipping V").
+ *
+ * For every sequence b and query head h (KV head kvh = h / (Hq/Hkv)):
+ *   q_hat = q[b,h] / sqrt(mean(q[b,h]^2) + eps)    (SSA_NORM_Q; else q as given)
+ *   k_hat = k[b,kvh,i]                              (SSA_NORM_K: RMS-normalised with eps)
+ *   s_i   = scale * dot(q_hat, k_hat),  i < ctx_lens[b]
+ *   w_i   = s_i > 0 ? s_i^2 : 0
+ *   out[b,h] = sum_i w_i v[b,kvh,i] / (c + sum_i w_i)   (0 when c + sum w == 0)
+ * Value rows are read only for keys with w_i > 0 for some head of the group.
+ *
+ * Optional outputs (pass NULL to skip):
+ *   scores           [B, Hq, Nmax] float32: s_i for i < ctx_lens[b] (raw, before ReLU);
+ *                    entries at or past ctx_lens[b] are left untouched.
+ *   nnz_per_head     [B, Hq]  int32: keys with w_i > 0.
+ *   vrows_per_kvhead [B, Hkv] int32: value rows read = keys with w_i > 0 for some head of the group.
+ * Requires c >= 0, scale finite, eps >= 0. */
+ssa_status ssa_decode_full(const ssa_shape* shape, const float* q, const void* k, const void* v,
+                           const int32_t* ctx_lens, float scale, float c, float eps, uint32_t flags,
+                           float* out, float* scores, int32_t* nnz_per_head,
+                           int32_t* vrows_per_kvhead, void* ws, size_t ws_bytes, void* stream);
+
+/* Selection for the sparse layers ("Three kinds of attention").
+ *
+ * For every (b, h): T = the k_top keys with the highest scores[b,h,i] over
+ * i < n = ctx_lens[b] (ties go to the lower index; -0.0 equals +0.0), R =
+ * {max(0, n - n_recent) .. n-1} (the current token included). The selection
+ * is T union R (SSA_SELECT_DISJOINT: R union the top k_top of the keys
+ * outside R), written in ascending key order to
+ *   sel_idx   [B, Hq, k_top + n_recent] int32, padded with -1
+ *   sel_count [B, Hq] int32.
+ * Scores must not be NaN. Requires 1 <= k_top, 0 <= n_recent,
+ * k_top + n_recent <= 4096. */
+ssa_status ssa_select_topk_recent(const ssa_shape* shape, const float* scores,
+                                  const int32_t* ctx_lens, int32_t k_top, int32_t n_recent,
+                                  uint32_t flags, int32_t* sel_idx, int32_t* sel_count, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* Sparse-layer decode over the full layer's cache ("Three kinds of attention").
+ *
+ * For every (b, h) with S = sel_idx[b,h,0 .. sel_count[b,h]-1] (row stride
+ * sel_stride, ascending, unique, each index < ctx_lens[b]):
+ *   q_hat = q[b,h] RMS-normalised (SSA_NORM_Q; else q as given)
+ *   t_j = scale * dot(q_hat, k[b,kvh,j]),  p = softmax(t) over S
+ *   out[b,h] = sum_j p_j v[b,kvh,j]        (0 for an empty selection)
+ * Rows shared by the heads of a KV group are read once. Indices outside
+ * [0, ctx_lens[b]) are rejected in the kernel by skipping them. */
+ssa_status ssa_decode_sparse(const ssa_shape* shape, const float* q, const void* k, const void* v,
+                             const int32_t* ctx_lens, const int32_t* sel_idx,
+                             const int32_t* sel_count, int32_t sel_stride, float scale, float eps,
+                             uint32_t flags, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Causal ReLU^2 prefill of a chunk of Tq prompt queries ("KV bridge, KV reuse,
+ * and prefill"; weights as in ssa_decode_full).
+ *
+ * q [B, Hq, Tq, D] bf16. Query t of sequence b sits at position
+ * q_pos0[b] + t (q_pos0 is device int32 [B]) and attends cache rows
+ * 0 .. q_pos0[b] + t. q_pos0[b] + Tq must not exceed ctx_lens[b] (the cache
+ * already holds the chunk's own keys). k, v must be SSA_BF16.
+ * out [B, Hq, Tq, D] float32. The products run on the matrix cores in bf16
+ * with float32 accumulation; the normalised query and the weights are
+ * rounded to bf16 before their products. */
+ssa_status ssa_prefill_full(const ssa_shape* shape, const void* q, int32_t n_query,
+                            const int32_t* q_pos0, const int32_t* ctx_lens, const void* k,
+                            const void* v, float scale, float c, float eps, uint32_t flags,
+                            float* out, void* ws, size_t ws_bytes, void* stream);
+
+const char* ssa_status_string(ssa_status status);
+int32_t ssa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H */

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssa {
+
+// Split-K partition length (keys per work item) for the full-layer decode.
+// Fixed by the shape so that the caller can size the workspace up front.
+int decode_full_chunk(int batch, int n_kv_heads, int max_ctx_len);
+
+struct DecodeFullArgs {
+  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;
+  const float* q;
+  const void* k;
+  const void* v;
+  const int32_t* ctx_lens;
+  float scale, c, eps;
+  uint32_t flags;
+  float* out;
+  float* scores;
+  int32_t* nnz;
+  int32_t* vrows;
+  void* ws;
+};
+size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int max_ctx);
+hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  int B, Hq, Nmax, max_ctx;
+  const float* scores;
+  const int32_t* ctx_lens;
+  int k_top, n_recent;
+  uint32_t flags;
+  int32_t* sel_idx;
+  int32_t* sel_count;
+  void* ws;
+};
+size_t select_ws_bytes(int B, int Hq, int max_ctx, int stride);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct DecodeSparseArgs {
+  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;
+  const float* q;
+  const void* k;
+  const void* v;
+  const int32_t* ctx_lens;
+  const int32_t* sel_idx;
+  const int32_t* sel_count;
+  int sel_stride;
+  float scale, eps;
+  uint32_t flags;
+  float* out;
+  void* ws;
+};
+size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int stride);
+hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  int B, Hq, Hkv, Nmax, max_ctx, Tq;
+  const void* q;
+  const int32_t* q_pos0;
+  const int32_t* ctx_lens;
+  const void* k;
+  const void* v;
+  float scale, c, eps;
+  uint32_t flags;
+  float* out;
+  void* ws;
+};
+size_t prefill_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int Tq);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Compute units and resident work-groups per CU for a kernel, cached per device.
+int device_cu_count();
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace ssa
