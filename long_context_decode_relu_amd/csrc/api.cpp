@@ -3,6 +3,7 @@
 // failing call leaves all outputs untouched.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -32,6 +33,11 @@ int device_cu_count() {
     g_cu_count[dev] = n;
   }
   return g_cu_count[dev];
+}
+
+bool verbose() {
+  static const bool v = std::getenv("SSA_VERBOSE") != nullptr;
+  return v;
 }
 
 }  // namespace ssa

@@ -14,14 +14,19 @@
 // partials of each (sequence, head) in a fixed order and divides. The weights
 // are not exponentiated, so the partials add without a running maximum.
 //
-// Inside a wave each lane owns one key: it loads the key's whole 256-byte row
-// (bf16) into registers, widens each bf16 exactly to float and accumulates
-// the g dot products in float32 with the group's query values taken from
-// uniform (scalar) loads. No cross-lane reduction is needed for the scores.
-// A wave ballot of "some head has a positive score" gives the survivor mask;
-// for each survivor the whole wave loads that key's value row (each lane two
+// Inside a wave each lane owns one key of a 64-key tile. For bf16 caches the
+// tile (16 KB) is copied HBM -> LDS by 16 direct-to-LDS loads of 1 KB each
+// (fully coalesced), with the 16-byte pieces of each row XOR-permuted so that
+// every lane can then read its own row from LDS without bank conflicts. The
+// next tile of the wave is already in flight while the current one is
+// scored. Each lane widens its row exactly to float and accumulates the g dot
+// products in float32 with the group's query values taken from uniform
+// (scalar) loads; no cross-lane reduction is needed for the scores. A wave
+// ballot of "some head has a positive score" gives the survivor mask; for each
+// survivor the whole wave loads that key's value row (each lane two
 // dimensions) and adds w_h * v into per-lane accumulators num[h][2 dims].
 // Rows of keys that no head kept are never touched.
+#include <cstdio>
 #include <utility>
 
 #include "common.h"
@@ -35,6 +40,8 @@ namespace {
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxBatch = 1024;         // prefix table of items per sequence lives in LDS
+constexpr int kTileKeys = kWave;        // one key per lane
+constexpr int kTileBytesBf16 = kTileKeys * kHeadDim * 2;
 
 struct FullParams {
   const float* q;
@@ -49,18 +56,17 @@ struct FullParams {
   float scale, eps;
 };
 
-// Widen one 16-byte piece of a key row (8 dims) to float.
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// One key row held by a lane, widened 8 dims at a time.
 template <bool BF16>
 struct KeyRow;
 
 template <>
 struct KeyRow<true> {
   u32x4 c[16];  // 128 bf16
-  __device__ __forceinline__ void load(const void* base, size_t row) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(base) + row * 16;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) c[j] = __builtin_nontemporal_load(p + j);
-  }
   __device__ __forceinline__ void chunk(int j, float (&e)[8]) const {
     e[0] = bf16_lo(c[j].x); e[1] = bf16_hi(c[j].x);
     e[2] = bf16_lo(c[j].y); e[3] = bf16_hi(c[j].y);
@@ -72,16 +78,63 @@ struct KeyRow<true> {
 template <>
 struct KeyRow<false> {
   f32x4 c[32];  // 128 float
-  __device__ __forceinline__ void load(const void* base, size_t row) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(base) + row * 32;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) c[j] = __builtin_nontemporal_load(p + j);
-  }
   __device__ __forceinline__ void chunk(int j, float (&e)[8]) const {
     e[0] = c[2 * j].x; e[1] = c[2 * j].y; e[2] = c[2 * j].z; e[3] = c[2 * j].w;
     e[4] = c[2 * j + 1].x; e[5] = c[2 * j + 1].y; e[6] = c[2 * j + 1].z; e[7] = c[2 * j + 1].w;
   }
 };
+
+// bf16 tile: HBM -> LDS. LDS byte k*256 + p*16 holds piece p ^ (k & 15) of tile
+// row k. Load i (of 16) moves rows 4i..4i+3: lane L fetches row 4i + L/16,
+// stored position L % 16, so each load reads 1 KB of contiguous HBM. The
+// lane's source offsets repeat every 4 loads (plus 4 KB), so they are
+// computed once per kernel.
+struct TileOffsets {
+  uint32_t off[4];
+  __device__ __forceinline__ explicit TileOffsets(int lane) {
+    const int kq = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kt = 4 * r + kq;
+      off[r] = (uint32_t)(kt * 256 + ((p ^ (kt & 15)) << 4));
+    }
+  }
+};
+
+// `src` points at the tile's first row; `nvalid` (1..64) rows are live. Rows
+// past the live ones are replaced by the last live row (read, never used).
+__device__ __forceinline__ void tile_issue_bf16(uint8_t* lds_tile, const uint8_t* src, int nvalid,
+                                                const TileOffsets& to, int lane) {
+  if (nvalid == kTileKeys) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds(src + to.off[i & 3] + (i >> 2) * 4096, lds_tile + i * 1024,
+                                       16, 0, 0);
+  } else {
+    const int kq = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kt = 4 * i + kq;
+      const int row = min(kt, nvalid - 1);
+      __builtin_amdgcn_global_load_lds(src + row * 256 + ((p ^ (kt & 15)) << 4),
+                                       lds_tile + i * 1024, 16, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void tile_read_bf16(const uint8_t* lds_tile, int lane,
+                                               KeyRow<true>& kr) {
+  const uint8_t* row = lds_tile + lane * 256;
+  const int x = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) kr.c[j] = *reinterpret_cast<const u32x4*>(row + ((j ^ x) << 4));
+}
+
+__device__ __forceinline__ void row_load_f32(const void* k, size_t row, KeyRow<false>& kr) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(k) + row * 32;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) kr.c[j] = __builtin_nontemporal_load(p + j);
+}
 
 // Two value dims (2*lane, 2*lane+1) of one row, widened to float.
 template <bool BF16>
@@ -189,31 +242,56 @@ __device__ __forceinline__ void score_row(const KeyRow<BF16>& kr, const float* q
   (step(std::integral_constant<int, SC>{}), ...);
 }
 
+struct Item {
+  int b, kvh, pc, key0, key1;
+};
+
+// Work item -> (sequence, KV head, partition, key range); all values uniform.
+__device__ __forceinline__ Item item_info(int item, const int* s_pref, int B, int Hkv, int C,
+                                          const int32_t* __restrict__ ctx_lens) {
+  int lo = 0, hi = B;  // s_pref[lo] <= item < s_pref[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= item) lo = mid; else hi = mid;
+  }
+  // LDS reads count as divergent for the compiler; the values are uniform.
+  Item it;
+  it.b = __builtin_amdgcn_readfirstlane(lo);
+  const int r = __builtin_amdgcn_readfirstlane(item - s_pref[it.b]);
+  const int n = ctx_lens[it.b];
+  const int nchunks = ceil_div(n, C);
+  it.kvh = r / nchunks;
+  it.pc = r - it.kvh * nchunks;
+  it.key0 = it.pc * C;
+  it.key1 = min(n, it.key0 + C);
+  return it;
+}
+
 template <int G, bool BF16, bool NORMQ, bool NORMK>
-__global__ __launch_bounds__(kThreads) void decode_full_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part,
     int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows, int B, int Hq, int Hkv,
-    int Nmax, int P, int chunk, float scale, float eps, int zero) {
+    int Nmax, int P, int chunk, float scale, float eps) {
   __shared__ int s_pref[kMaxBatch + 1];
-  __shared__ float s_num[kWaves][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
+  __shared__ float s_acc[G][kHeadDim];
   __shared__ float s_den[kWaves][G];
   __shared__ int s_nnz[kWaves][G];
   __shared__ int s_vrows[kWaves];
+  __shared__ int s_scan[kThreads];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int C = chunk;
+  uint8_t* my_tile = s_tile + (BF16 ? wave * kTileBytesBf16 : 0);
 
   // Items per sequence: Hkv * ceil(n_b / C); exclusive prefix in LDS.
   if (tid == 0) s_pref[0] = 0;
   for (int b0 = 0; b0 < B; b0 += kThreads) {
     int b = b0 + tid;
-    int cnt = b < B ? Hkv * ceil_div(ctx_lens[b], C) : 0;
-    // inclusive scan of cnt over the work-group
-    __shared__ int s_scan[kThreads];
-    s_scan[tid] = cnt;
+    s_scan[tid] = b < B ? Hkv * ceil_div(ctx_lens[b], C) : 0;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {
       int t = tid >= off ? s_scan[tid - off] : 0;
@@ -226,23 +304,42 @@ __global__ __launch_bounds__(kThreads) void decode_full_kernel(
     __syncthreads();
   }
   const int n_items = __builtin_amdgcn_readfirstlane(s_pref[B]);
+  const int grid = gridDim.x;
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    // locate the sequence by binary search over the prefix table
-    int lo = 0, hi = B;  // s_pref[lo] <= item < s_pref[hi]
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= item) lo = mid; else hi = mid;
+  // The wave's tile sequence runs over its tiles t = wave, wave+4, ... of each
+  // of the work-group's items. (nitem, nt) is the next tile to fetch; its
+  // first row is at n_src and n_valid of its rows are live.
+  auto ntiles = [&](const Item& I) { return ceil_div(I.key1 - I.key0, kTileKeys); };
+  int nitem = blockIdx.x, nt = wave;
+  const uint8_t* n_src = nullptr;
+  int n_valid = 0;
+  auto seek = [&]() {  // move (nitem, nt) forward to a tile that exists (or past the end)
+    n_valid = 0;
+    while (nitem < n_items) {
+      const Item nI = item_info(nitem, s_pref, B, Hkv, C, ctx_lens);
+      if (nt < ntiles(nI)) {
+        const int kb = nI.key0 + nt * kTileKeys;
+        n_valid = min(kTileKeys, nI.key1 - kb);
+        n_src = reinterpret_cast<const uint8_t*>(k) +
+                (((size_t)nI.b * Hkv + nI.kvh) * (size_t)Nmax + kb) * (kHeadDim * 2);
+        return;
+      }
+      nitem += grid;
+      nt = wave;
     }
-    // LDS reads count as divergent for the compiler; the values are uniform.
-    const int b = __builtin_amdgcn_readfirstlane(lo);
-    const int r = __builtin_amdgcn_readfirstlane(item - s_pref[b]);
-    const int n = ctx_lens[b];
-    const int nchunks = ceil_div(n, C);
-    const int kvh = r / nchunks;
-    const int pc = r - kvh * nchunks;
-    const int key0 = pc * C;
-    const int key1 = min(n, key0 + C);
+  };
+  const TileOffsets toff(lane);
+  auto issue = [&]() {
+    if constexpr (BF16) {
+      if (n_valid > 0) tile_issue_bf16(my_tile, n_src, n_valid, toff, lane);
+    }
+  };
+  seek();
+  issue();
+
+  for (int item = blockIdx.x; item < n_items; item += grid) {
+    const Item I = item_info(item, s_pref, B, Hkv, C, ctx_lens);
+    const int b = I.b, kvh = I.kvh;
 
     // Per-head score factor: scale / RMS(q_h) (or scale).
     const float* qg = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
@@ -267,12 +364,24 @@ __global__ __launch_bounds__(kThreads) void decode_full_kernel(
 
     const size_t row0 = ((size_t)b * Hkv + kvh) * (size_t)Nmax;
     float* srow = scores ? scores + ((size_t)b * Hq + (size_t)kvh * G) * Nmax : nullptr;
+    const int my_tiles = ntiles(I);
 
-    for (int base = key0 + wave * kWave; base < key1; base += kWaves * kWave) {
+    for (int t = wave; t < my_tiles; t += kWaves) {
+      // here (nitem, nt) == (item, t): its tile is in flight
+      const int base = I.key0 + t * kTileKeys;
       const int key = base + lane;
-      const bool valid = key < key1;
+      const bool valid = key < I.key1;
       KeyRow<BF16> kr;
-      kr.load(k, row0 + (valid ? key : key1 - 1));
+      if constexpr (BF16) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this tile has landed in LDS
+        tile_read_bf16(my_tile, lane, kr);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0); // rows are in registers: LDS may be refilled
+      } else {
+        row_load_f32(k, row0 + min(key, I.key1 - 1), kr);
+      }
+      nt += kWaves;
+      seek();
+      issue();  // next tile streams in while this one is scored
 
       float acc[G];
 #pragma unroll
@@ -327,26 +436,40 @@ __global__ __launch_bounds__(kThreads) void decode_full_kernel(
       }
     }
 
-    // wave -> work-group reduction, fixed order
+    // wave -> work-group reduction in a fixed order (wave 0, 1, 2, 3)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      s_num[wave][h][2 * lane] = num[h][0];
-      s_num[wave][h][2 * lane + 1] = num[h][1];
       float d = wave_sum(den[h]);
       int z = wave_sum_i(nnz[h]);
       if (lane == 0) { s_den[wave][h] = d; s_nnz[wave][h] = z; }
     }
     if (lane == 0) s_vrows[wave] = vrows;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      __syncthreads();
+      if (wave == wv) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (wv == 0) {
+            s_acc[h][2 * lane] = num[h][0];
+            s_acc[h][2 * lane + 1] = num[h][1];
+          } else {
+            s_acc[h][2 * lane] += num[h][0];
+            s_acc[h][2 * lane + 1] += num[h][1];
+          }
+        }
+      }
+    }
     __syncthreads();
-    const size_t slot = ((size_t)b * Hkv + kvh) * P + pc;
+    const size_t slot = ((size_t)b * Hkv + kvh) * P + I.pc;
     float* dst = part + slot * (size_t)(G * (kHeadDim + 1));
     for (int i = tid; i < G * (kHeadDim + 1); i += kThreads) {
       int h = i / (kHeadDim + 1), d = i - h * (kHeadDim + 1);
-      float s = 0.f;
+      float s;
       if (d < kHeadDim) {
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) s += s_num[wv][h][d];
+        s = s_acc[h][d];
       } else {
+        s = 0.f;
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) s += s_den[wv][h];
       }
@@ -366,39 +489,56 @@ __global__ __launch_bounds__(kThreads) void decode_full_kernel(
     }
     __syncthreads();
   }
+  if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 // Sum the partials of each (sequence, query head) and divide by (c + den).
-__global__ __launch_bounds__(kHeadDim) void decode_full_combine(
+// Four groups of 128 threads each sum every fourth partial; the four sums are
+// then added in a fixed order, so the result does not depend on timing.
+constexpr int kCombineGroups = 4;
+
+__global__ __launch_bounds__(kHeadDim * kCombineGroups) void decode_full_combine(
     const float* __restrict__ part, const int32_t* __restrict__ part_nnz,
     const int32_t* __restrict__ part_vrows, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv,
     int P, int chunk, float c, float* __restrict__ out, int32_t* __restrict__ nnz,
     int32_t* __restrict__ vrows) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  __shared__ float s_num[kCombineGroups][kHeadDim];
+  __shared__ float s_den[kCombineGroups][kHeadDim];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d = threadIdx.x % kHeadDim, grp = threadIdx.x / kHeadDim;
   const int G = Hq / Hkv;
   const int kvh = h / G, j = h - kvh * G;
   const int pb = ceil_div(ctx_lens[b], chunk);
-  const float* src = part + (((size_t)b * Hkv + kvh) * P) * (size_t)(G * (kHeadDim + 1)) +
-                     (size_t)j * (kHeadDim + 1);
+  const size_t stride = (size_t)G * (kHeadDim + 1);
+  const float* src = part + (((size_t)b * Hkv + kvh) * P) * stride + (size_t)j * (kHeadDim + 1);
   float sn = 0.f, sd = 0.f;
-  for (int pc = 0; pc < pb; ++pc) {
-    const float* e = src + (size_t)pc * (G * (kHeadDim + 1));
+#pragma unroll 8
+  for (int pc = grp; pc < pb; pc += kCombineGroups) {
+    const float* e = src + (size_t)pc * stride;
     sn += e[d];
     sd += e[kHeadDim];
   }
-  const float denom = c + sd;
-  out[((size_t)b * Hq + h) * kHeadDim + d] = denom == 0.f ? 0.f : sn / denom;
-  if (d == 0 && nnz) {
-    int z = 0;
-    const int32_t* e = part_nnz + ((size_t)b * Hkv + kvh) * P * G + j;
-    for (int pc = 0; pc < pb; ++pc) z += e[(size_t)pc * G];
-    nnz[(size_t)b * Hq + h] = z;
-  }
-  if (d == 0 && j == 0 && vrows) {
-    int z = 0;
-    const int32_t* e = part_vrows + ((size_t)b * Hkv + kvh) * P;
-    for (int pc = 0; pc < pb; ++pc) z += e[pc];
-    vrows[(size_t)b * Hkv + kvh] = z;
+  s_num[grp][d] = sn;
+  s_den[grp][d] = sd;
+  __syncthreads();
+  if (grp == 0) {
+    float tn = 0.f, td = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < kCombineGroups; ++g2) { tn += s_num[g2][d]; td += s_den[g2][d]; }
+    const float denom = c + td;
+    out[((size_t)b * Hq + h) * kHeadDim + d] = denom == 0.f ? 0.f : tn / denom;
+    if (d == 0 && nnz) {
+      int z = 0;
+      const int32_t* e = part_nnz + ((size_t)b * Hkv + kvh) * P * G + j;
+      for (int pc = 0; pc < pb; ++pc) z += e[(size_t)pc * G];
+      nnz[(size_t)b * Hq + h] = z;
+    }
+    if (d == 1 && j == 0 && vrows) {
+      int z = 0;
+      const int32_t* e = part_vrows + ((size_t)b * Hkv + kvh) * P;
+      for (int pc = 0; pc < pb; ++pc) z += e[pc];
+      vrows[(size_t)b * Hkv + kvh] = z;
+    }
   }
 }
 
@@ -429,9 +569,12 @@ hipError_t launch_t(const FullParams& fp, int max_items, hipStream_t stream) {
   int grid = device_cu_count() * per_cu;
   if (grid > max_items) grid = max_items;
   if (grid < 1) return hipSuccess;
+  if (verbose())
+    fprintf(stderr, "[ssa] decode_full G=%d bf16=%d grid=%d (cus=%d x %d/cu) items<=%d chunk=%d\n", G,
+            (int)BF16, grid, device_cu_count(), per_cu, max_items, fp.chunk);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, fp.q, fp.k, fp.v, fp.ctx_lens,
                      fp.scores, fp.part, fp.part_nnz, fp.part_vrows, fp.B, fp.Hq, fp.Hkv, fp.Nmax,
-                     fp.P, fp.chunk, fp.scale, fp.eps, 0);
+                     fp.P, fp.chunk, fp.scale, fp.eps);
   return hipGetLastError();
 }
 
@@ -501,7 +644,7 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
     }
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kHeadDim), 0, stream, fp.part,
+  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kHeadDim * kCombineGroups), 0, stream, fp.part,
                      fp.part_nnz, fp.part_vrows, a.ctx_lens, a.Hq, a.Hkv, P, chunk, a.c, a.out,
                      a.nnz, a.vrows);
   return hipGetLastError();

@@ -73,8 +73,12 @@ struct PrefillArgs {
 size_t prefill_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int Tq);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Compute units and resident work-groups per CU for a kernel, cached per device.
+// Compute units of the current device (cached per device).
 int device_cu_count();
+
+// True when the environment variable SSA_VERBOSE is set: launchers then print
+// their launch configuration to stderr.
+bool verbose();
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
