@@ -55,7 +55,8 @@ ssa_status check_shape(const ssa_shape* s, bool need_group) {
     return SSA_ERR_SHAPE;
   if (s->n_q_heads % s->n_kv_heads) return SSA_ERR_SHAPE;
   if (s->head_dim != 128) return SSA_ERR_UNSUPPORTED;
-  if (s->batch > kMaxBatch) return SSA_ERR_UNSUPPORTED;
+  if (s->batch > kMaxBatch || (int64_t)s->batch * s->n_kv_heads > kMaxBatch)
+    return SSA_ERR_UNSUPPORTED;
   if (need_group) {
     const int g = s->n_q_heads / s->n_kv_heads;
     if (g != 1 && g != 2 && g != 4 && g != 8) return SSA_ERR_UNSUPPORTED;

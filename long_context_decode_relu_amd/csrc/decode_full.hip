@@ -6,13 +6,15 @@
 // score of zero or below; a value row is fetched only when some head of the
 // group gives its key a nonzero weight; the output is sum(w v) / (c + sum w).
 //
-// Work decomposition (split-K). The live keys of every (sequence, KV head)
-// stream are cut into items of `chunk` consecutive keys. A persistent grid of
-// work-groups walks the item list with a fixed stride; an item is processed by
-// the 4 waves of a work-group and leaves one partial (num[g][D], den[g]) per
-// head plus survivor counts in the workspace. A second kernel sums the
-// partials of each (sequence, head) in a fixed order and divides. The weights
-// are not exponentiated, so the partials add without a running maximum.
+// Work decomposition (stream-K). The live keys of every (sequence, KV head)
+// stream are cut into 64-key tiles; the streams laid end to end are split
+// into equal contiguous tile ranges, one per wave of a persistent grid, so
+// ragged context lengths cost no balance. A wave leaves one partial
+// (num[g][D], den[g], survivor counts) in the workspace each time it leaves a
+// stream; a combine kernel adds the partials of each (sequence, head) in a
+// fixed order and divides. The weights are not exponentiated, so partials add
+// without a running maximum. A small prep kernel first normalises the queries
+// and builds the tile/slot prefix tables.
 //
 // Inside a wave each lane owns one key of a 64-key tile. For bf16 caches the
 // tile (16 KB) is copied HBM -> LDS by 16 direct-to-LDS loads of 1 KB each
@@ -26,6 +28,7 @@
 // survivor the whole wave loads that key's value row (each lane two
 // dimensions) and adds w_h * v into per-lane accumulators num[h][2 dims].
 // Rows of keys that no head kept are never touched.
+#include <algorithm>
 #include <cstdio>
 #include <utility>
 
@@ -39,22 +42,9 @@ namespace {
 
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxBatch = 1024;         // prefix table of items per sequence lives in LDS
+constexpr int kMaxStreams = 1024;       // (sequence, KV head) streams per call
 constexpr int kTileKeys = kWave;        // one key per lane
 constexpr int kTileBytesBf16 = kTileKeys * kHeadDim * 2;
-
-struct FullParams {
-  const float* q;
-  const void* k;
-  const void* v;
-  const int32_t* ctx_lens;
-  float* scores;
-  float* part;          // [B, Hkv, P, G, D+1]
-  int32_t* part_nnz;    // [B, Hkv, P, G]
-  int32_t* part_vrows;  // [B, Hkv, P]
-  int B, Hq, Hkv, Nmax, P, chunk;
-  float scale, eps;
-};
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
 constexpr int kWaitVm0 = 0x0F70;
@@ -91,6 +81,7 @@ struct KeyRow<false> {
 // computed once per kernel.
 struct TileOffsets {
   uint32_t off[4];
+  TileOffsets() = default;
   __device__ __forceinline__ explicit TileOffsets(int lane) {
     const int kq = lane >> 4, p = lane & 15;
 #pragma unroll
@@ -101,26 +92,28 @@ struct TileOffsets {
   }
 };
 
-// `src` points at the tile's first row; `nvalid` (1..64) rows are live. Rows
-// past the live ones are replaced by the last live row (read, never used).
-__device__ __forceinline__ void tile_issue_bf16(uint8_t* lds_tile, const uint8_t* src, int nvalid,
-                                                const TileOffsets& to, int lane) {
-  if (nvalid == kTileKeys) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      __builtin_amdgcn_global_load_lds(src + to.off[i & 3] + (i >> 2) * 4096, lds_tile + i * 1024,
-                                       16, 0, 0);
-  } else {
-    const int kq = lane >> 4, p = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kt = 4 * i + kq;
+// Fetch of the wave's next tile, one 1 KB load at a time. `src` points at the
+// tile's first row and `nvalid` (0..64) rows are live; rows past the live
+// ones are replaced by the last live row (read, never used). With nvalid == 0
+// there is no next tile and load() does nothing.
+struct TileFetch {
+  uint8_t* lds;
+  const uint8_t* src;
+  int nvalid;
+  TileOffsets to;
+  int lane;
+  __device__ __forceinline__ void load(int i) const {
+    if (nvalid == kTileKeys) {
+      __builtin_amdgcn_global_load_lds(src + to.off[i & 3] + (i >> 2) * 4096, lds + i * 1024, 16,
+                                       0, 0);
+    } else if (nvalid > 0) {
+      const int kt = 4 * i + (lane >> 4);
       const int row = min(kt, nvalid - 1);
-      __builtin_amdgcn_global_load_lds(src + row * 256 + ((p ^ (kt & 15)) << 4),
-                                       lds_tile + i * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + row * 256 + (((lane & 15) ^ (kt & 15)) << 4),
+                                       lds + i * 1024, 16, 0, 0);
     }
   }
-}
+};
 
 __device__ __forceinline__ void tile_read_bf16(const uint8_t* lds_tile, int lane,
                                                KeyRow<true>& kr) {
@@ -148,42 +141,61 @@ __device__ __forceinline__ float2 load_v_pair(const void* v, size_t row, int lan
   }
 }
 
-// Scalar loads of query dims [4*SC, 4*SC+4) of the G heads (rows of kHeadDim
-// floats) from a uniform base, at immediate offsets so that no per-load
-// address has to live in a scalar register. The accumulators pass through the
-// asm so that the FMAs of the previous sub-chunk are scheduled after these
-// loads (hiding their latency); swait() below waits for them.
+// The group's query values, prepared by decode_full_prep: RMS-normalised,
+// multiplied by `scale` and laid out as [32 sub-chunks][G heads][4 dims]
+// (fp32), so that the 4*G values of one sub-chunk are contiguous. They are
+// uniform across the wave and live in scalar registers, feeding the FMAs
+// directly. Sub-chunk SC is fetched with one or two wide scalar loads.
+template <int G>
+struct QBuf;
+template <>
+struct QBuf<1> {
+  f32x4 r;
+  __device__ __forceinline__ float at(int, int t) const { return r[t]; }
+};
+template <>
+struct QBuf<2> {
+  f32x8 r;
+  __device__ __forceinline__ float at(int h, int t) const { return r[4 * h + t]; }
+};
+template <>
+struct QBuf<4> {
+  f32x16 r;
+  __device__ __forceinline__ float at(int h, int t) const { return r[4 * h + t]; }
+};
+template <>
+struct QBuf<8> {
+  f32x16 r0, r1;
+  __device__ __forceinline__ float at(int h, int t) const {
+    return h < 4 ? r0[4 * h + t] : r1[4 * (h - 4) + t];
+  }
+};
+
+// Issue the scalar loads of sub-chunk SC. The loads are asm because the
+// compiler otherwise hoists and merges all of them out of the key loop and
+// spills; the offsets are immediates so that no per-load address occupies
+// scalar registers. The accumulators pass through the asm so that the FMAs of
+// the previous sub-chunk are scheduled after these loads (hiding their
+// latency); qwait() below waits for them.
 template <int G, int SC>
-__device__ __forceinline__ void sload_group(f32x4 (&r)[G], const float* q, float (&a)[G],
-                                            float& x) {
-  constexpr int o = 16 * SC;
+__device__ __forceinline__ void qload(QBuf<G>& r, const float* q, float (&a)[G], float& x) {
+  constexpr int o = 16 * G * SC;
   if constexpr (G == 1) {
-    asm volatile("s_load_dwordx4 %0, %3, %4"
-                 : "=&s"(r[0]), "+v"(a[0]), "+v"(x)
-                 : "s"(q), "n"(o));
+    asm volatile("s_load_dwordx4 %0, %3, %4" : "=&s"(r.r), "+v"(a[0]), "+v"(x) : "s"(q), "n"(o));
   } else if constexpr (G == 2) {
-    asm volatile("s_load_dwordx4 %0, %5, %6\n\ts_load_dwordx4 %1, %5, %7"
-                 : "=&s"(r[0]), "=&s"(r[1]), "+v"(a[0]), "+v"(a[1]), "+v"(x)
-                 : "s"(q), "n"(o), "n"(o + 512));
+    asm volatile("s_load_dwordx8 %0, %4, %5"
+                 : "=&s"(r.r), "+v"(a[0]), "+v"(a[1]), "+v"(x)
+                 : "s"(q), "n"(o));
   } else if constexpr (G == 4) {
-    asm volatile(
-        "s_load_dwordx4 %0, %9, %10\n\ts_load_dwordx4 %1, %9, %11\n\t"
-        "s_load_dwordx4 %2, %9, %12\n\ts_load_dwordx4 %3, %9, %13"
-        : "=&s"(r[0]), "=&s"(r[1]), "=&s"(r[2]), "=&s"(r[3]), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]),
-          "+v"(a[3]), "+v"(x)
-        : "s"(q), "n"(o), "n"(o + 512), "n"(o + 1024), "n"(o + 1536));
+    asm volatile("s_load_dwordx16 %0, %6, %7"
+                 : "=&s"(r.r), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(x)
+                 : "s"(q), "n"(o));
   } else {
     static_assert(G == 8, "group size");
-    asm volatile(
-        "s_load_dwordx4 %0, %17, %18\n\ts_load_dwordx4 %1, %17, %19\n\t"
-        "s_load_dwordx4 %2, %17, %20\n\ts_load_dwordx4 %3, %17, %21\n\t"
-        "s_load_dwordx4 %4, %17, %22\n\ts_load_dwordx4 %5, %17, %23\n\t"
-        "s_load_dwordx4 %6, %17, %24\n\ts_load_dwordx4 %7, %17, %25"
-        : "=&s"(r[0]), "=&s"(r[1]), "=&s"(r[2]), "=&s"(r[3]), "=&s"(r[4]), "=&s"(r[5]),
-          "=&s"(r[6]), "=&s"(r[7]), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]),
-          "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(x)
-        : "s"(q), "n"(o), "n"(o + 512), "n"(o + 1024), "n"(o + 1536), "n"(o + 2048),
-          "n"(o + 2560), "n"(o + 3072), "n"(o + 3584));
+    asm volatile("s_load_dwordx16 %0, %11, %12\n\ts_load_dwordx16 %1, %11, %13"
+                 : "=&s"(r.r0), "=&s"(r.r1), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]),
+                   "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(x)
+                 : "s"(q), "n"(o), "n"(o + 64));
   }
 }
 
@@ -192,460 +204,495 @@ __device__ __forceinline__ void sload_group(f32x4 (&r)[G], const float* q, float
 // the scheduler runs one head's chain across all sub-chunks first and keeps
 // all query values live at once.
 template <int G>
-__device__ __forceinline__ void swait(f32x4 (&r)[G], float (&a)[G], float& x) {
-  if constexpr (G == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r[0]), "+v"(a[0]), "+v"(x));
+__device__ __forceinline__ void qwait(QBuf<G>& r, float (&a)[G], float& x) {
+  if constexpr (G == 1) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.r), "+v"(a[0]), "+v"(x));
   if constexpr (G == 2)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+s"(r[0]), "+s"(r[1]), "+v"(a[0]), "+v"(a[1]), "+v"(x));
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r.r), "+v"(a[0]), "+v"(a[1]), "+v"(x));
   if constexpr (G == 4)
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+s"(r[0]), "+s"(r[1]), "+s"(r[2]), "+s"(r[3]), "+v"(a[0]), "+v"(a[1]),
-                   "+v"(a[2]), "+v"(a[3]), "+v"(x));
+                 : "+s"(r.r), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(x));
   if constexpr (G == 8)
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+s"(r[0]), "+s"(r[1]), "+s"(r[2]), "+s"(r[3]), "+s"(r[4]), "+s"(r[5]),
-                   "+s"(r[6]), "+s"(r[7]), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]),
+                 : "+s"(r.r0), "+s"(r.r1), "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]),
                    "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7]), "+v"(x));
 }
 
-// Scores of one key row against the G query heads: acc[h] = sum_d q[h][d] k[d].
-// The query values are uniform, so they live in scalar registers and feed the
-// FMAs directly. They are streamed four dims (4*G values) at a time: the loads
-// of sub-chunk SC+1 are issued before the FMAs of sub-chunk SC, so at most 8*G
-// scalar registers hold query values at once.
+// Scores of one key row against the G query heads: acc[h] = sum_d q[h][d] k[d],
+// streamed over 32 sub-chunks of 4 dims with one sub-chunk of lookahead.
+// The 16 loads of the wave's next tile (bf16) are spread over the sub-chunks,
+// one every second sub-chunk, so that a full memory queue delays at most one
+// load instead of stalling the wave before any FMA is issued.
 template <int G, bool BF16, bool NORMK, int... SC>
 __device__ __forceinline__ void score_row(const KeyRow<BF16>& kr, const float* qg, float (&acc)[G],
-                                          float& ksq, std::integer_sequence<int, SC...>) {
-  f32x4 qa[G], qb[G];
-  sload_group<G, 0>(qa, qg, acc, ksq);
+                                          float& ksq, const TileFetch& next,
+                                          std::integer_sequence<int, SC...>) {
+  QBuf<G> qa, qb;
+  qload<G, 0>(qa, qg, acc, ksq);
   auto step = [&](auto sc_c) {
     constexpr int sc = decltype(sc_c)::value;
-    swait(qa, acc, ksq);
-    if constexpr (sc + 1 < 32) sload_group<G, sc + 1>(qb, qg, acc, ksq);
+    qwait(qa, acc, ksq);
+    if constexpr (sc + 1 < 32) qload<G, sc + 1>(qb, qg, acc, ksq);
+    if constexpr (BF16 && (sc & 1) == 0) next.load(sc >> 1);
     float e[8];
     kr.chunk(sc >> 1, e);
     constexpr int o = 4 * (sc & 1);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      acc[h] = fmaf(qa[h].x, e[o + 0], acc[h]);
-      acc[h] = fmaf(qa[h].y, e[o + 1], acc[h]);
-      acc[h] = fmaf(qa[h].z, e[o + 2], acc[h]);
-      acc[h] = fmaf(qa[h].w, e[o + 3], acc[h]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[h] = fmaf(qa.at(h, t), e[o + t], acc[h]);
     }
     if constexpr (NORMK) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) ksq = fmaf(e[o + t], e[o + t], ksq);
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) qa[h] = qb[h];
+    qa = qb;
   };
   (step(std::integral_constant<int, SC>{}), ...);
 }
 
-struct Item {
-  int b, kvh, pc, key0, key1;
-};
+// ---------------------------------------------------------------------------
+// Work split: stream-K over 64-key tiles. Stream j = b*Hkv + kvh holds
+// ceil(n_b / 64) tiles; the streams laid end to end form T tiles, and wave w
+// of W takes tiles [w*T/W, (w+1)*T/W) (W is capped at T, so every working
+// wave owns at least one tile). Every wave therefore streams the same
+// number of bytes (to within one tile) whatever the context lengths. A wave
+// writes one partial (num, den, counts) each time it leaves a stream, into
+// slot slot_pre[j] + (w - first wave of j); the combine kernel adds the
+// partials of a stream in slot order.
 
-// Work item -> (sequence, KV head, partition, key range); all values uniform.
-__device__ __forceinline__ Item item_info(int item, const int* s_pref, int B, int Hkv, int C,
-                                          const int32_t* __restrict__ ctx_lens) {
-  int lo = 0, hi = B;  // s_pref[lo] <= item < s_pref[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (s_pref[mid] <= item) lo = mid; else hi = mid;
-  }
-  // LDS reads count as divergent for the compiler; the values are uniform.
-  Item it;
-  it.b = __builtin_amdgcn_readfirstlane(lo);
-  const int r = __builtin_amdgcn_readfirstlane(item - s_pref[it.b]);
-  const int n = ctx_lens[it.b];
-  const int nchunks = ceil_div(n, C);
-  it.kvh = r / nchunks;
-  it.pc = r - it.kvh * nchunks;
-  it.key0 = it.pc * C;
-  it.key1 = min(n, it.key0 + C);
-  return it;
+// The wave whose range holds tile t.
+__device__ __forceinline__ int64_t wave_of_tile(int64_t t, int64_t W, int64_t T) {
+  return ((t + 1) * W - 1) / T;
 }
 
-template <int G, bool BF16, bool NORMQ, bool NORMK>
-__global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
-    const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part,
-    int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows, int B, int Hq, int Hkv,
-    int Nmax, int P, int chunk, float scale, float eps) {
-  __shared__ int s_pref[kMaxBatch + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
-  __shared__ float s_acc[G][kHeadDim];
-  __shared__ float s_den[kWaves][G];
-  __shared__ int s_nnz[kWaves][G];
-  __shared__ int s_vrows[kWaves];
-  __shared__ int s_scan[kThreads];
+// Exclusive prefix sum of vals[0..n) (LDS) into out[0..n] (global), by one
+// work-group of nthr threads; n <= kMaxStreams.
+__device__ void block_exclusive_scan(const int* vals, int n, int* scratch, int* out) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int per = ceil_div(n, nthr);
+  int local = 0;
+  for (int i = tid * per; i < min(n, tid * per + per); ++i) local += vals[i];
+  scratch[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < nthr; off <<= 1) {
+    int t = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += t;
+    __syncthreads();
+  }
+  int run = scratch[tid] - local;  // exclusive prefix of this thread's block
+  for (int i = tid * per; i < min(n, tid * per + per); ++i) {
+    out[i] = run;
+    run += vals[i];
+  }
+  if (tid == nthr - 1) out[n] = scratch[tid];
+  __syncthreads();
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int C = chunk;
+// Work-group j < S prepares the queries of stream j:
+//   qt[j][sc][h][t] = fac_h * q[b][kvh*G + h][4*sc + t]
+// with fac_h = scale / sqrt(mean(q_h^2) + eps) (SSA_NORM_Q) or scale.
+// Work-group S builds the tile and slot prefix tables for W waves.
+__global__ __launch_bounds__(1024) void decode_full_prep(
+    const float* __restrict__ q, const int32_t* __restrict__ ctx_lens, int B, int Hq, int Hkv,
+    float scale, float eps, int normq, int W, float* __restrict__ qt, int* __restrict__ tile_pre,
+    int* __restrict__ slot_pre) {
+  __shared__ float s_part[16];
+  __shared__ int s_vals[kMaxStreams];
+  __shared__ int s_scan[1024];
+  const int S = B * Hkv;
+  const int G = Hq / Hkv;
+  const int j = blockIdx.x;
+  if (j < S) {
+    const int b = j / Hkv, kvh = j - b * Hkv;
+    const int h = threadIdx.x / kHeadDim, d = threadIdx.x % kHeadDim;
+    const float x = q[((size_t)b * Hq + (size_t)kvh * G + h) * kHeadDim + d];
+    float fac = scale;
+    if (normq) {
+      const float ws = wave_sum(x * x);
+      if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = ws;
+      __syncthreads();
+      const float ss = s_part[2 * h] + s_part[2 * h + 1];
+      fac = scale / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    }
+    qt[((size_t)j * 32 + d / 4) * (4 * G) + h * 4 + (d & 3)] = x * fac;
+    return;
+  }
+  for (int i = threadIdx.x; i < S; i += blockDim.x) s_vals[i] = ceil_div(ctx_lens[i / Hkv], kTileKeys);
+  __syncthreads();
+  block_exclusive_scan(s_vals, S, s_scan, tile_pre);
+  const int64_t T = tile_pre[S];
+  const int64_t We = min((int64_t)W, T);  // waves that own at least one tile
+  for (int i = threadIdx.x; i < S; i += blockDim.x) {
+    const int64_t s0 = tile_pre[i], s1 = tile_pre[i + 1];
+    s_vals[i] = s1 > s0 ? (int)(wave_of_tile(s1 - 1, We, T) - wave_of_tile(s0, We, T) + 1) : 0;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_vals, S, s_scan, slot_pre);
+}
+
+template <int G, bool BF16, bool NORMK>
+__global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
+    const float* __restrict__ qt, const void* __restrict__ k, const void* __restrict__ v,
+    const int32_t* __restrict__ ctx_lens, const int* __restrict__ tile_pre,
+    const int* __restrict__ slot_pre, float* __restrict__ scores, float* __restrict__ part_num,
+    float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
+    int B, int Hq, int Hkv, int Nmax, float eps) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* my_tile = s_tile + (BF16 ? wave * kTileBytesBf16 : 0);
 
-  // Items per sequence: Hkv * ceil(n_b / C); exclusive prefix in LDS.
-  if (tid == 0) s_pref[0] = 0;
-  for (int b0 = 0; b0 < B; b0 += kThreads) {
-    int b = b0 + tid;
-    s_scan[tid] = b < B ? Hkv * ceil_div(ctx_lens[b], C) : 0;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      int t = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += t;
-      __syncthreads();
-    }
-    int carry = s_pref[b0];
-    if (b < B) s_pref[b + 1] = carry + s_scan[tid];
-    __syncthreads();
-  }
-  const int n_items = __builtin_amdgcn_readfirstlane(s_pref[B]);
-  const int grid = gridDim.x;
+  const int S = B * Hkv;
+  const int64_t T = tile_pre[S];
+  // With more waves than tiles only the first T waves work (one tile each),
+  // so that every working wave owns at least one tile.
+  const int64_t W = min((int64_t)gridDim.x * kWaves, T);
+  const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+  if (w >= W) return;
+  const int64_t t0 = w * T / W, t1 = (w + 1) * T / W;
 
-  // The wave's tile sequence runs over its tiles t = wave, wave+4, ... of each
-  // of the work-group's items. (nitem, nt) is the next tile to fetch; its
-  // first row is at n_src and n_valid of its rows are live.
-  auto ntiles = [&](const Item& I) { return ceil_div(I.key1 - I.key0, kTileKeys); };
-  int nitem = blockIdx.x, nt = wave;
-  const uint8_t* n_src = nullptr;
-  int n_valid = 0;
-  auto seek = [&]() {  // move (nitem, nt) forward to a tile that exists (or past the end)
-    n_valid = 0;
-    while (nitem < n_items) {
-      const Item nI = item_info(nitem, s_pref, B, Hkv, C, ctx_lens);
-      if (nt < ntiles(nI)) {
-        const int kb = nI.key0 + nt * kTileKeys;
-        n_valid = min(kTileKeys, nI.key1 - kb);
-        n_src = reinterpret_cast<const uint8_t*>(k) +
-                (((size_t)nI.b * Hkv + nI.kvh) * (size_t)Nmax + kb) * (kHeadDim * 2);
-        return;
-      }
-      nitem += grid;
-      nt = wave;
+  // stream holding tile t: the largest j with tile_pre[j] <= t (never an empty stream)
+  auto stream_of = [&](int64_t t) {
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_pre[mid] <= t) lo = mid; else hi = mid;
     }
+    return lo;
   };
+  struct Stream {
+    int j, b, kvh, n, s0, s1;
+  };
+  auto stream_info = [&](int j) {
+    Stream st;
+    st.j = j;
+    st.b = j / Hkv;
+    st.kvh = j - st.b * Hkv;
+    st.n = ctx_lens[st.b];
+    st.s0 = tile_pre[j];
+    st.s1 = tile_pre[j + 1];
+    return st;
+  };
+
   const TileOffsets toff(lane);
-  auto issue = [&]() {
-    if constexpr (BF16) {
-      if (n_valid > 0) tile_issue_bf16(my_tile, n_src, n_valid, toff, lane);
-    }
+  // fetch descriptor of tile t of stream st
+  auto fetch_of = [&](const Stream& st, int64_t t) {
+    TileFetch f;
+    f.lds = my_tile;
+    f.to = toff;
+    f.lane = lane;
+    const int kb = (int)(t - st.s0) * kTileKeys;
+    f.nvalid = BF16 ? min(kTileKeys, st.n - kb) : 0;
+    f.src = reinterpret_cast<const uint8_t*>(k) + ((size_t)st.j * Nmax + kb) * (kHeadDim * 2);
+    return f;
   };
-  seek();
-  issue();
 
-  for (int item = blockIdx.x; item < n_items; item += grid) {
-    const Item I = item_info(item, s_pref, B, Hkv, C, ctx_lens);
-    const int b = I.b, kvh = I.kvh;
-
-    // Per-head score factor: scale / RMS(q_h) (or scale).
-    const float* qg = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
-    float fac[G];
+  Stream cur = stream_info(stream_of(t0));
+  {
+    const TileFetch f0 = fetch_of(cur, t0);
+    if constexpr (BF16) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if constexpr (NORMQ) {
-        float a0 = qg[h * kHeadDim + 2 * lane], a1 = qg[h * kHeadDim + 2 * lane + 1];
-        float ss = wave_sum(a0 * a0 + a1 * a1);
-        fac[h] = scale / sqrtf(ss * (1.0f / kHeadDim) + eps);
-      } else {
-        fac[h] = scale;
-      }
+      for (int i = 0; i < 16; ++i) f0.load(i);
     }
+  }
 
-    float num[G][2];
-    float den[G];
-    int nnz[G];
+  float num[G][2];
+  float den[G];
+  int nnz[G];
+  int vrows = 0;
+  auto reset = [&]() {
 #pragma unroll
     for (int h = 0; h < G; ++h) { num[h][0] = num[h][1] = 0.f; den[h] = 0.f; nnz[h] = 0; }
-    int vrows = 0;
-
-    const size_t row0 = ((size_t)b * Hkv + kvh) * (size_t)Nmax;
-    float* srow = scores ? scores + ((size_t)b * Hq + (size_t)kvh * G) * Nmax : nullptr;
-    const int my_tiles = ntiles(I);
-
-    for (int t = wave; t < my_tiles; t += kWaves) {
-      // here (nitem, nt) == (item, t): its tile is in flight
-      const int base = I.key0 + t * kTileKeys;
-      const int key = base + lane;
-      const bool valid = key < I.key1;
-      KeyRow<BF16> kr;
-      if constexpr (BF16) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this tile has landed in LDS
-        tile_read_bf16(my_tile, lane, kr);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0); // rows are in registers: LDS may be refilled
-      } else {
-        row_load_f32(k, row0 + min(key, I.key1 - 1), kr);
-      }
-      nt += kWaves;
-      seek();
-      issue();  // next tile streams in while this one is scored
-
-      float acc[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0.f;
-      float ksq = 0.f;
-      score_row<G, BF16, NORMK>(kr, qg, acc, ksq, std::make_integer_sequence<int, 32>{});
-      float kf = 1.f;
-      if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
-
-      float w[G];
-      bool any = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = NORMK ? acc[h] * fac[h] * kf : acc[h] * fac[h];
-        if (srow && valid) srow[(size_t)h * Nmax + key] = s;
-        bool pos = valid && s > 0.f;
-        w[h] = pos ? s * s : 0.f;
-        den[h] += w[h];
-        nnz[h] += pos ? 1 : 0;
-        any |= pos;
-      }
-
-      uint64_t mask = __ballot(any);
-      vrows += __popcll(mask);
-      // V rows of survivors only, four at a time.
-      while (mask) {
-        int js[4];
-        float live[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (mask) {
-            js[u] = __builtin_ctzll(mask);
-            mask &= mask - 1;
-            live[u] = 1.f;
-          } else {
-            js[u] = js[0];
-            live[u] = 0.f;
-          }
-        }
-        float2 vv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) vv[u] = load_v_pair<BF16>(v, row0 + base + js[u], lane);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            float wj = readlane_f(w[h], js[u]) * live[u];
-            num[h][0] = fmaf(wj, vv[u].x, num[h][0]);
-            num[h][1] = fmaf(wj, vv[u].y, num[h][1]);
-          }
-        }
-      }
-    }
-
-    // wave -> work-group reduction in a fixed order (wave 0, 1, 2, 3)
+    vrows = 0;
+  };
+  auto flush = [&](const Stream& st) {
+    const int64_t slot = slot_pre[st.j] + (w - wave_of_tile(st.s0, W, T));
+    float* pn = part_num + slot * (G * kHeadDim);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float d = wave_sum(den[h]);
-      int z = wave_sum_i(nnz[h]);
-      if (lane == 0) { s_den[wave][h] = d; s_nnz[wave][h] = z; }
+      pn[h * kHeadDim + 2 * lane] = num[h][0];
+      pn[h * kHeadDim + 2 * lane + 1] = num[h][1];
+      const float d = wave_sum(den[h]);
+      const int z = wave_sum_i(nnz[h]);
+      if (lane == 0) {
+        part_den[slot * G + h] = d;
+        part_nnz[slot * G + h] = z;
+      }
     }
-    if (lane == 0) s_vrows[wave] = vrows;
+    if (lane == 0) part_vrows[slot] = vrows;
+  };
+  reset();
+
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t >= cur.s1) {  // entering the next non-empty stream
+      flush(cur);
+      reset();
+      int nj = cur.j + 1;
+      while (tile_pre[nj + 1] <= t) ++nj;
+      cur = stream_info(nj);
+    }
+    const int b = cur.b, kvh = cur.kvh;
+    const float* qg = qt + (size_t)cur.j * (kHeadDim * G);
+    const size_t row0 = (size_t)cur.j * Nmax;
+    float* srow = scores ? scores + ((size_t)b * Hq + (size_t)kvh * G) * Nmax : nullptr;
+    const int base = (int)(t - cur.s0) * kTileKeys;
+    const int key = base + lane;
+    const bool valid = key < cur.n;
+
+    KeyRow<BF16> kr;
+    if constexpr (BF16) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this tile has landed in LDS
+      tile_read_bf16(my_tile, lane, kr);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0); // rows are in registers: LDS may be refilled
+    } else {
+      row_load_f32(k, row0 + min(key, cur.n - 1), kr);
+    }
+    // the next tile of this wave (possibly in the next stream) streams in
+    // while this one is scored
+    TileFetch next;
+    next.nvalid = 0;
+    if (t + 1 < t1) {
+      if (t + 1 < cur.s1) {
+        next = fetch_of(cur, t + 1);
+      } else {
+        int nj = cur.j + 1;
+        while (tile_pre[nj + 1] <= t + 1) ++nj;
+        next = fetch_of(stream_info(nj), t + 1);
+      }
+    }
+    if constexpr (!BF16) next.nvalid = 0;
+
+    float acc[G];
 #pragma unroll
-    for (int wv = 0; wv < kWaves; ++wv) {
-      __syncthreads();
-      if (wave == wv) {
+    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+    float ksq = 0.f;
+    score_row<G, BF16, NORMK>(kr, qg, acc, ksq, next, std::make_integer_sequence<int, 32>{});
+    float kf = 1.f;
+    if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
+
+    float wt[G];
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = NORMK ? acc[h] * kf : acc[h];
+      if (srow && valid) srow[(size_t)h * Nmax + key] = s;
+      bool pos = valid && s > 0.f;
+      wt[h] = pos ? s * s : 0.f;
+      den[h] += wt[h];
+      nnz[h] += pos ? 1 : 0;
+      any |= pos;
+    }
+
+    uint64_t mask = __ballot(any);
+    vrows += __popcll(mask);
+    // V rows of survivors only, four at a time.
+    while (mask) {
+      int js[4];
+      float live[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (mask) {
+          js[u] = __builtin_ctzll(mask);
+          mask &= mask - 1;
+          live[u] = 1.f;
+        } else {
+          js[u] = js[0];
+          live[u] = 0.f;
+        }
+      }
+      float2 vv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vv[u] = load_v_pair<BF16>(v, row0 + base + js[u], lane);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          if (wv == 0) {
-            s_acc[h][2 * lane] = num[h][0];
-            s_acc[h][2 * lane + 1] = num[h][1];
-          } else {
-            s_acc[h][2 * lane] += num[h][0];
-            s_acc[h][2 * lane + 1] += num[h][1];
-          }
+          float wj = readlane_f(wt[h], js[u]) * live[u];
+          num[h][0] = fmaf(wj, vv[u].x, num[h][0]);
+          num[h][1] = fmaf(wj, vv[u].y, num[h][1]);
         }
       }
     }
-    __syncthreads();
-    const size_t slot = ((size_t)b * Hkv + kvh) * P + I.pc;
-    float* dst = part + slot * (size_t)(G * (kHeadDim + 1));
-    for (int i = tid; i < G * (kHeadDim + 1); i += kThreads) {
-      int h = i / (kHeadDim + 1), d = i - h * (kHeadDim + 1);
-      float s;
-      if (d < kHeadDim) {
-        s = s_acc[h][d];
-      } else {
-        s = 0.f;
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) s += s_den[wv][h];
-      }
-      dst[i] = s;
-    }
-    if (tid < G) {
-      int z = 0;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) z += s_nnz[wv][tid];
-      part_nnz[slot * G + tid] = z;
-    }
-    if (tid == 0) {
-      int z = 0;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) z += s_vrows[wv];
-      part_vrows[slot] = z;
-    }
-    __syncthreads();
   }
+  flush(cur);
   if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
-// Sum the partials of each (sequence, query head) and divide by (c + den).
-// Four groups of 128 threads each sum every fourth partial; the four sums are
-// then added in a fixed order, so the result does not depend on timing.
+// Sum the partials of each (sequence, query head) in slot order and divide by
+// (c + den). Four groups of 128 threads each sum every fourth partial; the
+// four sums are then added in a fixed order, so the result does not depend on
+// timing.
 constexpr int kCombineGroups = 4;
 
 __global__ __launch_bounds__(kHeadDim * kCombineGroups) void decode_full_combine(
-    const float* __restrict__ part, const int32_t* __restrict__ part_nnz,
-    const int32_t* __restrict__ part_vrows, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv,
-    int P, int chunk, float c, float* __restrict__ out, int32_t* __restrict__ nnz,
-    int32_t* __restrict__ vrows) {
+    const float* __restrict__ part_num, const float* __restrict__ part_den,
+    const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
+    const int* __restrict__ slot_pre, int Hq, int Hkv, float c, float* __restrict__ out,
+    int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
   __shared__ float s_num[kCombineGroups][kHeadDim];
-  __shared__ float s_den[kCombineGroups][kHeadDim];
+  __shared__ float s_den[kCombineGroups];
   const int h = blockIdx.x, b = blockIdx.y;
   const int d = threadIdx.x % kHeadDim, grp = threadIdx.x / kHeadDim;
   const int G = Hq / Hkv;
-  const int kvh = h / G, j = h - kvh * G;
-  const int pb = ceil_div(ctx_lens[b], chunk);
-  const size_t stride = (size_t)G * (kHeadDim + 1);
-  const float* src = part + (((size_t)b * Hkv + kvh) * P) * stride + (size_t)j * (kHeadDim + 1);
+  const int kvh = h / G, jh = h - kvh * G;
+  const int j = b * Hkv + kvh;
+  const int p0 = slot_pre[j], p1 = slot_pre[j + 1];
   float sn = 0.f, sd = 0.f;
 #pragma unroll 8
-  for (int pc = grp; pc < pb; pc += kCombineGroups) {
-    const float* e = src + (size_t)pc * stride;
-    sn += e[d];
-    sd += e[kHeadDim];
+  for (int p = p0 + grp; p < p1; p += kCombineGroups) {
+    sn += part_num[((size_t)p * G + jh) * kHeadDim + d];
+    sd += part_den[(size_t)p * G + jh];
   }
   s_num[grp][d] = sn;
-  s_den[grp][d] = sd;
+  if (d == 0) s_den[grp] = sd;
   __syncthreads();
   if (grp == 0) {
     float tn = 0.f, td = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < kCombineGroups; ++g2) { tn += s_num[g2][d]; td += s_den[g2][d]; }
+    for (int g2 = 0; g2 < kCombineGroups; ++g2) { tn += s_num[g2][d]; td += s_den[g2]; }
     const float denom = c + td;
     out[((size_t)b * Hq + h) * kHeadDim + d] = denom == 0.f ? 0.f : tn / denom;
     if (d == 0 && nnz) {
       int z = 0;
-      const int32_t* e = part_nnz + ((size_t)b * Hkv + kvh) * P * G + j;
-      for (int pc = 0; pc < pb; ++pc) z += e[(size_t)pc * G];
+      for (int p = p0; p < p1; ++p) z += part_nnz[(size_t)p * G + jh];
       nnz[(size_t)b * Hq + h] = z;
     }
-    if (d == 1 && j == 0 && vrows) {
+    if (d == 1 && jh == 0 && vrows) {
       int z = 0;
-      const int32_t* e = part_vrows + ((size_t)b * Hkv + kvh) * P;
-      for (int pc = 0; pc < pb; ++pc) z += e[pc];
+      for (int p = p0; p < p1; ++p) z += part_vrows[p];
       vrows[(size_t)b * Hkv + kvh] = z;
     }
   }
 }
 
+constexpr int kMaxWaves = 8192;  // upper bound on W; sizes the partial slots
+
 struct WsLayout {
-  size_t part, nnz, vrows, total;
+  size_t num, den, nnz, vrows, tile_pre, slot_pre, qt, total;
 };
 
-WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
-  const int chunk = decode_full_chunk(B, Hkv, max_ctx);
-  const int P = ceil_div(max_ctx, chunk);
+WsLayout ws_layout(int B, int Hq, int Hkv) {
   const int G = Hkv > 0 ? Hq / Hkv : 0;
-  const size_t slots = (size_t)B * Hkv * P;
+  const size_t S = (size_t)B * Hkv;
+  const size_t slots = S + kMaxWaves;
   WsLayout l;
-  l.part = 0;
-  l.nnz = align_up(slots * G * (kHeadDim + 1) * sizeof(float), 256);
-  l.vrows = l.nnz + align_up(slots * G * sizeof(int32_t), 256);
-  l.total = l.vrows + align_up(slots * sizeof(int32_t), 256);
+  size_t o = 0;
+  l.num = o; o += align_up(slots * G * kHeadDim * sizeof(float), 256);
+  l.den = o; o += align_up(slots * G * sizeof(float), 256);
+  l.nnz = o; o += align_up(slots * G * sizeof(int32_t), 256);
+  l.vrows = o; o += align_up(slots * sizeof(int32_t), 256);
+  l.tile_pre = o; o += align_up((S + 1) * sizeof(int), 256);
+  l.slot_pre = o; o += align_up((S + 1) * sizeof(int), 256);
+  l.qt = o; o += align_up((size_t)B * Hq * kHeadDim * sizeof(float), 256);
+  l.total = o;
   return l;
 }
 
-template <int G, bool BF16, bool NORMQ, bool NORMK>
-hipError_t launch_t(const FullParams& fp, int max_items, hipStream_t stream) {
-  auto kern = decode_full_kernel<G, BF16, NORMQ, NORMK>;
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) per_cu = 1;
-  int grid = device_cu_count() * per_cu;
-  if (grid > max_items) grid = max_items;
-  if (grid < 1) return hipSuccess;
-  if (verbose())
-    fprintf(stderr, "[ssa] decode_full G=%d bf16=%d grid=%d (cus=%d x %d/cu) items<=%d chunk=%d\n", G,
-            (int)BF16, grid, device_cu_count(), per_cu, max_items, fp.chunk);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, fp.q, fp.k, fp.v, fp.ctx_lens,
-                     fp.scores, fp.part, fp.part_nnz, fp.part_vrows, fp.B, fp.Hq, fp.Hkv, fp.Nmax,
-                     fp.P, fp.chunk, fp.scale, fp.eps);
+struct Launch {
+  const float* qt;
+  const void* k;
+  const void* v;
+  const int32_t* ctx_lens;
+  const int* tile_pre;
+  const int* slot_pre;
+  float* scores;
+  float *num, *den;
+  int32_t *nnz, *vrows;
+  int B, Hq, Hkv, Nmax;
+  float eps;
+};
+
+template <int G, bool BF16, bool NORMK>
+hipError_t launch_t(const Launch& L, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_full_kernel<G, BF16, NORMK>), dim3(grid), dim3(kThreads), 0, stream,
+                     L.qt, L.k, L.v, L.ctx_lens, L.tile_pre, L.slot_pre, L.scores, L.num, L.den,
+                     L.nnz, L.vrows, L.B, L.Hq, L.Hkv, L.Nmax, L.eps);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t launch_g(const FullParams& fp, bool bf16, uint32_t flags, int max_items,
-                    hipStream_t stream) {
-  const bool nq = flags & SSA_NORM_Q, nk = flags & SSA_NORM_K;
-  if (bf16) {
-    if (nq && !nk) return launch_t<G, true, true, false>(fp, max_items, stream);
-    if (nq && nk) return launch_t<G, true, true, true>(fp, max_items, stream);
-    if (!nq && !nk) return launch_t<G, true, false, false>(fp, max_items, stream);
-    return launch_t<G, true, false, true>(fp, max_items, stream);
-  }
-  if (nq && !nk) return launch_t<G, false, true, false>(fp, max_items, stream);
-  if (nq && nk) return launch_t<G, false, true, true>(fp, max_items, stream);
-  if (!nq && !nk) return launch_t<G, false, false, false>(fp, max_items, stream);
-  return launch_t<G, false, false, true>(fp, max_items, stream);
+hipError_t launch_g(const Launch& L, bool bf16, bool normk, int grid, hipStream_t stream) {
+  if (bf16) return normk ? launch_t<G, true, true>(L, grid, stream) : launch_t<G, true, false>(L, grid, stream);
+  return normk ? launch_t<G, false, true>(L, grid, stream) : launch_t<G, false, false>(L, grid, stream);
+}
+
+template <int G>
+int blocks_per_cu(bool bf16, bool normk) {
+  int n = 0;
+  hipError_t e;
+  if (bf16)
+    e = normk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, true, true>, kThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, true, false>, kThreads, 0);
+  else
+    e = normk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, false, true>, kThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, false, false>, kThreads, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
 }
 
 }  // namespace
 
-int decode_full_chunk(int batch, int n_kv_heads, int max_ctx_len) {
-  // Aim for about 2048 items at the upper bound of the work so that a
-  // persistent grid of ~2 work-groups per CU sees several items each.
-  int64_t total = (int64_t)batch * n_kv_heads * max_ctx_len;
-  int c = 256;
-  while (c < 2048 && total / c > 2048) c <<= 1;
-  return c;
-}
+int decode_full_chunk(int, int, int) { return kTileKeys; }
 
-size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int max_ctx) {
-  return ws_layout(B, Hq, Hkv, max_ctx).total;
-}
+size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int) { return ws_layout(B, Hq, Hkv).total; }
 
 hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
-  const int chunk = decode_full_chunk(a.B, a.Hkv, a.max_ctx);
-  const int P = ceil_div(a.max_ctx, chunk);
-  const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
+  const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv);
   char* ws = static_cast<char*>(a.ws);
-  FullParams fp;
-  fp.q = a.q;
-  fp.k = a.k;
-  fp.v = a.v;
-  fp.ctx_lens = a.ctx_lens;
-  fp.scores = a.scores;
-  fp.part = reinterpret_cast<float*>(ws + l.part);
-  fp.part_nnz = reinterpret_cast<int32_t*>(ws + l.nnz);
-  fp.part_vrows = reinterpret_cast<int32_t*>(ws + l.vrows);
-  fp.B = a.B;
-  fp.Hq = a.Hq;
-  fp.Hkv = a.Hkv;
-  fp.Nmax = a.Nmax;
-  fp.P = P;
-  fp.chunk = chunk;
-  fp.scale = a.scale;
-  fp.eps = a.eps;
-  const int max_items = a.B * a.Hkv * P;
-  hipError_t e = hipSuccess;
-  if (max_items > 0) {
-    switch (G) {
-      case 1: e = launch_g<1>(fp, a.kv_bf16, a.flags, max_items, stream); break;
-      case 2: e = launch_g<2>(fp, a.kv_bf16, a.flags, max_items, stream); break;
-      case 4: e = launch_g<4>(fp, a.kv_bf16, a.flags, max_items, stream); break;
-      case 8: e = launch_g<8>(fp, a.kv_bf16, a.flags, max_items, stream); break;
-      default: return hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) return e;
+  Launch L;
+  L.qt = reinterpret_cast<const float*>(ws + l.qt);
+  L.k = a.k;
+  L.v = a.v;
+  L.ctx_lens = a.ctx_lens;
+  L.tile_pre = reinterpret_cast<const int*>(ws + l.tile_pre);
+  L.slot_pre = reinterpret_cast<const int*>(ws + l.slot_pre);
+  L.scores = a.scores;
+  L.num = reinterpret_cast<float*>(ws + l.num);
+  L.den = reinterpret_cast<float*>(ws + l.den);
+  L.nnz = reinterpret_cast<int32_t*>(ws + l.nnz);
+  L.vrows = reinterpret_cast<int32_t*>(ws + l.vrows);
+  L.B = a.B;
+  L.Hq = a.Hq;
+  L.Hkv = a.Hkv;
+  L.Nmax = a.Nmax;
+  L.eps = a.eps;
+  const bool normk = a.flags & SSA_NORM_K;
+  // Persistent grid: all resident work-groups, but no more than about four
+  // tiles' worth per wave at the host bound of the work.
+  int per_cu = 1;
+  switch (G) {
+    case 1: per_cu = blocks_per_cu<1>(a.kv_bf16, normk); break;
+    case 2: per_cu = blocks_per_cu<2>(a.kv_bf16, normk); break;
+    case 4: per_cu = blocks_per_cu<4>(a.kv_bf16, normk); break;
+    case 8: per_cu = blocks_per_cu<8>(a.kv_bf16, normk); break;
+    default: return hipErrorInvalidValue;
   }
-  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kHeadDim * kCombineGroups), 0, stream, fp.part,
-                     fp.part_nnz, fp.part_vrows, a.ctx_lens, a.Hq, a.Hkv, P, chunk, a.c, a.out,
+  const int64_t tiles_bound = (int64_t)a.B * a.Hkv * ceil_div(a.max_ctx, kTileKeys);
+  int64_t grid = (int64_t)device_cu_count() * per_cu;
+  grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div64(tiles_bound, kWaves * 4)));
+  grid = std::min<int64_t>(grid, kMaxWaves / kWaves);
+  const int W = (int)grid * kWaves;
+  if (verbose())
+    fprintf(stderr, "[ssa] decode_full G=%d bf16=%d grid=%d (cus=%d x %d/cu) W=%d tiles<=%lld\n", G,
+            a.kv_bf16, (int)grid, device_cu_count(), per_cu, W, (long long)tiles_bound);
+  const int S = a.B * a.Hkv;
+  hipLaunchKernelGGL(decode_full_prep, dim3(S + 1), dim3(G * kHeadDim), 0, stream, a.q, a.ctx_lens,
+                     a.B, a.Hq, a.Hkv, a.scale, a.eps, (a.flags & SSA_NORM_Q) ? 1 : 0, W,
+                     reinterpret_cast<float*>(ws + l.qt), reinterpret_cast<int*>(ws + l.tile_pre),
+                     reinterpret_cast<int*>(ws + l.slot_pre));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (G) {
+    case 1: e = launch_g<1>(L, a.kv_bf16, normk, (int)grid, stream); break;
+    case 2: e = launch_g<2>(L, a.kv_bf16, normk, (int)grid, stream); break;
+    case 4: e = launch_g<4>(L, a.kv_bf16, normk, (int)grid, stream); break;
+    case 8: e = launch_g<8>(L, a.kv_bf16, normk, (int)grid, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kHeadDim * kCombineGroups), 0,
+                     stream, L.num, L.den, L.nnz, L.vrows, L.slot_pre, a.Hq, a.Hkv, a.c, a.out,
                      a.nnz, a.vrows);
   return hipGetLastError();
 }
