@@ -1,7 +1,313 @@
-// Top-k + recent selection (placeholder until the radix-select kernel lands).
+// Top-k + recent selection for the sparse layers (gfx950).
+//
+// "The Architecture of Embla 1", section "Three kinds of attention": a sparse
+// layer reads the 1,024 keys its full layer scored highest -- by raw score,
+// so keys scored just below zero count -- plus the 128 most recent keys.
+//
+// One work-group of 1024 threads per (sequence, query head). Scores are
+// mapped to order-preserving 32-bit keys (larger score -> larger key, -0.0 ==
+// +0.0), so the k-th largest score is an exact radix select on integers. The
+// cut is found as a key value v* plus an index i*: a key is in the top k when
+// key > v*, or key == v* and its index <= i* (ties go to the lower index).
+//
+//   pass 1  histogram of the top 12 key bits over the pool (LDS atomics)
+//   pass 2  keys in the bin holding the cut (typically a few hundred) are
+//           gathered into LDS; the remaining 20 bits and the tie index are
+//           resolved there by 10-bit radix passes.
+//           If that bin is too large for LDS, further 10-bit histogram
+//           passes over global memory narrow it first; if all 32 bits are
+//           resolved and the tied keys still do not fit, the tie index is
+//           found by an ordered pass.
+//   pass 3  per segment of 2^18 keys: mark (top-k) union (recent window) in an
+//           LDS bitmap, then compact the bitmap into ascending indices.
+//
+// The pool is [0, n) (union with the window, duplicates removed) or, with
+// SSA_SELECT_DISJOINT, [0, n - n_recent).
+#include <climits>
+
+#include "common.h"
 #include "kernels.h"
+#include "../../include/ssa.h"
 
 namespace ssa {
+
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kBins = 4096;       // first-pass histogram (12 bits)
+constexpr int kCap = 4096;        // candidates held in LDS
+constexpr int kSegKeys = 1 << 18; // keys per output segment (LDS bitmap of 32 KB)
+constexpr int kSegWords = kSegKeys / 32;
+
+struct SelShared {
+  uint32_t hist[kBins];
+  uint32_t ckey[kCap];
+  int32_t cidx[kCap];
+  uint32_t bits[kSegWords];
+  int32_t scan[kSelThreads];
+  int32_t ccount;
+  int32_t bcast[4];
+};
+
+// Order-preserving key of a score (see ordered_key in common.h).
+__device__ __forceinline__ uint32_t skey(const float* s, int i) { return ordered_key(s[i]); }
+
+// Exclusive prefix over the work-group of one int per thread; returns the
+// thread's prefix and writes the total to *total.
+__device__ int block_scan_excl(int x, int32_t* scratch, int* total) {
+  const int tid = threadIdx.x;
+  scratch[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    int t = tid >= off ? scratch[tid - off] : 0;
+    __syncthreads();
+    scratch[tid] += t;
+    __syncthreads();
+  }
+  const int incl = scratch[tid];
+  *total = scratch[kSelThreads - 1];
+  __syncthreads();
+  return incl - x;
+}
+
+// Given a histogram hist[0..nb) and need >= 1, find the largest bin d whose
+// suffix count (bins >= d) is >= need. Returns d; *above = count in bins > d.
+__device__ int threshold_bin(const uint32_t* hist, int nb, int need, SelShared& sh, int* above) {
+  const int tid = threadIdx.x;
+  const int per = ceil_div(nb, kSelThreads);
+  // thread t owns bins [nb - (t+1)*per, nb - t*per) counted from the top
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = nb - 1 - (tid * per + i);
+    if (b >= 0) local += (int)hist[b];
+  }
+  int total;
+  const int before = block_scan_excl(local, sh.scan, &total);  // count in bins above my range
+  if (tid == 0) sh.bcast[0] = -1;
+  __syncthreads();
+  int run = before;
+  for (int i = 0; i < per; ++i) {
+    const int b = nb - 1 - (tid * per + i);
+    if (b < 0) break;
+    const int c = (int)hist[b];
+    if (run < need && run + c >= need) {
+      sh.bcast[0] = b;
+      sh.bcast[1] = run;
+    }
+    run += c;
+  }
+  __syncthreads();
+  const int d = sh.bcast[0];
+  *above = sh.bcast[1];
+  __syncthreads();
+  return d;
+}
+
+// Resolve the cut among the candidates held in LDS. All of them share the top
+// `known` bits of their key (value `prefix`); `need` of them must be taken.
+// Returns v* and i* through *vstar / *istar.
+__device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, int need,
+                              uint32_t* vstar, int* istar) {
+  const int tid = threadIdx.x;
+  uint32_t P = prefix;
+  int L = known;
+  int cnt_eq = c;  // candidates whose key matches the prefix P (L bits)
+  while (L < 32) {
+    const int D = min(10, 32 - L);
+    const int nb = 1 << D;
+    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < c; i += kSelThreads) {
+      const uint32_t key = sh.ckey[i];
+      const bool match = L == 0 ? true : (key >> (32 - L)) == P;
+      if (match) atomicAdd(&sh.hist[(key >> (32 - L - D)) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    int above;
+    const int d = threshold_bin(sh.hist, nb, need, sh, &above);
+    cnt_eq = (int)sh.hist[d];
+    need -= above;
+    P = (P << D) | (uint32_t)d;
+    L += D;
+    __syncthreads();
+  }
+  *vstar = P;
+  if (need >= cnt_eq) {
+    *istar = INT_MAX;
+    return;
+  }
+  // the `need` smallest indices among candidates with key == v*: select on
+  // the complemented index (largest complement = smallest index)
+  uint32_t Q = 0;
+  int M = 0;
+  int need2 = need;
+  while (M < 32) {
+    const int D = min(10, 32 - M);
+    const int nb = 1 << D;
+    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < c; i += kSelThreads) {
+      if (sh.ckey[i] != P) continue;
+      const uint32_t ci = ~(uint32_t)sh.cidx[i];
+      const bool match = M == 0 ? true : (ci >> (32 - M)) == Q;
+      if (match) atomicAdd(&sh.hist[(ci >> (32 - M - D)) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    int above;
+    const int d = threshold_bin(sh.hist, nb, need2, sh, &above);
+    need2 -= above;
+    Q = (Q << D) | (uint32_t)d;
+    M += D;
+    __syncthreads();
+  }
+  *istar = (int)~Q;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
+    int k_top, int n_recent, int disjoint, int32_t* __restrict__ sel_idx,
+    int32_t* __restrict__ sel_count, int stride) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / Hq;
+  const int n = ctx_lens[b];
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  const float* s = scores + (size_t)row * Nmax;
+
+  uint32_t vstar = 0;
+  int istar = INT_MAX;  // k == pool: every pool key is selected
+  if (k < pool) {
+    // pass 1: histogram of the top 12 bits
+    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < pool; i += kSelThreads) atomicAdd(&sh.hist[skey(s, i) >> 20], 1u);
+    __syncthreads();
+    int above;
+    const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
+    int need = k - above;
+    uint32_t P = (uint32_t)d1;
+    int L = 12;
+    int c = (int)sh.hist[d1];
+    __syncthreads();
+    // narrow the cut bin over global memory until it fits in LDS
+    while (c > kCap && L < 32) {
+      const int D = min(10, 32 - L);
+      const int nb = 1 << D;
+      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < pool; i += kSelThreads) {
+        const uint32_t key = skey(s, i);
+        if ((key >> (32 - L)) == P) atomicAdd(&sh.hist[(key >> (32 - L - D)) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      const int d = threshold_bin(sh.hist, nb, need, sh, &above);
+      need -= above;
+      P = (P << D) | (uint32_t)d;
+      L += D;
+      c = (int)sh.hist[d];
+      __syncthreads();
+    }
+    if (c <= kCap) {
+      // pass 2: gather the keys of the cut bin
+      if (tid == 0) sh.ccount = 0;
+      __syncthreads();
+      for (int i = tid; i < pool; i += kSelThreads) {
+        const uint32_t key = skey(s, i);
+        if ((L == 32 ? key : key >> (32 - L)) == P) {
+          const int pos = atomicAdd(&sh.ccount, 1);
+          sh.ckey[pos] = key;
+          sh.cidx[pos] = i;
+        }
+      }
+      __syncthreads();
+      finish_in_lds(sh, c, P, L, need, &vstar, &istar);
+    } else {
+      // all 32 bits known and more than kCap keys tie at v*: the need-th
+      // smallest tied index, by an ordered pass over blocks of the row
+      vstar = P;
+      int run = 0;
+      istar = -1;
+      for (int base = 0; base < pool && istar < 0; base += kSelThreads) {
+        const int i = base + tid;
+        const int tie = (i < pool && skey(s, i) == vstar) ? 1 : 0;
+        int total;
+        const int before = block_scan_excl(tie, sh.scan, &total);
+        if (tie && run + before + 1 == need) sh.bcast[2] = i;
+        if (run + total >= need) {
+          __syncthreads();
+          istar = sh.bcast[2];
+        }
+        run += total;
+        __syncthreads();
+      }
+    }
+  }
+
+  // pass 3: mark and compact, one segment of 2^18 keys at a time
+  const int r0 = max(0, n - n_recent);
+  int written = 0;
+  int32_t* out = sel_idx + (size_t)row * stride;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  for (int seg0 = 0; seg0 < n; seg0 += kSegKeys) {
+    const int seg1 = min(n, seg0 + kSegKeys);
+    for (int base = seg0 + wave * kWave; base < seg1; base += kSelThreads) {
+      const int i = base + lane;
+      bool sel = false;
+      if (i < seg1) {
+        if (i >= r0) {
+          sel = true;
+        } else if (i < pool) {
+          const uint32_t key = skey(s, i);
+          sel = key > vstar || (key == vstar && i <= istar);
+        }
+      }
+      const uint64_t m = __ballot(sel);
+      const int w0 = (base - seg0) >> 5;
+      if (lane == 0) sh.bits[w0] = (uint32_t)m;
+      if (lane == 32 && w0 + 1 < kSegWords) sh.bits[w0 + 1] = (uint32_t)(m >> 32);
+    }
+    __syncthreads();
+    const int nwords = ceil_div(seg1 - seg0, 32);
+    const int per = ceil_div(nwords, kSelThreads);
+    int local = 0;
+    for (int j = 0; j < per; ++j) {
+      const int wi = tid * per + j;
+      if (wi < nwords) local += __popc(sh.bits[wi]);
+    }
+    int total;
+    int pos = written + block_scan_excl(local, sh.scan, &total);
+    for (int j = 0; j < per; ++j) {
+      const int wi = tid * per + j;
+      if (wi >= nwords) break;
+      uint32_t m = sh.bits[wi];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        if (pos < stride) out[pos] = seg0 + wi * 32 + bit;
+        ++pos;
+      }
+    }
+    written += total;
+    __syncthreads();
+  }
+  for (int p = written + tid; p < stride; p += kSelThreads) out[p] = -1;
+  if (tid == 0) sel_count[row] = written;
+}
+
+}  // namespace
+
 size_t select_ws_bytes(int, int, int, int) { return 0; }
-hipError_t launch_select(const SelectArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
+  const int rows = a.B * a.Hq;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
+                     a.Hq, a.Nmax, a.k_top, a.n_recent, (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0,
+                     a.sel_idx, a.sel_count, a.k_top + a.n_recent);
+  return hipGetLastError();
+}
+
 }  // namespace ssa

@@ -1,0 +1,216 @@
+"""GPU parity of ssa_select_topk_recent and ssa_decode_sparse against the CPU oracle.
+
+Selection is integer work: given the same float32 scores, the GPU's index sets
+must equal the oracle's exactly (ties to the lower index). When the scores
+come from each side's own full-layer pass, sets may differ only at keys whose
+score lies within the float32 rounding band of the cut.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_rows_close, score_bound
+from oracle import ssa_oracle as O
+from long_context_decode_relu_amd import ssa, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def fake_cache(B, Hkv, nmax, ctx):
+    k = torch.zeros((B, Hkv, max(nmax, 1), 128), dtype=torch.bfloat16, device=DEV)
+    return ssa.Cache(k=k, v=k, ctx_lens=torch.tensor(ctx, dtype=torch.int32, device=DEV),
+                     max_ctx_len=int(max(ctx)) if len(ctx) else 0)
+
+
+def run_select(scores_np, ctx, k_top=1024, n_recent=128, flags=0, Hkv=1):
+    B, Hq, nmax = scores_np.shape
+    cache = fake_cache(B, Hkv, nmax, ctx)
+    sc = torch.from_numpy(np.ascontiguousarray(scores_np, dtype=np.float32)).to(DEV)
+    sel, cnt = ssa.ssa_select_topk_recent(sc, cache, k_top=k_top, n_recent=n_recent, flags=flags)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), cnt.cpu().numpy()
+
+
+def check_select_exact(scores_np, ctx, k_top=1024, n_recent=128, flags=0):
+    sel, cnt = run_select(scores_np, ctx, k_top, n_recent, flags)
+    B, Hq, _ = scores_np.shape
+    disjoint = bool(flags & O.SSA_SELECT_DISJOINT)
+    for b in range(B):
+        for h in range(Hq):
+            want = O.select_topk_recent(scores_np[b, h].astype(np.float64), int(ctx[b]), k_top,
+                                        n_recent, disjoint)
+            c = int(cnt[b, h])
+            assert c == len(want), (b, h, c, len(want))
+            assert np.array_equal(sel[b, h, :c], want), (b, h)
+            assert np.all(sel[b, h, c:] == -1)
+
+
+@pytest.mark.parametrize("n", [0, 1, 127, 128, 129, 1023, 1024, 1025, 1151, 1152, 1153, 5000, 70001])
+def test_select_boundary_sizes(n):
+    rng = np.random.default_rng(n)
+    s = rng.standard_normal((1, 2, max(n, 1))).astype(np.float32)
+    check_select_exact(s, [n])
+
+
+def test_select_heavy_ties_and_signed_zero():
+    rng = np.random.default_rng(5)
+    n = 20000
+    s = rng.integers(-3, 4, size=(2, 3, n)).astype(np.float32)
+    s[0, 0, rng.random(n) < 0.3] = -0.0
+    s[1, 2] = 0.0  # every key ties
+    check_select_exact(s, [n, 17000])
+    check_select_exact(s, [n, 17000], k_top=100, n_recent=7)
+
+
+def test_select_all_equal_long_row():
+    """More keys tie at the cut than fit in LDS: the ordered tie pass decides."""
+    n = 300000
+    s = np.full((1, 1, n), 1.5, dtype=np.float32)
+    s[0, 0, ::97] = 2.0
+    check_select_exact(s, [n])
+
+
+def test_select_disjoint_and_small_k():
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal((3, 2, 9000)).astype(np.float32)
+    for flags in (0, O.SSA_SELECT_DISJOINT):
+        check_select_exact(s, [9000, 130, 1100], k_top=1024, n_recent=128, flags=flags)
+        check_select_exact(s, [9000, 5, 1], k_top=16, n_recent=0, flags=flags)
+        check_select_exact(s, [9000, 300, 64], k_top=1, n_recent=1, flags=flags)
+
+
+def test_select_negative_scores_pick_just_below_zero():
+    """Fewer than k positive scores: the rest are the keys scored just below zero."""
+    rng = np.random.default_rng(7)
+    n = 50000
+    s = -rng.random((1, 1, n)).astype(np.float32) - 0.01
+    s[0, 0, rng.choice(n, 300, replace=False)] = 1.0 + rng.random(300).astype(np.float32)
+    check_select_exact(s, [n])
+
+
+def test_select_after_full_layer_within_tie_band():
+    """Scores from each side's own full layer: sets agree except inside the rounding band of the cut."""
+    wl = synth.make_workload("selchain", seed=31, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[40000, 9000], recipe="planted", p=0.01)
+    cache = ssa.cache_from_workload(wl, DEV)
+    q = torch.from_numpy(wl.q).to(DEV)
+    _, scores, _, _ = ssa.ssa_decode_full(q, cache, want_scores=True)
+    sel, cnt = ssa.ssa_select_topk_recent(scores, cache)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    bounds = score_bound(wl, 1.0)
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        for h in range(16):
+            s = ref["scores"][b][h]
+            want = set(O.select_topk_recent(s, n).tolist())
+            got = set(sel[b, h, :cnt[b, h]].tolist())
+            order = np.lexsort((np.arange(n), -s))
+            cut = s[order[min(1024, n) - 1]]
+            band = 2 * float(bounds[b][h].max())
+            for i in want ^ got:
+                assert abs(s[i] - cut) <= band, (b, h, i, s[i], cut)
+
+
+# ---------------------------------------------------------------------------
+# sparse layer
+# ---------------------------------------------------------------------------
+
+def sel_tensors(selections, B, Hq, stride):
+    idx = np.full((B, Hq, stride), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hq), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            s = np.asarray(selections[b][h], dtype=np.int32)
+            idx[b, h, :len(s)] = s
+            cnt[b, h] = len(s)
+    return torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+
+
+def check_sparse(wl, selections, scale=None, flags=O.SSA_NORM_Q, stride=1152, qs=None, v_override=None):
+    qs = wl.q_sparse[0] if qs is None else qs
+    cache = ssa.cache_from_workload(wl, DEV)
+    if v_override is not None:
+        cache.v = ssa.kv_tensor(v_override, DEV)
+    si, sc = sel_tensors(selections, wl.batch, wl.n_q_heads, stride)
+    out = ssa.ssa_decode_sparse(torch.from_numpy(qs).to(DEV), cache, si, sc, scale=scale, flags=flags)
+    torch.cuda.synchronize()
+    ref = O.decode_sparse(qs, wl.k, wl.v, selections, scale=scale, flags=flags)
+    assert_rows_close(out.cpu().numpy(), ref, TOL_BF16 if wl.kv_dtype == "bf16" else TOL_F32, wl.name)
+    return out.cpu().numpy()
+
+
+def oracle_selection(wl):
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    return O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
+
+
+def test_sparse_single_sequence_bf16():
+    wl = synth.single_decode(n=9000)
+    check_sparse(wl, oracle_selection(wl))
+
+
+@pytest.mark.parametrize("hq,hkv,dtype", [(4, 4, "f32"), (4, 2, "bf16"), (8, 2, "bf16"), (16, 2, "f32"),
+                                          (8, 1, "bf16")])
+def test_sparse_group_sizes(hq, hkv, dtype):
+    wl = synth.make_workload("spg", seed=33, batch=2, n_q_heads=hq, n_kv_heads=hkv,
+                             ctx_lens=[6000, 700], kv_dtype=dtype, recipe="planted", p=0.1)
+    check_sparse(wl, oracle_selection(wl))
+
+
+def test_sparse_short_context_is_full_softmax_and_empty():
+    """n <= 1024: every key is selected; an empty selection returns 0."""
+    wl = synth.make_workload("spshort", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[900, 1, 0], recipe="iid")
+    sels = oracle_selection(wl)
+    out = check_sparse(wl, sels)
+    assert np.all(out[2] == 0.0)
+
+
+def test_sparse_scale_flags_and_nan_poison():
+    """Rows no head selected are never read: poisoning them with NaN changes nothing."""
+    wl = synth.make_workload("sppois", seed=35, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[12000, 5000], recipe="planted", p=0.02)
+    sels = oracle_selection(wl)
+    base = check_sparse(wl, sels)
+    v = wl.v.copy()
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        for kvh in range(2):
+            used = np.zeros(n, dtype=bool)
+            for h in range(kvh * 8, kvh * 8 + 8):
+                used[sels[b][h]] = True
+            v[b, kvh, :n][~used] = synth.BF16_NAN
+    again = check_sparse(wl, sels, v_override=v)
+    assert np.array_equal(again, base)
+    check_sparse(wl, sels, scale=0.3, flags=0)
+    wl.k = synth.to_bf16_bits(synth.bf16_bits_to_f32(wl.k) * np.float32(1.7))
+    check_sparse(wl, sels, flags=O.SSA_NORM_Q | O.SSA_NORM_K)
+
+
+def test_block_step_sampled_full_size():
+    """The batch-8 64K-128K workload end to end: full layer -> selection -> sparse layer.
+
+    Every sparse output is compared with the oracle run on the oracle's own
+    selection; heads whose GPU selection differs from the oracle's (only
+    possible inside the rounding band of the cut) are compared on the GPU's
+    selection instead.
+    """
+    wl = synth.batched_decode()
+    cache = ssa.cache_from_workload(wl, DEV)
+    q = torch.from_numpy(wl.q).to(DEV)
+    _, scores, _, _ = ssa.ssa_decode_full(q, cache, want_scores=True)
+    sel, cnt = ssa.ssa_select_topk_recent(scores, cache)
+    out = ssa.ssa_decode_sparse(torch.from_numpy(wl.q_sparse[0]).to(DEV), cache, sel, cnt)
+    torch.cuda.synchronize()
+    sel, cnt, out = sel.cpu().numpy(), cnt.cpu().numpy(), out.cpu().numpy()
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    osel = O.select_all(ref["scores"], wl.ctx_lens)
+    gsel = [[sel[b, h, :cnt[b, h]] for h in range(16)] for b in range(wl.batch)]
+    same = [[np.array_equal(gsel[b][h], osel[b][h]) for h in range(16)] for b in range(wl.batch)]
+    assert np.mean(same) > 0.9
+    use = [[osel[b][h] if same[b][h] else gsel[b][h] for h in range(16)] for b in range(wl.batch)]
+    want = O.decode_sparse(wl.q_sparse[0], wl.k, wl.v, use)
+    assert_rows_close(out, want, TOL_BF16, "block step sparse")
