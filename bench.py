@@ -68,6 +68,31 @@ def alg_bytes_full(wl, vrows: np.ndarray, with_scores: bool = True) -> dict:
             "v_dense": int(wl.n_kv_heads * D * kvb * n.sum())}
 
 
+PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_step_b8_64k_128k.txt")
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_decode_relu_amd", "csrc",
+                          "decode_full.hip")
+
+
+def measured_traffic():
+    """HBM bytes per ssa_decode_full call from the committed counter summary.
+
+    The summary records the bytes (calibrated FETCH_SIZE + WRITE_SIZE of the
+    prep, main and combine kernels) and the hash of the kernel source they
+    were taken on; once the source changes the figure no longer applies.
+    """
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE).read()
+        m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)", text)
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if m and m.group(2) == src:
+        return int(m.group(1))
+    return None
+
+
 def copy_probe():
     import torch
     n = 1 << 30
@@ -81,28 +106,31 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
 
 
-def cpu_baseline(wl) -> dict:
-    """The CPU oracle, as it stands, on the whole batch (about 10-30 s on a server CPU)."""
+def cpu_baseline(wl, reps: int = 3) -> dict:
+    """The CPU oracle, as it stands, on the whole batch: full layer, selection, one sparse layer."""
     from oracle import ssa_oracle as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = 1
-    t0 = time.perf_counter()
-    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
-    sel = O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
-    O.decode_sparse(wl.q_sparse[0], wl.k, wl.v, sel)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+        sel = O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
+        O.decode_sparse(wl.q_sparse[0], wl.k, wl.v, sel)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     kv = alg_bytes_full(wl, ref["vrows"], with_scores=False)
-    sparse_rows = sum(len(functools.reduce(np.union1d, sel[b][kvh * 8:(kvh + 1) * 8]))
+    g = wl.n_q_heads // wl.n_kv_heads
+    sparse_rows = sum(len(functools.reduce(np.union1d, sel[b][kvh * g:(kvh + 1) * g]))
                       for b in range(wl.batch) for kvh in range(wl.n_kv_heads))
-    kvb = 2
-    kv_total = kv["k"] + kv["v"] + 2 * wl.head_dim * kvb * sparse_rows
+    kv_total = kv["k"] + kv["v"] + 2 * wl.head_dim * 2 * sparse_rows
     return {"value": round(kv_total / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "query_tok_per_s": round(wl.batch / dt, 3), "seconds": round(dt, 2),
-            "sample": f"the whole batch ({wl.batch} sequences, {int(wl.ctx_lens.sum())} keys per KV "
-                      "head): full layer, selection and one sparse layer, float64 NumPy, one pass"}
+            "kind": "oracle", "query_tok_per_s": round(wl.batch / dt, 3), "seconds_per_step": round(dt, 3),
+            "sample": f"the whole batch ({wl.batch} sequences, {int(wl.ctx_lens.sum())} keys per KV head): "
+                      f"full layer, selection and one sparse layer in float64 NumPy; median of {reps} passes"}
 
 
 def main():
@@ -131,6 +159,17 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws_full = ssa.workspace(ssa.SSA_OP_DECODE_FULL, caches[0].shape(Hq), 0, dev)
 
+    qs = torch.from_numpy(wl.q_sparse[0]).to(dev)
+    stride = 1024 + 128
+    sel = torch.empty((B, Hq, stride), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    out_sp = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    shp = caches[0].shape(Hq)
+    ws_sel = ssa.workspace(ssa.SSA_OP_SELECT, shp, stride, dev)
+    ws_sp = ssa.workspace(ssa.SSA_OP_DECODE_SPARSE, shp, stride, dev)
+    L = ssa.lib()
+    import ctypes
+
     def step(i, ev=None):
         c = caches[i % len(caches)]
         if ev is not None:
@@ -138,36 +177,64 @@ def main():
         ssa.ssa_decode_full(q, c, out=out, scores=scores, ws=ws_full, want_scores=True)
         if ev is not None:
             ev[1].record()
+        st = L.ssa_select_topk_recent(ctypes.byref(shp), scores.data_ptr(), c.ctx_lens.data_ptr(),
+                                      1024, 128, 0, sel.data_ptr(), cnt.data_ptr(), ws_sel.data_ptr(),
+                                      ws_sel.numel(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+        if ev is not None:
+            ev[2].record()
+        ssa.ssa_decode_sparse(qs, c, sel, cnt, out=out_sp, ws=ws_sp)
+        if ev is not None:
+            ev[3].record()
 
-    # stats once (not timed): rows fetched, for the algorithmic byte count
-    _, _, nnz, vrows = ssa.ssa_decode_full(q, caches[0], want_scores=True, want_stats=True)
+    # stats once (not timed): rows fetched and rows gathered, for the algorithmic byte counts
+    _, _, nnz, vrows = ssa.ssa_decode_full(q, caches[0], want_scores=True, want_stats=True,
+                                           scores=scores)
+    step(0)
     torch.cuda.synchronize()
     vrows_np = vrows.cpu().numpy()
     nnz_np = nnz.cpu().numpy()
+    sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    g = Hq // wl.n_kv_heads
+    union_rows = 0
+    for b in range(B):
+        for kvh in range(wl.n_kv_heads):
+            u = set()
+            for h in range(kvh * g, (kvh + 1) * g):
+                u.update(sel_np[b, h, :cnt_np[b, h]].tolist())
+            union_rows += len(u)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    full_ms = [a.elapsed_time(b) for a, b in evs]
+    full_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sel_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    sp_ms = [e[2].elapsed_time(e[3]) for e in evs]
     log(f"[bench] timed {args.steps} steps in {wall:.3f}s")
 
     ms_step = wall * 1e3 / args.steps
     ab = alg_bytes_full(wl, vrows_np)
-    kv_read = ab["k"] + ab["v"]
+    kvb = 2
+    sparse_bytes = 2 * D * kvb * union_rows
+    kv_read = ab["k"] + ab["v"] + sparse_bytes
     full_alg = ab["k"] + ab["v"] + ab["q_out"] + ab["scores"]
+    sel_alg = ab["scores"] + 4 * B * Hq * stride
     full_avg_ms = float(np.mean(full_ms))
     achieved = full_alg / (full_avg_ms * 1e-3) / 1e9
     value = kv_read / (ms_step * 1e-3) / 1e9
+
+    def op(ms_list, nbytes):
+        m = float(np.mean(ms_list))
+        return {"avg_ms": round(m, 4), "alg_bytes": int(nbytes), "gb_s": round(nbytes / (m * 1e-3) / 1e9, 1)}
 
     res = {
         "metric": "KV GB/s (% of HBM peak) + query-tok/s, ReLU² decode, 128K ctx, batch 8",
@@ -184,19 +251,22 @@ def main():
         "data": "synthetic (seeded planted-direction keys, 95% sparsity)",
         "config": {"workload": WORKLOAD if args.fixed_len is None else f"batched_decode_b8_fixed{args.fixed_len}",
                    "batch": B, "n_q_heads": Hq, "n_kv_heads": wl.n_kv_heads, "head_dim": D,
-                   "ctx_lens": wl.ctx_lens.tolist(), "kv_capacity": Nmax,
-                   "step": "ssa_decode_full"},
+                   "ctx_lens": wl.ctx_lens.tolist(), "kv_capacity": Nmax, "k_top": 1024, "n_recent": 128,
+                   "step": "ssa_decode_full + ssa_select_topk_recent + ssa_decode_sparse"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "query_tok_per_s": round(B / (ms_step * 1e-3), 1),
-        "kv_bytes_read_per_step": kv_read,
+        "kv_bytes_read_per_step": int(kv_read),
+        "ops": {"decode_full": op(full_ms, full_alg), "select": op(sel_ms, sel_alg),
+                "decode_sparse": op(sp_ms, sparse_bytes)},
         "vskip": {"v_rows_fetched": int(vrows_np.sum()),
                   "v_rows_dense": int(wl.n_kv_heads * wl.ctx_lens.astype(np.int64).sum()),
                   "v_traffic_saved": round(1 - ab["v"] / ab["v_dense"], 4),
                   "measured_zero_weight_fraction": round(
                       1 - float(nnz_np.sum()) / (Hq * float(wl.ctx_lens.astype(np.int64).sum())), 4)},
-        "roofline": {"kernel": "ssa_decode_full (decode_full_kernel + decode_full_combine)",
+        "sparse_union_rows": int(union_rows),
+        "roofline": {"kernel": "ssa_decode_full (prep + decode_full_kernel + combine)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},
     }
     if not args.no_cpu_baseline:
