@@ -43,6 +43,23 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum across the 64 lanes of a wave with DPP moves within rows of 16 lanes and
+// read-lanes across the four rows; every lane receives the bitwise-same total.
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_move<0x141>(x);  // row_half_mirror: the other quad of the half row
+  x += dpp_move<0x140>(x);  // row_mirror: the other half of the row
+  const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16);
+  const float r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Order-preserving map of a float's bits to uint32 (larger float -> larger key).
 // -0.0 is mapped like +0.0 so that the two compare equal.
 __device__ __forceinline__ uint32_t ordered_key(float x) {

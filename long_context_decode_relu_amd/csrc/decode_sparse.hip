@@ -10,7 +10,8 @@
 // (sequence, KV head, range of 4096 keys): it marks, per key of the range, the
 // heads whose selection holds it (LDS bitmask), compacts the marked keys in
 // key order and then streams their K and V rows, 16 rows per batch with all
-// loads of a batch in flight together. Each wave keeps an online softmax
+// loads of a batch in flight together. Per row, each head's dot product is
+// summed across the wave with DPP moves (no LDS round trips). Each wave keeps an online softmax
 // (running max m, sum l, accumulator acc) per head; the waves, and then the
 // ranges (in a second kernel), are merged by log-sum-exp in a fixed order.
 #include <cmath>
@@ -39,16 +40,6 @@ __device__ __forceinline__ float2 load_pair(const void* base, size_t row, int la
   }
 }
 
-// First position in the ascending list[0..cnt) whose value is >= x (uniform).
-__device__ __forceinline__ int lower_bound(const int32_t* list, int cnt, int x) {
-  int lo = 0, hi = cnt;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (list[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
 template <int G, bool BF16, bool NORMQ, bool NORMK>
 __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -72,17 +63,25 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
 
   for (int i = tid; i < kRange / 4; i += kSpThreads) s_mask[i] = 0;
   __syncthreads();
-  // 1. head bits per key of the range
+  // 1. head bits per key of the range: each wave scans whole selection lists
+  //    (all loads of a list in flight together) and marks the entries in range
   for (int h = wave; h < G; h += kSpWaves) {
     const size_t row = (size_t)b * Hq + (size_t)kvh * G + h;
     const int32_t* list = sel_idx + row * stride;
     const int cnt = min(sel_count[row], stride);
-    const int a0 = lower_bound(list, cnt, lo), a1 = lower_bound(list, cnt, hi);
-    for (int i = a0 + lane; i < a1; i += kWave) {
-      const int idx = list[i];
-      if (idx >= lo && idx < hi) {
-        const int off = idx - lo;
-        atomicOr(&s_mask[off >> 2], 1u << (h + 8 * (off & 3)));
+    for (int i0 = 0; i0 < cnt; i0 += kWave * 8) {
+      int idx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) idx[u] = list[min(i0 + u * kWave + lane, cnt - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * kWave + lane >= cnt) idx[u] = -1;  // unconditional loads, masked after
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (idx[u] >= lo && idx[u] < hi) {
+          const int off = idx[u] - lo;
+          atomicOr(&s_mask[off >> 2], 1u << (h + 8 * (off & 3)));
+        }
       }
     }
   }
@@ -113,14 +112,16 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
   }
   __syncthreads();
 
-  // 3. queries of the group: lane owns dims (2*lane, 2*lane+1); scale folded in
+  // 3. queries of the group: lane owns dims (2*lane, 2*lane+1). The softmax
+  //    runs in base 2, so scale * log2(e) is folded into the query:
+  //    exp(t - m) = exp2(t2 - m2) with t2 = t * log2(e).
   const float* qg = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
   float qa[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float a0 = qg[h * kHeadDim + 2 * lane], a1 = qg[h * kHeadDim + 2 * lane + 1];
-    float f = scale;
-    if constexpr (NORMQ) f = scale / sqrtf(wave_sum(a0 * a0 + a1 * a1) * (1.0f / kHeadDim) + eps);
+    float f = scale * 1.4426950408889634f;
+    if constexpr (NORMQ) f = f / sqrtf(wave_sum(a0 * a0 + a1 * a1) * (1.0f / kHeadDim) + eps);
     qa[h][0] = a0 * f;
     qa[h][1] = a1 * f;
   }
@@ -147,24 +148,26 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
       if (u >= nb) break;
       float kf = 1.f;
       if constexpr (NORMK)
-        kf = 1.f / sqrtf(wave_sum(kk[u].x * kk[u].x + kk[u].y * kk[u].y) * (1.0f / kHeadDim) + eps);
+        kf = 1.f / sqrtf(wave_sum_dpp(kk[u].x * kk[u].x + kk[u].y * kk[u].y) * (1.0f / kHeadDim) + eps);
       const int hb = ent[u] & 0xff;
+      // all heads' dot products, reduced together (independent chains)
+      float t[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) t[h] = fmaf(qa[h][0], kk[u].x, qa[h][1] * kk[u].y);
+#pragma unroll
+      for (int h = 0; h < G; ++h) t[h] = wave_sum_dpp(t[h]) * kf;
+      // online softmax (base 2); heads that did not select this row keep their state
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        if (!((hb >> h) & 1)) continue;  // uniform: the row's head bits
-        const float t = wave_sum(fmaf(qa[h][0], kk[u].x, qa[h][1] * kk[u].y)) * kf;
-        if (t > m[h]) {
-          const float sc = expf(m[h] - t);  // 0 when m was -inf
-          l[h] = l[h] * sc + 1.f;
-          acc[h][0] = fmaf(acc[h][0], sc, vv[u].x);
-          acc[h][1] = fmaf(acc[h][1], sc, vv[u].y);
-          m[h] = t;
-        } else {
-          const float e = expf(t - m[h]);
-          l[h] += e;
-          acc[h][0] = fmaf(e, vv[u].x, acc[h][0]);
-          acc[h][1] = fmaf(e, vv[u].y, acc[h][1]);
-        }
+        const bool on = (hb >> h) & 1;
+        const float mn = on ? fmaxf(m[h], t[h]) : m[h];
+        // 1 when the max is unchanged, 0 when it rises from -inf (no row yet)
+        const float sc = mn == -INFINITY ? 1.f : exp2f(m[h] - mn);
+        const float e = on ? exp2f(t[h] - mn) : 0.f;
+        l[h] = fmaf(l[h], sc, e);
+        acc[h][0] = fmaf(acc[h][0], sc, e * vv[u].x);
+        acc[h][1] = fmaf(acc[h][1], sc, e * vv[u].y);
+        m[h] = mn;
       }
     }
   }
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kSpWaves; ++w) {
-        const float e = s_m[w][h] == -INFINITY ? 0.f : expf(s_m[w][h] - M);
+        const float e = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
         a = fmaf(e, s_acc[w][h][d], a);
         ls = fmaf(e, s_l[w][h], ls);
       }
@@ -200,7 +203,8 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
   }
 }
 
-// out[b][h] = sum_p exp(m_p - M) acc_p / sum_p exp(m_p - M) l_p over the ranges
+// out[b][h] = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p over the ranges (the running
+// maxima are kept in base-2 units)
 // p of the sequence, in range order; 0 for an empty selection.
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
@@ -218,7 +222,7 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(
     for (int p = 0; p < pb; ++p) {
       const float mp = part_m[(s0 + p) * G + jh];
       if (mp == -INFINITY) continue;
-      const float e = expf(mp - M);
+      const float e = exp2f(mp - M);
       a = fmaf(e, part_acc[((s0 + p) * G + jh) * kHeadDim + d], a);
       ls = fmaf(e, part_l[(s0 + p) * G + jh], ls);
     }

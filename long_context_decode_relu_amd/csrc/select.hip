@@ -10,16 +10,22 @@
 // cut is found as a key value v* plus an index i*: a key is in the top k when
 // key > v*, or key == v* and its index <= i* (ties go to the lower index).
 //
-//   pass 1  histogram of the top 12 key bits over the pool (LDS atomics)
-//   pass 2  keys in the bin holding the cut (typically a few hundred) are
-//           gathered into LDS; the remaining 20 bits and the tie index are
-//           resolved there by 10-bit radix passes.
+//   pass 1  histogram of the top 13 key bits over the pool. Scores cluster
+//           (most keys of a planted cache share one or two bins), so each
+//           wave first adds whole groups of lanes that share a bin with one
+//           LDS atomic, and only the leftovers add one by one.
+//   pass 2  keys in the bin holding the cut (typically a few thousand) are
+//           gathered into LDS while the keys above it are marked in an LDS
+//           bitmap; the remaining bits and the tie index are resolved in LDS
+//           by 10-bit radix passes.
 //           If that bin is too large for LDS, further 10-bit histogram
 //           passes over global memory narrow it first; if all 32 bits are
 //           resolved and the tied keys still do not fit, the tie index is
 //           found by an ordered pass.
-//   pass 3  per segment of 2^18 keys: mark (top-k) union (recent window) in an
-//           LDS bitmap, then compact the bitmap into ascending indices.
+//   pass 3  the selected candidates and the recent window are added to the
+//           bitmap, which is compacted into ascending indices. Rows longer
+//           than 2^18 keys (one bitmap) are marked and compacted segment by
+//           segment in an extra pass.
 //
 // The pool is [0, n) (union with the window, duplicates removed) or, with
 // SSA_SELECT_DISJOINT, [0, n - n_recent).
@@ -35,8 +41,9 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kBins = 4096;       // first-pass histogram (12 bits)
-constexpr int kCap = 4096;        // candidates held in LDS
+constexpr int kBits1 = 13;        // first-pass histogram digit
+constexpr int kBins = 1 << kBits1;
+constexpr int kCap = 8192;        // candidates held in LDS
 constexpr int kSegKeys = 1 << 18; // keys per output segment (LDS bitmap of 32 KB)
 constexpr int kSegWords = kSegKeys / 32;
 
@@ -52,6 +59,41 @@ struct SelShared {
 
 // Order-preserving key of a score (see ordered_key in common.h).
 __device__ __forceinline__ uint32_t skey(const float* s, int i) { return ordered_key(s[i]); }
+
+// kUnroll keys per thread are loaded before any is used, so that a pass over
+// a row keeps kUnroll loads per lane in flight instead of one.
+constexpr int kUnroll = 16;
+
+// keys[u] = key of position first + u*step for positions < end (end >= 1).
+// Positions past the end load position end-1 instead: the loads carry no
+// condition, so all kUnroll of them are issued before the first wait; the
+// callers mask those lanes out.
+__device__ __forceinline__ void load_keys(const float* s, int first, int step, int end,
+                                          uint32_t (&keys)[kUnroll]) {
+  float v[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) v[u] = s[min(first + u * step, end - 1)];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) keys[u] = ordered_key(v[u]);
+}
+
+// hist[bin] += 1 for every active lane, aggregating lanes that share a bin:
+// up to four distinct bins per wave are added with one atomic each, the rest
+// (scattered bins, little contention) one by one.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool act) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const uint64_t m = __ballot(act);
+    if (!m) return;
+    const int leader = __builtin_ctzll(m);
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+    const uint64_t same = __ballot(act && bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    act = act && bin != lb;
+  }
+  if (act) atomicAdd(&hist[bin], 1u);
+}
 
 // Exclusive prefix over the work-group of one int per thread; returns the
 // thread's prefix and writes the total to *total.
@@ -118,10 +160,10 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
     const int nb = 1 << D;
     for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < c; i += kSelThreads) {
-      const uint32_t key = sh.ckey[i];
-      const bool match = L == 0 ? true : (key >> (32 - L)) == P;
-      if (match) atomicAdd(&sh.hist[(key >> (32 - L - D)) & (nb - 1)], 1u);
+    for (int base = 0; base < c; base += kSelThreads) {
+      const int i = base + tid;
+      const uint32_t key = i < c ? sh.ckey[i] : 0u;
+      hist_add(sh.hist, (key >> (32 - L - D)) & (nb - 1), i < c && (key >> (32 - L)) == P);
     }
     __syncthreads();
     int above;
@@ -147,11 +189,12 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
     const int nb = 1 << D;
     for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < c; i += kSelThreads) {
-      if (sh.ckey[i] != P) continue;
-      const uint32_t ci = ~(uint32_t)sh.cidx[i];
-      const bool match = M == 0 ? true : (ci >> (32 - M)) == Q;
-      if (match) atomicAdd(&sh.hist[(ci >> (32 - M - D)) & (nb - 1)], 1u);
+    for (int base = 0; base < c; base += kSelThreads) {
+      const int i = base + tid;
+      const bool tie = i < c && sh.ckey[i] == P;
+      const uint32_t ci = tie ? ~(uint32_t)sh.cidx[i] : 0u;
+      const bool match = tie && (M == 0 || (ci >> (32 - M)) == Q);
+      hist_add(sh.hist, (ci >> (32 - M - D)) & (nb - 1), match);
     }
     __syncthreads();
     int above;
@@ -179,17 +222,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   uint32_t vstar = 0;
   int istar = INT_MAX;  // k == pool: every pool key is selected
+  bool marked = false;  // bitmap already holds the keys above the cut bin
   if (k < pool) {
     // pass 1: histogram of the top 12 bits
     for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < pool; i += kSelThreads) atomicAdd(&sh.hist[skey(s, i) >> 20], 1u);
+    for (int base = 0; base < pool; base += kSelThreads * kUnroll) {
+      uint32_t keys[kUnroll];
+      load_keys(s, base + tid, kSelThreads, pool, keys);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const bool act = base + u * kSelThreads + tid < pool;
+        hist_add(sh.hist, keys[u] >> (32 - kBits1), act);
+      }
+    }
     __syncthreads();
     int above;
     const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
     int need = k - above;
     uint32_t P = (uint32_t)d1;
-    int L = 12;
+    int L = kBits1;
     int c = (int)sh.hist[d1];
     __syncthreads();
     // narrow the cut bin over global memory until it fits in LDS
@@ -198,9 +250,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       const int nb = 1 << D;
       for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < pool; i += kSelThreads) {
-        const uint32_t key = skey(s, i);
-        if ((key >> (32 - L)) == P) atomicAdd(&sh.hist[(key >> (32 - L - D)) & (nb - 1)], 1u);
+      for (int base = 0; base < pool; base += kSelThreads * kUnroll) {
+        uint32_t keys[kUnroll];
+        load_keys(s, base + tid, kSelThreads, pool, keys);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const bool act = base + u * kSelThreads + tid < pool && (keys[u] >> (32 - L)) == P;
+          hist_add(sh.hist, (keys[u] >> (32 - L - D)) & (nb - 1), act);
+        }
       }
       __syncthreads();
       const int d = threshold_bin(sh.hist, nb, need, sh, &above);
@@ -211,19 +268,41 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       __syncthreads();
     }
     if (c <= kCap) {
-      // pass 2: gather the keys of the cut bin
+      // pass 2: gather the keys of the cut bin; for a single-segment row also
+      // mark the keys above it in the bitmap (one word per 32 keys)
       if (tid == 0) sh.ccount = 0;
       __syncthreads();
-      for (int i = tid; i < pool; i += kSelThreads) {
-        const uint32_t key = skey(s, i);
-        if ((L == 32 ? key : key >> (32 - L)) == P) {
-          const int pos = atomicAdd(&sh.ccount, 1);
+      const int lane = tid & (kWave - 1), wave = tid >> 6;
+      for (int base0 = wave * kWave; base0 < pool; base0 += kSelThreads * kUnroll) {
+       uint32_t keys[kUnroll];
+       load_keys(s, base0 + lane, kSelThreads, pool, keys);
+#pragma unroll
+       for (int u = 0; u < kUnroll; ++u) {
+        const int base = base0 + u * kSelThreads;
+        if (base >= pool) break;
+        const int i = base + lane;
+        const uint32_t key = keys[u];
+        const uint32_t pre = L == 32 ? key : key >> (32 - L);
+        const bool cand = i < pool && pre == P;
+        const uint64_t cm = __ballot(cand);
+        int wbase = 0;
+        if (lane == 0 && cm) wbase = atomicAdd(&sh.ccount, __popcll(cm));
+        wbase = __builtin_amdgcn_readfirstlane(wbase);
+        if (cand) {
+          const int pos = wbase + __popcll(cm & ((1ull << lane) - 1));
           sh.ckey[pos] = key;
           sh.cidx[pos] = i;
         }
+        if (n <= kSegKeys) {
+          const uint64_t am = __ballot(i < pool && pre > P);
+          if (lane == 0) sh.bits[base >> 5] = (uint32_t)am;
+          if (lane == 32) sh.bits[(base >> 5) + 1] = (uint32_t)(am >> 32);
+        }
+       }
       }
       __syncthreads();
       finish_in_lds(sh, c, P, L, need, &vstar, &istar);
+      marked = n <= kSegKeys;
     } else {
       // all 32 bits known and more than kCap keys tie at v*: the need-th
       // smallest tied index, by an ordered pass over blocks of the row
@@ -251,23 +330,45 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   int written = 0;
   int32_t* out = sel_idx + (size_t)row * stride;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
+  if (marked) {
+    // single segment, keys above the cut bin already marked: add the selected
+    // candidates and the recent window (bits of words past the pool are 0)
+    const int c = sh.ccount;
+    for (int j = tid; j < c; j += kSelThreads) {
+      const uint32_t key = sh.ckey[j];
+      const int i = sh.cidx[j];
+      if (key > vstar || (key == vstar && i <= istar)) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+    }
+    const int pw = ceil_div(pool, kWave) * 2;  // words written by pass 2
+    for (int wi = pw + tid; wi < ceil_div(n, 32); wi += kSelThreads) sh.bits[wi] = 0u;
+    __syncthreads();
+    for (int i = r0 + tid; i < n; i += kSelThreads) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+    __syncthreads();
+  }
   for (int seg0 = 0; seg0 < n; seg0 += kSegKeys) {
     const int seg1 = min(n, seg0 + kSegKeys);
-    for (int base = seg0 + wave * kWave; base < seg1; base += kSelThreads) {
-      const int i = base + lane;
-      bool sel = false;
-      if (i < seg1) {
-        if (i >= r0) {
-          sel = true;
-        } else if (i < pool) {
-          const uint32_t key = skey(s, i);
-          sel = key > vstar || (key == vstar && i <= istar);
+    for (int base0 = seg0 + wave * kWave; base0 < seg1 && !marked; base0 += kSelThreads * kUnroll) {
+      uint32_t keys[kUnroll];
+      const int kend = min(seg1, pool);
+      if (kend > 0) load_keys(s, base0 + lane, kSelThreads, kend, keys);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int base = base0 + u * kSelThreads;
+        if (base >= seg1) break;
+        const int i = base + lane;
+        bool sel = false;
+        if (i < seg1) {
+          if (i >= r0) {
+            sel = true;
+          } else if (i < pool) {
+            sel = keys[u] > vstar || (keys[u] == vstar && i <= istar);
+          }
         }
+        const uint64_t m = __ballot(sel);
+        const int w0 = (base - seg0) >> 5;
+        if (lane == 0) sh.bits[w0] = (uint32_t)m;
+        if (lane == 32 && w0 + 1 < kSegWords) sh.bits[w0 + 1] = (uint32_t)(m >> 32);
       }
-      const uint64_t m = __ballot(sel);
-      const int w0 = (base - seg0) >> 5;
-      if (lane == 0) sh.bits[w0] = (uint32_t)m;
-      if (lane == 32 && w0 + 1 < kSegWords) sh.bits[w0 + 1] = (uint32_t)(m >> 32);
     }
     __syncthreads();
     const int nwords = ceil_div(seg1 - seg0, 32);
