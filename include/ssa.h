@@ -157,8 +157,13 @@ ssa_status ssa_decode_sparse(const ssa_shape* shape, const float* q, const void*
  * 0 .. q_pos0[b] + t. q_pos0[b] + Tq must not exceed ctx_lens[b] (the cache
  * already holds the chunk's own keys). k, v must be SSA_BF16.
  * out [B, Hq, Tq, D] float32. The products run on the matrix cores in bf16
- * with float32 accumulation; the normalised query and the weights are
- * rounded to bf16 before their products. */
+ * with float32 accumulation; the scaled normalised query and the weights are
+ * each carried as a sum of two bf16 values (about 16 significant bits), so
+ * the result stays within the bf16-cache tolerance of the exact value.
+ * Rows whose position falls outside [0, ctx_lens[b]) attend only the keys
+ * below min(position + 1, ctx_lens[b]); no such access leaves the cache.
+ * Workspace: ssa_workspace_bytes(SSA_OP_PREFILL_FULL, shape, n_query), which
+ * holds V repacked for the matrix cores and the split-key partial sums. */
 ssa_status ssa_prefill_full(const ssa_shape* shape, const void* q, int32_t n_query,
                             const int32_t* q_pos0, const int32_t* ctx_lens, const void* k,
                             const void* v, float scale, float c, float eps, uint32_t flags,

@@ -1,7 +1,420 @@
-// Chunked ReLU^2 prefill on the matrix cores (placeholder until the kernel lands).
+// Chunked causal ReLU^2 prefill on the gfx950 matrix cores.
+//
+// Query t of sequence b sits at position q_pos0[b] + t and attends cache rows
+// 0 .. q_pos0[b] + t with the full layer's weights w = ReLU(scale * q_hat . k)^2
+// and output sum(w v) / (c + sum w) ("The Architecture of Embla 1": "Sevren
+// Sparse Attention learns to be sparse" for the weights, "KV bridge, KV reuse,
+// and prefill" for the chunked prompt pass).
+//
+// Both products are dense contractions and run on v_mfma_f32_32x32x16_bf16:
+//   S^T[key][row] = sum_d K[key][d] * Qs[row][d]      (A = K tile, B = Qs^T)
+//   O[row][d]    += sum_key W[row][key] * V[key][d]   (A = W, B = V tile)
+// K and V are bf16 and exact. The scaled normalised query Qs and the weights W
+// are float; each is carried as hi + lo, two bf16 values whose sum keeps about
+// 16 significant bits, so every product is issued twice (hi and lo) and
+// accumulated in float. A single bf16 copy of either operand would put the
+// relative output error near 3e-3.
+//
+// Rows of a workgroup are (position, head) pairs of one KV head, head fastest,
+// so the G query heads that share a KV head read each K/V tile once. Four
+// waves own 32 rows each; a 32-key tile of K (8 KB) and of V (8 KB) is staged
+// in LDS with direct-to-LDS loads, double-buffered. K is fetched straight into
+// the A-fragment order of the MFMA; V would need a transpose, so a first pass
+// packs V once into B-fragment order in the workspace (zero past ctx_lens).
+// Long key ranges are split over S workgroups whose partial sums are added in
+// a fixed order by a combine pass (the weights carry no running maximum, so
+// partials add without rescaling).
+#include <algorithm>
+#include <cstdio>
+
+#include "common.h"
 #include "kernels.h"
 
 namespace ssa {
-size_t prefill_ws_bytes(int, int, int, int, int) { return 0; }
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;         // four waves
+constexpr int kRowsPerBlock = 128;    // (position, head) rows per workgroup
+constexpr int kKeyTile = 32;          // keys per tile
+constexpr int kFragBytes = 1024;      // one MFMA operand fragment: 64 lanes x 16 B
+constexpr int kTileBytes = 8 * kFragBytes;  // 32 keys x 128 dims x bf16
+constexpr int kMaxSplit = 16;
+constexpr int kTargetBlocks = 512;    // two resident workgroups per CU on 256 CUs
+constexpr int kWaitVm0 = 0x0F70;      // s_waitcnt vmcnt(0)
+
+__device__ __forceinline__ uint32_t bits2(bf16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+
+// (a, b) -> packed bf16 hi pair and lo pair with a ~= hi + lo to ~2^-17.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  bf16x2 h;
+  h[0] = (__bf16)a;
+  h[1] = (__bf16)b;
+  hi = bits2(h);
+  bf16x2 l;
+  l[0] = (__bf16)(a - bf16_lo(hi));
+  l[1] = (__bf16)(b - bf16_hi(hi));
+  lo = bits2(l);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// ---------------------------------------------------------------------------
+// V packing: vp[bkv][tile][f = 2*nb + s][lane][j] =
+//   V[tile*32 + 16*s + 8*(j/4) + 4*(lane/32) + (j%4)][32*nb + lane%32]
+// which is the B fragment of k-step s (16 keys) for dims 32*nb .. 32*nb+31.
+// The key order inside a k-step matches the rows the S^T accumulator hands
+// each lane (see prefill_kernel), so W needs no shuffle. Keys >= ctx_lens[b]
+// are written as zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void prefill_pack_v(const uint16_t* __restrict__ v,
+                                                           const int32_t* __restrict__ ctx_lens,
+                                                           int Hkv, int Nmax, int max_ctx,
+                                                           int ntiles, uint16_t* __restrict__ vp) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kKeyTile][kHeadDim];
+  const int tile = blockIdx.x;
+  const int bkv = blockIdx.y;
+  const int b = bkv / Hkv;
+  const int n = min(ctx_lens[b], max_ctx);
+  const int tid = threadIdx.x;
+  const uint16_t* src = v + (size_t)bkv * Nmax * kHeadDim;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + u * kThreads;  // 16-byte chunk of the tile
+    const int key = tile * kKeyTile + c / 16;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < n) x = *reinterpret_cast<const u32x4*>(src + (size_t)key * kHeadDim + (c % 16) * 8);
+    *reinterpret_cast<u32x4*>(&s_v[c / 16][(c % 16) * 8]) = x;
+  }
+  __syncthreads();
+  uint16_t* dst = vp + ((size_t)bkv * ntiles + tile) * (kTileBytes / 2);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int idx = tid + u * kThreads;  // fragment f = idx / 64, lane = idx % 64
+    const int f = idx / 64, lane = idx % 64;
+    const int nb = f / 2, s = f % 2;
+    const int d = 32 * nb + lane % 32;
+    const int kb = 16 * s + 4 * (lane / 32);
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // slots j = 2p, 2p+1 -> keys kb + 8*(j/4) + j%4
+      const int j0 = 2 * p, j1 = 2 * p + 1;
+      const uint32_t e0 = s_v[kb + 8 * (j0 / 4) + (j0 % 4)][d];
+      const uint32_t e1 = s_v[kb + 8 * (j1 / 4) + (j1 % 4)][d];
+      w[p] = e0 | (e1 << 16);
+    }
+    u32x4 out = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(dst + (size_t)idx * 8) = out;
+  }
+}
+
+struct PrefillGeom {
+  int B, Hq, Hkv, G, Nmax, max_ctx, Tq, QB, ntiles, S;
+};
+
+// ---------------------------------------------------------------------------
+// Main kernel. Block = (b, kvh, query block qb, split sp).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos0,
+    const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ vp, PrefillGeom g, float scale, float c, float eps, int norm_q,
+    float* __restrict__ out, float* __restrict__ part, float* __restrict__ pden) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][2 * kTileBytes];
+  __shared__ float s_den[4][32];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int r = lane & 31;
+
+  const int sp = blockIdx.x % g.S;
+  const int unit = blockIdx.x / g.S;
+  const int qb = unit % g.QB;
+  const int bkv = unit / g.QB;
+  const int b = bkv / g.Hkv;
+  const int kvh = bkv % g.Hkv;
+  const int G = g.G;
+
+  const int n = min(ctx_lens[b], g.max_ctx);
+  const int p0 = q_pos0[b];
+
+  // this lane's query row
+  const int row = qb * kRowsPerBlock + wave * 32 + r;
+  const int t = row / G;
+  const int head = kvh * G + row % G;
+  const bool valid = t < g.Tq;
+  const int lim = valid ? max(-1, min(p0 + t, n - 1)) : -1;
+
+  // wave / block bounds on the visible keys (positions grow with the row)
+  const int t_lo_wave = (qb * kRowsPerBlock + wave * 32) / G;
+  const int wave_min_lim = max(-1, min(p0 + t_lo_wave, n - 1));
+  const bool wave_live = t_lo_wave < g.Tq;
+  const int t_hi_blk = min((qb + 1) * kRowsPerBlock / G, g.Tq) - 1;
+  const int blk_max_lim = max(-1, min(p0 + t_hi_blk, n - 1));
+  const int t_vis = blk_max_lim >= 0 ? blk_max_lim / kKeyTile + 1 : 0;
+  const int per = (t_vis + g.S - 1) / g.S;
+  const int tb = min(sp * per, t_vis);
+  const int te = min(tb + per, t_vis);
+
+  // ---- query: RMS-normalise, scale, split into hi + lo bf16 B fragments ----
+  bf16x8 qhi[8], qlo[8];
+  {
+    u32x4 raw[8];
+    const uint16_t* qrow = q + ((size_t)(b * g.Hq + head) * g.Tq + (valid ? t : 0)) * kHeadDim;
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      raw[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * half)
+                     : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo(raw[s][e]), x1 = bf16_hi(raw[s][e]);
+        ss += x0 * x0 + x1 * x1;
+      }
+    }
+    ss += __shfl_xor(ss, 32, kWave);
+    const float f = norm_q ? scale / sqrtf(ss * (1.0f / kHeadDim) + eps) : scale;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t hh, ll;
+        split_pair(bf16_lo(raw[s][e]) * f, bf16_hi(raw[s][e]) * f, hh, ll);
+        h[e] = hh;
+        l[e] = ll;
+      }
+      qhi[s] = as_bf16x8(h);
+      qlo[s] = as_bf16x8(l);
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+  float den = 0.f;
+
+  const uint8_t* kbase = k + (size_t)bkv * g.Nmax * (kHeadDim * 2);
+  const uint8_t* vbase = vp + (size_t)bkv * g.ntiles * kTileBytes;
+
+  // Wave w issues fragments 4w .. 4w+3 of the 16 per tile: 0-7 are the K
+  // A-fragments (k-step s = dims 16s .. 16s+15), 8-15 the packed V fragments.
+  auto issue = [&](int tile, int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int fi = wave * 4 + u;
+      uint8_t* dst = &s_buf[buf][fi * kFragBytes];
+      const uint8_t* src;
+      if (fi < 8) {
+        const int key = min(tile * kKeyTile + r, n - 1);
+        src = kbase + (size_t)key * (kHeadDim * 2) + fi * 32 + half * 16;
+      } else {
+        src = vbase + (size_t)tile * kTileBytes + (fi - 8) * kFragBytes + lane * 16;
+      }
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    }
+  };
+
+  if (tb < te) issue(tb, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int buf = (tile - tb) & 1;
+    if (tile + 1 < te) issue(tile + 1, buf ^ 1);
+    if (wave_live) {
+      const uint8_t* kt = &s_buf[buf][0];
+      const uint8_t* vt = &s_buf[buf][kTileBytes];
+      f32x16 st;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + s * kFragBytes + lane * 16));
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[s], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[s], st, 0, 0, 0);
+      }
+      // st[i] is the score of this lane's row against key 8*(i/4) + 4*half + i%4
+      const bool full = tile * kKeyTile + kKeyTile - 1 <= wave_min_lim;
+      const int key0 = tile * kKeyTile + 4 * half;
+      uint32_t whi[8], wlo[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float w2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int i = 2 * p + e;
+          const float x = fmaxf(st[i], 0.f);
+          float w = x * x;
+          if (!full) w = (key0 + 8 * (i / 4) + (i % 4) <= lim) ? w : 0.f;
+          den += w;
+          w2[e] = w;
+        }
+        split_pair(w2[0], w2[1], whi[p], wlo[p]);
+      }
+      const bf16x8 wh0 = as_bf16x8(u32x4{whi[0], whi[1], whi[2], whi[3]});
+      const bf16x8 wh1 = as_bf16x8(u32x4{whi[4], whi[5], whi[6], whi[7]});
+      const bf16x8 wl0 = as_bf16x8(u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
+      const bf16x8 wl1 = as_bf16x8(u32x4{wlo[4], wlo[5], wlo[6], wlo[7]});
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8 v0 =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + (2 * nb) * kFragBytes + lane * 16));
+        const bf16x8 v1 =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + (2 * nb + 1) * kFragBytes + lane * 16));
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh0, v0, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl0, v0, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1, v1, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1, v1, acc[nb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+
+  // den of row r: this lane holds half of its keys, the lane 32 away the rest
+  den += __shfl_xor(den, 32, kWave);
+  if (half == 0) s_den[wave][r] = den;
+  __syncthreads();
+
+  // acc[nb][i] is O[row m][dim 32*nb + lane%32] with m = 8*(i/4) + 4*half + i%4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = 8 * (i / 4) + 4 * half + (i % 4);
+    const int brow = wave * 32 + m;  // row inside the block
+    const int grow = qb * kRowsPerBlock + brow;
+    const int tt = grow / G;
+    if (tt >= g.Tq) continue;
+    const float dsum = s_den[wave][m];
+    if (g.S == 1) {
+      const float z = c + dsum;
+      const float inv = z == 0.f ? 0.f : 1.0f / z;
+      const int hh = kvh * G + grow % G;
+      float* o = out + ((size_t)(b * g.Hq + hh) * g.Tq + tt) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) o[32 * nb + r] = z == 0.f ? 0.f : acc[nb][i] * inv;
+    } else {
+      float* o = part + ((size_t)(unit * g.S + sp) * kRowsPerBlock + brow) * kHeadDim;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) o[32 * nb + r] = acc[nb][i];
+      if (r == 0 && (i % 4) == 0) {
+        // one lane per group of four rows writes their dens
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pden[(size_t)(unit * g.S + sp) * kRowsPerBlock + wave * 32 + m + e] = s_den[wave][m + e];
+      }
+    }
+  }
+}
+
+// Adds the S partials of each row in split order and normalises.
+__global__ __launch_bounds__(kHeadDim) void prefill_combine(const float* __restrict__ part,
+                                                            const float* __restrict__ pden,
+                                                            PrefillGeom g, float c,
+                                                            float* __restrict__ out) {
+  const int unit = blockIdx.x;
+  const int qb = unit % g.QB;
+  const int bkv = unit / g.QB;
+  const int b = bkv / g.Hkv;
+  const int kvh = bkv % g.Hkv;
+  const int d = threadIdx.x;
+  for (int brow = 0; brow < kRowsPerBlock; ++brow) {
+    const int grow = qb * kRowsPerBlock + brow;
+    const int tt = grow / g.G;
+    if (tt >= g.Tq) break;
+    float num = 0.f, dsum = 0.f;
+    for (int sp = 0; sp < g.S; ++sp) {
+      const size_t base = (size_t)(unit * g.S + sp) * kRowsPerBlock + brow;
+      num += part[base * kHeadDim + d];
+      dsum += pden[base];
+    }
+    const float z = c + dsum;
+    const int hh = kvh * g.G + grow % g.G;
+    out[((size_t)(b * g.Hq + hh) * g.Tq + tt) * kHeadDim + d] = z == 0.f ? 0.f : num / z;
+  }
+}
+
+PrefillGeom geometry(int B, int Hq, int Hkv, int max_ctx, int Tq) {
+  PrefillGeom g;
+  g.B = B;
+  g.Hq = Hq;
+  g.Hkv = Hkv;
+  g.G = Hq / Hkv;
+  g.Nmax = 0;
+  g.max_ctx = max_ctx;
+  g.Tq = Tq;
+  g.QB = (int)(((int64_t)Tq * g.G + kRowsPerBlock - 1) / kRowsPerBlock);
+  g.ntiles = (max_ctx + kKeyTile - 1) / kKeyTile;
+  const int64_t units = (int64_t)B * Hkv * g.QB;
+  int64_t s = units > 0 ? (kTargetBlocks + units - 1) / units : 1;
+  s = std::min<int64_t>(s, kMaxSplit);
+  s = std::min<int64_t>(s, std::max(1, g.ntiles / 4));
+  g.S = (int)std::max<int64_t>(s, 1);
+  return g;
+}
+
+struct WsLayout {
+  size_t vp, part, pden, total;
+};
+
+WsLayout ws_layout(const PrefillGeom& g) {
+  WsLayout w;
+  const size_t units = (size_t)g.B * g.Hkv * g.QB;
+  w.vp = 0;
+  size_t off = align_up((size_t)g.B * g.Hkv * g.ntiles * kTileBytes, 256);
+  if (g.S > 1) {
+    w.part = off;
+    off = align_up(off + units * g.S * kRowsPerBlock * kHeadDim * sizeof(float), 256);
+    w.pden = off;
+    off = align_up(off + units * g.S * kRowsPerBlock * sizeof(float), 256);
+  } else {
+    w.part = w.pden = 0;
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t prefill_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int Tq) {
+  if (B == 0 || Tq == 0 || max_ctx == 0) return 0;
+  return ws_layout(geometry(B, Hq, Hkv, max_ctx, Tq)).total;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  PrefillGeom g = geometry(a.B, a.Hq, a.Hkv, a.max_ctx, a.Tq);
+  g.Nmax = a.Nmax;
+  const int64_t units = (int64_t)a.B * a.Hkv * g.QB;
+  // row and block indices are int inside the kernels
+  if (units * g.S > 0x7fffffff || (int64_t)g.QB * kRowsPerBlock > 0x7fffffff)
+    return hipErrorNotSupported;
+  const WsLayout w = ws_layout(g);
+  uint8_t* ws = static_cast<uint8_t*>(a.ws);
+  uint16_t* vp = reinterpret_cast<uint16_t*>(ws + w.vp);
+  hipLaunchKernelGGL(prefill_pack_v, dim3(g.ntiles, a.B * a.Hkv), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.v), a.ctx_lens, a.Hkv, a.Nmax, a.max_ctx, g.ntiles,
+                     vp);
+  float* part = g.S > 1 ? reinterpret_cast<float*>(ws + w.part) : nullptr;
+  float* pden = g.S > 1 ? reinterpret_cast<float*>(ws + w.pden) : nullptr;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(units * g.S)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.q), a.q_pos0, a.ctx_lens,
+                     static_cast<const uint8_t*>(a.k), reinterpret_cast<const uint8_t*>(vp), g,
+                     a.scale, a.c, a.eps, (int)(a.flags & 1u), a.out, part, pden);
+  if (g.S > 1)
+    hipLaunchKernelGGL(prefill_combine, dim3((unsigned)units), dim3(kHeadDim), 0, stream, part,
+                       pden, g, a.c, a.out);
+  if (verbose())
+    fprintf(stderr, "[ssa] prefill: G=%d QB=%d S=%d units=%lld ntiles=%d\n", g.G, g.QB, g.S,
+            (long long)units, g.ntiles);
+  return hipGetLastError();
+}
+
 }  // namespace ssa

@@ -219,15 +219,29 @@ class PrefillWorkload:
     q: np.ndarray                 # [B, Hq, Tq, D] uint16 (bf16 bits, raw)
     k: np.ndarray                 # [B, Hkv, Nmax, D] uint16
     v: np.ndarray
+    ctx_lens: np.ndarray          # [B] int32
 
 
 def prefill_chunk(seed: int = 5, batch: int = 1, n_query: int = 2048, n_keys: int = 65536,
-                  p: float = 0.05, recipe: str = "planted") -> PrefillWorkload:
-    """2048 prompt queries at the end of a 64K cache (q_pos0 = n_keys - n_query)."""
-    Hq, Hkv, D = 16, 2, 128
+                  p: float = 0.05, recipe: str = "planted", n_q_heads: int = 16,
+                  n_kv_heads: int = 2, ctx_lens=None, q_pos0=None,
+                  kv_capacity: int | None = None) -> PrefillWorkload:
+    """A chunk of n_query prompt queries over a full layer's cache.
+
+    By default: 2048 queries at the end of a 64K cache (q_pos0 = n_keys - n_query),
+    16 query heads over 2 KV heads. ``ctx_lens``/``q_pos0`` give per-sequence
+    cache lengths and chunk starts (q_pos0[b] + n_query <= ctx_lens[b]). Queries
+    follow the cache recipe: planted queries lean on the KV head's direction u,
+    i.i.d. queries are standard normal.
+    """
+    Hq, Hkv, D = n_q_heads, n_kv_heads, 128
     g = Hq // Hkv
+    ctx = np.asarray([n_keys] * batch if ctx_lens is None else ctx_lens, dtype=np.int32)
+    pos0 = (ctx - n_query) if q_pos0 is None else np.asarray(q_pos0, dtype=np.int32)
+    assert np.all(pos0 >= 0) and np.all(pos0 + n_query <= ctx)
     wl = make_workload("prefill", seed=seed, batch=batch, n_q_heads=Hq, n_kv_heads=Hkv,
-                       ctx_lens=[n_keys] * batch, p=p, recipe=recipe)
+                       ctx_lens=list(ctx), p=p, recipe=recipe,
+                       kv_capacity=kv_capacity if kv_capacity is not None else int(ctx.max()))
     q = np.empty((batch, Hq, n_query, D), dtype=np.float32)
     sigma = 1.0 / np.sqrt(D)
     for b in range(batch):
@@ -238,7 +252,7 @@ def prefill_chunk(seed: int = 5, batch: int = 1, n_query: int = 2048, n_keys: in
                 q[b, kvh * g:(kvh + 1) * g] = u + 0.5 * sigma * r.standard_normal((g, n_query, D))
             else:
                 q[b, kvh * g:(kvh + 1) * g] = r.standard_normal((g, n_query, D))
-    return PrefillWorkload(name=f"prefill_{n_query}x{n_keys}", batch=batch, n_q_heads=Hq,
-                           n_kv_heads=Hkv, head_dim=D, n_query=n_query, kv_capacity=n_keys,
-                           q_pos0=np.full(batch, n_keys - n_query, dtype=np.int32),
-                           q=to_bf16_bits(q), k=wl.k, v=wl.v)
+    return PrefillWorkload(name=f"prefill_{n_query}x{int(ctx.max())}", batch=batch, n_q_heads=Hq,
+                           n_kv_heads=Hkv, head_dim=D, n_query=n_query,
+                           kv_capacity=wl.kv_capacity, q_pos0=pos0.astype(np.int32),
+                           q=to_bf16_bits(q), k=wl.k, v=wl.v, ctx_lens=ctx)
