@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--copies", type=int, default=3, help="cache copies used in rotation")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true", help="skip the separate prefill measurement")
+    p.add_argument("--prefill-reps", type=int, default=20)
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only run the prefill measurement (prints its JSON object)")
     p.add_argument("--fixed-len", type=int, default=None,
                    help="use this context length for every sequence instead of U[64K,128K]")
     p.add_argument("--copy-probe", action="store_true",
@@ -133,6 +137,47 @@ def cpu_baseline(wl, reps: int = 3) -> dict:
                       f"full layer, selection and one sparse layer in float64 NumPy; median of {reps} passes"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(reps: int, warmup: int = 3) -> dict:
+    """Chunked ReLU^2 prefill: 2048 queries at the end of a 64K cache (B1, 16/2 heads, bf16).
+
+    Algorithmic work counts 4*D flops per visible (query, key) pair (QK^T and
+    AV); the kernel issues each product twice (hi and lo operand halves).
+    """
+    import torch
+    from long_context_decode_relu_amd import ssa, synth
+    dev = torch.device("cuda:0")
+    pw = synth.prefill_chunk()
+    cache = ssa.Cache(k=ssa.kv_tensor(pw.k, dev), v=ssa.kv_tensor(pw.v, dev),
+                      ctx_lens=torch.from_numpy(pw.ctx_lens.astype(np.int32)).to(dev),
+                      max_ctx_len=int(pw.ctx_lens.max()))
+    q = ssa.kv_tensor(pw.q, dev)
+    pos0 = torch.from_numpy(pw.q_pos0.astype(np.int32)).to(dev)
+    B, Hq, Tq, D = q.shape
+    out = torch.empty((B, Hq, Tq, D), dtype=torch.float32, device=dev)
+    ws = ssa.workspace(ssa.SSA_OP_PREFILL_FULL, cache.shape(Hq), Tq, dev)
+    for _ in range(warmup):
+        ssa.ssa_prefill_full(q, pos0, cache, out=out, ws=ws)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        ssa.ssa_prefill_full(q, pos0, cache, out=out, ws=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    pairs = sum(Hq * (int(pw.q_pos0[b]) * Tq + Tq * (Tq + 1) // 2) for b in range(B))
+    flops = 4 * D * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"prefill_b{B}_q{Tq}_ctx{int(pw.ctx_lens.max())}_bf16_p0.05",
+            "avg_ms": round(ms, 4), "alg_flops": int(flops), "achieved_tflops": round(tf, 1),
+            "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_issued_frac": round(2 * tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -141,6 +186,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill(args.prefill_reps)}), flush=True)
         return
 
     import torch
@@ -269,6 +317,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},
     }
+    if not args.no_prefill:
+        log("[bench] prefill ...")
+        res["prefill"] = bench_prefill(args.prefill_reps)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(wl)

@@ -38,12 +38,34 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;         // four waves
 constexpr int kRowsPerBlock = 128;    // (position, head) rows per workgroup
-constexpr int kKeyTile = 32;          // keys per tile
+constexpr int kSub = 32;              // keys per MFMA score block
+constexpr int kKeyTile = 64;          // keys per LDS tile: two score blocks
 constexpr int kFragBytes = 1024;      // one MFMA operand fragment: 64 lanes x 16 B
-constexpr int kTileBytes = 8 * kFragBytes;  // 32 keys x 128 dims x bf16
+constexpr int kTileBytes = 8 * kFragBytes;  // 32 keys x 128 dims x bf16 (one score block)
 constexpr int kMaxSplit = 16;
 constexpr int kTargetBlocks = 512;    // two resident workgroups per CU on 256 CUs
 constexpr int kWaitVm0 = 0x0F70;      // s_waitcnt vmcnt(0)
+constexpr int kSlots = 2;
+// slot layout: K block 0, K block 1, V block 0, V block 1 (8 KB each)
+constexpr int kSlotBytes = 4 * kTileBytes;
+
+// One 16-byte direct-to-LDS load per lane from base + voff (base is
+// wave-uniform, voff a 32-bit per-lane byte offset): the wave's 64 pieces land
+// at lds_off + 16 * lane. Issued from asm so that the compiler does not treat
+// every later LDS read as possibly overlapping it (it would wait for the load
+// before each one); the kernel waits for these loads itself (vmcnt(0) ahead
+// of each barrier). Nothing else in these kernels uses m0.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_off)
+               : "memory");
+}
+
+// ReLU(x)^2 as max(x * |x|, 0): two instructions (|x| is a free source
+// modifier, and a product needs no NaN canonicalisation before the max).
+// A NaN score gives 0.
+__device__ __forceinline__ float relu_sq(float x) { return fmaxf(x * fabsf(x), 0.f); }
 
 __device__ __forceinline__ uint32_t bits2(bf16x2 x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -61,9 +83,14 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// Eight MFMA operand fragments (one tile of K, or of packed V).
+struct Frags {
+  bf16x8 f[8];
+};
+
 // ---------------------------------------------------------------------------
-// V packing: vp[bkv][tile][f = 2*nb + s][lane][j] =
-//   V[tile*32 + 16*s + 8*(j/4) + 4*(lane/32) + (j%4)][32*nb + lane%32]
+// V packing, in 32-key blocks: vp[bkv][blk][f = 2*nb + s][lane][j] =
+//   V[blk*32 + 16*s + 8*(j/4) + 4*(lane/32) + (j%4)][32*nb + lane%32]
 // which is the B fragment of k-step s (16 keys) for dims 32*nb .. 32*nb+31.
 // The key order inside a k-step matches the rows the S^T accumulator hands
 // each lane (see prefill_kernel), so W needs no shuffle. Keys >= ctx_lens[b]
@@ -73,8 +100,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pack_v(const uint16_t* __res
                                                            const int32_t* __restrict__ ctx_lens,
                                                            int Hkv, int Nmax, int max_ctx,
                                                            int ntiles, uint16_t* __restrict__ vp) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kKeyTile][kHeadDim];
-  const int tile = blockIdx.x;
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kSub][kHeadDim];
+  const int tile = blockIdx.x;  // 32-key block
   const int bkv = blockIdx.y;
   const int b = bkv / Hkv;
   const int n = min(ctx_lens[b], max_ctx);
@@ -82,8 +109,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pack_v(const uint16_t* __res
   const uint16_t* src = v + (size_t)bkv * Nmax * kHeadDim;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * kThreads;  // 16-byte chunk of the tile
-    const int key = tile * kKeyTile + c / 16;
+    const int c = tid + u * kThreads;  // 16-byte chunk of the block
+    const int key = tile * kSub + c / 16;
     u32x4 x = {0u, 0u, 0u, 0u};
     if (key < n) x = *reinterpret_cast<const u32x4*>(src + (size_t)key * kHeadDim + (c % 16) * 8);
     *reinterpret_cast<u32x4*>(&s_v[c / 16][(c % 16) * 8]) = x;
@@ -123,7 +150,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ vp, PrefillGeom g, float scale, float c, float eps, int norm_q,
     float* __restrict__ out, float* __restrict__ part, float* __restrict__ pden) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_buf[2][2 * kTileBytes];
+  // two tile slots: one being read, one filling
+  __shared__ __attribute__((aligned(16))) uint8_t s_buf[kSlots][kSlotBytes];
   __shared__ float s_den[4][32];
 
   const int tid = threadIdx.x;
@@ -152,7 +180,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
 
   // wave / block bounds on the visible keys (positions grow with the row)
   const int t_lo_wave = (qb * kRowsPerBlock + wave * 32) / G;
-  const int wave_min_lim = max(-1, min(p0 + t_lo_wave, n - 1));
   const bool wave_live = t_lo_wave < g.Tq;
   const int t_hi_blk = min((qb + 1) * kRowsPerBlock / G, g.Tq) - 1;
   const int blk_max_lim = max(-1, min(p0 + t_hi_blk, n - 1));
@@ -160,6 +187,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const int per = (t_vis + g.S - 1) / g.S;
   const int tb = min(sp * per, t_vis);
   const int te = min(tb + per, t_vis);
+  // tiles below tm lie wholly inside every row's causal window (no mask)
+  const int t_lo_blk = qb * kRowsPerBlock / G;
+  const int blk_min_lim = max(-1, min(p0 + t_lo_blk, n - 1));
+  const int tm = max(tb, min(te, (blk_min_lim + 1) / kKeyTile));
 
   // ---- query: RMS-normalise, scale, split into hi + lo bf16 B fragments ----
   bf16x8 qhi[8], qlo[8];
@@ -202,81 +233,117 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   float den = 0.f;
 
   const uint8_t* kbase = k + (size_t)bkv * g.Nmax * (kHeadDim * 2);
-  const uint8_t* vbase = vp + (size_t)bkv * g.ntiles * kTileBytes;
+  const uint8_t* vbase = vp + (size_t)bkv * g.ntiles * 2 * kTileBytes;
 
-  // Wave w issues fragments 4w .. 4w+3 of the 16 per tile: 0-7 are the K
-  // A-fragments (k-step s = dims 16s .. 16s+15), 8-15 the packed V fragments.
-  auto issue = [&](int tile, int buf) {
+  // A 64-key tile is 32 fragments of 1 KB: K block 0 (k-steps 0-7), K block 1,
+  // then the packed V of blocks 0 and 1. Wave w issues fragments 8w .. 8w+7.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&s_buf[0][0];
+  auto issue = [&](int tile, int slot) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int fi = wave * 4 + u;
-      uint8_t* dst = &s_buf[buf][fi * kFragBytes];
-      const uint8_t* src;
-      if (fi < 8) {
-        const int key = min(tile * kKeyTile + r, n - 1);
-        src = kbase + (size_t)key * (kHeadDim * 2) + fi * 32 + half * 16;
+    for (int u = 0; u < 8; ++u) {
+      const int fi = wave * 8 + u;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + slot * kSlotBytes + fi * kFragBytes);
+      if (fi < 16) {
+        // K: rows past the context repeat its last row (read, then masked);
+        // tile * 64 <= n - 1 for every issued tile, so krow is in [0, 63]
+        const uint8_t* kt = kbase + (size_t)tile * kKeyTile * (kHeadDim * 2);
+        const int krow = min(tile * kKeyTile + (fi / 8) * kSub + r, n - 1) - tile * kKeyTile;
+        lds_dma16(kt, (uint32_t)(krow * (kHeadDim * 2) + (fi % 8) * 32 + half * 16), lds);
       } else {
-        src = vbase + (size_t)tile * kTileBytes + (fi - 8) * kFragBytes + lane * 16;
+        const uint8_t* vt = vbase + (size_t)tile * 2 * kTileBytes;
+        lds_dma16(vt, (uint32_t)((fi - 16) * kFragBytes + lane * 16), lds);
       }
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
   };
 
+  auto frag = [&](int slot, int fi) {
+    return as_bf16x8(
+        *reinterpret_cast<const u32x4*>(&s_buf[slot][fi * kFragBytes + lane * 16]));
+  };
+
+  // S^T of one 32-key block: st[i] = score of this lane's row against key
+  // 8*(i/4) + 4*half + i%4 of the block.
+  auto qk = [&](int slot, int blk, f32x16& st) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a = frag(slot, blk * 8 + s);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[s], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[s], st, 0, 0, 0);
+    }
+  };
+
+  // ReLU^2 weights of one block (causal mask if MASKED), den update, and the
+  // split into the two k-step A operands (hi and lo).
+  struct W {
+    bf16x8 h0, h1, l0, l1;
+  };
+  auto weights = [&](const f32x16& st, int key0, bool masked, W& w) {
+    uint32_t whi[8], wlo[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      float w2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * p + e;
+        float wv = relu_sq(st[i]);
+        if (masked) wv = (key0 + 8 * (i / 4) + 4 * half + (i % 4) <= lim) ? wv : 0.f;
+        den += wv;
+        w2[e] = wv;
+      }
+      split_pair(w2[0], w2[1], whi[p], wlo[p]);
+    }
+    w.h0 = as_bf16x8(u32x4{whi[0], whi[1], whi[2], whi[3]});
+    w.h1 = as_bf16x8(u32x4{whi[4], whi[5], whi[6], whi[7]});
+    w.l0 = as_bf16x8(u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
+    w.l1 = as_bf16x8(u32x4{wlo[4], wlo[5], wlo[6], wlo[7]});
+  };
+
+  auto pv = [&](int slot, int blk, const W& w) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const bf16x8 v0 = frag(slot, 16 + blk * 8 + 2 * nb);
+      const bf16x8 v1 = frag(slot, 16 + blk * 8 + 2 * nb + 1);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h0, v0, acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l0, v0, acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h1, v1, acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l1, v1, acc[nb], 0, 0, 0);
+    }
+  };
+
+  // One 64-key tile: the second block's scores run on the matrix cores while
+  // the first block's weights are formed, and the first block's W x V while
+  // the second block's weights are formed.
+  auto tile_step = [&](int slot, int tile, bool masked) {
+    f32x16 s0, s1;
+    W w0, w1;
+    qk(slot, 0, s0);
+    qk(slot, 1, s1);
+    weights(s0, tile * kKeyTile, masked, w0);
+    pv(slot, 0, w0);
+    weights(s1, tile * kKeyTile + kSub, masked, w1);
+    pv(slot, 1, w1);
+  };
+
+  // Double-buffered tiles; tiles [tb, tm) need no causal mask, [tm, te) do.
   if (tb < te) issue(tb, 0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-
-  for (int tile = tb; tile < te; ++tile) {
-    const int buf = (tile - tb) & 1;
-    if (tile + 1 < te) issue(tile + 1, buf ^ 1);
-    if (wave_live) {
-      const uint8_t* kt = &s_buf[buf][0];
-      const uint8_t* vt = &s_buf[buf][kTileBytes];
-      f32x16 st;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st[i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + s * kFragBytes + lane * 16));
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[s], st, 0, 0, 0);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[s], st, 0, 0, 0);
-      }
-      // st[i] is the score of this lane's row against key 8*(i/4) + 4*half + i%4
-      const bool full = tile * kKeyTile + kKeyTile - 1 <= wave_min_lim;
-      const int key0 = tile * kKeyTile + 4 * half;
-      uint32_t whi[8], wlo[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        float w2[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = 2 * p + e;
-          const float x = fmaxf(st[i], 0.f);
-          float w = x * x;
-          if (!full) w = (key0 + 8 * (i / 4) + (i % 4) <= lim) ? w : 0.f;
-          den += w;
-          w2[e] = w;
-        }
-        split_pair(w2[0], w2[1], whi[p], wlo[p]);
-      }
-      const bf16x8 wh0 = as_bf16x8(u32x4{whi[0], whi[1], whi[2], whi[3]});
-      const bf16x8 wh1 = as_bf16x8(u32x4{whi[4], whi[5], whi[6], whi[7]});
-      const bf16x8 wl0 = as_bf16x8(u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
-      const bf16x8 wl1 = as_bf16x8(u32x4{wlo[4], wlo[5], wlo[6], wlo[7]});
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const bf16x8 v0 =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + (2 * nb) * kFragBytes + lane * 16));
-        const bf16x8 v1 =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + (2 * nb + 1) * kFragBytes + lane * 16));
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh0, v0, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl0, v0, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh1, v1, acc[nb], 0, 0, 0);
-        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl1, v1, acc[nb], 0, 0, 0);
-      }
-    }
+  int slot = 0;
+  for (int j = tb; j < tm; ++j) {
+    if (j + 1 < te) issue(j + 1, slot ^ 1);
+    if (wave_live) tile_step(slot, j, false);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    slot ^= 1;
+  }
+  for (int j = tm; j < te; ++j) {
+    if (j + 1 < te) issue(j + 1, slot ^ 1);
+    if (wave_live) tile_step(slot, j, true);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    slot ^= 1;
   }
 
   // den of row r: this lane holds half of its keys, the lane 32 away the rest
@@ -295,11 +362,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     const float dsum = s_den[wave][m];
     if (g.S == 1) {
       const float z = c + dsum;
-      const float inv = z == 0.f ? 0.f : 1.0f / z;
       const int hh = kvh * G + grow % G;
       float* o = out + ((size_t)(b * g.Hq + hh) * g.Tq + tt) * kHeadDim;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) o[32 * nb + r] = z == 0.f ? 0.f : acc[nb][i] * inv;
+      for (int nb = 0; nb < 4; ++nb) o[32 * nb + r] = z == 0.f ? 0.f : acc[nb][i] / z;
     } else {
       float* o = part + ((size_t)(unit * g.S + sp) * kRowsPerBlock + brow) * kHeadDim;
 #pragma unroll
@@ -314,31 +380,36 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   }
 }
 
-// Adds the S partials of each row in split order and normalises.
-__global__ __launch_bounds__(kHeadDim) void prefill_combine(const float* __restrict__ part,
+// Adds the S partials of each row in split order and normalises. A block
+// covers 8 rows of one query block; a thread owns 4 consecutive dims.
+constexpr int kCombineRows = 8;
+
+__global__ __launch_bounds__(kThreads) void prefill_combine(const float* __restrict__ part,
                                                             const float* __restrict__ pden,
                                                             PrefillGeom g, float c,
                                                             float* __restrict__ out) {
-  const int unit = blockIdx.x;
+  const int unit = blockIdx.x / (kRowsPerBlock / kCombineRows);
+  const int brow = (blockIdx.x % (kRowsPerBlock / kCombineRows)) * kCombineRows + threadIdx.x / 32;
+  const int d4 = threadIdx.x % 32;
   const int qb = unit % g.QB;
   const int bkv = unit / g.QB;
   const int b = bkv / g.Hkv;
   const int kvh = bkv % g.Hkv;
-  const int d = threadIdx.x;
-  for (int brow = 0; brow < kRowsPerBlock; ++brow) {
-    const int grow = qb * kRowsPerBlock + brow;
-    const int tt = grow / g.G;
-    if (tt >= g.Tq) break;
-    float num = 0.f, dsum = 0.f;
-    for (int sp = 0; sp < g.S; ++sp) {
-      const size_t base = (size_t)(unit * g.S + sp) * kRowsPerBlock + brow;
-      num += part[base * kHeadDim + d];
-      dsum += pden[base];
-    }
-    const float z = c + dsum;
-    const int hh = kvh * g.G + grow % g.G;
-    out[((size_t)(b * g.Hq + hh) * g.Tq + tt) * kHeadDim + d] = z == 0.f ? 0.f : num / z;
+  const int grow = qb * kRowsPerBlock + brow;
+  const int tt = grow / g.G;
+  if (tt >= g.Tq) return;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float dsum = 0.f;
+  for (int sp = 0; sp < g.S; ++sp) {
+    const size_t base = (size_t)(unit * g.S + sp) * kRowsPerBlock + brow;
+    num += reinterpret_cast<const f32x4*>(part + base * kHeadDim)[d4];
+    dsum += pden[base];
   }
+  const float z = c + dsum;
+  const int hh = kvh * g.G + grow % g.G;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (z != 0.f) o = num / z;
+  reinterpret_cast<f32x4*>(out + ((size_t)(b * g.Hq + hh) * g.Tq + tt) * kHeadDim)[d4] = o;
 }
 
 PrefillGeom geometry(int B, int Hq, int Hkv, int max_ctx, int Tq) {
@@ -351,7 +422,7 @@ PrefillGeom geometry(int B, int Hq, int Hkv, int max_ctx, int Tq) {
   g.max_ctx = max_ctx;
   g.Tq = Tq;
   g.QB = (int)(((int64_t)Tq * g.G + kRowsPerBlock - 1) / kRowsPerBlock);
-  g.ntiles = (max_ctx + kKeyTile - 1) / kKeyTile;
+  g.ntiles = (max_ctx + kKeyTile - 1) / kKeyTile;  // 64-key tiles (V packed as 2 blocks each)
   const int64_t units = (int64_t)B * Hkv * g.QB;
   int64_t s = units > 0 ? (kTargetBlocks + units - 1) / units : 1;
   s = std::min<int64_t>(s, kMaxSplit);
@@ -368,7 +439,7 @@ WsLayout ws_layout(const PrefillGeom& g) {
   WsLayout w;
   const size_t units = (size_t)g.B * g.Hkv * g.QB;
   w.vp = 0;
-  size_t off = align_up((size_t)g.B * g.Hkv * g.ntiles * kTileBytes, 256);
+  size_t off = align_up((size_t)g.B * g.Hkv * g.ntiles * 2 * kTileBytes, 256);
   if (g.S > 1) {
     w.part = off;
     off = align_up(off + units * g.S * kRowsPerBlock * kHeadDim * sizeof(float), 256);
@@ -394,14 +465,15 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   g.Nmax = a.Nmax;
   const int64_t units = (int64_t)a.B * a.Hkv * g.QB;
   // row and block indices are int inside the kernels
-  if (units * g.S > 0x7fffffff || (int64_t)g.QB * kRowsPerBlock > 0x7fffffff)
+  if (units * g.S > 0x7fffffff || units * (kRowsPerBlock / kCombineRows) > 0x7fffffff ||
+      (int64_t)g.QB * kRowsPerBlock > 0x7fffffff)
     return hipErrorNotSupported;
   const WsLayout w = ws_layout(g);
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
   uint16_t* vp = reinterpret_cast<uint16_t*>(ws + w.vp);
-  hipLaunchKernelGGL(prefill_pack_v, dim3(g.ntiles, a.B * a.Hkv), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(a.v), a.ctx_lens, a.Hkv, a.Nmax, a.max_ctx, g.ntiles,
-                     vp);
+  hipLaunchKernelGGL(prefill_pack_v, dim3(2 * g.ntiles, a.B * a.Hkv), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a.v), a.ctx_lens, a.Hkv, a.Nmax, a.max_ctx,
+                     2 * g.ntiles, vp);
   float* part = g.S > 1 ? reinterpret_cast<float*>(ws + w.part) : nullptr;
   float* pden = g.S > 1 ? reinterpret_cast<float*>(ws + w.pden) : nullptr;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(units * g.S)), dim3(kThreads), 0, stream,
@@ -409,8 +481,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                      static_cast<const uint8_t*>(a.k), reinterpret_cast<const uint8_t*>(vp), g,
                      a.scale, a.c, a.eps, (int)(a.flags & 1u), a.out, part, pden);
   if (g.S > 1)
-    hipLaunchKernelGGL(prefill_combine, dim3((unsigned)units), dim3(kHeadDim), 0, stream, part,
-                       pden, g, a.c, a.out);
+    hipLaunchKernelGGL(prefill_combine, dim3((unsigned)(units * (kRowsPerBlock / kCombineRows))),
+                       dim3(kThreads), 0, stream, part, pden, g, a.c, a.out);
   if (verbose())
     fprintf(stderr, "[ssa] prefill: G=%d QB=%d S=%d units=%lld ntiles=%d\n", g.G, g.QB, g.S,
             (long long)units, g.ntiles);
