@@ -4,28 +4,32 @@
 // layer reads the 1,024 keys its full layer scored highest -- by raw score,
 // so keys scored just below zero count -- plus the 128 most recent keys.
 //
-// One work-group of 1024 threads per (sequence, query head). Scores are
-// mapped to order-preserving 32-bit keys (larger score -> larger key, -0.0 ==
-// +0.0), so the k-th largest score is an exact radix select on integers. The
-// cut is found as a key value v* plus an index i*: a key is in the top k when
-// key > v*, or key == v* and its index <= i* (ties go to the lower index).
+// Scores are mapped to order-preserving 32-bit keys (larger score -> larger
+// key, -0.0 == +0.0), so the k-th largest score is an exact select on
+// integers. The cut is a key value v* plus an index i*: a key is in the top k
+// when key > v*, or key == v* and its index <= i* (ties go to the lower index).
 //
-//   pass 1  histogram of the top 13 key bits over the pool. Scores cluster
-//           (most keys of a planted cache share one or two bins), so each
-//           wave first adds whole groups of lanes that share a bin with one
-//           LDS atomic, and only the leftovers add one by one.
-//   pass 2  keys in the bin holding the cut (typically a few thousand) are
-//           gathered into LDS while the keys above it are marked in an LDS
-//           bitmap; the remaining bits and the tie index are resolved in LDS
-//           by 10-bit radix passes.
-//           If that bin is too large for LDS, further 10-bit histogram
-//           passes over global memory narrow it first; if all 32 bits are
-//           resolved and the tied keys still do not fit, the tie index is
-//           found by an ordered pass.
-//   pass 3  the selected candidates and the recent window are added to the
-//           bitmap, which is compacted into ascending indices. Rows longer
-//           than 2^18 keys (one bitmap) are marked and compacted segment by
-//           segment in an extra pass.
+// Three kernels per call:
+//   sample   one work-group per (sequence, query head) reads 64 evenly spaced
+//            runs of 64 scores and takes the key t whose rank in that sample
+//            predicts about 2k keys >= t in the whole row.
+//   collect  many work-groups per row stream the scores once and append every
+//            key >= t (key and index) to the row's candidate list.
+//   finish   one work-group per row. If the list holds between k and 8192
+//            candidates it contains the whole top k, and the cut is resolved
+//            exactly among them in LDS. Otherwise (an unlucky sample, or
+//            heavy ties) the row is selected exactly from the scores:
+//              pass 1  histogram of the top 13 key bits, wave-aggregated;
+//              pass 2  the keys of the bin holding the cut are gathered into
+//                      LDS (after narrowing 10 bits at a time over global
+//                      memory while that bin is too large), or, when all 32
+//                      bits tie beyond LDS, the tie index is found by an
+//                      ordered pass.
+//            Either way the selected keys and the recent window are marked in
+//            an LDS bitmap and compacted into ascending indices; rows longer
+//            than 2^18 keys are marked and compacted segment by segment.
+// The sample only decides how much work the exact step sees, never the
+// result, so the output is the same for any sample.
 //
 // The pool is [0, n) (union with the window, duplicates removed) or, with
 // SSA_SELECT_DISJOINT, [0, n - n_recent).
@@ -163,7 +167,8 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
     for (int base = 0; base < c; base += kSelThreads) {
       const int i = base + tid;
       const uint32_t key = i < c ? sh.ckey[i] : 0u;
-      hist_add(sh.hist, (key >> (32 - L - D)) & (nb - 1), i < c && (key >> (32 - L)) == P);
+      hist_add(sh.hist, (key >> (32 - L - D)) & (nb - 1),
+               i < c && (L == 0 || (key >> (32 - L)) == P));
     }
     __syncthreads();
     int above;
@@ -207,77 +212,71 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
   *istar = (int)~Q;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ sel_count, int stride) {
-  __shared__ SelShared sh;
+// ---------------------------------------------------------------------------
+// Exact cut from the scores of one row (pass 1 + pass 2). On return the
+// bitmap holds the keys above the cut bin when *marked is set (rows of at
+// most kSegKeys keys whose cut bin fitted in LDS).
+// ---------------------------------------------------------------------------
+__device__ void exact_cut(SelShared& sh, const float* s, int n, int pool, int k, uint32_t* vstar_out,
+                          int* istar_out, bool* marked_out) {
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;
-  const int b = row / Hq;
-  const int n = ctx_lens[b];
-  const int pool = disjoint ? max(0, n - n_recent) : n;
-  const int k = min(k_top, pool);
-  const float* s = scores + (size_t)row * Nmax;
-
   uint32_t vstar = 0;
-  int istar = INT_MAX;  // k == pool: every pool key is selected
-  bool marked = false;  // bitmap already holds the keys above the cut bin
-  if (k < pool) {
-    // pass 1: histogram of the top 12 bits
-    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+  int istar = INT_MAX;
+  bool marked = false;
+  // pass 1: histogram of the top kBits1 bits
+  for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+  __syncthreads();
+  for (int base = 0; base < pool; base += kSelThreads * kUnroll) {
+    uint32_t keys[kUnroll];
+    load_keys(s, base + tid, kSelThreads, pool, keys);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool act = base + u * kSelThreads + tid < pool;
+      hist_add(sh.hist, keys[u] >> (32 - kBits1), act);
+    }
+  }
+  __syncthreads();
+  int above;
+  const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
+  int need = k - above;
+  uint32_t P = (uint32_t)d1;
+  int L = kBits1;
+  int c = (int)sh.hist[d1];
+  __syncthreads();
+  // narrow the cut bin over global memory until it fits in LDS
+  while (c > kCap && L < 32) {
+    const int D = min(10, 32 - L);
+    const int nb = 1 << D;
+    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int base = 0; base < pool; base += kSelThreads * kUnroll) {
       uint32_t keys[kUnroll];
       load_keys(s, base + tid, kSelThreads, pool, keys);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const bool act = base + u * kSelThreads + tid < pool;
-        hist_add(sh.hist, keys[u] >> (32 - kBits1), act);
+        const bool act = base + u * kSelThreads + tid < pool && (keys[u] >> (32 - L)) == P;
+        hist_add(sh.hist, (keys[u] >> (32 - L - D)) & (nb - 1), act);
       }
     }
     __syncthreads();
-    int above;
-    const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
-    int need = k - above;
-    uint32_t P = (uint32_t)d1;
-    int L = kBits1;
-    int c = (int)sh.hist[d1];
+    const int d = threshold_bin(sh.hist, nb, need, sh, &above);
+    need -= above;
+    P = (P << D) | (uint32_t)d;
+    L += D;
+    c = (int)sh.hist[d];
     __syncthreads();
-    // narrow the cut bin over global memory until it fits in LDS
-    while (c > kCap && L < 32) {
-      const int D = min(10, 32 - L);
-      const int nb = 1 << D;
-      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
-      __syncthreads();
-      for (int base = 0; base < pool; base += kSelThreads * kUnroll) {
-        uint32_t keys[kUnroll];
-        load_keys(s, base + tid, kSelThreads, pool, keys);
+  }
+  if (c <= kCap) {
+    // pass 2: gather the keys of the cut bin; for a single-segment row also
+    // mark the keys above it in the bitmap (one word per 32 keys)
+    if (tid == 0) sh.ccount = 0;
+    __syncthreads();
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    for (int base0 = wave * kWave; base0 < pool; base0 += kSelThreads * kUnroll) {
+      uint32_t keys[kUnroll];
+      load_keys(s, base0 + lane, kSelThreads, pool, keys);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const bool act = base + u * kSelThreads + tid < pool && (keys[u] >> (32 - L)) == P;
-          hist_add(sh.hist, (keys[u] >> (32 - L - D)) & (nb - 1), act);
-        }
-      }
-      __syncthreads();
-      const int d = threshold_bin(sh.hist, nb, need, sh, &above);
-      need -= above;
-      P = (P << D) | (uint32_t)d;
-      L += D;
-      c = (int)sh.hist[d];
-      __syncthreads();
-    }
-    if (c <= kCap) {
-      // pass 2: gather the keys of the cut bin; for a single-segment row also
-      // mark the keys above it in the bitmap (one word per 32 keys)
-      if (tid == 0) sh.ccount = 0;
-      __syncthreads();
-      const int lane = tid & (kWave - 1), wave = tid >> 6;
-      for (int base0 = wave * kWave; base0 < pool; base0 += kSelThreads * kUnroll) {
-       uint32_t keys[kUnroll];
-       load_keys(s, base0 + lane, kSelThreads, pool, keys);
-#pragma unroll
-       for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnroll; ++u) {
         const int base = base0 + u * kSelThreads;
         if (base >= pool) break;
         const int i = base + lane;
@@ -298,49 +297,258 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           if (lane == 0) sh.bits[base >> 5] = (uint32_t)am;
           if (lane == 32) sh.bits[(base >> 5) + 1] = (uint32_t)(am >> 32);
         }
-       }
       }
-      __syncthreads();
-      finish_in_lds(sh, c, P, L, need, &vstar, &istar);
-      marked = n <= kSegKeys;
-    } else {
-      // all 32 bits known and more than kCap keys tie at v*: the need-th
-      // smallest tied index, by an ordered pass over blocks of the row
-      vstar = P;
-      int run = 0;
-      istar = -1;
-      for (int base = 0; base < pool && istar < 0; base += kSelThreads) {
-        const int i = base + tid;
-        const int tie = (i < pool && skey(s, i) == vstar) ? 1 : 0;
-        int total;
-        const int before = block_scan_excl(tie, sh.scan, &total);
-        if (tie && run + before + 1 == need) sh.bcast[2] = i;
-        if (run + total >= need) {
-          __syncthreads();
-          istar = sh.bcast[2];
-        }
-        run += total;
+    }
+    __syncthreads();
+    finish_in_lds(sh, c, P, L, need, &vstar, &istar);
+    if (n <= kSegKeys) {
+      // words past the pool were not written by pass 2
+      const int pw = ceil_div(pool, kWave) * 2;
+      for (int wi = pw + tid; wi < ceil_div(n, 32); wi += kSelThreads) sh.bits[wi] = 0u;
+      marked = true;
+    }
+  } else {
+    // all 32 bits known and more than kCap keys tie at v*: the need-th
+    // smallest tied index, by an ordered pass over blocks of the row
+    vstar = P;
+    int run = 0;
+    istar = -1;
+    for (int base = 0; base < pool && istar < 0; base += kSelThreads) {
+      const int i = base + tid;
+      const int tie = (i < pool && skey(s, i) == vstar) ? 1 : 0;
+      int total;
+      const int before = block_scan_excl(tie, sh.scan, &total);
+      if (tie && run + before + 1 == need) sh.bcast[2] = i;
+      if (run + total >= need) {
         __syncthreads();
+        istar = sh.bcast[2];
+      }
+      run += total;
+      __syncthreads();
+    }
+  }
+  *vstar_out = vstar;
+  *istar_out = istar;
+  *marked_out = marked;
+}
+
+// ---------------------------------------------------------------------------
+// Sample kernel: the provisional threshold of each row.
+// ---------------------------------------------------------------------------
+constexpr int kSmpThreads = 256;
+constexpr int kSmpRuns = 64;                       // runs of consecutive keys
+constexpr int kSmpRun = 64;                        // keys per run
+constexpr int kSmp = kSmpRuns * kSmpRun;           // 4096 sampled keys
+constexpr int kSmpPer = kSmp / kSmpThreads;        // 16 per thread
+
+__global__ __launch_bounds__(kSmpThreads) void select_sample(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
+    int k_top, int n_recent, int disjoint, uint32_t* __restrict__ thr, int32_t* __restrict__ ccount) {
+  __shared__ uint32_t hist[256];
+  __shared__ int bc[2];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int row = blockIdx.x;
+  const int b = row / Hq;
+  const int n = min(ctx_lens[b], Nmax);
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  if (tid == 0) ccount[row] = 0;
+  if (k >= pool || pool <= kCap) {
+    // every pool key becomes a candidate (or every one is selected)
+    if (tid == 0) thr[row] = 0u;
+    return;
+  }
+  const float* s = scores + (size_t)row * Nmax;
+  // run r starts at floor(r * (pool - 64) / 63): the runs span the pool
+  const int run = tid / (kSmpRun / kSmpPer), part = tid % (kSmpRun / kSmpPer);
+  const int start = (int)((int64_t)run * (pool - kSmpRun) / (kSmpRuns - 1)) + part * kSmpPer;
+  uint32_t key[kSmpPer];
+  {
+    float v[kSmpPer];
+#pragma unroll
+    for (int u = 0; u < kSmpPer; ++u) v[u] = s[start + u];
+#pragma unroll
+    for (int u = 0; u < kSmpPer; ++u) key[u] = ordered_key(v[u]);
+  }
+  // rank of the threshold in the sample: about 2k keys of the row lie above it
+  int need = (int)min<int64_t>(kSmp, ((int64_t)2 * k * kSmp + pool - 1) / pool + 8);
+  uint32_t P = 0;
+  for (int L = 0; L < 32; L += 8) {
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSmpPer; ++u)
+      hist_add(hist, (key[u] >> (24 - L)) & 255u, L == 0 || (key[u] >> (32 - L)) == P);
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l holds bins 255-4l .. 252-4l (from the top); inclusive scan
+      int c[4], sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { c[e] = (int)hist[255 - 4 * lane - e]; sum += c[e]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+      }
+      const int before = incl - sum;
+      if (before < need && incl >= need) {
+        int run2 = before;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (run2 < need && run2 + c[e] >= need) { bc[0] = 255 - 4 * lane - e; bc[1] = run2; }
+          run2 += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    const int d = bc[0];
+    need -= bc[1];
+    P = (P << 8) | (uint32_t)d;
+    __syncthreads();
+  }
+  if (tid == 0) thr[row] = P;
+}
+
+// ---------------------------------------------------------------------------
+// Collect kernel: every pool key >= thr[row] joins the row's candidate list.
+// Each work-group gathers its segment's candidates in LDS, reserves space in
+// the row's list with one atomic, then copies them out. Counts keep growing
+// past the list's capacity, so the finish kernel sees an overflow.
+// ---------------------------------------------------------------------------
+constexpr int kColThreads = 256;
+constexpr int kColSeg = 16384;                     // keys per work-group
+constexpr int kColPer = kColSeg / kColThreads;     // 64 per thread
+constexpr int kColLocal = 2048;                    // candidates buffered per work-group
+
+__global__ __launch_bounds__(kColThreads) void select_collect(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
+    int k_top, int n_recent, int disjoint, const uint32_t* __restrict__ thr,
+    int32_t* __restrict__ ccount, uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
+  __shared__ uint32_t lkey[kColLocal];
+  __shared__ int32_t lidx[kColLocal];
+  __shared__ int lcount, gbase;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int row = blockIdx.y;
+  const int b = row / Hq;
+  const int n = min(ctx_lens[b], Nmax);
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  const int lo = blockIdx.x * kColSeg;
+  if (k >= pool || lo >= pool) return;
+  const int hi = min(pool, lo + kColSeg);
+  const uint32_t t = thr[row];
+  const float* s = scores + (size_t)row * Nmax;
+  if (tid == 0) lcount = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < kColPer; c0 += kUnroll) {
+    uint32_t keys[kUnroll];
+    load_keys(s, lo + c0 * kColThreads + tid, kColThreads, hi, keys);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = lo + (c0 + u) * kColThreads + tid;
+      const bool cand = i < hi && keys[u] >= t;
+      const uint64_t m = __ballot(cand);
+      if (m) {
+        int wb = 0;
+        if (lane == 0) wb = atomicAdd(&lcount, __popcll(m));
+        wb = __builtin_amdgcn_readfirstlane(wb);
+        const int pos = wb + __popcll(m & ((1ull << lane) - 1));
+        if (cand && pos < kColLocal) {
+          lkey[pos] = keys[u];
+          lidx[pos] = i;
+        }
       }
     }
   }
+  __syncthreads();
+  const int c = lcount;
+  if (c == 0) return;
+  if (tid == 0) gbase = atomicAdd(&ccount[row], c > kColLocal ? kCap + 1 : c);
+  __syncthreads();
+  const int g0 = gbase;
+  if (c > kColLocal) return;  // the row overflows: the finish kernel selects it exactly
+  uint32_t* okey = ckey + (size_t)row * kCap;
+  int32_t* oidx = cidx + (size_t)row * kCap;
+  for (int j = tid; j < c; j += kColThreads) {
+    const int pos = g0 + j;
+    if (pos < kCap) {
+      okey[pos] = lkey[j];
+      oidx[pos] = lidx[j];
+    }
+  }
+}
 
-  // pass 3: mark and compact, one segment of 2^18 keys at a time
+// ---------------------------------------------------------------------------
+// Finish kernel: exact cut (from the candidates when they hold the top k,
+// else from the scores), then mark and compact.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void select_finish(
+    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
+    int k_top, int n_recent, int disjoint, const int32_t* __restrict__ ccount,
+    const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cidx,
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int stride) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / Hq;
+  const int n = min(ctx_lens[b], Nmax);
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  const float* s = scores + (size_t)row * Nmax;
+
+  uint32_t vstar = 0;
+  int istar = INT_MAX;  // k == pool: every pool key is selected
+  bool marked = false;  // bitmap already holds every selected pool key
+  if (k < pool) {
+    const int cnt = ccount[row];
+    if (cnt >= k && cnt <= kCap) {
+      // the candidates (every key >= the sampled threshold) hold the top k
+      for (int j = tid; j < cnt; j += kSelThreads) {
+        sh.ckey[j] = ckey[(size_t)row * kCap + j];
+        sh.cidx[j] = cidx[(size_t)row * kCap + j];
+      }
+      __syncthreads();
+      finish_in_lds(sh, cnt, 0u, 0, k, &vstar, &istar);
+      if (n <= kSegKeys) {
+        for (int wi = tid; wi < ceil_div(n, 32); wi += kSelThreads) sh.bits[wi] = 0u;
+        __syncthreads();
+        for (int j = tid; j < cnt; j += kSelThreads) {
+          const uint32_t key = sh.ckey[j];
+          const int i = sh.cidx[j];
+          if (key > vstar || (key == vstar && i <= istar)) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+        }
+        marked = true;
+      }
+    } else {
+      exact_cut(sh, s, n, pool, k, &vstar, &istar, &marked);
+      if (marked) {
+        // add the selected keys of the cut bin (held in LDS) to the bitmap
+        __syncthreads();
+        const int c = sh.ccount;
+        for (int j = tid; j < c; j += kSelThreads) {
+          const uint32_t key = sh.ckey[j];
+          const int i = sh.cidx[j];
+          if (key > vstar || (key == vstar && i <= istar)) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+        }
+      }
+    }
+  } else if (n <= kSegKeys) {
+    // every pool key is selected: mark [0, pool)
+    for (int wi = tid; wi < ceil_div(n, 32); wi += kSelThreads) {
+      const int first = wi * 32;
+      const int cntb = max(0, min(32, pool - first));
+      sh.bits[wi] = cntb == 32 ? 0xffffffffu : ((1u << cntb) - 1u);
+    }
+    marked = true;
+  }
+
+  // mark the recent window, then compact, one segment of 2^18 keys at a time
   const int r0 = max(0, n - n_recent);
   int written = 0;
   int32_t* out = sel_idx + (size_t)row * stride;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
   if (marked) {
-    // single segment, keys above the cut bin already marked: add the selected
-    // candidates and the recent window (bits of words past the pool are 0)
-    const int c = sh.ccount;
-    for (int j = tid; j < c; j += kSelThreads) {
-      const uint32_t key = sh.ckey[j];
-      const int i = sh.cidx[j];
-      if (key > vstar || (key == vstar && i <= istar)) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
-    }
-    const int pw = ceil_div(pool, kWave) * 2;  // words written by pass 2
-    for (int wi = pw + tid; wi < ceil_div(n, 32); wi += kSelThreads) sh.bits[wi] = 0u;
     __syncthreads();
     for (int i = r0 + tid; i < n; i += kSelThreads) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
     __syncthreads();
@@ -398,16 +606,46 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   if (tid == 0) sel_count[row] = written;
 }
 
+struct SelLayout {
+  size_t thr, cnt, key, idx, total;
+};
+
+SelLayout sel_layout(int rows) {
+  SelLayout l;
+  l.thr = 0;
+  l.cnt = align_up((size_t)rows * 4, 256);
+  l.key = l.cnt + align_up((size_t)rows * 4, 256);
+  l.idx = l.key + align_up((size_t)rows * kCap * 4, 256);
+  l.total = l.idx + align_up((size_t)rows * kCap * 4, 256);
+  return l;
+}
+
 }  // namespace
 
-size_t select_ws_bytes(int, int, int, int) { return 0; }
+size_t select_ws_bytes(int B, int Hq, int, int) {
+  const int rows = B * Hq;
+  return rows > 0 ? sel_layout(rows).total : 0;
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const int rows = a.B * a.Hq;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
-                     a.Hq, a.Nmax, a.k_top, a.n_recent, (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0,
-                     a.sel_idx, a.sel_count, a.k_top + a.n_recent);
+  const SelLayout l = sel_layout(rows);
+  char* ws = static_cast<char*>(a.ws);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(ws + l.thr);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + l.cnt);
+  uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + l.key);
+  int32_t* cidx = reinterpret_cast<int32_t*>(ws + l.idx);
+  const int disjoint = (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0;
+  hipLaunchKernelGGL(select_sample, dim3(rows), dim3(kSmpThreads), 0, stream, a.scores, a.ctx_lens,
+                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, thr, cnt);
+  const int segs = ceil_div(a.max_ctx, kColSeg);
+  if (segs > 0)
+    hipLaunchKernelGGL(select_collect, dim3(segs, rows), dim3(kColThreads), 0, stream, a.scores,
+                       a.ctx_lens, a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, thr, cnt, ckey, cidx);
+  hipLaunchKernelGGL(select_finish, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
+                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, cnt, ckey, cidx, a.sel_idx,
+                     a.sel_count, a.k_top + a.n_recent);
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ def test_workspace_sizes():
     assert ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(n_q_heads=3)) == 0
     assert ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(max_ctx_len=5000)) == 0  # > capacity
     assert ws_bytes(ssa.SSA_OP_SELECT, s, 0) == 0
+    # selection keeps a candidate list of up to 8192 (key, index) pairs per row
+    assert ws_bytes(ssa.SSA_OP_SELECT, s, 1152) >= 2 * 16 * 8192 * 8
     assert ws_bytes(99, s) == 0
     # the decode workspace holds one partial (D+1 floats) per head per split
     big = ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(batch=8, kv_capacity=131072, max_ctx_len=131072))
@@ -102,6 +104,8 @@ def test_select_rejects():
     assert f(s, 4000, 128) == ssa.SSA_ERR_SHAPE
     assert f(s, 1024, 128, sc=None) == ssa.SSA_ERR_NULL
     assert f(s, 1024, 128, fl=2) == ssa.SSA_ERR_UNSUPPORTED
+    assert f(s, 1024, 128, ws_=None) == ssa.SSA_ERR_WORKSPACE
+    assert f(s, 1024, 128, wb=64) == ssa.SSA_ERR_WORKSPACE
     assert f(shape(batch=0), 1024, 128) == ssa.SSA_OK
 
 

@@ -71,6 +71,26 @@ def test_select_all_equal_long_row():
     check_select_exact(s, [n])
 
 
+def test_select_sample_misses_fall_back_to_exact():
+    """Rows where the sampled threshold keeps fewer than k keys, or far too many, are still exact.
+
+    The selection samples 64 runs of 64 scores, run r starting at
+    floor(r * (n - 64) / 63). Row 0 puts a few large scores inside the runs and
+    many medium ones outside, so the sample's threshold keeps only 128 keys;
+    row 1 ties nearly everything, so the threshold keeps the whole row.
+    """
+    n = 100000
+    s = np.full((2, 1, n), 4.0, dtype=np.float32)
+    for r in range(64):
+        st = r * (n - 64) // 63
+        s[0, 0, st:st + 64] = -1.0
+        s[0, 0, st:st + 2] = 5.0
+    s[1, 0] = 3.0
+    s[1, 0, ::1000] = 3.5
+    check_select_exact(s, [n, n])
+    check_select_exact(s, [n, n], flags=O.SSA_SELECT_DISJOINT)
+
+
 def test_select_disjoint_and_small_k():
     rng = np.random.default_rng(6)
     s = rng.standard_normal((3, 2, 9000)).astype(np.float32)
