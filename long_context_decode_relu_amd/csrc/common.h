@@ -60,6 +60,18 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Maximum across the 64 lanes of a wave (same DPP pattern); every lane
+// receives the result.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_move<0xB1>(x));
+  x = fmaxf(x, dpp_move<0x4E>(x));
+  x = fmaxf(x, dpp_move<0x141>(x));
+  x = fmaxf(x, dpp_move<0x140>(x));
+  const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16);
+  const float r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Order-preserving map of a float's bits to uint32 (larger float -> larger key).
 // -0.0 is mapped like +0.0 so that the two compare equal.
 __device__ __forceinline__ uint32_t ordered_key(float x) {
