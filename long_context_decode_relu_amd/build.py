@@ -8,6 +8,7 @@ long_context_decode_relu_amd/libssa.so.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import os
 import shutil
 import subprocess
@@ -49,6 +50,16 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_resolved(path: str) -> None:
+    """Load the library with every symbol bound now (no GPU needed): a kernel
+    whose host stub the compiler silently dropped shows up here as an
+    undefined symbol instead of at the first call."""
+    try:
+        ctypes.CDLL(os.path.abspath(path), mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        raise RuntimeError(f"{path} does not load: {e}") from None
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
@@ -58,6 +69,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_resolved(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -6,18 +6,22 @@
 // selected key gets some weight). No position encoding is applied.
 //
 // The G query heads that share a KV head usually select many of the same
-// rows, so each row is read once for all of them. One work-group (two waves)
-// handles a (sequence, KV head, range of 4096 keys): it marks, per key of the
-// range, the heads whose selection holds it (LDS bitmask) and compacts the
-// marked keys in key order. Each wave then takes 64 of those rows at a time,
-// one row per lane: the K rows are gathered HBM -> LDS by direct-to-LDS loads
-// (16-byte pieces XOR-permuted so that each lane reads its own row without
-// bank conflicts), every lane scores its row against all G heads (queries
-// broadcast from LDS), and the softmax statistics are updated once per 64
-// rows and head. The V rows, loaded meanwhile with two dims per lane, are
-// accumulated with the row weights read back from LDS. The softmax runs in
-// base 2 (log2(e) folded into the query). The waves, and then the ranges (in
-// a second kernel), are merged by log-sum-exp in a fixed order.
+// rows, so each row is read once for all of them. Three kernels per call:
+//   bounds   per (sequence, head): where each 2048-key range starts in the
+//            (ascending) selection list, so that a range reads only its part.
+//   sparse   one work-group (two waves) per (sequence, KV head, range of 2048
+//            keys): marks, per key of the range, the heads whose selection
+//            holds it (LDS bitmask) and compacts the marked keys in key order.
+//            Then, 64 rows at a time: the K rows are gathered HBM -> LDS by
+//            direct-to-LDS loads (16-byte pieces XOR-permuted so that each
+//            lane reads its own row without bank conflicts); with one row per
+//            lane, each wave scores the rows against its half of the heads
+//            (queries broadcast from LDS) and updates their softmax
+//            statistics once per 64 rows; each wave then accumulates half of
+//            the value dims for all heads from V rows loaded meanwhile, with
+//            the row weights read back from LDS. The softmax runs in base 2
+//            (log2(e) folded into the query).
+//   combine  merges the ranges by log-sum-exp in a fixed order.
 #include <cmath>
 
 #include "common.h"
@@ -28,52 +32,57 @@ namespace ssa {
 
 namespace {
 
-constexpr int kSpThreads = 128;
-constexpr int kSpWaves = kSpThreads / kWave;
-constexpr int kRange = 4096;   // keys per work-group
-constexpr int kRows = kWave;   // rows per batch: one per lane
+constexpr int kSpThreads = 128;   // two waves
+constexpr int kRange = 2048;       // keys per work-group
+constexpr int kRows = kWave;       // rows per batch: one per lane
 constexpr int kTileBytes = kRows * kHeadDim * 2;  // bf16 rows of a batch
 constexpr int kWaitVm0 = 0x0F70;                  // s_waitcnt vmcnt(0)
 
-// Two dims (2*lane, 2*lane+1) of one V row as stored: a bf16 pair in one
-// register, or two floats.
+// One value dim (64 * wave + lane) of one V row, widened to float.
 template <bool BF16>
-struct VPair;
-template <>
-struct VPair<true> {
-  uint32_t r;
-  __device__ __forceinline__ void load(const void* base, size_t row, int lane) {
-    r = reinterpret_cast<const uint32_t*>(base)[row * 64 + lane];
+__device__ __forceinline__ float load_vdim(const void* base, size_t row, int dim) {
+  if constexpr (BF16)
+    return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[row * kHeadDim + dim] << 16);
+  else
+    return reinterpret_cast<const float*>(base)[row * kHeadDim + dim];
+}
+
+// bounds[row][p] = first position of the row's selection list whose index is
+// >= p * kRange (p = 0 .. P); the lists are ascending, so range p of the
+// list is [bounds[p], bounds[p+1]). Every value lies in [0, count].
+__global__ __launch_bounds__(256) void sparse_bounds(const int32_t* __restrict__ sel_idx,
+                                                     const int32_t* __restrict__ sel_count,
+                                                     int stride, int P, int32_t* __restrict__ bounds) {
+  const int row = blockIdx.x;
+  const int cnt = max(0, min(sel_count[row], stride));
+  const int32_t* list = sel_idx + (size_t)row * stride;
+  int32_t* out = bounds + (size_t)row * (P + 1);
+  auto range_of = [&](int i) { return min(max(list[i], 0) / kRange, P); };
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const int r = range_of(i);
+    const int rp = i == 0 ? -1 : range_of(i - 1);
+    for (int q = rp + 1; q <= r; ++q) out[q] = i;
   }
-  __device__ __forceinline__ float x() const { return bf16_lo(r); }
-  __device__ __forceinline__ float y() const { return bf16_hi(r); }
-};
-template <>
-struct VPair<false> {
-  f32x2 r;
-  __device__ __forceinline__ void load(const void* base, size_t row, int lane) {
-    r = reinterpret_cast<const f32x2*>(base)[row * 64 + lane];
-  }
-  __device__ __forceinline__ float x() const { return r.x; }
-  __device__ __forceinline__ float y() const { return r.y; }
-};
+  const int rl = cnt > 0 ? range_of(cnt - 1) : -1;
+  for (int q = threadIdx.x; q <= P; q += blockDim.x)
+    if (q > rl) out[q] = cnt;
+}
 
 template <int G, bool BF16, bool NORMQ, bool NORMK>
 __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ sel_idx,
-    const int32_t* __restrict__ sel_count, int stride, int Hq, int Hkv, int Nmax, int P,
-    float scale, float eps, float* __restrict__ part_m, float* __restrict__ part_l,
-    float* __restrict__ part_acc) {
+    const int32_t* __restrict__ sel_count, const int32_t* __restrict__ bounds, int stride, int Hq,
+    int Hkv, int Nmax, int P, float scale, float eps, float* __restrict__ part_m,
+    float* __restrict__ part_l, float* __restrict__ part_acc) {
+  constexpr int HW = G > 1 ? G / 2 : 1;  // heads scored by each wave
   __shared__ uint32_t s_mask[kRange / 4];   // one byte of head bits per key
   __shared__ int32_t s_list[kRange];        // (offset << 8) | head bits, key order
-  __shared__ int32_t s_scan[kSpThreads];
+  __shared__ int32_t s_tot[2];
   __shared__ __attribute__((aligned(16))) float s_q[G][kHeadDim];
-  __shared__ __attribute__((aligned(16))) float s_p[kSpWaves][kRows][G];
-  __shared__ float s_m[kSpWaves][G], s_l[kSpWaves][G];
-  // K rows of the current batch (bf16); reused for the wave merge at the end
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[kSpWaves][BF16 ? kTileBytes : 16];
-  __shared__ float s_acc[kSpWaves][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_p[kRows][G < 4 ? 4 : G];
+  __shared__ __attribute__((aligned(16))) float s_sc[G < 4 ? 4 : G];
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kTileBytes : 16];
 
   const int p = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -82,34 +91,35 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
   const int lo = p * kRange;
   if (lo >= n) return;  // the combine reads only the ranges that exist
   const int hi = min(n, lo + kRange);
+  const size_t hrow0 = (size_t)b * Hq + (size_t)kvh * G;
+
+  // this wave's query heads (raw values; normalised below)
+  float qa[HW][2];
+#pragma unroll
+  for (int j = 0; j < HW; ++j) {
+    const int h = min(wave * HW + j, G - 1);
+    const float* qh = q + (hrow0 + h) * kHeadDim;
+    qa[j][0] = qh[2 * lane];
+    qa[j][1] = qh[2 * lane + 1];
+  }
 
   for (int i = tid; i < kRange / 4; i += kSpThreads) s_mask[i] = 0;
   __syncthreads();
-  // 1. head bits per key of the range: each wave scans whole selection lists
-  //    of G / 2 heads, with all loads of a list in flight together, and marks
-  //    the entries in range
-  constexpr int kLoads = 4;  // list entries per lane per round
-  for (int h = wave; h < G; h += kSpWaves) {
-    const size_t row = (size_t)b * Hq + (size_t)kvh * G + h;
-    const int32_t* list = sel_idx + row * stride;
-    const int cnt = min(sel_count[row], stride);
-    for (int i0 = 0; i0 < cnt; i0 += kWave * 16) {
-      int idx[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) idx[u] = list[min(i0 + u * kWave + lane, max(cnt - 1, 0))];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = idx[u];
-        if (i0 + u * kWave + lane < cnt && i >= lo && i < hi) {
-          const int off = i - lo;
-          atomicOr(&s_mask[off >> 2], 1u << (h + 8 * (off & 3)));
-        }
+  // 1. head bits per key of the range, from each list's part for this range
+  for (int h = wave; h < G; h += 2) {
+    const int32_t* list = sel_idx + (hrow0 + h) * stride;
+    const int32_t* bd = bounds + (hrow0 + h) * (P + 1);
+    const int a0 = bd[p], a1 = bd[p + 1];
+    for (int i = a0 + lane; i < a1; i += kWave) {
+      const int idx = list[i];
+      if (idx >= lo && idx < hi) {
+        const int off = idx - lo;
+        atomicOr(&s_mask[off >> 2], 1u << (h + 8 * (off & 3)));
       }
     }
   }
-  (void)kLoads;
   __syncthreads();
-  // 2. compact the marked keys in key order (each thread owns 32 consecutive keys)
+  // 2. compact the marked keys in key order (each thread owns 16 consecutive keys)
   constexpr int kPer = kRange / kSpThreads;
   int mine = 0;
 #pragma unroll
@@ -118,16 +128,16 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) mine += ((w >> (8 * e)) & 0xffu) ? 1 : 0;
   }
-  s_scan[tid] = mine;
-  __syncthreads();
-  for (int o = 1; o < kSpThreads; o <<= 1) {
-    const int t = tid >= o ? s_scan[tid - o] : 0;
-    __syncthreads();
-    s_scan[tid] += t;
-    __syncthreads();
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
   }
-  const int total = __builtin_amdgcn_readfirstlane(s_scan[kSpThreads - 1]);
-  int pos = s_scan[tid] - mine;
+  if (lane == kWave - 1) s_tot[wave] = incl;
+  __syncthreads();
+  const int total = s_tot[0] + s_tot[1];
+  int pos = incl - mine + (wave == 1 ? s_tot[0] : 0);
 #pragma unroll
   for (int j = 0; j < kPer / 4; ++j) {
     const uint32_t w = s_mask[tid * (kPer / 4) + j];
@@ -137,62 +147,68 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
       if (hb) s_list[pos++] = ((tid * kPer + 4 * j + e) << 8) | (int)hb;
     }
   }
-
-  // 3. queries of the group in LDS, normalised and scaled by scale * log2(e)
+  // 3. this wave's queries in LDS, normalised and scaled by scale * log2(e)
   //    (the softmax runs in base 2: exp(t - m) = exp2(t2 - m2), t2 = t log2 e)
-  {
-    const float* qg = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
-    for (int h = wave; h < G; h += kSpWaves) {
-      const float a0 = qg[h * kHeadDim + 2 * lane], a1 = qg[h * kHeadDim + 2 * lane + 1];
-      float f = scale * 1.4426950408889634f;
-      if constexpr (NORMQ) f = f / sqrtf(wave_sum(a0 * a0 + a1 * a1) * (1.0f / kHeadDim) + eps);
-      s_q[h][2 * lane] = a0 * f;
-      s_q[h][2 * lane + 1] = a1 * f;
+#pragma unroll
+  for (int j = 0; j < HW; ++j) {
+    const int h = wave * HW + j;
+    float f = scale * 1.4426950408889634f;
+    if constexpr (NORMQ)
+      f = f / sqrtf(wave_sum_dpp(qa[j][0] * qa[j][0] + qa[j][1] * qa[j][1]) * (1.0f / kHeadDim) + eps);
+    if (h < G) {
+      s_q[h][2 * lane] = qa[j][0] * f;
+      s_q[h][2 * lane + 1] = qa[j][1] * f;
     }
   }
   __syncthreads();
 
-  float m[G], l[G], acc[G][2];
+  float m[HW], l[HW];  // softmax state of this wave's heads (l: this lane's rows)
+  float acc[G];        // dim 64 * wave + lane of every head
 #pragma unroll
-  for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; acc[h][0] = acc[h][1] = 0.f; }
+  for (int j = 0; j < HW; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.f;
 
   const size_t row0 = ((size_t)b * Hkv + kvh) * (size_t)Nmax + lo;
   const uint8_t* kb8 = static_cast<const uint8_t*>(k);
-  uint8_t* tile = &s_tile[wave][0];
-  for (int r0 = wave * kRows; r0 < total; r0 += kSpWaves * kRows) {
+  // through a plain pointer: the direct-to-LDS builtin called on the
+  // __shared__ array itself makes the host pass drop this kernel's stub
+  uint8_t* tile = s_tile;
+  const int vdim = kWave * wave + lane;
+  for (int r0 = 0; r0 < total; r0 += kRows) {
     const int nb = min(kRows, total - r0);
     const int ent = s_list[r0 + min(lane, nb - 1)];
+    const int off = ent >> 8;  // this lane's row (rows past nb repeat the last one)
     const int hb = lane < nb ? (ent & 0xff) : 0;
-    // V rows of the batch: two dims of every row per lane, issued once the K
-    // rows are in LDS so that they are in flight while the scores are formed
-    VPair<BF16> vv[kRows];
-    auto load_v = [&](VPair<BF16>(&dst)[kRows]) {
+    float vv[kRows];
+    auto load_v = [&]() {
 #pragma unroll
-      for (int j = 0; j < kRows; ++j) {
-        const int ej = __builtin_amdgcn_readfirstlane(s_list[r0 + min(j, nb - 1)]) >> 8;
-        dst[j].load(v, row0 + ej, lane);
-      }
+      for (int j = 0; j < kRows; ++j)
+        vv[j] = load_vdim<BF16>(v, row0 + __builtin_amdgcn_readlane(off, j), vdim);
     };
-    // 4a. this lane's K row, widened to float 8 dims at a time
-    float t[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) t[h] = 0.f;
-    float ss = 0.f;
+    // 4a. K rows: each wave copies half of them to LDS; V dims in flight meanwhile
     if constexpr (BF16) {
       // rows 4i .. 4i+3 per 1 KB load; piece c of row r lands in slot c ^ (r & 15)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int u = 0; u < 8; ++u) {
+        const int i = wave * 8 + u;
         const int r = 4 * i + (lane >> 4);
-        const int er = s_list[r0 + min(r, nb - 1)] >> 8;
+        const int er = __shfl(off, r, kWave);
         __builtin_amdgcn_global_load_lds(
-            kb8 + (row0 + er) * (kHeadDim * 2) + ((((lane & 15) ^ (r & 15))) << 4), tile + i * 1024,
-            16, 0, 0);
+            kb8 + (row0 + er) * (kHeadDim * 2) + (((lane & 15) ^ (r & 15)) << 4),
+            tile + i * 1024, 16, 0, 0);
       }
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      load_v(vv);
+    }
+    load_v();
+    __syncthreads();  // both halves of the K rows are in LDS
+    // 4b. scores of this lane's row against this wave's heads
+    float t[HW];
+#pragma unroll
+    for (int j = 0; j < HW; ++j) t[j] = 0.f;
+    float ss = 0.f;
+    if constexpr (BF16) {
       const uint8_t* myrow = tile + lane * (kHeadDim * 2);
-      // not unrolled further: keeps the broadcast query reads of only a few
-      // chunks live at a time
 #pragma unroll 2
       for (int c = 0; c < 16; ++c) {
         const u32x4 pc = *reinterpret_cast<const u32x4*>(myrow + ((c ^ (lane & 15)) << 4));
@@ -204,107 +220,105 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
           for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const f32x4 qa = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c]);
-          const f32x4 qb = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c + 4]);
-          t[h] = fmaf(qa[0], x[0], t[h]);
-          t[h] = fmaf(qa[1], x[1], t[h]);
-          t[h] = fmaf(qa[2], x[2], t[h]);
-          t[h] = fmaf(qa[3], x[3], t[h]);
-          t[h] = fmaf(qb[0], x[4], t[h]);
-          t[h] = fmaf(qb[1], x[5], t[h]);
-          t[h] = fmaf(qb[2], x[6], t[h]);
-          t[h] = fmaf(qb[3], x[7], t[h]);
+        for (int j = 0; j < HW; ++j) {
+          const int h = min(wave * HW + j, G - 1);
+          const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c]);
+          const f32x4 qb4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c + 4]);
+          t[j] = fmaf(qa4[0], x[0], t[j]);
+          t[j] = fmaf(qa4[1], x[1], t[j]);
+          t[j] = fmaf(qa4[2], x[2], t[j]);
+          t[j] = fmaf(qa4[3], x[3], t[j]);
+          t[j] = fmaf(qb4[0], x[4], t[j]);
+          t[j] = fmaf(qb4[1], x[5], t[j]);
+          t[j] = fmaf(qb4[2], x[6], t[j]);
+          t[j] = fmaf(qb4[3], x[7], t[j]);
         }
       }
     } else {
-      load_v(vv);
-      const f32x4* kr = reinterpret_cast<const f32x4*>(k) + (row0 + (ent >> 8)) * (kHeadDim / 4);
+      const f32x4* kr = reinterpret_cast<const f32x4*>(k) + (row0 + off) * (kHeadDim / 4);
 #pragma unroll 2
       for (int c = 0; c < kHeadDim / 4; ++c) {
         const f32x4 x = kr[c];
         if constexpr (NORMK) ss = fmaf(x[0], x[0], fmaf(x[1], x[1], fmaf(x[2], x[2], fmaf(x[3], x[3], ss))));
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const f32x4 qa = *reinterpret_cast<const f32x4*>(&s_q[h][4 * c]);
-          t[h] = fmaf(qa[0], x[0], fmaf(qa[1], x[1], fmaf(qa[2], x[2], fmaf(qa[3], x[3], t[h]))));
+        for (int j = 0; j < HW; ++j) {
+          const int h = min(wave * HW + j, G - 1);
+          const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][4 * c]);
+          t[j] = fmaf(qa4[0], x[0], fmaf(qa4[1], x[1], fmaf(qa4[2], x[2], fmaf(qa4[3], x[3], t[j]))));
         }
       }
     }
     float kf = 1.f;
     if constexpr (NORMK) kf = 1.f / sqrtf(ss * (1.0f / kHeadDim) + eps);
-    // 4c. per head: batch maximum, rescale, row weights p = 2^(t - m)
+    // 4c. this wave's heads: batch maximum, rescale factor, row weights
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int j = 0; j < HW; ++j) {
+      const int h = wave * HW + j;
+      if (h >= G) break;
       const bool on = (hb >> h) & 1;
-      const float th = on ? t[h] * kf : -INFINITY;
+      const float th = on ? t[j] * kf : -INFINITY;
       const float bm = wave_max_dpp(th);
-      float pr = 0.f;
+      float pr = 0.f, sc = 1.f;
       if (bm != -INFINITY) {  // some row of the batch is selected by head h
-        const float mn = fmaxf(m[h], bm);
-        const float sc = exp2f(m[h] - mn);  // 0 while m is still -inf
+        const float mn = fmaxf(m[j], bm);
+        sc = exp2f(m[j] - mn);  // 0 while m is still -inf
         pr = on ? exp2f(th - mn) : 0.f;
-        l[h] = fmaf(l[h], sc, pr);
-        acc[h][0] *= sc;
-        acc[h][1] *= sc;
-        m[h] = mn;
+        l[j] = fmaf(l[j], sc, pr);
+        m[j] = mn;
       }
-      s_p[wave][lane][h] = pr;
+      s_p[lane][h] = pr;
+      if (lane == 0) s_sc[h] = sc;
     }
-    // 4d. acc[h] += p[row][h] * v[row] over the batch
-    //     (rows past nb have p = 0 and repeat a valid row)
+    __syncthreads();  // every head's weights and rescale factor are in LDS
+    // 4d. acc[h] (this lane's dim) = acc[h] * sc[h] + sum_j p[j][h] v[j]
+    {
+      float sc[G];
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int h = 0; h < G; h += 4) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(&s_sc[h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[h + e] = s4[e];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h] = s_sc[h];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] *= sc[h];
+    }
 #pragma unroll
     for (int j = 0; j < kRows; ++j) {
       float pj[G];
       if constexpr (G >= 4) {
 #pragma unroll
         for (int h = 0; h < G; h += 4) {
-          const f32x4 pq = *reinterpret_cast<const f32x4*>(&s_p[wave][j][h]);
+          const f32x4 pq = *reinterpret_cast<const f32x4*>(&s_p[j][h]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) pj[h + e] = pq[e];
         }
       } else {
 #pragma unroll
-        for (int h = 0; h < G; ++h) pj[h] = s_p[wave][j][h];
+        for (int h = 0; h < G; ++h) pj[h] = s_p[j][h];
       }
-      const float vx = vv[j].x(), vy = vv[j].y();
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        acc[h][0] = fmaf(pj[h], vx, acc[h][0]);
-        acc[h][1] = fmaf(pj[h], vy, acc[h][1]);
-      }
+      for (int h = 0; h < G; ++h) acc[h] = fmaf(pj[h], vv[j], acc[h]);
     }
+    __syncthreads();  // the next batch overwrites the K rows and the weights
   }
 
-  // 5. merge the waves (fixed order) and write this range's partial; each
-  //    lane's l holds the weights of its own rows
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lh = wave_sum_dpp(l[h]);
-    if (lane == 0) { s_m[wave][h] = m[h]; s_l[wave][h] = lh; }
-    s_acc[wave][h][2 * lane] = acc[h][0];
-    s_acc[wave][h][2 * lane + 1] = acc[h][1];
-  }
-  __syncthreads();
+  // 5. this range's partial: each wave writes its dims of every head and the
+  //    statistics of its own heads (l summed over the lanes' rows)
   const size_t slot = ((size_t)b * Hkv + kvh) * P + p;
-  for (int i = tid; i < G * kHeadDim; i += kSpThreads) {
-    const int h = i / kHeadDim, d = i - h * kHeadDim;
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSpWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float a = 0.f, ls = 0.f;
-    if (M != -INFINITY) {
+  for (int h = 0; h < G; ++h) part_acc[(slot * G + h) * kHeadDim + vdim] = acc[h];
 #pragma unroll
-      for (int w = 0; w < kSpWaves; ++w) {
-        const float e = s_m[w][h] == -INFINITY ? 0.f : exp2f(s_m[w][h] - M);
-        a = fmaf(e, s_acc[w][h][d], a);
-        ls = fmaf(e, s_l[w][h], ls);
-      }
-    }
-    part_acc[(slot * G + h) * kHeadDim + d] = a;
-    if (d == 0) {
-      part_m[slot * G + h] = M;
-      part_l[slot * G + h] = ls;
+  for (int j = 0; j < HW; ++j) {
+    const int h = wave * HW + j;
+    const float lh = wave_sum_dpp(l[j]);
+    if (h < G && lane == 0) {
+      part_m[slot * G + h] = m[j];
+      part_l[slot * G + h] = lh;
     }
   }
 }
@@ -359,7 +373,7 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(
 }
 
 struct SpLayout {
-  size_t m, l, acc, total;
+  size_t m, l, acc, bounds, total;
   int P;
 };
 
@@ -371,15 +385,17 @@ SpLayout sp_layout(int B, int Hq, int Hkv, int max_ctx) {
   s.m = 0;
   s.l = align_up(slots * G * sizeof(float), 256);
   s.acc = s.l + align_up(slots * G * sizeof(float), 256);
-  s.total = s.acc + align_up(slots * G * kHeadDim * sizeof(float), 256);
+  s.bounds = s.acc + align_up(slots * G * kHeadDim * sizeof(float), 256);
+  s.total = s.bounds + align_up((size_t)B * Hq * (s.P + 1) * sizeof(int32_t), 256);
   return s;
 }
 
 template <int G, bool BF16, bool NORMQ, bool NORMK>
 void launch_t(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_t stream) {
   hipLaunchKernelGGL((sparse_kernel<G, BF16, NORMQ, NORMK>), dim3(s.P, a.Hkv, a.B), dim3(kSpThreads),
-                     0, stream, a.q, a.k, a.v, a.ctx_lens, a.sel_idx, a.sel_count, a.sel_stride,
-                     a.Hq, a.Hkv, a.Nmax, s.P, a.scale, a.eps, reinterpret_cast<float*>(ws + s.m),
+                     0, stream, a.q, a.k, a.v, a.ctx_lens, a.sel_idx, a.sel_count,
+                     reinterpret_cast<const int32_t*>(ws + s.bounds), a.sel_stride, a.Hq, a.Hkv,
+                     a.Nmax, s.P, a.scale, a.eps, reinterpret_cast<float*>(ws + s.m),
                      reinterpret_cast<float*>(ws + s.l), reinterpret_cast<float*>(ws + s.acc));
 }
 
@@ -406,6 +422,8 @@ hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream) {
   const SpLayout s = sp_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
   char* ws = static_cast<char*>(a.ws);
   if (s.P > 0) {
+    hipLaunchKernelGGL(sparse_bounds, dim3(a.B * a.Hq), dim3(256), 0, stream, a.sel_idx,
+                       a.sel_count, a.sel_stride, s.P, reinterpret_cast<int32_t*>(ws + s.bounds));
     switch (G) {
       case 1: launch_g<1>(a, s, ws, stream); break;
       case 2: launch_g<2>(a, s, ws, stream); break;
