@@ -45,6 +45,8 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxStreams = 1024;       // (sequence, KV head) streams per call
 constexpr int kTileKeys = kWave;        // one key per lane
 constexpr int kTileBytesBf16 = kTileKeys * kHeadDim * 2;
+constexpr int kVS = 16;                 // survivor V rows of a tile loaded ahead
+constexpr int kXcds = 8;                // accelerator dies of an MI355X
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
 constexpr int kWaitVm0 = 0x0F70;
@@ -219,20 +221,15 @@ __device__ __forceinline__ void qwait(QBuf<G>& r, float (&a)[G], float& x) {
 
 // Scores of one key row against the G query heads: acc[h] = sum_d q[h][d] k[d],
 // streamed over 32 sub-chunks of 4 dims with one sub-chunk of lookahead.
-// The 16 loads of the wave's next tile (bf16) are spread over the sub-chunks,
-// one every second sub-chunk, so that a full memory queue delays at most one
-// load instead of stalling the wave before any FMA is issued.
 template <int G, bool BF16, bool NORMK, int... SC>
 __device__ __forceinline__ void score_row(const KeyRow<BF16>& kr, const float* qg, float (&acc)[G],
-                                          float& ksq, const TileFetch& next,
-                                          std::integer_sequence<int, SC...>) {
+                                          float& ksq, std::integer_sequence<int, SC...>) {
   QBuf<G> qa, qb;
   qload<G, 0>(qa, qg, acc, ksq);
   auto step = [&](auto sc_c) {
     constexpr int sc = decltype(sc_c)::value;
     qwait(qa, acc, ksq);
     if constexpr (sc + 1 < 32) qload<G, sc + 1>(qb, qg, acc, ksq);
-    if constexpr (BF16 && (sc & 1) == 0) next.load(sc >> 1);
     float e[8];
     kr.chunk(sc >> 1, e);
     constexpr int o = 4 * (sc & 1);
@@ -337,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const int32_t* __restrict__ ctx_lens, const int* __restrict__ tile_pre,
     const int* __restrict__ slot_pre, float* __restrict__ scores, float* __restrict__ part_num,
     float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
-    int B, int Hq, int Hkv, int Nmax, float eps) {
+    int B, int Hq, int Hkv, int Nmax, float eps, int cus_per_xcd) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -349,7 +346,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   // With more waves than tiles only the first T waves work (one tile each),
   // so that every working wave owns at least one tile.
   const int64_t W = min((int64_t)gridDim.x * kWaves, T);
-  const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+  // XCD-aware numbering: work-group b runs on XCD b % 8 and, within it, the
+  // work-groups fill the CUs in turn. Renumbering them so that the
+  // work-groups sharing a CU, and neighbouring CUs, hold neighbouring tile
+  // ranges keeps each XCD's L2 and each CU's scalar cache on few streams
+  // (the query table of a stream is read by scalar loads on every tile).
+  int lb = blockIdx.x;
+  {
+    const int nb = gridDim.x;
+    if (cus_per_xcd > 0 && nb % kXcds == 0) {
+      const int per = nb / kXcds;
+      const int x = blockIdx.x % kXcds, i = blockIdx.x / kXcds;
+      lb = per % cus_per_xcd == 0
+               ? x * per + (i % cus_per_xcd) * (per / cus_per_xcd) + i / cus_per_xcd
+               : x * per + i;
+    }
+  }
+  const int64_t w = (int64_t)lb * kWaves + wave;
   if (w >= W) return;
   const int64_t t0 = w * T / W, t1 = (w + 1) * T / W;
 
@@ -425,99 +438,237 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   };
   reset();
 
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t >= cur.s1) {  // entering the next non-empty stream
-      flush(cur);
-      reset();
-      int nj = cur.j + 1;
-      while (tile_pre[nj + 1] <= t) ++nj;
-      cur = stream_info(nj);
-    }
-    const int b = cur.b, kvh = cur.kvh;
-    const float* qg = qt + (size_t)cur.j * (kHeadDim * G);
-    const size_t row0 = (size_t)cur.j * Nmax;
-    float* srow = scores ? scores + ((size_t)b * Hq + (size_t)kvh * G) * Nmax : nullptr;
-    const int base = (int)(t - cur.s0) * kTileKeys;
-    const int key = base + lane;
-    const bool valid = key < cur.n;
+  // the stream holding tile t (t >= cur.s0)
+  auto stream_at = [&](int64_t t) {
+    if (t < cur.s1) return cur;
+    int nj = cur.j + 1;
+    while (tile_pre[nj + 1] <= t) ++nj;
+    return stream_info(nj);
+  };
 
-    KeyRow<BF16> kr;
-    if constexpr (BF16) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this tile has landed in LDS
+  if constexpr (BF16) {
+    // Pipelined over the wave's tiles. Iteration t reads tile t from LDS,
+    // then issues the score stores of tile t-1, the copy of tile t+1 into LDS
+    // and the V rows of tile t-1's survivors, scores tile t while all of that
+    // is in flight, waits once, and only then adds tile t-1's V rows. Every
+    // memory operation therefore has a whole scoring pass to complete, and
+    // no V row is ever waited for behind a tile copy issued after it (the
+    // vector-memory counter completes in order).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // tile t0 is in LDS
+    bool has_prev = false;
+    size_t p_row = 0;      // cache row of key 0 of tile t-1
+    int p_key = 0;         // this lane's key in tile t-1
+    bool p_valid = false;
+    uint64_t p_mask = 0;   // tile t-1's survivors
+    float* p_srow = nullptr;
+    float p_wt[G], p_s[G];
+
+    // V rows of tile t-1's survivors still in `m` (after the first kVS), four
+    // at a time; nothing else is in flight when this runs
+    auto v_rows_sync = [&](uint64_t m) {
+      while (m) {
+        int js[4];
+        float live[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (m) {
+            js[u] = __builtin_ctzll(m);
+            m &= m - 1;
+            live[u] = 1.f;
+          } else {
+            js[u] = js[0];
+            live[u] = 0.f;
+          }
+        }
+        float2 vv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vv[u] = load_v_pair<BF16>(v, p_row + js[u], lane);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float wj = readlane_f(p_wt[h], js[u]) * live[u];
+            num[h][0] = fmaf(wj, vv[u].x, num[h][0]);
+            num[h][1] = fmaf(wj, vv[u].y, num[h][1]);
+          }
+        }
+      }
+    };
+
+    for (int64_t t = t0; t < t1; ++t) {
+      const Stream st = stream_at(t);
+      const int base = (int)(t - st.s0) * kTileKeys;
+      const int key = base + lane;
+      const bool valid = key < st.n;
+
+      // 1. tile t: LDS -> registers, after which the LDS copy may be refilled
+      KeyRow<BF16> kr;
       tile_read_bf16(my_tile, lane, kr);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0); // rows are in registers: LDS may be refilled
-    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+
+      // 2a. score stores of tile t-1
+      if (has_prev && p_srow && p_valid) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) p_srow[(size_t)h * Nmax + p_key] = p_s[h];
+      }
+      // 2b. tile t+1 -> LDS
+      if (t + 1 < t1) {
+        const TileFetch next = fetch_of(stream_at(t + 1), t + 1);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) next.load(i);
+      }
+      // 2c. the first kVS survivors of tile t-1 (raw bf16 pairs)
+      uint64_t m = p_mask;
+      int vj[kVS];
+      uint32_t vr[kVS];
+      int nv = 0;
+#pragma unroll
+      for (int u = 0; u < kVS; ++u) {
+        if (m) {
+          vj[u] = __builtin_ctzll(m);
+          m &= m - 1;
+          vr[u] = reinterpret_cast<const uint32_t*>(v)[(p_row + vj[u]) * 64 + lane];
+          nv = u + 1;
+        }
+      }
+
+      // 3. scores of tile t
+      const float* qg = qt + (size_t)st.j * (kHeadDim * G);
+      float acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.f;
+      float ksq = 0.f;
+      score_row<G, BF16, NORMK>(kr, qg, acc, ksq, std::make_integer_sequence<int, 32>{});
+      float kf = 1.f;
+      if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
+
+      // 4. everything issued in step 2 has landed
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+      // 5. tile t-1's V rows, into the accumulators of its stream
+#pragma unroll
+      for (int u = 0; u < kVS; ++u) {
+        if (u < nv) {
+          const float vx = bf16_lo(vr[u]), vy = bf16_hi(vr[u]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float wj = readlane_f(p_wt[h], vj[u]);
+            num[h][0] = fmaf(wj, vx, num[h][0]);
+            num[h][1] = fmaf(wj, vy, num[h][1]);
+          }
+        }
+      }
+      if (m) v_rows_sync(m);
+
+      // 6. entering the next non-empty stream: tile t-1 closed the last one
+      if (st.j != cur.j) {
+        flush(cur);
+        reset();
+        cur = st;
+      }
+
+      // 7. weights of tile t
+      float* srow = scores ? scores + ((size_t)st.b * Hq + (size_t)st.kvh * G) * Nmax : nullptr;
+      bool any = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sv = NORMK ? acc[h] * kf : acc[h];
+        const bool pos = valid && sv > 0.f;
+        p_s[h] = sv;
+        p_wt[h] = pos ? sv * sv : 0.f;
+        den[h] += p_wt[h];
+        nnz[h] += pos ? 1 : 0;
+        any |= pos;
+      }
+      p_mask = __ballot(any);
+      vrows += __popcll(p_mask);
+      p_row = (size_t)st.j * Nmax + base;
+      p_key = key;
+      p_valid = valid;
+      p_srow = srow;
+      has_prev = true;
+    }
+    // the last tile's score stores and V rows
+    if (has_prev) {
+      if (p_srow && p_valid) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) p_srow[(size_t)h * Nmax + p_key] = p_s[h];
+      }
+      v_rows_sync(p_mask);
+    }
+    flush(cur);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  } else {
+    for (int64_t t = t0; t < t1; ++t) {
+      if (t >= cur.s1) {  // entering the next non-empty stream
+        flush(cur);
+        reset();
+        cur = stream_at(t);
+      }
+      const int b = cur.b, kvh = cur.kvh;
+      const float* qg = qt + (size_t)cur.j * (kHeadDim * G);
+      const size_t row0 = (size_t)cur.j * Nmax;
+      float* srow = scores ? scores + ((size_t)b * Hq + (size_t)kvh * G) * Nmax : nullptr;
+      const int base = (int)(t - cur.s0) * kTileKeys;
+      const int key = base + lane;
+      const bool valid = key < cur.n;
+
+      KeyRow<BF16> kr;
       row_load_f32(k, row0 + min(key, cur.n - 1), kr);
-    }
-    // the next tile of this wave (possibly in the next stream) streams in
-    // while this one is scored
-    TileFetch next;
-    next.nvalid = 0;
-    if (t + 1 < t1) {
-      if (t + 1 < cur.s1) {
-        next = fetch_of(cur, t + 1);
-      } else {
-        int nj = cur.j + 1;
-        while (tile_pre[nj + 1] <= t + 1) ++nj;
-        next = fetch_of(stream_info(nj), t + 1);
+      float acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.f;
+      float ksq = 0.f;
+      score_row<G, BF16, NORMK>(kr, qg, acc, ksq, std::make_integer_sequence<int, 32>{});
+      float kf = 1.f;
+      if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
+
+      float wt[G];
+      bool any = false;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sv = NORMK ? acc[h] * kf : acc[h];
+        if (srow && valid) srow[(size_t)h * Nmax + key] = sv;
+        const bool pos = valid && sv > 0.f;
+        wt[h] = pos ? sv * sv : 0.f;
+        den[h] += wt[h];
+        nnz[h] += pos ? 1 : 0;
+        any |= pos;
       }
-    }
-    if constexpr (!BF16) next.nvalid = 0;
 
-    float acc[G];
+      uint64_t mask = __ballot(any);
+      vrows += __popcll(mask);
+      // V rows of survivors only, four at a time.
+      while (mask) {
+        int js[4];
+        float live[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-    float ksq = 0.f;
-    score_row<G, BF16, NORMK>(kr, qg, acc, ksq, next, std::make_integer_sequence<int, 32>{});
-    float kf = 1.f;
-    if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
-
-    float wt[G];
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s = NORMK ? acc[h] * kf : acc[h];
-      if (srow && valid) srow[(size_t)h * Nmax + key] = s;
-      bool pos = valid && s > 0.f;
-      wt[h] = pos ? s * s : 0.f;
-      den[h] += wt[h];
-      nnz[h] += pos ? 1 : 0;
-      any |= pos;
-    }
-
-    uint64_t mask = __ballot(any);
-    vrows += __popcll(mask);
-    // V rows of survivors only, four at a time.
-    while (mask) {
-      int js[4];
-      float live[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (mask) {
-          js[u] = __builtin_ctzll(mask);
-          mask &= mask - 1;
-          live[u] = 1.f;
-        } else {
-          js[u] = js[0];
-          live[u] = 0.f;
+        for (int u = 0; u < 4; ++u) {
+          if (mask) {
+            js[u] = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            live[u] = 1.f;
+          } else {
+            js[u] = js[0];
+            live[u] = 0.f;
+          }
         }
-      }
-      float2 vv[4];
+        float2 vv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vv[u] = load_v_pair<BF16>(v, row0 + base + js[u], lane);
+        for (int u = 0; u < 4; ++u) vv[u] = load_v_pair<BF16>(v, row0 + base + js[u], lane);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float wj = readlane_f(wt[h], js[u]) * live[u];
-          num[h][0] = fmaf(wj, vv[u].x, num[h][0]);
-          num[h][1] = fmaf(wj, vv[u].y, num[h][1]);
+          for (int h = 0; h < G; ++h) {
+            const float wj = readlane_f(wt[h], js[u]) * live[u];
+            num[h][0] = fmaf(wj, vv[u].x, num[h][0]);
+            num[h][1] = fmaf(wj, vv[u].y, num[h][1]);
+          }
         }
       }
     }
+    flush(cur);
   }
-  flush(cur);
-  if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 // Sum the partials of each (sequence, query head) in slot order and divide by
@@ -608,7 +759,8 @@ template <int G, bool BF16, bool NORMK>
 hipError_t launch_t(const Launch& L, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_full_kernel<G, BF16, NORMK>), dim3(grid), dim3(kThreads), 0, stream,
                      L.qt, L.k, L.v, L.ctx_lens, L.tile_pre, L.slot_pre, L.scores, L.num, L.den,
-                     L.nnz, L.vrows, L.B, L.Hq, L.Hkv, L.Nmax, L.eps);
+                     L.nnz, L.vrows, L.B, L.Hq, L.Hkv, L.Nmax, L.eps,
+                     device_cu_count() % kXcds == 0 ? device_cu_count() / kXcds : 0);
   return hipGetLastError();
 }
 
