@@ -30,6 +30,9 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
@@ -62,9 +65,10 @@ def _unit(rng: np.random.Generator, d: int) -> np.ndarray:
 
 
 def _rows_to_rms1(x: np.ndarray) -> np.ndarray:
-    """Scale each row to Euclidean norm sqrt(D) (the stored-key recipe)."""
-    nrm = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True))
-    return (x * (np.sqrt(x.shape[-1]) / nrm)).astype(np.float32)
+    """Scale each row to Euclidean norm sqrt(D) (the stored-key recipe), in float32."""
+    x = np.asarray(x, dtype=np.float32)
+    nrm = np.sqrt(np.einsum("ij,ij->i", x, x))
+    return x * (np.float32(np.sqrt(x.shape[-1])) / nrm)[:, None]
 
 
 @dataclass
@@ -113,9 +117,12 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
     L = n_sparse_layers
     qs = np.empty((L, B, Hq, D), dtype=np.float32)
     sigma = 1.0 / np.sqrt(D)
-    for b in range(B):
+
+    def fill_stream(b: int, kvh: int) -> None:
+        # every (sequence, KV head) draws from its own seeded stream, so the
+        # streams can be filled in any order (or concurrently)
         n = int(ctx[b])
-        for kvh in range(Hkv):
+        if True:
             r = _rng(seed, 1, b, kvh)
             heads = slice(kvh * g, (kvh + 1) * g)
             if recipe == "planted":
@@ -141,6 +148,14 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
             else:
                 k[b, kvh, n:] = 0
                 v[b, kvh, n:] = 0
+
+    jobs = [(b, kvh) for b in range(B) for kvh in range(Hkv)]
+    if sum(int(ctx[b]) for b, _ in jobs) > (1 << 18):
+        with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda j: fill_stream(*j), jobs))
+    else:
+        for j in jobs:
+            fill_stream(*j)
     return Workload(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
                     kv_capacity=nmax, kv_dtype=kv_dtype, ctx_lens=ctx, q=q, k=k, v=v,
                     q_sparse=qs, planted_p=p if recipe == "planted" else None,
