@@ -100,21 +100,34 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool act)
 }
 
 // Exclusive prefix over the work-group of one int per thread; returns the
-// thread's prefix and writes the total to *total.
+// thread's prefix and writes the total to *total. Waves scan with shuffles;
+// the 16 wave totals are then scanned by one wave (two barriers in all).
 __device__ int block_scan_excl(int x, int32_t* scratch, int* total) {
-  const int tid = threadIdx.x;
-  scratch[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    int t = tid >= off ? scratch[tid - off] : 0;
-    __syncthreads();
-    scratch[tid] += t;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
   }
-  const int incl = scratch[tid];
-  *total = scratch[kSelThreads - 1];
+  if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
-  return incl - x;
+  if (wave == 0) {
+    const int wt = lane < kSelWaves ? scratch[lane] : 0;
+    int wi = wt;
+#pragma unroll
+    for (int off = 1; off < kSelWaves; off <<= 1) {
+      const int t = __shfl_up(wi, off, kWave);
+      if (lane >= off) wi += t;
+    }
+    if (lane < kSelWaves) scratch[kSelWaves + lane] = wi - wt;  // exclusive wave offsets
+    if (lane == kSelWaves - 1) scratch[2 * kSelWaves] = wi;
+  }
+  __syncthreads();
+  const int before = scratch[kSelWaves + wave] + incl - x;
+  *total = scratch[2 * kSelWaves];
+  __syncthreads();
+  return before;
 }
 
 // Given a histogram hist[0..nb) and need >= 1, find the largest bin d whose
@@ -160,7 +173,7 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
   int L = known;
   int cnt_eq = c;  // candidates whose key matches the prefix P (L bits)
   while (L < 32) {
-    const int D = min(10, 32 - L);
+    const int D = min(11, 32 - L);
     const int nb = 1 << D;
     for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
@@ -190,7 +203,7 @@ __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, 
   int M = 0;
   int need2 = need;
   while (M < 32) {
-    const int D = min(10, 32 - M);
+    const int D = min(11, 32 - M);
     const int nb = 1 << D;
     for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
     __syncthreads();
@@ -372,8 +385,10 @@ __global__ __launch_bounds__(kSmpThreads) void select_sample(
   }
   // rank of the threshold in the sample: about 2k keys of the row lie above it
   int need = (int)min<int64_t>(kSmp, ((int64_t)2 * k * kSmp + pool - 1) / pool + 8);
+  // the threshold only needs to land near the predicted rank: the top 16
+  // key bits (two 8-bit passes) are enough; t = that prefix with zero low bits
   uint32_t P = 0;
-  for (int L = 0; L < 32; L += 8) {
+  for (int L = 0; L < 16; L += 8) {
     hist[tid] = 0;
     __syncthreads();
 #pragma unroll
@@ -407,7 +422,7 @@ __global__ __launch_bounds__(kSmpThreads) void select_sample(
     P = (P << 8) | (uint32_t)d;
     __syncthreads();
   }
-  if (tid == 0) thr[row] = P;
+  if (tid == 0) thr[row] = P << 16;
 }
 
 // ---------------------------------------------------------------------------
@@ -441,23 +456,47 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
   const float* s = scores + (size_t)row * Nmax;
   if (tid == 0) lcount = 0;
   __syncthreads();
-  for (int c0 = 0; c0 < kColPer; c0 += kUnroll) {
-    uint32_t keys[kUnroll];
-    load_keys(s, lo + c0 * kColThreads + tid, kColThreads, hi, keys);
+  auto append = [&](bool cand, uint32_t key, int i) {
+    const uint64_t m = __ballot(cand);
+    if (m) {
+      int wb = 0;
+      if (lane == 0) wb = atomicAdd(&lcount, __popcll(m));
+      wb = __builtin_amdgcn_readfirstlane(wb);
+      const int pos = wb + __popcll(m & ((1ull << lane) - 1));
+      if (cand && pos < kColLocal) {
+        lkey[pos] = key;
+        lidx[pos] = i;
+      }
+    }
+  };
+  if ((Nmax & 3) == 0) {
+    // 16-byte loads: four consecutive keys per lane; the last group of the
+    // segment is read from an aligned start inside it and masked
+    constexpr int kV = 8;
+    const int last4 = (hi - 1) & ~3;
+    for (int c0 = 0; c0 < kColPer / 4; c0 += kV) {
+      f32x4 x[kV];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = lo + (c0 + u) * kColThreads + tid;
-      const bool cand = i < hi && keys[u] >= t;
-      const uint64_t m = __ballot(cand);
-      if (m) {
-        int wb = 0;
-        if (lane == 0) wb = atomicAdd(&lcount, __popcll(m));
-        wb = __builtin_amdgcn_readfirstlane(wb);
-        const int pos = wb + __popcll(m & ((1ull << lane) - 1));
-        if (cand && pos < kColLocal) {
-          lkey[pos] = keys[u];
-          lidx[pos] = i;
+      for (int u = 0; u < kV; ++u)
+        x[u] = *reinterpret_cast<const f32x4*>(s + min(lo + ((c0 + u) * kColThreads + tid) * 4, last4));
+#pragma unroll
+      for (int u = 0; u < kV; ++u) {
+        const int i4 = lo + ((c0 + u) * kColThreads + tid) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = ordered_key(x[u][e]);
+          append(i4 + e < hi && key >= t, key, i4 + e);
         }
+      }
+    }
+  } else {
+    for (int c0 = 0; c0 < kColPer; c0 += kUnroll) {
+      uint32_t keys[kUnroll];
+      load_keys(s, lo + c0 * kColThreads + tid, kColThreads, hi, keys);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = lo + (c0 + u) * kColThreads + tid;
+        append(i < hi && keys[u] >= t, keys[u], i);
       }
     }
   }
