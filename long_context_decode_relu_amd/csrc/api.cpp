@@ -122,6 +122,8 @@ ssa_status ssa_decode_full(const ssa_shape* s, const float* q, const void* k, co
   if (!q || !k || !v || !ctx_lens || !out) return SSA_ERR_NULL;
   if (!finite(scale) || !finite(c) || c < 0.0f || !finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
   if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  if (decode_full_tiles_bound(s->batch, s->n_kv_heads, s->max_ctx_len) >= ((int64_t)1 << 31))
+    return SSA_ERR_UNSUPPORTED;
   const size_t need = decode_full_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads, s->max_ctx_len);
   if (need && (!ws || ws_bytes < need)) return SSA_ERR_WORKSPACE;
   DecodeFullArgs a;

@@ -26,6 +26,8 @@ struct DecodeFullArgs {
   void* ws;
 };
 size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int max_ctx);
+// Upper bound on the 64-key tiles of one call (tile indices are 32-bit).
+int64_t decode_full_tiles_bound(int B, int Hkv, int max_ctx);
 hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream);
 
 struct SelectArgs {
