@@ -696,23 +696,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   }
 }
 
-// Sum the partials of each (sequence, query head) in slot order and divide by
-// (c + den). The partials of stream j are slots j + w for the waves w whose
-// tile ranges meet the stream. Eight groups of 128 threads each sum every
-// eighth partial; the eight sums are then added in a fixed order, so the
-// result does not depend on timing.
+// Sum the partials of each (sequence, query head) and divide by (c + den).
+// The partials of stream j are slots j + w for the waves w whose tile ranges
+// meet the stream. The numerators are summed by eight groups of 128 threads
+// (one dimension each, every eighth slot, in slot order) and the eight sums
+// added in a fixed order; den and the counts are summed one slot per thread
+// and reduced in a fixed order too, so the result does not depend on timing.
 constexpr int kCombineGroups = 8;
+constexpr int kCombineThreads = kHeadDim * kCombineGroups;
+constexpr int kCombineWaves = kCombineThreads / kWave;
 
-__global__ __launch_bounds__(kHeadDim * kCombineGroups) void decode_full_combine(
+__global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
     const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
     float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
   __shared__ float s_num[kCombineGroups][kHeadDim];
-  __shared__ float s_den[kCombineGroups];
-  __shared__ int s_cnt[kCombineGroups][2];
+  __shared__ float s_den[kCombineWaves];
+  __shared__ int s_cnt[kCombineWaves][2];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int d = threadIdx.x % kHeadDim, grp = threadIdx.x / kHeadDim;
+  const int d = tid % kHeadDim, grp = tid / kHeadDim;
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
   const int j = b * Hkv + kvh;
@@ -723,38 +727,55 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void decode_full_combine
     p0 = j + wave_of_tile(s0, W, T);
     p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
   }
-  float sn = 0.f, sd = 0.f;
+  // den and the counts: one slot per thread
+  float sd = 0.f;
   int zn = 0, zv = 0;
-#pragma unroll 16
-  for (int p = p0 + grp; p < p1; p += kCombineGroups) {
-    sn += part_num[((size_t)p * G + jh) * kHeadDim + d];
+  for (int p = p0 + tid; p < p1; p += kCombineThreads) {
     sd += part_den[(size_t)p * G + jh];
-    if (d == 0) zn += part_nnz[(size_t)p * G + jh];
-    if (d == 1) zv += part_vrows[p];
+    zn += part_nnz[(size_t)p * G + jh];
+    zv += part_vrows[p];
+  }
+  // numerators: group grp takes slots p0 + grp, p0 + grp + 8, ... (loads
+  // issued eight at a time, added in slot order)
+  float sn = 0.f;
+  for (int p = p0 + grp; p < p1; p += 8 * kCombineGroups) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = p + u * kCombineGroups;
+      x[u] = q < p1 ? part_num[((size_t)q * G + jh) * kHeadDim + d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sn += x[u];
   }
   s_num[grp][d] = sn;
-  if (d == 0) {
-    s_den[grp] = sd;
-    s_cnt[grp][0] = zn;
+  sd = wave_sum_dpp(sd);
+  zn = wave_sum_i(zn);
+  zv = wave_sum_i(zv);
+  if (lane == 0) {
+    s_den[wave] = sd;
+    s_cnt[wave][0] = zn;
+    s_cnt[wave][1] = zv;
   }
-  if (d == 1) s_cnt[grp][1] = zv;
   __syncthreads();
   if (grp == 0) {
     float tn = 0.f, td = 0.f;
 #pragma unroll
-    for (int g2 = 0; g2 < kCombineGroups; ++g2) { tn += s_num[g2][d]; td += s_den[g2]; }
+    for (int g2 = 0; g2 < kCombineGroups; ++g2) tn += s_num[g2][d];
+#pragma unroll
+    for (int w2 = 0; w2 < kCombineWaves; ++w2) td += s_den[w2];
     const float denom = c + td;
     out[((size_t)b * Hq + h) * kHeadDim + d] = denom == 0.f ? 0.f : tn / denom;
     if (d == 0 && nnz) {
       int z = 0;
 #pragma unroll
-      for (int g2 = 0; g2 < kCombineGroups; ++g2) z += s_cnt[g2][0];
+      for (int w2 = 0; w2 < kCombineWaves; ++w2) z += s_cnt[w2][0];
       nnz[(size_t)b * Hq + h] = z;
     }
     if (d == 1 && jh == 0 && vrows) {
       int z = 0;
 #pragma unroll
-      for (int g2 = 0; g2 < kCombineGroups; ++g2) z += s_cnt[g2][1];
+      for (int w2 = 0; w2 < kCombineWaves; ++w2) z += s_cnt[w2][1];
       vrows[(size_t)b * Hkv + kvh] = z;
     }
   }
@@ -881,7 +902,7 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
     case 8: e = launch_g<8>(L, a.kv_bf16, normk, (int)grid, stream); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kHeadDim * kCombineGroups), 0,
+  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kCombineThreads), 0,
                      stream, L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      (int)grid * kWaves, a.c, a.out, a.nnz, a.vrows);
   return hipGetLastError();

@@ -9,16 +9,18 @@
 // integers. The cut is a key value v* plus an index i*: a key is in the top k
 // when key > v*, or key == v* and its index <= i* (ties go to the lower index).
 //
-// Three kernels per call:
-//   sample   one work-group per (sequence, query head) reads 64 evenly spaced
-//            runs of 64 scores and takes the key t whose rank in that sample
-//            predicts about 2k keys >= t in the whole row.
-//   collect  many work-groups per row stream the scores once and append every
-//            key >= t (key and index) to the row's candidate list.
-//   finish   one work-group per row. If the list holds between k and 8192
-//            candidates it contains the whole top k, and the cut is resolved
-//            exactly among them in LDS. Otherwise (an unlucky sample, or
-//            heavy ties) the row is selected exactly from the scores:
+// Two kernels per call:
+//   collect  many work-groups per (sequence, query head) row. Each first
+//            reads the same 64 evenly spaced runs of 64 scores and takes the
+//            key t whose rank in that sample predicts about 2k keys >= t in
+//            the whole row (every work-group of the row finds the same t),
+//            then streams its segment of the row once and writes every key
+//            >= t (key and index) to the segment's own candidate region.
+//   finish   one work-group per row. If the regions hold between k and 8192
+//            candidates in all they contain the whole top k, and the cut is
+//            resolved exactly among them in LDS. Otherwise (an unlucky
+//            sample, heavy ties, a short row) the row is selected exactly
+//            from the scores:
 //              pass 1  histogram of the top 13 key bits, wave-aggregated;
 //              pass 2  the keys of the bin holding the cut are gathered into
 //                      LDS (after narrowing 10 bits at a time over global
@@ -33,6 +35,7 @@
 //
 // The pool is [0, n) (union with the window, duplicates removed) or, with
 // SSA_SELECT_DISJOINT, [0, n - n_recent).
+#include <algorithm>
 #include <climits>
 
 #include "common.h"
@@ -346,33 +349,20 @@ __device__ void exact_cut(SelShared& sh, const float* s, int n, int pool, int k,
 }
 
 // ---------------------------------------------------------------------------
-// Sample kernel: the provisional threshold of each row.
+// Provisional threshold of a row from a sample (computed by every collect
+// work-group of the row, identically): 64 evenly spaced runs of 16 scores.
 // ---------------------------------------------------------------------------
 constexpr int kSmpThreads = 256;
 constexpr int kSmpRuns = 64;                       // runs of consecutive keys
-constexpr int kSmpRun = 64;                        // keys per run
-constexpr int kSmp = kSmpRuns * kSmpRun;           // 4096 sampled keys
-constexpr int kSmpPer = kSmp / kSmpThreads;        // 16 per thread
+constexpr int kSmpRun = 16;                        // keys per run
+constexpr int kSmp = kSmpRuns * kSmpRun;           // 1024 sampled keys
+constexpr int kSmpPer = kSmp / kSmpThreads;        // 4 per thread
 
-__global__ __launch_bounds__(kSmpThreads) void select_sample(
-    const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, uint32_t* __restrict__ thr, int32_t* __restrict__ ccount) {
-  __shared__ uint32_t hist[256];
-  __shared__ int bc[2];
+// The key t whose rank in the sample predicts about 2k keys >= t in the row
+// (pool > kCap). Uses hist[256] and bc[2] of LDS; ends with a barrier.
+__device__ uint32_t sample_threshold(const float* s, int pool, int k, uint32_t* hist, int* bc) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int row = blockIdx.x;
-  const int b = row / Hq;
-  const int n = min(ctx_lens[b], Nmax);
-  const int pool = disjoint ? max(0, n - n_recent) : n;
-  const int k = min(k_top, pool);
-  if (tid == 0) ccount[row] = 0;
-  if (k >= pool || pool <= kCap) {
-    // every pool key becomes a candidate (or every one is selected)
-    if (tid == 0) thr[row] = 0u;
-    return;
-  }
-  const float* s = scores + (size_t)row * Nmax;
-  // run r starts at floor(r * (pool - 64) / 63): the runs span the pool
+  // run r starts at floor(r * (pool - 16) / 63): the runs span the pool
   const int run = tid / (kSmpRun / kSmpPer), part = tid % (kSmpRun / kSmpPer);
   const int start = (int)((int64_t)run * (pool - kSmpRun) / (kSmpRuns - 1)) + part * kSmpPer;
   uint32_t key[kSmpPer];
@@ -422,40 +412,46 @@ __global__ __launch_bounds__(kSmpThreads) void select_sample(
     P = (P << 8) | (uint32_t)d;
     __syncthreads();
   }
-  if (tid == 0) thr[row] = P << 16;
+  return P << 16;
 }
 
 // ---------------------------------------------------------------------------
-// Collect kernel: every pool key >= thr[row] joins the row's candidate list.
-// Each work-group gathers its segment's candidates in LDS, reserves space in
-// the row's list with one atomic, then copies them out. Counts keep growing
-// past the list's capacity, so the finish kernel sees an overflow.
+// Collect kernel: work-group (seg, row) streams keys [seg*kColSeg, ...) of the
+// row once and writes every pool key >= the row's sampled threshold to its own
+// region of the candidate lists (cap entries), with the count in
+// cseg[row][seg] (cap + 1: the region overflowed). Rows whose pool is at most
+// kCap keys go straight to the exact path and need no candidates.
 // ---------------------------------------------------------------------------
 constexpr int kColThreads = 256;
 constexpr int kColSeg = 16384;                     // keys per work-group
 constexpr int kColPer = kColSeg / kColThreads;     // 64 per thread
 constexpr int kColLocal = 2048;                    // candidates buffered per work-group
+static_assert(kColThreads == kSmpThreads, "the sample runs on the collect work-group");
 
 __global__ __launch_bounds__(kColThreads) void select_collect(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, const uint32_t* __restrict__ thr,
-    int32_t* __restrict__ ccount, uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
+    int k_top, int n_recent, int disjoint, int segs, int cap, int32_t* __restrict__ cseg,
+    uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
   __shared__ uint32_t lkey[kColLocal];
   __shared__ int32_t lidx[kColLocal];
-  __shared__ int lcount, gbase;
+  __shared__ uint32_t hist[256];
+  __shared__ int bc[2];
+  __shared__ int lcount;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int row = blockIdx.y;
+  const int row = blockIdx.y, seg = blockIdx.x;
   const int b = row / Hq;
   const int n = min(ctx_lens[b], Nmax);
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
-  const int lo = blockIdx.x * kColSeg;
-  if (k >= pool || lo >= pool) return;
+  const int lo = seg * kColSeg;
+  int32_t* count = cseg + (size_t)row * segs + seg;
+  if (k >= pool || pool <= kCap || lo >= pool) {  // the finish kernel needs no candidates
+    if (tid == 0) *count = 0;
+    return;
+  }
   const int hi = min(pool, lo + kColSeg);
-  const uint32_t t = thr[row];
   const float* s = scores + (size_t)row * Nmax;
   if (tid == 0) lcount = 0;
-  __syncthreads();
   auto append = [&](bool cand, uint32_t key, int i) {
     const uint64_t m = __ballot(cand);
     if (m) {
@@ -470,26 +466,27 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
     }
   };
   if ((Nmax & 3) == 0) {
-    // 16-byte loads: four consecutive keys per lane; the last group of the
-    // segment is read from an aligned start inside it and masked
-    constexpr int kV = 8;
+    // the whole segment is loaded first (16-byte loads, four consecutive keys
+    // per lane; the last group is read from an aligned start inside it and
+    // masked), so that it streams in while the threshold is worked out
+    constexpr int kV = kColPer / 4;
     const int last4 = (hi - 1) & ~3;
-    for (int c0 = 0; c0 < kColPer / 4; c0 += kV) {
-      f32x4 x[kV];
+    f32x4 x[kV];
 #pragma unroll
-      for (int u = 0; u < kV; ++u)
-        x[u] = *reinterpret_cast<const f32x4*>(s + min(lo + ((c0 + u) * kColThreads + tid) * 4, last4));
+    for (int u = 0; u < kV; ++u)
+      x[u] = *reinterpret_cast<const f32x4*>(s + min(lo + (u * kColThreads + tid) * 4, last4));
+    const uint32_t t = sample_threshold(s, pool, k, hist, bc);
 #pragma unroll
-      for (int u = 0; u < kV; ++u) {
-        const int i4 = lo + ((c0 + u) * kColThreads + tid) * 4;
+    for (int u = 0; u < kV; ++u) {
+      const int i4 = lo + (u * kColThreads + tid) * 4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = ordered_key(x[u][e]);
-          append(i4 + e < hi && key >= t, key, i4 + e);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = ordered_key(x[u][e]);
+        append(i4 + e < hi && key >= t, key, i4 + e);
       }
     }
   } else {
+    const uint32_t t = sample_threshold(s, pool, k, hist, bc);
     for (int c0 = 0; c0 < kColPer; c0 += kUnroll) {
       uint32_t keys[kUnroll];
       load_keys(s, lo + c0 * kColThreads + tid, kColThreads, hi, keys);
@@ -502,20 +499,17 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
   }
   __syncthreads();
   const int c = lcount;
-  if (c == 0) return;
-  if (tid == 0) gbase = atomicAdd(&ccount[row], c > kColLocal ? kCap + 1 : c);
-  __syncthreads();
-  const int g0 = gbase;
-  if (c > kColLocal) return;  // the row overflows: the finish kernel selects it exactly
-  uint32_t* okey = ckey + (size_t)row * kCap;
-  int32_t* oidx = cidx + (size_t)row * kCap;
-  for (int j = tid; j < c; j += kColThreads) {
-    const int pos = g0 + j;
-    if (pos < kCap) {
-      okey[pos] = lkey[j];
-      oidx[pos] = lidx[j];
-    }
+  if (c > cap) {  // the region overflows: the finish kernel selects the row exactly
+    if (tid == 0) *count = cap + 1;
+    return;
   }
+  uint32_t* okey = ckey + ((size_t)row * segs + seg) * cap;
+  int32_t* oidx = cidx + ((size_t)row * segs + seg) * cap;
+  for (int j = tid; j < c; j += kColThreads) {
+    okey[j] = lkey[j];
+    oidx[j] = lidx[j];
+  }
+  if (tid == 0) *count = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -524,7 +518,7 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_finish(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, const int32_t* __restrict__ ccount,
+    int k_top, int n_recent, int disjoint, int segs, int cap, const int32_t* __restrict__ cseg,
     const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cidx,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int stride) {
   __shared__ SelShared sh;
@@ -540,12 +534,33 @@ __global__ __launch_bounds__(kSelThreads) void select_finish(
   int istar = INT_MAX;  // k == pool: every pool key is selected
   bool marked = false;  // bitmap already holds every selected pool key
   if (k < pool) {
-    const int cnt = ccount[row];
+    // candidates of the row's segments: every key >= the sampled threshold.
+    // Thread g loads segment g's count; an exclusive scan gives each region's
+    // place in the gathered list (held in sh.hist), then every candidate is
+    // copied by one thread, all loads in flight together.
+    const int nseg = ceil_div(pool, kColSeg);
+    const int32_t* counts = cseg + (size_t)row * segs;
+    int cnt = INT_MAX;  // short rows and rows of very many segments: exact path
+    if (pool > kCap && nseg <= kSelThreads) {
+      const int c = tid < nseg ? counts[tid] : 0;
+      int total;
+      const int before = block_scan_excl(c, sh.scan, &total);
+      if (tid < nseg) sh.hist[tid] = (uint32_t)before;
+      if (tid == 0) sh.hist[nseg] = (uint32_t)total;
+      const bool over = __syncthreads_or(c > cap);
+      if (!over) cnt = total;
+    }
     if (cnt >= k && cnt <= kCap) {
-      // the candidates (every key >= the sampled threshold) hold the top k
+      // the candidates hold the top k: gather the regions into LDS, in order
       for (int j = tid; j < cnt; j += kSelThreads) {
-        sh.ckey[j] = ckey[(size_t)row * kCap + j];
-        sh.cidx[j] = cidx[(size_t)row * kCap + j];
+        int lo = 0, hi = nseg;  // the region holding j: the last g with start(g) <= j
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)sh.hist[mid] <= j) lo = mid; else hi = mid;
+        }
+        const size_t e = ((size_t)row * segs + lo) * cap + (j - (int)sh.hist[lo]);
+        sh.ckey[j] = ckey[e];
+        sh.cidx[j] = cidx[e];
       }
       __syncthreads();
       finish_in_lds(sh, cnt, 0u, 0, k, &vstar, &istar);
@@ -646,45 +661,47 @@ __global__ __launch_bounds__(kSelThreads) void select_finish(
 }
 
 struct SelLayout {
-  size_t thr, cnt, key, idx, total;
+  size_t cnt, key, idx, total;
+  int segs, cap;
 };
 
-SelLayout sel_layout(int rows) {
+// Candidate regions: `segs` per row of `cap` entries each. A region holds the
+// expected 2k * kColSeg / pool candidates of its segment with room to spare;
+// the whole row's list stays near 2 kCap entries.
+SelLayout sel_layout(int rows, int max_ctx) {
   SelLayout l;
-  l.thr = 0;
-  l.cnt = align_up((size_t)rows * 4, 256);
-  l.key = l.cnt + align_up((size_t)rows * 4, 256);
-  l.idx = l.key + align_up((size_t)rows * kCap * 4, 256);
-  l.total = l.idx + align_up((size_t)rows * kCap * 4, 256);
+  l.segs = std::max(1, ceil_div(max_ctx, kColSeg));
+  l.cap = std::min(kColLocal, std::max(256, 2 * kCap / l.segs));
+  const size_t ents = (size_t)rows * l.segs * l.cap;
+  l.cnt = 0;
+  l.key = align_up((size_t)rows * l.segs * 4, 256);
+  l.idx = l.key + align_up(ents * 4, 256);
+  l.total = l.idx + align_up(ents * 4, 256);
   return l;
 }
 
 }  // namespace
 
-size_t select_ws_bytes(int B, int Hq, int, int) {
+size_t select_ws_bytes(int B, int Hq, int max_ctx, int) {
   const int rows = B * Hq;
-  return rows > 0 ? sel_layout(rows).total : 0;
+  return rows > 0 ? sel_layout(rows, max_ctx).total : 0;
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   const int rows = a.B * a.Hq;
   if (rows == 0) return hipSuccess;
-  const SelLayout l = sel_layout(rows);
+  const SelLayout l = sel_layout(rows, a.max_ctx);
   char* ws = static_cast<char*>(a.ws);
-  uint32_t* thr = reinterpret_cast<uint32_t*>(ws + l.thr);
   int32_t* cnt = reinterpret_cast<int32_t*>(ws + l.cnt);
   uint32_t* ckey = reinterpret_cast<uint32_t*>(ws + l.key);
   int32_t* cidx = reinterpret_cast<int32_t*>(ws + l.idx);
   const int disjoint = (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0;
-  hipLaunchKernelGGL(select_sample, dim3(rows), dim3(kSmpThreads), 0, stream, a.scores, a.ctx_lens,
-                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, thr, cnt);
-  const int segs = ceil_div(a.max_ctx, kColSeg);
-  if (segs > 0)
-    hipLaunchKernelGGL(select_collect, dim3(segs, rows), dim3(kColThreads), 0, stream, a.scores,
-                       a.ctx_lens, a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, thr, cnt, ckey, cidx);
+  hipLaunchKernelGGL(select_collect, dim3(l.segs, rows), dim3(kColThreads), 0, stream, a.scores,
+                     a.ctx_lens, a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt,
+                     ckey, cidx);
   hipLaunchKernelGGL(select_finish, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
-                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, cnt, ckey, cidx, a.sel_idx,
-                     a.sel_count, a.k_top + a.n_recent);
+                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt, ckey, cidx,
+                     a.sel_idx, a.sel_count, a.k_top + a.n_recent);
   return hipGetLastError();
 }
 

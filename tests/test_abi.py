@@ -57,8 +57,11 @@ def test_workspace_sizes():
     assert ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(n_q_heads=3)) == 0
     assert ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(max_ctx_len=5000)) == 0  # > capacity
     assert ws_bytes(ssa.SSA_OP_SELECT, s, 0) == 0
-    # selection keeps a candidate list of up to 8192 (key, index) pairs per row
-    assert ws_bytes(ssa.SSA_OP_SELECT, s, 1152) >= 2 * 16 * 8192 * 8
+    # selection keeps room for the ~2 k_top (key, index) candidates that its
+    # sampled threshold aims at, per row, at every context bound
+    for cap in (4096, 131072, 262144, 1 << 20):
+        sc = shape(kv_capacity=cap, max_ctx_len=cap)
+        assert ws_bytes(ssa.SSA_OP_SELECT, sc, 1152) >= 2 * 16 * 2 * 1024 * 8, cap
     assert ws_bytes(99, s) == 0
     # the decode workspace holds one partial (D+1 floats) per head per split
     big = ws_bytes(ssa.SSA_OP_DECODE_FULL, shape(batch=8, kv_capacity=131072, max_ctx_len=131072))
