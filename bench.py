@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--prefill-only", action="store_true",
                    help="only run the prefill measurement (prints its JSON object)")
+    p.add_argument("--unfused", action="store_true",
+                   help="run the step as ssa_decode_full + ssa_select_topk_recent + ssa_decode_sparse "
+                        "(default: ssa_decode_full_select + ssa_decode_sparse)")
     p.add_argument("--fixed-len", type=int, default=None,
                    help="use this context length for every sequence instead of U[64K,128K]")
     p.add_argument("--copy-probe", action="store_true",
@@ -215,19 +218,31 @@ def main():
     shp = caches[0].shape(Hq)
     ws_sel = ssa.workspace(ssa.SSA_OP_SELECT, shp, stride, dev)
     ws_sp = ssa.workspace(ssa.SSA_OP_DECODE_SPARSE, shp, stride, dev)
+    ws_fs = None if args.unfused else ssa.workspace(ssa.SSA_OP_DECODE_FULL_SELECT, shp, 0, dev)
     L = ssa.lib()
     import ctypes
+    cur = torch.cuda.current_stream().cuda_stream
 
     def step(i, ev=None):
         c = caches[i % len(caches)]
         if ev is not None:
             ev[0].record()
-        ssa.ssa_decode_full(q, c, out=out, scores=scores, ws=ws_full, want_scores=True)
-        if ev is not None:
-            ev[1].record()
-        st = L.ssa_select_topk_recent(ctypes.byref(shp), scores.data_ptr(), c.ctx_lens.data_ptr(),
-                                      1024, 128, 0, sel.data_ptr(), cnt.data_ptr(), ws_sel.data_ptr(),
-                                      ws_sel.numel(), torch.cuda.current_stream().cuda_stream)
+        if args.unfused:
+            ssa.ssa_decode_full(q, c, out=out, scores=scores, ws=ws_full, want_scores=True)
+            if ev is not None:
+                ev[1].record()
+            st = L.ssa_select_topk_recent(ctypes.byref(shp), scores.data_ptr(), c.ctx_lens.data_ptr(),
+                                          1024, 128, 0, sel.data_ptr(), cnt.data_ptr(),
+                                          ws_sel.data_ptr(), ws_sel.numel(), cur)
+        else:
+            # the full layer and its selection in one call (no score round trip)
+            st = L.ssa_decode_full_select(ctypes.byref(shp), q.data_ptr(), c.k.data_ptr(),
+                                          c.v.data_ptr(), c.ctx_lens.data_ptr(), 1.0, 1.0, 1e-6,
+                                          ssa.SSA_NORM_Q, 1024, 128, 0, out.data_ptr(), None,
+                                          sel.data_ptr(), cnt.data_ptr(), None, None,
+                                          ws_fs.data_ptr(), ws_fs.numel(), cur)
+            if ev is not None:
+                ev[1].record()
         assert st == 0, st
         if ev is not None:
             ev[2].record()
@@ -274,8 +289,16 @@ def main():
     kvb = 2
     sparse_bytes = 2 * D * kvb * union_rows
     kv_read = ab["k"] + ab["v"] + sparse_bytes
-    full_alg = ab["k"] + ab["v"] + ab["q_out"] + ab["scores"]
-    sel_alg = ab["scores"] + 4 * B * Hq * stride
+    sel_out = 4 * B * Hq * (stride + 1)
+    if args.unfused:
+        # ssa_decode_full writes the scores; ssa_select_topk_recent reads them back
+        full_alg = ab["k"] + ab["v"] + ab["q_out"] + ab["scores"]
+        sel_alg = ab["scores"] + sel_out
+    else:
+        # ssa_decode_full_select: keys, fetched value rows, queries and outputs,
+        # and the selections written (the candidate lists are internal)
+        full_alg = ab["k"] + ab["v"] + ab["q_out"] + sel_out
+        sel_alg = 0
     full_avg_ms = float(np.mean(full_ms))
     achieved = full_alg / (full_avg_ms * 1e-3) / 1e9
     value = kv_read / (ms_step * 1e-3) / 1e9
@@ -300,19 +323,23 @@ def main():
         "config": {"workload": WORKLOAD if args.fixed_len is None else f"batched_decode_b8_fixed{args.fixed_len}",
                    "batch": B, "n_q_heads": Hq, "n_kv_heads": wl.n_kv_heads, "head_dim": D,
                    "ctx_lens": wl.ctx_lens.tolist(), "kv_capacity": Nmax, "k_top": 1024, "n_recent": 128,
-                   "step": "ssa_decode_full + ssa_select_topk_recent + ssa_decode_sparse"},
+                   "step": ("ssa_decode_full + ssa_select_topk_recent + ssa_decode_sparse" if args.unfused
+                            else "ssa_decode_full_select + ssa_decode_sparse")},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "query_tok_per_s": round(B / (ms_step * 1e-3), 1),
         "kv_bytes_read_per_step": int(kv_read),
-        "ops": {"decode_full": op(full_ms, full_alg), "select": op(sel_ms, sel_alg),
-                "decode_sparse": op(sp_ms, sparse_bytes)},
+        "ops": ({"decode_full": op(full_ms, full_alg), "select": op(sel_ms, sel_alg),
+                 "decode_sparse": op(sp_ms, sparse_bytes)} if args.unfused else
+                {"decode_full_select": op(full_ms, full_alg), "decode_sparse": op(sp_ms, sparse_bytes)}),
         "vskip": {"v_rows_fetched": int(vrows_np.sum()),
                   "v_rows_dense": int(wl.n_kv_heads * wl.ctx_lens.astype(np.int64).sum()),
                   "v_traffic_saved": round(1 - ab["v"] / ab["v_dense"], 4),
                   "measured_zero_weight_fraction": round(
                       1 - float(nnz_np.sum()) / (Hq * float(wl.ctx_lens.astype(np.int64).sum())), 4)},
         "sparse_union_rows": int(union_rows),
-        "roofline": {"kernel": "ssa_decode_full (prep + decode_full_kernel + combine)",
+        "roofline": {"kernel": ("ssa_decode_full (decode_full_kernel + combine)" if args.unfused else
+                                "ssa_decode_full_select (decode_full_kernel with candidate lists + "
+                                "combine_select + rescore/select of flagged rows)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},

@@ -88,7 +88,8 @@ enum {
   SSA_OP_DECODE_FULL = 0,
   SSA_OP_SELECT = 1,
   SSA_OP_DECODE_SPARSE = 2,
-  SSA_OP_PREFILL_FULL = 3
+  SSA_OP_PREFILL_FULL = 3,
+  SSA_OP_DECODE_FULL_SELECT = 4
 };
 
 /* Bytes of scratch the operation needs for this shape. `aux` is the query
@@ -118,6 +119,29 @@ ssa_status ssa_decode_full(const ssa_shape* shape, const float* q, const void* k
                            const int32_t* ctx_lens, float scale, float c, float eps, uint32_t flags,
                            float* out, float* scores, int32_t* nnz_per_head,
                            int32_t* vrows_per_kvhead, void* ws, size_t ws_bytes, void* stream);
+
+/* The full layer and the selection of its scores in one call: the outputs
+ * of ssa_decode_full (out, and optionally scores, nnz_per_head,
+ * vrows_per_kvhead) and those of ssa_select_topk_recent on its scores
+ * (sel_idx [B, Hq, k_top + n_recent], sel_count [B, Hq]), bit for bit, without
+ * writing or re-reading the [B, Hq, Nmax] scores unless `scores` is given.
+ * The selection is the one of "Three kinds of attention" (see below); the
+ * full layer lists, per head, the keys that can still make the cut (those
+ * with a positive score; every key of a context of at most 8192) as it scores
+ * them, and the cut is resolved among that list. A row whose list does not
+ * hold the whole top k_top (fewer positive scores than k_top in a longer
+ * context) is rescored and selected exactly from its scores, which costs
+ * another pass over its keys. Same argument rules as the two calls; sel_flags
+ * as their `flags` (SSA_SELECT_DISJOINT).
+ * Workspace: ssa_workspace_bytes(SSA_OP_DECODE_FULL_SELECT, shape, 0) (it
+ * holds the per-head lists and room for rescored rows). */
+ssa_status ssa_decode_full_select(const ssa_shape* shape, const float* q, const void* k,
+                                  const void* v, const int32_t* ctx_lens, float scale, float c,
+                                  float eps, uint32_t flags, int32_t k_top, int32_t n_recent,
+                                  uint32_t sel_flags, float* out, float* scores, int32_t* sel_idx,
+                                  int32_t* sel_count, int32_t* nnz_per_head,
+                                  int32_t* vrows_per_kvhead, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Selection for the sparse layers ("Three kinds of attention").
  *

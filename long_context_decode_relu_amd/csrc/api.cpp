@@ -108,6 +108,8 @@ size_t ssa_workspace_bytes(int32_t op, const ssa_shape* s, int32_t aux) {
     case SSA_OP_PREFILL_FULL:
       if (aux < 0) return 0;
       return prefill_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads, s->max_ctx_len, aux);
+    case SSA_OP_DECODE_FULL_SELECT:
+      return decode_full_select_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads, s->max_ctx_len);
   }
   return 0;
 }
@@ -147,6 +149,54 @@ ssa_status ssa_decode_full(const ssa_shape* s, const float* q, const void* k, co
   a.vrows = vrows_per_kvhead;
   a.ws = ws;
   return from_hip(launch_decode_full(a, static_cast<hipStream_t>(stream)));
+}
+
+ssa_status ssa_decode_full_select(const ssa_shape* s, const float* q, const void* k,
+                                  const void* v, const int32_t* ctx_lens, float scale, float c,
+                                  float eps, uint32_t flags, int32_t k_top, int32_t n_recent,
+                                  uint32_t sel_flags, float* out, float* scores, int32_t* sel_idx,
+                                  int32_t* sel_count, int32_t* nnz_per_head,
+                                  int32_t* vrows_per_kvhead, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  ssa_status st = check_shape(s, true);
+  if (st != SSA_OK) return st;
+  if (k_top < 1 || n_recent < 0 || (int64_t)k_top + n_recent > kMaxSel) return SSA_ERR_SHAPE;
+  if (s->batch == 0) return SSA_OK;
+  if (!q || !k || !v || !ctx_lens || !out || !sel_idx || !sel_count) return SSA_ERR_NULL;
+  if (!finite(scale) || !finite(c) || c < 0.0f || !finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
+  if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  if (sel_flags & ~(uint32_t)SSA_SELECT_DISJOINT) return SSA_ERR_UNSUPPORTED;
+  if (decode_full_tiles_bound(s->batch, s->n_kv_heads, s->max_ctx_len) >= ((int64_t)1 << 31))
+    return SSA_ERR_UNSUPPORTED;
+  const size_t need =
+      decode_full_select_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads, s->max_ctx_len);
+  if (need && (!ws || ws_bytes < need)) return SSA_ERR_WORKSPACE;
+  DecodeFullSelectArgs a;
+  a.full.B = s->batch;
+  a.full.Hq = s->n_q_heads;
+  a.full.Hkv = s->n_kv_heads;
+  a.full.Nmax = s->kv_capacity;
+  a.full.max_ctx = s->max_ctx_len;
+  a.full.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.full.q = q;
+  a.full.k = k;
+  a.full.v = v;
+  a.full.ctx_lens = ctx_lens;
+  a.full.scale = scale;
+  a.full.c = c;
+  a.full.eps = eps;
+  a.full.flags = flags;
+  a.full.out = out;
+  a.full.scores = scores;
+  a.full.nnz = nnz_per_head;
+  a.full.vrows = vrows_per_kvhead;
+  a.full.ws = ws;
+  a.k_top = k_top;
+  a.n_recent = n_recent;
+  a.sel_flags = sel_flags;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  return from_hip(launch_decode_full_select(a, static_cast<hipStream_t>(stream)));
 }
 
 ssa_status ssa_select_topk_recent(const ssa_shape* s, const float* scores, const int32_t* ctx_lens,

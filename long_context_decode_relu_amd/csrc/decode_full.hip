@@ -39,6 +39,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "select_core.h"
 #include "../../include/ssa.h"
 
 namespace ssa {
@@ -275,13 +276,52 @@ __device__ void tile_prefix(const int32_t* ctx_lens, int S, int Hkv, int max_ctx
   if (lane == kWave - 1) tp[S] = incl;
 }
 
-template <int G, bool BF16, bool NORMK>
+// scale / sqrt(mean(q_h^2) + eps) for the G query heads of one KV head
+// (rows qrow + h*128), computed by one wave: lane l holds the factor of head
+// l / (64/G) (every lane of a head the same value). The sum of squares is
+// formed in one fixed order, so every caller gets the same bits.
+template <int G>
+__device__ __forceinline__ float head_rms_factor(const float* qrow, int lane, float scale,
+                                                 float eps) {
+  constexpr int kLanesPerHead = kWave / G;
+  constexpr int kDimsPerLane = kHeadDim / kLanesPerHead;  // 2G
+  const int hl = lane / kLanesPerHead, part = lane % kLanesPerHead;
+  const float* src = qrow + hl * kHeadDim + part * kDimsPerLane;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDimsPerLane; ++i) ss = fmaf(src[i], src[i], ss);
+#pragma unroll
+  for (int off = kLanesPerHead / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+  return scale / sqrtf(ss * (1.0f / kHeadDim) + eps);
+}
+
+// Selection candidates. For each (stream, wave) slot the full layer lists its
+// surviving keys (some head of the group gives a positive score), in key
+// order: the key index and the group's G scores. A row (sequence, head)
+// then takes the keys of its stream's lists whose own score is positive.
+// Streams of at most kCandAll keys list every key instead, so that the exact
+// cut among the list always holds the top k.
+constexpr int kCandAll = 8192;
+
+// First tile and tile count of the part of stream [s0, s1) that wave w of W
+// (over T tiles) takes: the candidate list of that (stream, wave) slot has
+// room for entries [first*64, (first + nt)*64).
+__device__ __forceinline__ void slot_tiles(int s0, int s1, int w, int W, int T, int* first,
+                                           int* nt) {
+  const int t0 = (int)((int64_t)w * T / W), t1 = (int)((int64_t)(w + 1) * T / W);
+  *first = max(s0, t0);
+  *nt = min(s1, t1) - *first;
+}
+
+template <int G, bool BF16, bool NORMK, bool CAND>
 __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part_num,
     float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
-    int* __restrict__ tile_pre_out, int B, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
-    float eps, int normq, int cus_per_xcd) {
+    int* __restrict__ tile_pre_out, int32_t* __restrict__ cand_idx, float* __restrict__ cand_sc,
+    int32_t* __restrict__ cand_cnt,
+    int B, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps, int normq,
+    int cus_per_xcd) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
   __shared__ __attribute__((aligned(16))) float s_w[BF16 ? kWaves * kTileKeys * kMaxG : 4];
   __shared__ int s_tpre[kMaxStreams + 1];
@@ -360,28 +400,55 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       for (int h = 0; h < G; ++h) fac[h] = scale;
       return;
     }
-    constexpr int kLanesPerHead = kWave / G;
-    constexpr int kDimsPerLane = kHeadDim / kLanesPerHead;  // 2G
-    const int hl = lane / kLanesPerHead, part = lane % kLanesPerHead;
-    const float* src = qrow_of(st) + hl * kHeadDim + part * kDimsPerLane;
-    float ss = 0.f;
+    const float f = head_rms_factor<G>(qrow_of(st), lane, scale, eps);
 #pragma unroll
-    for (int i = 0; i < kDimsPerLane; ++i) ss = fmaf(src[i], src[i], ss);
-#pragma unroll
-    for (int off = kLanesPerHead / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-    const float f = scale / sqrtf(ss * (1.0f / kHeadDim) + eps);
-#pragma unroll
-    for (int h = 0; h < G; ++h) fac[h] = __shfl(f, h * kLanesPerHead, kWave);
+    for (int h = 0; h < G; ++h) fac[h] = __shfl(f, h * (kWave / G), kWave);
   };
 
   float num[G][2];
   float den[G];
   int nnz[G];
   int vrows = 0;
+  int ccount = 0;              // entries listed in the current slot
+  int32_t* lidx = nullptr;     // the current slot's list: key indices
+  float* lsc = nullptr;        //   and the group's scores, G per entry
   auto reset = [&]() {
 #pragma unroll
     for (int h = 0; h < G; ++h) { num[h][0] = num[h][1] = 0.f; den[h] = 0.f; nnz[h] = 0; }
     vrows = 0;
+    ccount = 0;
+  };
+  // the candidate list of slot (st, this wave)
+  auto open_slot = [&](const Stream& st) {
+    if constexpr (CAND) {
+      int first, nt;
+      slot_tiles(st.s0, st.s1, w, W, T, &first, &nt);
+      lidx = cand_idx + (size_t)first * kTileKeys;
+      lsc = cand_sc + (size_t)first * kTileKeys * G;
+    }
+  };
+  // list the keys of mask m (this lane's key when `mine`: index key, scores sv)
+  auto list_keys = [&](uint64_t m, bool mine, int key, const float (&sv)[G]) {
+    if constexpr (CAND) {
+      if (m) {
+        const int e = ccount + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (mine) {
+          lidx[e] = key;
+          float* d = lsc + (size_t)e * G;
+          if constexpr (G >= 4) {
+#pragma unroll
+            for (int p = 0; p < G / 4; ++p)
+              *reinterpret_cast<f32x4*>(d + 4 * p) = f32x4{sv[4 * p], sv[4 * p + 1], sv[4 * p + 2], sv[4 * p + 3]};
+          } else if constexpr (G == 2) {
+            *reinterpret_cast<f32x2*>(d) = f32x2{sv[0], sv[1]};
+          } else {
+            d[0] = sv[0];
+          }
+        }
+        ccount += __popcll(m);
+      }
+    }
   };
   auto flush = [&](const Stream& st) {
     const int64_t slot = (int64_t)st.j + w;
@@ -397,6 +464,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       }
     }
     if (lane == 0) part_vrows[slot] = vrows;
+    if constexpr (CAND) {
+      if (lane == 0) cand_cnt[slot] = ccount;
+    }
   };
   reset();
 
@@ -487,6 +557,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     float fac[G];
     issue_tile(&cur, t0, nullptr);
     load_fac(cur, fac);
+    open_slot(cur);
 
     // Pipelined over the wave's tiles. Iteration t waits for tile t, reads
     // it from LDS, issues the V rows of tile t-1's survivors, the copy of
@@ -597,12 +668,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
         reset();
         cur = st;
         load_fac(cur, fac);
+        open_slot(cur);
       }
 
       // 9. weights of tile t; survivors list theirs by rank
       float wt[G];
       const bool any = weigh(fac, kf, valid, p_s, wt);
       p_mask = __ballot(any);
+      if constexpr (CAND) {
+        const bool all = st.n <= kCandAll;
+        list_keys(all ? __ballot(valid) : p_mask, all ? valid : any, base + lane, p_s);
+      }
       if (any) {
         const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(p_mask >> 32),
                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)p_mask, 0));
@@ -633,12 +709,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     Stream cur = stream_of(t0);
     float fac[G];
     load_fac(cur, fac);
+    open_slot(cur);
     for (int t = t0; t < t1; ++t) {
       if (t >= cur.s1) {  // entering the next non-empty stream
         flush(cur);
         reset();
         cur = stream_after(cur, t);
         load_fac(cur, fac);
+        open_slot(cur);
       }
       const size_t row0 = (size_t)cur.j * Nmax;
       float* srow = scores ? scores + ((size_t)cur.b * Hq + (size_t)cur.kvh * G) * Nmax : nullptr;
@@ -656,7 +734,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
 
       float sv[G], wt[G];
-      uint64_t mask = __ballot(weigh(fac, kf, valid, sv, wt));
+      const bool any = weigh(fac, kf, valid, sv, wt);
+      uint64_t mask = __ballot(any);
+      if constexpr (CAND) {
+        const bool all = cur.n <= kCandAll;
+        list_keys(all ? __ballot(valid) : mask, all ? valid : any, key, sv);
+      }
       if (srow && valid) {
 #pragma unroll
         for (int h = 0; h < G; ++h) srow[(size_t)h * Nmax + key] = sv[h];
@@ -706,7 +789,7 @@ constexpr int kCombineGroups = 8;
 constexpr int kCombineThreads = kHeadDim * kCombineGroups;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
-__global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
+__device__ void combine_row(
     const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
@@ -781,14 +864,283 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
   }
 }
 
+__global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
+    const float* __restrict__ part_num, const float* __restrict__ part_den,
+    const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
+    const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
+    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
+  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
+              vrows);
+}
+
+// ---------------------------------------------------------------------------
+// Selection from the candidate lists (the fused full layer + selection).
+// The lists of row (b, h) are those of its stream's slots, in slot order. If
+// they hold every key above the top-k cut the cut is exact among them;
+// otherwise (fewer than k candidates in a long row, or a cut bin too large
+// for LDS) the row is flagged and selected from rescored scores.
+// ---------------------------------------------------------------------------
+
+// Entries a thread of the row's work-group gathers into registers: rows whose
+// lists hold more entries than kSelThreads * kGatherPer are flagged.
+constexpr int kGatherPer = 16;
+
+// Selects row (b, h) into out[0..stride) and *count, or sets *flag. The
+// row's candidates are the entries of its stream's slot lists, in slot order
+// (ascending key index), whose score for head jh is positive (every entry
+// when the stream lists all its keys), restricted to the pool.
+__device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ cand_idx,
+                                  const float* __restrict__ cand_sc,
+                                  const int32_t* __restrict__ cand_cnt,
+                                  const int* __restrict__ tile_pre, int S, int G, int jh, int j,
+                                  int Wl, int n, int k_top, int n_recent, int disjoint,
+                                  int32_t* __restrict__ out, int stride,
+                                  int32_t* __restrict__ count, int32_t* __restrict__ flag) {
+  const int tid = threadIdx.x;
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  const int r0 = max(0, n - n_recent);
+  if (k >= pool) {  // every key of [0, n) is selected
+    for (int p = tid; p < stride; p += kSelThreads) out[p] = p < n ? p : -1;
+    if (tid == 0) {
+      *count = n;
+      *flag = 0;
+    }
+    return;
+  }
+  const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
+  const int W = min(Wl, T);
+  const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+  const int np = p1 - p0;
+  if (np >= kSegWords) {
+    if (tid == 0) *flag = 1;
+    return;
+  }
+  // slot offsets of the row's entries (in sh.bits) and their total
+  uint32_t* offs = sh.bits;
+  {
+    const int per = ceil_div(np, kSelThreads);
+    int local = 0;
+    for (int q = tid * per; q < min(np, tid * per + per); ++q) local += cand_cnt[p0 + q];
+    int total;
+    int run = block_scan_excl(local, sh.scan, &total);
+    for (int q = tid * per; q < min(np, tid * per + per); ++q) {
+      offs[q] = (uint32_t)run;
+      run += cand_cnt[p0 + q];
+    }
+    if (tid == 0) offs[np] = (uint32_t)total;
+    __syncthreads();
+  }
+  const int E = (int)offs[np];
+  if (E > kSelThreads * kGatherPer) {
+    if (tid == 0) *flag = 1;
+    return;
+  }
+  // thread t takes entries [t*per, t*per + per): key and index of each into
+  // registers, with whether it is a candidate of this row
+  const bool all = n <= kCandAll;
+  const int per = ceil_div(E, kSelThreads);
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  uint32_t key[kGatherPer];
+  int32_t idx[kGatherPer];
+  bool cnd[kGatherPer];
+  {
+    // the entries' places first (slot lookups in LDS), then all the loads at
+    // once, then their use
+    size_t at[kGatherPer];
+    int lo = 0, hi = np;  // the slot holding e0: the last q with offs[q] <= e0
+    if (e0 < E) {
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)offs[mid] <= e0) lo = mid; else hi = mid;
+      }
+    }
+    int q = lo, first = 0, nt = 0;
+    slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) {
+      const int e = e0 + u;
+      at[u] = 0;
+      if (e < e1) {
+        while ((int)offs[q + 1] <= e) {
+          ++q;
+          slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
+        }
+        at[u] = (size_t)first * kTileKeys + (e - (int)offs[q]);
+      }
+    }
+    float sc[kGatherPer];
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) {
+      sc[u] = 0.f;
+      idx[u] = 0;
+      if (e0 + u < e1) {
+        sc[u] = cand_sc[at[u] * G + jh];
+        idx[u] = cand_idx[at[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) {
+      key[u] = ordered_key(sc[u]);
+      cnd[u] = e0 + u < e1 && (all || sc[u] > 0.f);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u) cnd[u] = cnd[u] && idx[u] < pool;
+  // the candidates to LDS in order; when there are more than kCap, only
+  // those from the cut bin of a kBits1-bit histogram up
+  auto place = [&](uint32_t d0) {
+    int local = 0;
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) local += (cnd[u] && (key[u] >> (32 - kBits1)) >= d0) ? 1 : 0;
+    int total;
+    int pos = block_scan_excl(local, sh.scan, &total);
+    if (total <= kCap) {
+#pragma unroll
+      for (int u = 0; u < kGatherPer; ++u) {
+        if (cnd[u] && (key[u] >> (32 - kBits1)) >= d0) {
+          sh.ckey[pos] = key[u];
+          sh.cidx[pos] = idx[u];
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+    return total;
+  };
+  int c = place(0u);
+  if (c > kCap) {
+    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u) hist_add(sh.hist, key[u] >> (32 - kBits1), cnd[u]);
+    __syncthreads();
+    int above;
+    const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
+    c = place((uint32_t)d1);
+  }
+  if (c < k || c > kCap) {  // the lists do not hold the whole top k, or it does not fit in LDS
+    if (tid == 0) *flag = 1;
+    return;
+  }
+  uint32_t vstar;
+  int istar;
+  finish_in_lds(sh, c, 0u, 0, k, &vstar, &istar);
+  // the selected candidates below the recent window, in order, then the window
+  const int per2 = ceil_div(c, kSelThreads);
+  const int a0 = tid * per2, a1 = min(c, a0 + per2);
+  int local = 0;
+  for (int i = a0; i < a1; ++i) {
+    const uint32_t kk = sh.ckey[i];
+    const int ii = sh.cidx[i];
+    local += (ii < r0 && (kk > vstar || (kk == vstar && ii <= istar))) ? 1 : 0;
+  }
+  int nsel;
+  int pos = block_scan_excl(local, sh.scan, &nsel);
+  for (int i = a0; i < a1; ++i) {
+    const uint32_t kk = sh.ckey[i];
+    const int ii = sh.cidx[i];
+    if (ii < r0 && (kk > vstar || (kk == vstar && ii <= istar))) out[pos++] = ii;
+  }
+  const int total = nsel + (n - r0);
+  for (int p = nsel + tid; p < stride; p += kSelThreads) out[p] = p < total ? r0 + (p - nsel) : -1;
+  if (tid == 0) {
+    *count = total;
+    *flag = 0;
+  }
+}
+
+// The combine of each (sequence, query head) followed by its selection.
+__global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
+    const float* __restrict__ part_num, const float* __restrict__ part_den,
+    const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
+    const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
+    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows,
+    const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_sc,
+    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ ctx_lens, int max_ctx,
+    int k_top, int n_recent, int disjoint,
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int32_t* __restrict__ row_flag) {
+  __shared__ SelShared sh;
+  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
+              vrows);
+  __syncthreads();
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int kvh = h / G, jh = h - kvh * G;
+  const int row = b * Hq + h;
+  const int stride = k_top + n_recent;
+  const int n = live_keys(ctx_lens, b, max_ctx);
+  select_from_cands(sh, cand_idx, cand_sc, cand_cnt, tile_pre, S, G, jh, b * Hkv + kvh, Wl, n,
+                    k_top, n_recent,
+                    disjoint, sel_idx + (size_t)row * stride, stride, sel_count + row,
+                    row_flag + row);
+}
+
+// Scores of the flagged rows, computed exactly as the full-layer kernel does
+// (same widening, same FMA order over the dimensions, same query factor), into
+// rows of `max_ctx` floats for the exact selection. One key per thread;
+// kRescoreBlocks work-groups per row stride over its keys (rows that need no
+// rescoring cost one early exit per work-group).
+constexpr int kRescoreBlocks = 16;
+
+template <int G, bool BF16, bool NORMK>
+__global__ __launch_bounds__(256) void decode_full_rescore(
+    const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
+    const int32_t* __restrict__ row_flag, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
+    float eps, int normq, float* __restrict__ rs) {
+  const int row = blockIdx.y;
+  if (!row_flag[row]) return;
+  const int b = row / Hq, h = row - b * Hq;
+  const int kvh = h / G, jh = h - kvh * G;
+  const int n = live_keys(ctx_lens, b, max_ctx);
+  const float* qrow = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
+  const int lane = threadIdx.x & (kWave - 1);
+  float fac = scale;
+  if (normq) fac = __shfl(head_rms_factor<G>(qrow, lane, scale, eps), jh * (kWave / G), kWave);
+  const float* qh = qrow + jh * kHeadDim;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const size_t r = ((size_t)b * Hkv + kvh) * Nmax + i;
+    float acc = 0.f, ksq = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < 8; ++c) {
+      float e[16];
+      if constexpr (BF16) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(k) + r * 16 + 2 * c;
+        KeyRow<true> one;
+        one.c[0] = kp[0];
+        one.c[1] = kp[1];
+        one.chunk16(0, e);
+      } else {
+        const f32x4* kp = reinterpret_cast<const f32x4*>(k) + r * 32 + 4 * c;
+        KeyRow<false> one;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) one.c[p] = kp[p];
+        one.chunk16(0, e);
+      }
+      if constexpr (NORMK) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) ksq = fmaf(e[t], e[t], ksq);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc = fmaf(qh[16 * c + t], e[t], acc);
+    }
+    float kf = 1.f;
+    if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
+    rs[(size_t)row * max_ctx + i] = NORMK ? acc * fac * kf : acc * fac;
+  }
+}
+
 struct WsLayout {
   size_t num, den, nnz, vrows, tile_pre, total;
+  // the fused selection: candidate lists and counts, row flags, rescored rows
+  size_t cand_idx, cand_sc, cand_cnt, flag, rescored, total_sel;
 };
 
-WsLayout ws_layout(int B, int Hq, int Hkv) {
+WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   const int G = Hkv > 0 ? Hq / Hkv : 0;
   const size_t S = (size_t)B * Hkv;
   const size_t slots = S + kMaxWaves;
+  const size_t rows = (size_t)B * Hq;
   WsLayout l;
   size_t o = 0;
   l.num = o; o += align_up(slots * G * kHeadDim * sizeof(float), 256);
@@ -797,6 +1149,13 @@ WsLayout ws_layout(int B, int Hq, int Hkv) {
   l.vrows = o; o += align_up(slots * sizeof(int32_t), 256);
   l.tile_pre = o; o += align_up((S + 1) * sizeof(int), 256);
   l.total = o;
+  const size_t tiles = (size_t)B * Hkv * (size_t)ceil_div(max_ctx, kTileKeys);
+  l.cand_idx = o; o += align_up(tiles * kTileKeys * sizeof(int32_t), 256);
+  l.cand_sc = o; o += align_up(tiles * kTileKeys * G * sizeof(float), 256);
+  l.cand_cnt = o; o += align_up(slots * sizeof(int32_t), 256);
+  l.flag = o; o += align_up(rows * sizeof(int32_t), 256);
+  l.rescored = o; o += align_up(rows * (size_t)max_ctx * sizeof(float), 256);
+  l.total_sel = o;
   return l;
 }
 
@@ -809,52 +1168,62 @@ struct Launch {
   float *num, *den;
   int32_t *nnz, *vrows;
   int* tile_pre;
+  int32_t* cand_idx;
+  float* cand_sc;
+  int32_t* cand_cnt;
   int B, Hq, Hkv, Nmax, max_ctx;
   float scale, eps;
   int normq;
 };
 
-template <int G, bool BF16, bool NORMK>
-hipError_t launch_t(const Launch& L, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_full_kernel<G, BF16, NORMK>), dim3(grid), dim3(kThreads), 0, stream,
-                     L.q, L.k, L.v, L.ctx_lens, L.scores, L.num, L.den, L.nnz, L.vrows, L.tile_pre,
-                     L.B, L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale, L.eps, L.normq,
-                     device_cu_count() % kXcds == 0 ? device_cu_count() / kXcds : 0);
-  return hipGetLastError();
+// f.template operator()<G, BF16, NORMK>() for the runtime choice
+template <class F>
+hipError_t dispatch(int G, bool bf16, bool normk, F&& f) {
+  auto by_g = [&](auto gc) -> hipError_t {
+    constexpr int g = decltype(gc)::value;
+    if (bf16) return normk ? f.template operator()<g, true, true>() : f.template operator()<g, true, false>();
+    return normk ? f.template operator()<g, false, true>() : f.template operator()<g, false, false>();
+  };
+  switch (G) {
+    case 1: return by_g(std::integral_constant<int, 1>{});
+    case 2: return by_g(std::integral_constant<int, 2>{});
+    case 4: return by_g(std::integral_constant<int, 4>{});
+    case 8: return by_g(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
-template <int G>
-hipError_t launch_g(const Launch& L, bool bf16, bool normk, int grid, hipStream_t stream) {
-  if (bf16) return normk ? launch_t<G, true, true>(L, grid, stream) : launch_t<G, true, false>(L, grid, stream);
-  return normk ? launch_t<G, false, true>(L, grid, stream) : launch_t<G, false, false>(L, grid, stream);
-}
-
-template <int G>
-int blocks_per_cu(bool bf16, bool normk) {
-  int n = 0;
-  hipError_t e;
-  if (bf16)
-    e = normk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, true, true>, kThreads, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, true, false>, kThreads, 0);
-  else
-    e = normk ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, false, true>, kThreads, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_full_kernel<G, false, false>, kThreads, 0);
-  return (e == hipSuccess && n > 0) ? n : 1;
-}
-
-}  // namespace
-
-int decode_full_chunk(int, int, int) { return kTileKeys; }
-
-int64_t decode_full_tiles_bound(int B, int Hkv, int max_ctx) {
-  return (int64_t)B * Hkv * ceil_div64(max_ctx, kTileKeys);
-}
-
-size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int) { return ws_layout(B, Hq, Hkv).total; }
-
-hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
+// Launch of the full-layer kernel (CAND: with candidate lists) on a
+// persistent grid: all resident work-groups, but no more than about four
+// tiles' worth per wave at the host bound of the work. Returns the grid.
+template <bool CAND>
+hipError_t launch_full(const DecodeFullArgs& a, const Launch& L, hipStream_t stream, int* grid_out) {
   const int G = a.Hq / a.Hkv;
-  const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv);
+  const bool normk = a.flags & SSA_NORM_K;
+  const int64_t tiles_bound = decode_full_tiles_bound(a.B, a.Hkv, a.max_ctx);
+  const int cus_per_xcd = device_cu_count() % kXcds == 0 ? device_cu_count() / kXcds : 0;
+  return dispatch(G, a.kv_bf16, normk, [&]<int g, bool bf16, bool nk>() -> hipError_t {
+    auto kern = decode_full_kernel<g, bf16, nk, CAND>;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    int64_t grid = (int64_t)device_cu_count() * per_cu;
+    grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div64(tiles_bound, kWaves * 4)));
+    grid = std::min<int64_t>(grid, kMaxWaves / kWaves);
+    if (verbose())
+      fprintf(stderr, "[ssa] decode_full G=%d bf16=%d cand=%d grid=%d (cus=%d x %d/cu) tiles<=%lld\n",
+              g, (int)bf16, (int)CAND, (int)grid, device_cu_count(), per_cu, (long long)tiles_bound);
+    *grid_out = (int)grid;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, L.q, L.k, L.v, L.ctx_lens,
+                       L.scores, L.num, L.den, L.nnz, L.vrows, L.tile_pre, L.cand_idx, L.cand_sc,
+                       L.cand_cnt, L.B,
+                       L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale, L.eps, L.normq, cus_per_xcd);
+    return hipGetLastError();
+  });
+}
+
+Launch make_launch(const DecodeFullArgs& a, const WsLayout& l, bool cand) {
   char* ws = static_cast<char*>(a.ws);
   Launch L;
   L.q = a.q;
@@ -867,6 +1236,9 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   L.nnz = reinterpret_cast<int32_t*>(ws + l.nnz);
   L.vrows = reinterpret_cast<int32_t*>(ws + l.vrows);
   L.tile_pre = reinterpret_cast<int*>(ws + l.tile_pre);
+  L.cand_idx = cand ? reinterpret_cast<int32_t*>(ws + l.cand_idx) : nullptr;
+  L.cand_sc = cand ? reinterpret_cast<float*>(ws + l.cand_sc) : nullptr;
+  L.cand_cnt = cand ? reinterpret_cast<int32_t*>(ws + l.cand_cnt) : nullptr;
   L.B = a.B;
   L.Hq = a.Hq;
   L.Hkv = a.Hkv;
@@ -875,37 +1247,79 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   L.scale = a.scale;
   L.eps = a.eps;
   L.normq = (a.flags & SSA_NORM_Q) ? 1 : 0;
-  const bool normk = a.flags & SSA_NORM_K;
-  // Persistent grid: all resident work-groups, but no more than about four
-  // tiles' worth per wave at the host bound of the work.
-  int per_cu = 1;
-  switch (G) {
-    case 1: per_cu = blocks_per_cu<1>(a.kv_bf16, normk); break;
-    case 2: per_cu = blocks_per_cu<2>(a.kv_bf16, normk); break;
-    case 4: per_cu = blocks_per_cu<4>(a.kv_bf16, normk); break;
-    case 8: per_cu = blocks_per_cu<8>(a.kv_bf16, normk); break;
-    default: return hipErrorInvalidValue;
-  }
-  const int64_t tiles_bound = decode_full_tiles_bound(a.B, a.Hkv, a.max_ctx);
-  int64_t grid = (int64_t)device_cu_count() * per_cu;
-  grid = std::min<int64_t>(grid, std::max<int64_t>(1, ceil_div64(tiles_bound, kWaves * 4)));
-  grid = std::min<int64_t>(grid, kMaxWaves / kWaves);
-  if (verbose())
-    fprintf(stderr, "[ssa] decode_full G=%d bf16=%d grid=%d (cus=%d x %d/cu) W=%d tiles<=%lld\n", G,
-            a.kv_bf16, (int)grid, device_cu_count(), per_cu, (int)grid * kWaves,
-            (long long)tiles_bound);
-  hipError_t e = hipSuccess;
-  switch (G) {
-    case 1: e = launch_g<1>(L, a.kv_bf16, normk, (int)grid, stream); break;
-    case 2: e = launch_g<2>(L, a.kv_bf16, normk, (int)grid, stream); break;
-    case 4: e = launch_g<4>(L, a.kv_bf16, normk, (int)grid, stream); break;
-    case 8: e = launch_g<8>(L, a.kv_bf16, normk, (int)grid, stream); break;
-  }
+  return L;
+}
+
+}  // namespace
+
+int decode_full_chunk(int, int, int) { return kTileKeys; }
+
+int64_t decode_full_tiles_bound(int B, int Hkv, int max_ctx) {
+  return (int64_t)B * Hkv * ceil_div64(max_ctx, kTileKeys);
+}
+
+size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int max_ctx) {
+  return ws_layout(B, Hq, Hkv, max_ctx).total;
+}
+
+size_t decode_full_select_ws_bytes(int B, int Hq, int Hkv, int max_ctx) {
+  return ws_layout(B, Hq, Hkv, max_ctx).total_sel;
+}
+
+hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
+  const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
+  const Launch L = make_launch(a, l, false);
+  int grid = 0;
+  hipError_t e = launch_full<false>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kCombineThreads), 0,
                      stream, L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
-                     (int)grid * kWaves, a.c, a.out, a.nnz, a.vrows);
+                     grid * kWaves, a.c, a.out, a.nnz, a.vrows);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t stream) {
+  const DecodeFullArgs& a = s.full;
+  const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
+  const Launch L = make_launch(a, l, true);
+  char* ws = static_cast<char*>(a.ws);
+  int32_t* flag = reinterpret_cast<int32_t*>(ws + l.flag);
+  float* rescored = reinterpret_cast<float*>(ws + l.rescored);
+  const int disjoint = (s.sel_flags & SSA_SELECT_DISJOINT) ? 1 : 0;
+  int grid = 0;
+  hipError_t e = launch_full<true>(a, L, stream, &grid);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_full_combine_select, dim3(a.Hq, a.B), dim3(kCombineThreads), 0, stream,
+                     L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
+                     grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
+                     a.ctx_lens,
+                     a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count, flag);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.max_ctx == 0) return e;
+  // rows whose lists did not hold the top k: rescored, then selected exactly
+  const int G = a.Hq / a.Hkv;
+  e = dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
+    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>),
+                       dim3(std::min(kRescoreBlocks, ceil_div(a.max_ctx, 256)), a.B * a.Hq),
+                       dim3(256), 0, stream, a.q, a.k, a.ctx_lens, flag, a.Hq, a.Hkv, a.Nmax,
+                       a.max_ctx, a.scale, a.eps, L.normq, rescored);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  SelectArgs sa;
+  sa.B = a.B;
+  sa.Hq = a.Hq;
+  sa.Nmax = a.max_ctx;  // row stride of the rescored rows
+  sa.max_ctx = a.max_ctx;
+  sa.scores = rescored;
+  sa.ctx_lens = a.ctx_lens;
+  sa.k_top = s.k_top;
+  sa.n_recent = s.n_recent;
+  sa.flags = s.sel_flags;
+  sa.sel_idx = s.sel_idx;
+  sa.sel_count = s.sel_count;
+  sa.ws = nullptr;
+  return launch_select_rows(sa, flag, stream);
 }
 
 }  // namespace ssa

@@ -26,6 +26,17 @@ struct DecodeFullArgs {
   void* ws;
 };
 size_t decode_full_ws_bytes(int B, int Hq, int Hkv, int max_ctx);
+
+// The full layer and the selection of its scores in one call.
+struct DecodeFullSelectArgs {
+  DecodeFullArgs full;  // full.scores may be null
+  int k_top, n_recent;
+  uint32_t sel_flags;
+  int32_t* sel_idx;
+  int32_t* sel_count;
+};
+size_t decode_full_select_ws_bytes(int B, int Hq, int Hkv, int max_ctx);
+hipError_t launch_decode_full_select(const DecodeFullSelectArgs& a, hipStream_t stream);
 // Upper bound on the 64-key tiles of one call (tile indices are 32-bit).
 int64_t decode_full_tiles_bound(int B, int Hkv, int max_ctx);
 hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream);
@@ -42,6 +53,8 @@ struct SelectArgs {
 };
 size_t select_ws_bytes(int B, int Hq, int max_ctx, int stride);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// The exact selection of the rows with row_flag[row] != 0 only (no workspace).
+hipError_t launch_select_rows(const SelectArgs& a, const int32_t* row_flag, hipStream_t stream);
 
 struct DecodeSparseArgs {
   int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;

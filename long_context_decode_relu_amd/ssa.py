@@ -38,9 +38,10 @@ SSA_OP_DECODE_FULL = 0
 SSA_OP_SELECT = 1
 SSA_OP_DECODE_SPARSE = 2
 SSA_OP_PREFILL_FULL = 3
+SSA_OP_DECODE_FULL_SELECT = 4
 
 EXPORTED = ("ssa_abi_version", "ssa_status_string", "ssa_workspace_bytes", "ssa_decode_full",
-            "ssa_select_topk_recent", "ssa_decode_sparse", "ssa_prefill_full")
+            "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse", "ssa_prefill_full")
 
 
 class SsaError(RuntimeError):
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.ssa_workspace_bytes.argtypes = [I32, SP, I32]
         L.ssa_decode_full.restype = I32
         L.ssa_decode_full.argtypes = [SP, P, P, P, P, F, F, F, U32, P, P, P, P, P, SZ, P]
+        L.ssa_decode_full_select.restype = I32
+        L.ssa_decode_full_select.argtypes = [SP, P, P, P, P, F, F, F, U32, I32, I32, U32, P, P, P, P,
+                                             P, P, P, SZ, P]
         L.ssa_select_topk_recent.restype = I32
         L.ssa_select_topk_recent.argtypes = [SP, P, P, I32, I32, U32, P, P, P, SZ, P]
         L.ssa_decode_sparse.restype = I32
@@ -169,6 +173,41 @@ def ssa_decode_full(q: torch.Tensor, cache: Cache, *, scale: float = 1.0, c: flo
                                _ptr(nnz), _ptr(vrows), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssa_decode_full")
     return out, scores, nnz, vrows
+
+
+def ssa_decode_full_select(q: torch.Tensor, cache: Cache, *, scale: float = 1.0, c: float = 1.0,
+                           eps: float = 1e-6, flags: int = SSA_NORM_Q, k_top: int = 1024,
+                           n_recent: int = 128, sel_flags: int = 0, want_scores: bool = False,
+                           want_stats: bool = False, out: torch.Tensor | None = None,
+                           ws: torch.Tensor | None = None):
+    """Full layer and selection in one call.
+
+    Returns (out, sel_idx, sel_count, scores, nnz, vrows); scores, nnz and vrows
+    are None unless asked for.
+    """
+    cache.check()
+    _need(q.is_cuda and q.dtype == torch.float32 and q.dim() == 3 and q.is_contiguous(),
+          "q must be contiguous float32 [B, Hq, D] on the GPU")
+    B, Hq, D = q.shape
+    _need(B == cache.k.shape[0] and D == cache.k.shape[3], "q and cache disagree")
+    dev = q.device
+    shp = cache.shape(Hq)
+    stride = k_top + n_recent
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, Hq, cache.k.shape[2]), dtype=torch.float32, device=dev) if want_scores else None
+    sel = torch.empty((B, Hq, stride), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    nnz = torch.empty((B, Hq), dtype=torch.int32, device=dev) if want_stats else None
+    vrows = torch.empty((B, cache.k.shape[1]), dtype=torch.int32, device=dev) if want_stats else None
+    if ws is None:
+        ws = workspace(SSA_OP_DECODE_FULL_SELECT, shp, 0, dev)
+    st = lib().ssa_decode_full_select(ctypes.byref(shp), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                      _ptr(cache.ctx_lens), scale, c, eps, flags, k_top, n_recent,
+                                      sel_flags, _ptr(out), _ptr(scores), _ptr(sel), _ptr(cnt),
+                                      _ptr(nnz), _ptr(vrows), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ssa_decode_full_select")
+    return out, sel, cnt, scores, nnz, vrows
 
 
 def ssa_select_topk_recent(scores: torch.Tensor, cache: Cache, *, n_q_heads: int | None = None,

@@ -1,0 +1,116 @@
+"""GPU checks of ssa_decode_full_select, the full layer fused with the selection.
+
+Its outputs must be bit for bit those of ssa_decode_full followed by
+ssa_select_topk_recent on that call's scores (both sides run on the GPU from
+the same inputs). That two-call path is itself checked against the CPU oracle
+in the other GPU tests; one case here also compares the fused selection with
+the oracle directly. The cases reach every way the fused selection resolves a
+row: the cut among the per-head candidate lists (keys with a positive score),
+the lists of short rows (every key), the two-pass cut for lists longer than
+8192, and the exact fallback on rescored rows when a long row has fewer
+positive scores than k_top.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, score_bound
+from oracle import ssa_oracle as O
+from long_context_decode_relu_amd import ssa, synth
+from test_gpu_workloads import selection_vs_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def two_calls(wl, cache, q, *, scale, c, eps, flags, k_top, n_recent, sel_flags):
+    out, scores, nnz, vrows = ssa.ssa_decode_full(q, cache, scale=scale, c=c, eps=eps, flags=flags,
+                                                  want_scores=True, want_stats=True)
+    sel, cnt = ssa.ssa_select_topk_recent(scores, cache, k_top=k_top, n_recent=n_recent,
+                                          flags=sel_flags)
+    return out, scores, nnz, vrows, sel, cnt
+
+
+def check_fused(wl, *, scale=1.0, c=1.0, eps=1e-6, flags=ssa.SSA_NORM_Q, k_top=1024, n_recent=128,
+                sel_flags=0, want_scores=False):
+    cache = ssa.cache_from_workload(wl, DEV)
+    q = torch.from_numpy(wl.q).to(DEV)
+    ref = [t.cpu().numpy() for t in two_calls(wl, cache, q, scale=scale, c=c, eps=eps, flags=flags,
+                                              k_top=k_top, n_recent=n_recent, sel_flags=sel_flags)]
+    out, sel, cnt, scores, nnz, vrows = ssa.ssa_decode_full_select(
+        q, cache, scale=scale, c=c, eps=eps, flags=flags, k_top=k_top, n_recent=n_recent,
+        sel_flags=sel_flags, want_scores=want_scores, want_stats=True)
+    torch.cuda.synchronize()
+    r_out, r_scores, r_nnz, r_vrows, r_sel, r_cnt = ref
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), r_out.view(np.uint32)), wl.name
+    assert np.array_equal(nnz.cpu().numpy(), r_nnz) and np.array_equal(vrows.cpu().numpy(), r_vrows)
+    assert np.array_equal(cnt.cpu().numpy(), r_cnt), wl.name
+    assert np.array_equal(sel.cpu().numpy(), r_sel), wl.name
+    if want_scores:
+        for b in range(wl.batch):
+            n = int(wl.ctx_lens[b])
+            got = scores.cpu().numpy()[b, :, :n].view(np.uint32)
+            assert np.array_equal(got, r_scores[b, :, :n].view(np.uint32)), wl.name
+    return sel.cpu().numpy(), cnt.cpu().numpy(), r_scores
+
+
+def test_fused_single_sequence_lists():
+    """32K keys at 95% sparsity: every head has > 1024 positive scores, so the
+    cut is resolved among the candidate lists; full scores also written."""
+    check_fused(synth.single_decode(n=32768), want_scores=True)
+
+
+def test_fused_ragged_batch_mixed_paths():
+    """Short rows (every key listed), a ragged tail, and long rows, in one batch."""
+    wl = synth.make_workload("fused_ragged", seed=31, batch=5, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[100, 1500, 8192, 8193, 40000], kv_capacity=40000, p=0.05)
+    check_fused(wl)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.01])
+def test_fused_sweep_two_pass_and_fallback(p):
+    """p = 0.5: lists far longer than 8192 (two-pass cut over the lists);
+    p = 0.01: fewer than 1024 positive scores (rows rescored and selected exactly)."""
+    check_fused(synth.sweep_decode(p))
+
+
+def test_fused_disjoint_small_k_and_window():
+    wl = synth.make_workload("fused_disjoint", seed=32, batch=3, n_q_heads=8, n_kv_heads=2,
+                             ctx_lens=[20000, 300, 50000], kv_capacity=50000, p=0.05)
+    check_fused(wl, k_top=64, n_recent=32, sel_flags=ssa.SSA_SELECT_DISJOINT)
+    check_fused(wl, k_top=2000, n_recent=0)
+
+
+def test_fused_fp32_group1_and_flags():
+    """fp32 cache, one query head per KV head (about 50% zero weights), with and
+    without query normalisation, key normalisation, a scale and c = 0."""
+    wl = synth.tiny_decode(n=4096)
+    check_fused(wl)
+    wl2 = synth.make_workload("fused_iid_long", seed=33, batch=2, n_q_heads=4, n_kv_heads=1,
+                              ctx_lens=[12000, 9000], kv_dtype="f32", recipe="iid")
+    check_fused(wl2, flags=ssa.SSA_NORM_Q | ssa.SSA_NORM_K, scale=0.5, c=0.0)
+    check_fused(wl2, flags=0, k_top=100)
+
+
+def test_fused_empty_and_tiny_contexts():
+    wl = synth.make_workload("fused_empty", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[0, 1, 1100], kv_capacity=2048, p=0.05)
+    check_fused(wl, k_top=1024, n_recent=128)
+
+
+def test_fused_block_step_vs_oracle():
+    """Batch 32, contexts log-uniform in [1K, 256K]: all paths at once (short
+    rows, list cuts, two-pass cuts at 256K, rescored rows); equality with the
+    two calls, and the selection of four sequences against the oracle."""
+    wl = synth.block_step()
+    sel, cnt, scores = check_fused(wl)
+    seqs = sorted({int(np.argmin(wl.ctx_lens)), int(np.argmax(wl.ctx_lens)), 7, 20})
+    sub = synth.Workload(name="fused_block_sub", batch=len(seqs), n_q_heads=16, n_kv_heads=2,
+                         head_dim=128, kv_capacity=wl.kv_capacity, kv_dtype="bf16",
+                         ctx_lens=wl.ctx_lens[seqs], q=wl.q[seqs], k=wl.k[seqs], v=wl.v[seqs],
+                         q_sparse=wl.q_sparse[:, seqs])
+    ref = O.decode_full(sub.q, sub.k, sub.v, sub.ctx_lens)
+    bounds = score_bound(sub, 1.0)
+    _, same = selection_vs_oracle(sub, ref["scores"], sel[seqs], cnt[seqs], bounds,
+                                  range(len(seqs)))
+    assert same >= 0.75 * len(seqs) * 16
