@@ -76,23 +76,26 @@ def alg_bytes_full(wl, vrows: np.ndarray, with_scores: bool = True) -> dict:
 
 
 PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_step_b8_64k_128k.txt")
-KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_decode_relu_amd", "csrc",
-                          "decode_full.hip")
+KERNEL_SRCS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_decode_relu_amd", "csrc", f)
+               for f in ("decode_full.hip", "select_core.h", "select.hip")]
 
 
 def measured_traffic():
-    """HBM bytes per ssa_decode_full call from the committed counter summary.
+    """HBM bytes per ssa_decode_full_select call from the committed counter summary.
 
     The summary records the bytes (calibrated FETCH_SIZE + WRITE_SIZE of the
-    prep, main and combine kernels) and the hash of the kernel source they
-    were taken on; once the source changes the figure no longer applies.
+    call's kernels) and the hash of the kernel sources they were taken on;
+    once a source changes the figure no longer applies.
     """
     import hashlib
     import re
     try:
         text = open(PROFILE).read()
         m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)", text)
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for path in KERNEL_SRCS:
+            h.update(open(path, "rb").read())
+        src = h.hexdigest()
     except OSError:
         return None
     if m and m.group(2) == src:
@@ -341,7 +344,8 @@ def main():
                                 "ssa_decode_full_select (decode_full_kernel with candidate lists + "
                                 "combine_select + rescore/select of flagged rows)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if args.unfused else measured_traffic(),
                      "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},
     }
     if not args.no_prefill:

@@ -789,6 +789,24 @@ constexpr int kCombineGroups = 8;
 constexpr int kCombineThreads = kHeadDim * kCombineGroups;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
+// (sequence, query head) of work-group L of the per-row kernels (a 1-D grid of
+// B*Hq). Work-group L runs on XCD L % 8; when the S streams are a multiple of
+// eight, L is numbered so that the G heads of a stream share one XCD (and its
+// L2), since they all read that stream's partials and candidate lists.
+__device__ __forceinline__ void row_of_block(int L, int Hq, int Hkv, int* b, int* h) {
+  const int G = Hq / Hkv, S = (int)(gridDim.x / G);
+  int j, jh;
+  if (S % kXcds == 0) {
+    j = L % kXcds + kXcds * ((L / kXcds) / G);
+    jh = (L / kXcds) % G;
+  } else {
+    j = L / G;
+    jh = L % G;
+  }
+  *b = j / Hkv;
+  *h = (j - *b * Hkv) * G + jh;
+}
+
 __device__ void combine_row(
     const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
@@ -798,7 +816,8 @@ __device__ void combine_row(
   __shared__ float s_den[kCombineWaves];
   __shared__ int s_cnt[kCombineWaves][2];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int h = blockIdx.x, b = blockIdx.y;
+  int b, h;
+  row_of_block(blockIdx.x, Hq, Hkv, &b, &h);
   const int d = tid % kHeadDim, grp = tid / kHeadDim;
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
@@ -1064,7 +1083,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
               vrows);
   __syncthreads();
-  const int h = blockIdx.x, b = blockIdx.y;
+  int b, h;
+  row_of_block(blockIdx.x, Hq, Hkv, &b, &h);
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
   const int row = b * Hq + h;
@@ -1272,7 +1292,7 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   int grid = 0;
   hipError_t e = launch_full<false>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq, a.B), dim3(kCombineThreads), 0,
+  hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq * a.B), dim3(kCombineThreads), 0,
                      stream, L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows);
   return hipGetLastError();
@@ -1289,7 +1309,7 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   int grid = 0;
   hipError_t e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_full_combine_select, dim3(a.Hq, a.B), dim3(kCombineThreads), 0, stream,
+  hipLaunchKernelGGL(decode_full_combine_select, dim3(a.Hq * a.B), dim3(kCombineThreads), 0, stream,
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
                      a.ctx_lens,
