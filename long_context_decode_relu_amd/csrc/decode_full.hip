@@ -427,27 +427,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       lsc = cand_sc + (size_t)first * kTileKeys * G;
     }
   };
-  // list the keys of mask m (this lane's key when `mine`: index key, scores sv)
-  auto list_keys = [&](uint64_t m, bool mine, int key, const float (&sv)[G]) {
+  // Entry of this lane's key among the keys of mask m listed next in the
+  // current slot (-1 unless `mine`); advances the slot's count.
+  auto list_entry = [&](uint64_t m, bool mine) {
+    int e = -1;
     if constexpr (CAND) {
       if (m) {
-        const int e = ccount + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (mine) {
-          lidx[e] = key;
-          float* d = lsc + (size_t)e * G;
-          if constexpr (G >= 4) {
-#pragma unroll
-            for (int p = 0; p < G / 4; ++p)
-              *reinterpret_cast<f32x4*>(d + 4 * p) = f32x4{sv[4 * p], sv[4 * p + 1], sv[4 * p + 2], sv[4 * p + 3]};
-          } else if constexpr (G == 2) {
-            *reinterpret_cast<f32x2*>(d) = f32x2{sv[0], sv[1]};
-          } else {
-            d[0] = sv[0];
-          }
-        }
+        if (mine)
+          e = ccount + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
         ccount += __popcll(m);
       }
+    }
+    return e;
+  };
+  // entry e of list (li, ls): key index and the group's scores sv
+  auto list_store = [&](int32_t* li, float* ls, int e, int key, const float (&sv)[G]) {
+    li[e] = key;
+    float* d = ls + (size_t)e * G;
+    if constexpr (G >= 4) {
+#pragma unroll
+      for (int p = 0; p < G / 4; ++p)
+        *reinterpret_cast<f32x4*>(d + 4 * p) = f32x4{sv[4 * p], sv[4 * p + 1], sv[4 * p + 2], sv[4 * p + 3]};
+    } else if constexpr (G == 2) {
+      *reinterpret_cast<f32x2*>(d) = f32x2{sv[0], sv[1]};
+    } else {
+      d[0] = sv[0];
     }
   };
   auto flush = [&](const Stream& st) {
@@ -560,12 +565,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     open_slot(cur);
 
     // Pipelined over the wave's tiles. Iteration t waits for tile t, reads
-    // it from LDS, issues the V rows of tile t-1's survivors, the copy of
-    // tile t+1 and the score stores of tile t-1, in that order, scores tile
-    // t, then waits only for the V rows (the vector-memory counter completes
-    // in issue order, so the tile copy and the stores behind them stay in
-    // flight) and adds them. The tile copy therefore has a whole iteration to
-    // arrive, the V rows a whole scoring pass.
+    // it from LDS, issues the score stores (or candidate-list entries) of
+    // tile t-1, the V rows of its survivors and the copy of tile t+1, in that
+    // order, scores tile t, then waits only for the stores and the V rows
+    // (the vector-memory counter completes in issue order, so the tile copy
+    // behind them stays in flight) and adds the rows. The tile copy therefore
+    // has a whole iteration to arrive, the stores and V rows a whole scoring
+    // pass; no store is outstanding at the wait for the next tile.
     Stream st = cur;                   // stream of tile t
     bool has_prev = false;
     // value row of key 0 of tile t-1; before the first tile, that of tile t0
@@ -576,6 +582,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     bool p_valid = false;
     uint64_t p_mask = 0;               // tile t-1's survivors
     float p_s[G];
+    // tile t-1's candidate-list entry of this lane (-1: none) and its list;
+    // stored with the score stores, so that the wait for the stores is the
+    // one after the scoring pass rather than the one for the next tile
+    int p_e = -1, p_key = 0;
+    int32_t* p_li = nullptr;
+    float* p_ls = nullptr;
 
     // V rows of tile t-1's survivors still in `m`, the first of rank r0,
     // four at a time (the compiler waits for these loads itself)
@@ -619,8 +631,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       tile_read_bf16(my_tile, lane, kr);
       wait_lgkm0();
 
-      // 2. score stores of tile t-1
+      // 2. score stores (or candidate-list entry) of tile t-1
       if (has_prev && p_sc0) store_scores();
+      if constexpr (CAND) {
+        if (p_e >= 0) list_store(p_li, p_ls, p_e, p_key, p_s);
+      }
       // 3. the first kVS survivors of tile t-1 (raw bf16 pairs): always kVS
       //    loads, the spare ones repeating a row already being loaded
       uint64_t m = p_mask;
@@ -677,7 +692,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       p_mask = __ballot(any);
       if constexpr (CAND) {
         const bool all = st.n <= kCandAll;
-        list_keys(all ? __ballot(valid) : p_mask, all ? valid : any, base + lane, p_s);
+        p_e = list_entry(all ? __ballot(valid) : p_mask, all ? valid : any);
+        p_key = base + lane;
+        p_li = lidx;
+        p_ls = lsc;
       }
       if (any) {
         const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(p_mask >> 32),
@@ -698,9 +716,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       p_valid = valid;
       has_prev = true;
     }
-    // the last tile's score stores and V rows
+    // the last tile's score stores (or list entry) and V rows
     if (has_prev) {
       if (p_sc0) store_scores();
+      if constexpr (CAND) {
+        if (p_e >= 0) list_store(p_li, p_ls, p_e, p_key, p_s);
+      }
       v_rows_sync(p_mask, 0);
     }
     flush(cur);
@@ -738,7 +759,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       uint64_t mask = __ballot(any);
       if constexpr (CAND) {
         const bool all = cur.n <= kCandAll;
-        list_keys(all ? __ballot(valid) : mask, all ? valid : any, key, sv);
+        const int e = list_entry(all ? __ballot(valid) : mask, all ? valid : any);
+        if (e >= 0) list_store(lidx, lsc, e, key, sv);
       }
       if (srow && valid) {
 #pragma unroll

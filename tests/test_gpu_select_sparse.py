@@ -210,6 +210,31 @@ def test_sparse_scale_flags_and_nan_poison():
     check_sparse(wl, sels, flags=O.SSA_NORM_Q | O.SSA_NORM_K)
 
 
+def test_sparse_union_extremes():
+    """Heads of a group select disjoint blocks (the union is the largest the
+    stride allows, 8 * 1152 rows spread over several 64K-key planning passes),
+    or all the same rows, or one dense window shared with a sparse tail."""
+    wl = synth.make_workload("spunion", seed=36, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[150000, 70000], kv_capacity=150000, recipe="planted", p=0.05)
+    rng = np.random.default_rng(36)
+    sels = []
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        row = []
+        for h in range(16):
+            g = h % 8
+            if b == 0:   # disjoint: head g of each group takes every 8th key of its own stripe
+                s = np.arange(g, n, 8)[: 1152 * 16: 16][:1152]
+            elif h < 8:  # group 0: all heads select the same rows
+                s = np.sort(rng.choice(n, 1152, replace=False)) if g == 0 else row[0]
+            else:        # group 1: a dense recent window plus a sparse tail of its own per head
+                tail = np.sort(rng.choice(n - 128, 1024, replace=False))
+                s = np.concatenate([tail, np.arange(n - 128, n)])
+            row.append(np.asarray(s, dtype=np.int64))
+        sels.append(row)
+    check_sparse(wl, sels)
+
+
 def test_block_step_sampled_full_size():
     """The batch-8 64K-128K workload end to end: full layer -> selection -> sparse layer.
 
