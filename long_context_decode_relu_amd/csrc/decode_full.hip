@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part_num,
     float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
     int* __restrict__ tile_pre_out, int32_t* __restrict__ cand_idx, float* __restrict__ cand_sc,
-    int32_t* __restrict__ cand_cnt,
+    int32_t* __restrict__ cand_cnt, int32_t* __restrict__ fb_count,
     int B, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps, int normq,
     int cus_per_xcd) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
@@ -332,8 +332,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
 
   if (wave == 0) tile_prefix(ctx_lens, S, Hkv, max_ctx, lane, s_tpre);
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= S; i += kThreads) tile_pre_out[i] = s_tpre[i];
+    // the list of rows the selection falls back on starts empty
+    if (fb_count && threadIdx.x == 0) *fb_count = 0;
+  }
 
   const int T = s_tpre[S];
   // With more waves than tiles only the first T waves work (one tile each),
@@ -936,7 +939,8 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
                                   const int* __restrict__ tile_pre, int S, int G, int jh, int j,
                                   int Wl, int n, int k_top, int n_recent, int disjoint,
                                   int32_t* __restrict__ out, int stride,
-                                  int32_t* __restrict__ count, int32_t* __restrict__ flag) {
+                                  int32_t* __restrict__ count, int32_t* __restrict__ flag,
+                                  int pre_cnt) {
   const int tid = threadIdx.x;
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
@@ -953,21 +957,30 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
   const int W = min(Wl, T);
   const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
   const int np = p1 - p0;
-  if (np >= kSegWords) {
+  if (2 * np + 1 > kSegWords) {
     if (tid == 0) *flag = 1;
     return;
   }
-  // slot offsets of the row's entries (in sh.bits) and their total
+  // slot offsets of the row's entries (offs, in sh.bits), their total, and
+  // where each slot's list starts (base, after them)
   uint32_t* offs = sh.bits;
+  uint32_t* base = sh.bits + np + 1;
   {
     const int per = ceil_div(np, kSelThreads);
     int local = 0;
-    for (int q = tid * per; q < min(np, tid * per + per); ++q) local += cand_cnt[p0 + q];
+    if (per == 1) {
+      local = tid < np ? pre_cnt : 0;
+    } else {
+      for (int q = tid * per; q < min(np, tid * per + per); ++q) local += cand_cnt[p0 + q];
+    }
     int total;
     int run = block_scan_excl(local, sh.scan, &total);
     for (int q = tid * per; q < min(np, tid * per + per); ++q) {
       offs[q] = (uint32_t)run;
-      run += cand_cnt[p0 + q];
+      run += per == 1 ? pre_cnt : cand_cnt[p0 + q];
+      int first, nt;
+      slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
+      base[q] = (uint32_t)(first * kTileKeys);
     }
     if (tid == 0) offs[np] = (uint32_t)total;
     __syncthreads();
@@ -996,18 +1009,14 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
         if ((int)offs[mid] <= e0) lo = mid; else hi = mid;
       }
     }
-    int q = lo, first = 0, nt = 0;
-    slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
+    int q = lo;
 #pragma unroll
     for (int u = 0; u < kGatherPer; ++u) {
       const int e = e0 + u;
       at[u] = 0;
       if (e < e1) {
-        while ((int)offs[q + 1] <= e) {
-          ++q;
-          slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
-        }
-        at[u] = (size_t)first * kTileKeys + (e - (int)offs[q]);
+        while ((int)offs[q + 1] <= e) ++q;
+        at[u] = (size_t)base[q] + (e - (int)offs[q]);
       }
     }
     float sc[kGatherPer];
@@ -1100,82 +1109,127 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_sc,
     const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ ctx_lens, int max_ctx,
     int k_top, int n_recent, int disjoint,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int32_t* __restrict__ row_flag) {
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int32_t* __restrict__ row_flag,
+    int32_t* __restrict__ fb) {
   __shared__ SelShared sh;
-  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
-              vrows);
-  __syncthreads();
   int b, h;
   row_of_block(blockIdx.x, Hq, Hkv, &b, &h);
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
+  const int j = b * Hkv + kvh;
+  // the entry count of this thread's slot of the row's stream, loaded before
+  // the combine so that the two rounds of loads overlap
+  int pre_cnt = 0;
+  {
+    const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
+    const int W = min(Wl, T);
+    if (s1 > s0) {
+      const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+      if ((int)threadIdx.x < p1 - p0) pre_cnt = cand_cnt[p0 + threadIdx.x];
+    }
+  }
+  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
+              vrows);
+  __syncthreads();
   const int row = b * Hq + h;
   const int stride = k_top + n_recent;
   const int n = live_keys(ctx_lens, b, max_ctx);
-  select_from_cands(sh, cand_idx, cand_sc, cand_cnt, tile_pre, S, G, jh, b * Hkv + kvh, Wl, n,
-                    k_top, n_recent,
-                    disjoint, sel_idx + (size_t)row * stride, stride, sel_count + row,
-                    row_flag + row);
+  select_from_cands(sh, cand_idx, cand_sc, cand_cnt, tile_pre, S, G, jh, j, Wl, n, k_top,
+                    n_recent, disjoint, sel_idx + (size_t)row * stride, stride, sel_count + row,
+                    row_flag + row, pre_cnt);
+  // a flagged row joins the fallback list (fb[0] rows at fb[1 ..], their
+  // done counters at fb[1 + rows + row]); thread 0 wrote the flag
+  if (threadIdx.x == 0 && row_flag[row]) {
+    const int rows = (int)gridDim.x;
+    fb[1 + rows + row] = 0;
+    fb[1 + atomicAdd(fb, 1)] = row;
+  }
 }
 
-// Scores of the flagged rows, computed exactly as the full-layer kernel does
-// (same widening, same FMA order over the dimensions, same query factor), into
-// rows of `max_ctx` floats for the exact selection. One key per thread;
-// kRescoreBlocks work-groups per row stride over its keys (rows that need no
-// rescoring cost one early exit per work-group).
-constexpr int kRescoreBlocks = 16;
+// The rows whose candidate lists did not decide the selection (listed by
+// the combine), rescored and selected exactly. Work item (f, s) scores slice s
+// of the keys of listed row f exactly as the full-layer kernel does (same
+// widening, same FMA order over the dimensions, same query factor) into the
+// row's buffer of `max_ctx` floats; the work-group that completes the last
+// slice of a row (a counter per row, zeroed by the combine) selects it from
+// the buffer. The items run on a persistent grid; with no listed row every
+// work-group exits after one load.
+constexpr int kFallbackBlocks = 128;
+constexpr int kFallbackSlices = 16;
 
 template <int G, bool BF16, bool NORMK>
-__global__ __launch_bounds__(256) void decode_full_rescore(
+__global__ __launch_bounds__(kSelThreads) void decode_full_fallback(
     const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ row_flag, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
-    float eps, int normq, float* __restrict__ rs) {
-  const int row = blockIdx.y;
-  if (!row_flag[row]) return;
-  const int b = row / Hq, h = row - b * Hq;
-  const int kvh = h / G, jh = h - kvh * G;
-  const int n = live_keys(ctx_lens, b, max_ctx);
-  const float* qrow = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
-  const int lane = threadIdx.x & (kWave - 1);
-  float fac = scale;
-  if (normq) fac = __shfl(head_rms_factor<G>(qrow, lane, scale, eps), jh * (kWave / G), kWave);
-  const float* qh = qrow + jh * kHeadDim;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-    const size_t r = ((size_t)b * Hkv + kvh) * Nmax + i;
-    float acc = 0.f, ksq = 0.f;
+    int32_t* __restrict__ fb, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps,
+    int normq, int k_top, int n_recent, int disjoint, int rows, float* __restrict__ rs,
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count) {
+  const int nf = fb[0];
+  if (nf == 0) return;
+  __shared__ SelShared sh;
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int stride = k_top + n_recent;
+  for (int it = blockIdx.x; it < nf * kFallbackSlices; it += gridDim.x) {
+    const int f = it / kFallbackSlices, sl = it - f * kFallbackSlices;
+    const int row = fb[1 + f];
+    const int b = row / Hq, h = row - b * Hq;
+    const int kvh = h / G, jh = h - kvh * G;
+    const int n = live_keys(ctx_lens, b, max_ctx);
+    const float* qrow = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
+    float fac = scale;
+    if (normq) fac = __shfl(head_rms_factor<G>(qrow, lane, scale, eps), jh * (kWave / G), kWave);
+    const float* qh = qrow + jh * kHeadDim;
+    const int per = ceil_div(n, kFallbackSlices);
+    const int i1 = min(n, sl * per + per);
+    for (int i = sl * per + tid; i < i1; i += kSelThreads) {
+      const size_t r = ((size_t)b * Hkv + kvh) * Nmax + i;
+      float acc = 0.f, ksq = 0.f;
 #pragma unroll 4
-    for (int c = 0; c < 8; ++c) {
-      float e[16];
-      if constexpr (BF16) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(k) + r * 16 + 2 * c;
-        KeyRow<true> one;
-        one.c[0] = kp[0];
-        one.c[1] = kp[1];
-        one.chunk16(0, e);
-      } else {
-        const f32x4* kp = reinterpret_cast<const f32x4*>(k) + r * 32 + 4 * c;
-        KeyRow<false> one;
+      for (int c = 0; c < 8; ++c) {
+        float e[16];
+        if constexpr (BF16) {
+          const u32x4* kp = reinterpret_cast<const u32x4*>(k) + r * 16 + 2 * c;
+          KeyRow<true> one;
+          one.c[0] = kp[0];
+          one.c[1] = kp[1];
+          one.chunk16(0, e);
+        } else {
+          const f32x4* kp = reinterpret_cast<const f32x4*>(k) + r * 32 + 4 * c;
+          KeyRow<false> one;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) one.c[p] = kp[p];
-        one.chunk16(0, e);
+          for (int p = 0; p < 4; ++p) one.c[p] = kp[p];
+          one.chunk16(0, e);
+        }
+        if constexpr (NORMK) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) ksq = fmaf(e[t], e[t], ksq);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc = fmaf(qh[16 * c + t], e[t], acc);
       }
-      if constexpr (NORMK) {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) ksq = fmaf(e[t], e[t], ksq);
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) acc = fmaf(qh[16 * c + t], e[t], acc);
+      float kf = 1.f;
+      if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
+      rs[(size_t)row * max_ctx + i] = NORMK ? acc * fac * kf : acc * fac;
     }
-    float kf = 1.f;
-    if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
-    rs[(size_t)row * max_ctx + i] = NORMK ? acc * fac * kf : acc * fac;
+    // the slice's scores are visible device-wide before it is counted; the
+    // work-group that counts the row's last slice reads them all
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&fb[1 + rows + row], 1) == kFallbackSlices - 1;
+    __syncthreads();
+    if (s_last) {
+      __threadfence();
+      select_row_exact(sh, rs + (size_t)row * max_ctx, n, k_top, n_recent, disjoint,
+                       sel_idx + (size_t)row * stride, stride, sel_count + row);
+    }
+    __syncthreads();
   }
 }
 
 struct WsLayout {
   size_t num, den, nnz, vrows, tile_pre, total;
   // the fused selection: candidate lists and counts, row flags, rescored rows
-  size_t cand_idx, cand_sc, cand_cnt, flag, rescored, total_sel;
+  size_t cand_idx, cand_sc, cand_cnt, flag, fb, rescored, total_sel;
 };
 
 WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
@@ -1196,6 +1250,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   l.cand_sc = o; o += align_up(tiles * kTileKeys * G * sizeof(float), 256);
   l.cand_cnt = o; o += align_up(slots * sizeof(int32_t), 256);
   l.flag = o; o += align_up(rows * sizeof(int32_t), 256);
+  l.fb = o; o += align_up((1 + 2 * rows) * sizeof(int32_t), 256);
   l.rescored = o; o += align_up(rows * (size_t)max_ctx * sizeof(float), 256);
   l.total_sel = o;
   return l;
@@ -1213,6 +1268,7 @@ struct Launch {
   int32_t* cand_idx;
   float* cand_sc;
   int32_t* cand_cnt;
+  int32_t* fb;  // fallback rows: count, list, per-row done counters
   int B, Hq, Hkv, Nmax, max_ctx;
   float scale, eps;
   int normq;
@@ -1259,7 +1315,7 @@ hipError_t launch_full(const DecodeFullArgs& a, const Launch& L, hipStream_t str
     *grid_out = (int)grid;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, L.q, L.k, L.v, L.ctx_lens,
                        L.scores, L.num, L.den, L.nnz, L.vrows, L.tile_pre, L.cand_idx, L.cand_sc,
-                       L.cand_cnt, L.B,
+                       L.cand_cnt, L.fb, L.B,
                        L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale, L.eps, L.normq, cus_per_xcd);
     return hipGetLastError();
   });
@@ -1281,6 +1337,7 @@ Launch make_launch(const DecodeFullArgs& a, const WsLayout& l, bool cand) {
   L.cand_idx = cand ? reinterpret_cast<int32_t*>(ws + l.cand_idx) : nullptr;
   L.cand_sc = cand ? reinterpret_cast<float*>(ws + l.cand_sc) : nullptr;
   L.cand_cnt = cand ? reinterpret_cast<int32_t*>(ws + l.cand_cnt) : nullptr;
+  L.fb = cand ? reinterpret_cast<int32_t*>(ws + l.fb) : nullptr;
   L.B = a.B;
   L.Hq = a.Hq;
   L.Hkv = a.Hkv;
@@ -1335,33 +1392,18 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
                      a.ctx_lens,
-                     a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count, flag);
+                     a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count, flag, L.fb);
   e = hipGetLastError();
   if (e != hipSuccess || a.max_ctx == 0) return e;
   // rows whose lists did not hold the top k: rescored, then selected exactly
   const int G = a.Hq / a.Hkv;
-  e = dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
-    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>),
-                       dim3(std::min(kRescoreBlocks, ceil_div(a.max_ctx, 256)), a.B * a.Hq),
-                       dim3(256), 0, stream, a.q, a.k, a.ctx_lens, flag, a.Hq, a.Hkv, a.Nmax,
-                       a.max_ctx, a.scale, a.eps, L.normq, rescored);
+  return dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
+    hipLaunchKernelGGL((decode_full_fallback<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kSelThreads),
+                       0, stream, a.q, a.k, a.ctx_lens, L.fb, a.Hq, a.Hkv, a.Nmax, a.max_ctx,
+                       a.scale, a.eps, L.normq, s.k_top, s.n_recent, disjoint, a.B * a.Hq,
+                       rescored, s.sel_idx, s.sel_count);
     return hipGetLastError();
   });
-  if (e != hipSuccess) return e;
-  SelectArgs sa;
-  sa.B = a.B;
-  sa.Hq = a.Hq;
-  sa.Nmax = a.max_ctx;  // row stride of the rescored rows
-  sa.max_ctx = a.max_ctx;
-  sa.scores = rescored;
-  sa.ctx_lens = a.ctx_lens;
-  sa.k_top = s.k_top;
-  sa.n_recent = s.n_recent;
-  sa.flags = s.sel_flags;
-  sa.sel_idx = s.sel_idx;
-  sa.sel_count = s.sel_count;
-  sa.ws = nullptr;
-  return launch_select_rows(sa, flag, stream);
 }
 
 }  // namespace ssa

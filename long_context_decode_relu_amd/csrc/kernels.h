@@ -54,7 +54,6 @@ struct SelectArgs {
 size_t select_ws_bytes(int B, int Hq, int max_ctx, int stride);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 // The exact selection of the rows with row_flag[row] != 0 only (no workspace).
-hipError_t launch_select_rows(const SelectArgs& a, const int32_t* row_flag, hipStream_t stream);
 
 struct DecodeSparseArgs {
   int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;

@@ -219,13 +219,10 @@ __global__ __launch_bounds__(kSelThreads) void select_finish(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
     int k_top, int n_recent, int disjoint, int segs, int cap, const int32_t* __restrict__ cseg,
     const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cidx,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int stride,
-    const int32_t* __restrict__ row_flag) {
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int stride) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
-  // with row_flag, only the flagged rows, exactly from the scores
-  if (row_flag && !row_flag[row]) return;
   const int b = row / Hq;
   const int n = min(ctx_lens[b], Nmax);
   const int pool = disjoint ? max(0, n - n_recent) : n;
@@ -243,7 +240,7 @@ __global__ __launch_bounds__(kSelThreads) void select_finish(
     const int nseg = ceil_div(pool, kColSeg);
     const int32_t* counts = cseg + (size_t)row * segs;
     int cnt = INT_MAX;  // short rows and rows of very many segments: exact path
-    if (!row_flag && pool > kCap && nseg <= kSelThreads) {
+    if (pool > kCap && nseg <= kSelThreads) {
       const int c = tid < nseg ? counts[tid] : 0;
       int total;
       const int before = block_scan_excl(c, sh.scan, &total);
@@ -299,67 +296,8 @@ __global__ __launch_bounds__(kSelThreads) void select_finish(
     marked = true;
   }
 
-  // mark the recent window, then compact, one segment of 2^18 keys at a time
-  const int r0 = max(0, n - n_recent);
-  int written = 0;
-  int32_t* out = sel_idx + (size_t)row * stride;
-  const int lane = tid & (kWave - 1), wave = tid >> 6;
-  if (marked) {
-    __syncthreads();
-    for (int i = r0 + tid; i < n; i += kSelThreads) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
-    __syncthreads();
-  }
-  for (int seg0 = 0; seg0 < n; seg0 += kSegKeys) {
-    const int seg1 = min(n, seg0 + kSegKeys);
-    for (int base0 = seg0 + wave * kWave; base0 < seg1 && !marked; base0 += kSelThreads * kUnroll) {
-      uint32_t keys[kUnroll];
-      const int kend = min(seg1, pool);
-      if (kend > 0) load_keys(s, base0 + lane, kSelThreads, kend, keys);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int base = base0 + u * kSelThreads;
-        if (base >= seg1) break;
-        const int i = base + lane;
-        bool sel = false;
-        if (i < seg1) {
-          if (i >= r0) {
-            sel = true;
-          } else if (i < pool) {
-            sel = keys[u] > vstar || (keys[u] == vstar && i <= istar);
-          }
-        }
-        const uint64_t m = __ballot(sel);
-        const int w0 = (base - seg0) >> 5;
-        if (lane == 0) sh.bits[w0] = (uint32_t)m;
-        if (lane == 32 && w0 + 1 < kSegWords) sh.bits[w0 + 1] = (uint32_t)(m >> 32);
-      }
-    }
-    __syncthreads();
-    const int nwords = ceil_div(seg1 - seg0, 32);
-    const int per = ceil_div(nwords, kSelThreads);
-    int local = 0;
-    for (int j = 0; j < per; ++j) {
-      const int wi = tid * per + j;
-      if (wi < nwords) local += __popc(sh.bits[wi]);
-    }
-    int total;
-    int pos = written + block_scan_excl(local, sh.scan, &total);
-    for (int j = 0; j < per; ++j) {
-      const int wi = tid * per + j;
-      if (wi >= nwords) break;
-      uint32_t m = sh.bits[wi];
-      while (m) {
-        const int bit = __ffs(m) - 1;
-        m &= m - 1;
-        if (pos < stride) out[pos] = seg0 + wi * 32 + bit;
-        ++pos;
-      }
-    }
-    written += total;
-    __syncthreads();
-  }
-  for (int p = written + tid; p < stride; p += kSelThreads) out[p] = -1;
-  if (tid == 0) sel_count[row] = written;
+  emit_selection(sh, s, n, pool, vstar, istar, marked, n_recent, sel_idx + (size_t)row * stride,
+                 stride, sel_count + row);
 }
 
 struct SelLayout {
@@ -403,17 +341,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
                      ckey, cidx);
   hipLaunchKernelGGL(select_finish, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
                      a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt, ckey, cidx,
-                     a.sel_idx, a.sel_count, a.k_top + a.n_recent, nullptr);
-  return hipGetLastError();
-}
-
-hipError_t launch_select_rows(const SelectArgs& a, const int32_t* row_flag, hipStream_t stream) {
-  const int rows = a.B * a.Hq;
-  if (rows == 0) return hipSuccess;
-  const int disjoint = (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0;
-  hipLaunchKernelGGL(select_finish, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
-                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, 1, 0, nullptr, nullptr, nullptr,
-                     a.sel_idx, a.sel_count, a.k_top + a.n_recent, row_flag);
+                     a.sel_idx, a.sel_count, a.k_top + a.n_recent);
   return hipGetLastError();
 }
 

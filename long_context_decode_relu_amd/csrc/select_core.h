@@ -371,4 +371,108 @@ __device__ int compact_candidates(SelShared& sh, int c, int n, int r0, uint32_t 
 }
 
 }  // namespace
+// The selection of one row written out: the pool keys above the cut
+// (key > v*, or key == v* and index <= i*; already in sh.bits when `marked`)
+// and the recent window [n - n_recent, n), in ascending order, to
+// out[0 .. stride) (padded with -1) and *count. One segment of kSegKeys keys
+// at a time.
+__device__ void emit_selection(SelShared& sh, const float* s, int n, int pool, uint32_t vstar,
+                               int istar, bool marked, int n_recent, int32_t* __restrict__ out,
+                               int stride, int32_t* __restrict__ count) {
+  const int tid = threadIdx.x;
+  // mark the recent window, then compact, one segment of 2^18 keys at a time
+  const int r0 = max(0, n - n_recent);
+  int written = 0;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  if (marked) {
+    __syncthreads();
+    for (int i = r0 + tid; i < n; i += kSelThreads) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+    __syncthreads();
+  }
+  for (int seg0 = 0; seg0 < n; seg0 += kSegKeys) {
+    const int seg1 = min(n, seg0 + kSegKeys);
+    for (int base0 = seg0 + wave * kWave; base0 < seg1 && !marked; base0 += kSelThreads * kUnroll) {
+      uint32_t keys[kUnroll];
+      const int kend = min(seg1, pool);
+      if (kend > 0) load_keys(s, base0 + lane, kSelThreads, kend, keys);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int base = base0 + u * kSelThreads;
+        if (base >= seg1) break;
+        const int i = base + lane;
+        bool sel = false;
+        if (i < seg1) {
+          if (i >= r0) {
+            sel = true;
+          } else if (i < pool) {
+            sel = keys[u] > vstar || (keys[u] == vstar && i <= istar);
+          }
+        }
+        const uint64_t m = __ballot(sel);
+        const int w0 = (base - seg0) >> 5;
+        if (lane == 0) sh.bits[w0] = (uint32_t)m;
+        if (lane == 32 && w0 + 1 < kSegWords) sh.bits[w0 + 1] = (uint32_t)(m >> 32);
+      }
+    }
+    __syncthreads();
+    const int nwords = ceil_div(seg1 - seg0, 32);
+    const int per = ceil_div(nwords, kSelThreads);
+    int local = 0;
+    for (int j = 0; j < per; ++j) {
+      const int wi = tid * per + j;
+      if (wi < nwords) local += __popc(sh.bits[wi]);
+    }
+    int total;
+    int pos = written + block_scan_excl(local, sh.scan, &total);
+    for (int j = 0; j < per; ++j) {
+      const int wi = tid * per + j;
+      if (wi >= nwords) break;
+      uint32_t m = sh.bits[wi];
+      while (m) {
+        const int bit = __ffs(m) - 1;
+        m &= m - 1;
+        if (pos < stride) out[pos] = seg0 + wi * 32 + bit;
+        ++pos;
+      }
+    }
+    written += total;
+    __syncthreads();
+  }
+  for (int p = written + tid; p < stride; p += kSelThreads) out[p] = -1;
+  if (tid == 0) *count = written;
+}
+
+// Exact selection of one row from its full scores s[0 .. n): the top k_top of
+// the pool by (score, lower index first) plus the recent window.
+__device__ void select_row_exact(SelShared& sh, const float* s, int n, int k_top, int n_recent,
+                                 int disjoint, int32_t* __restrict__ out, int stride,
+                                 int32_t* __restrict__ count) {
+  const int tid = threadIdx.x;
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  uint32_t vstar = 0;
+  int istar = INT_MAX;
+  bool marked = false;
+  if (k < pool) {
+    exact_cut(sh, s, n, pool, k, &vstar, &istar, &marked);
+    if (marked) {
+      __syncthreads();
+      const int c = sh.ccount;
+      for (int j = tid; j < c; j += kSelThreads) {
+        const uint32_t key = sh.ckey[j];
+        const int i = sh.cidx[j];
+        if (key > vstar || (key == vstar && i <= istar)) atomicOr(&sh.bits[i >> 5], 1u << (i & 31));
+      }
+    }
+  } else if (n <= kSegKeys) {
+    for (int wi = tid; wi < ceil_div(n, 32); wi += kSelThreads) {
+      const int first = wi * 32;
+      const int cntb = max(0, min(32, pool - first));
+      sh.bits[wi] = cntb == 32 ? 0xffffffffu : ((1u << cntb) - 1u);
+    }
+    marked = true;
+  }
+  emit_selection(sh, s, n, pool, vstar, istar, marked, n_recent, out, stride, count);
+}
+
 }  // namespace ssa
