@@ -814,12 +814,12 @@ constexpr int kCombineGroups = 8;
 constexpr int kCombineThreads = kHeadDim * kCombineGroups;
 constexpr int kCombineWaves = kCombineThreads / kWave;
 
-// (sequence, query head) of work-group L of the per-row kernels (a 1-D grid of
-// B*Hq). Work-group L runs on XCD L % 8; when the S streams are a multiple of
+// (sequence, query head) of row-block L (0 <= L < B*Hq) of the per-row kernels
+// for S = B*Hkv streams. Work-group L runs on XCD L % 8; when S is a multiple of
 // eight, L is numbered so that the G heads of a stream share one XCD (and its
 // L2), since they all read that stream's partials and candidate lists.
-__device__ __forceinline__ void row_of_block(int L, int Hq, int Hkv, int* b, int* h) {
-  const int G = Hq / Hkv, S = (int)(gridDim.x / G);
+__device__ __forceinline__ void row_of_block(int L, int S, int Hq, int Hkv, int* b, int* h) {
+  const int G = Hq / Hkv;
   int j, jh;
   if (S % kXcds == 0) {
     j = L % kXcds + kXcds * ((L / kXcds) / G);
@@ -833,7 +833,7 @@ __device__ __forceinline__ void row_of_block(int L, int Hq, int Hkv, int* b, int
 }
 
 __device__ void combine_row(
-    const float* __restrict__ part_num, const float* __restrict__ part_den,
+    int blk, const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
     float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
@@ -842,7 +842,7 @@ __device__ void combine_row(
   __shared__ int s_cnt[kCombineWaves][2];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   int b, h;
-  row_of_block(blockIdx.x, Hq, Hkv, &b, &h);
+  row_of_block(blk, S, Hq, Hkv, &b, &h);
   const int d = tid % kHeadDim, grp = tid / kHeadDim;
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
@@ -913,8 +913,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
     float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
-  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
-              vrows);
+  combine_row(blockIdx.x, part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out,
+              nnz, vrows);
 }
 
 // ---------------------------------------------------------------------------
@@ -1100,7 +1100,9 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
   }
 }
 
-// The combine of each (sequence, query head) followed by its selection.
+// The combine of each (sequence, query head) and its selection, on separate
+// work-groups of one grid (the first B*Hq combine, the others select), so
+// that the two run side by side.
 __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
@@ -1112,13 +1114,19 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int32_t* __restrict__ row_flag,
     int32_t* __restrict__ fb) {
   __shared__ SelShared sh;
+  const int rows = S / Hkv * Hq;
+  if ((int)blockIdx.x < rows) {
+    combine_row(blockIdx.x, part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c,
+                out, nnz, vrows);
+    return;
+  }
   int b, h;
-  row_of_block(blockIdx.x, Hq, Hkv, &b, &h);
+  row_of_block(blockIdx.x - rows, S, Hq, Hkv, &b, &h);
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
   const int j = b * Hkv + kvh;
-  // the entry count of this thread's slot of the row's stream, loaded before
-  // the combine so that the two rounds of loads overlap
+  // the entry count of this thread's slot of the row's stream (loaded before
+  // the offsets are needed)
   int pre_cnt = 0;
   {
     const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
@@ -1128,9 +1136,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
       if ((int)threadIdx.x < p1 - p0) pre_cnt = cand_cnt[p0 + threadIdx.x];
     }
   }
-  combine_row(part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out, nnz,
-              vrows);
-  __syncthreads();
   const int row = b * Hq + h;
   const int stride = k_top + n_recent;
   const int n = live_keys(ctx_lens, b, max_ctx);
@@ -1140,7 +1145,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   // a flagged row joins the fallback list (fb[0] rows at fb[1 ..], their
   // done counters at fb[1 + rows + row]); thread 0 wrote the flag
   if (threadIdx.x == 0 && row_flag[row]) {
-    const int rows = (int)gridDim.x;
     fb[1 + rows + row] = 0;
     fb[1 + atomicAdd(fb, 1)] = row;
   }
@@ -1388,7 +1392,7 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   int grid = 0;
   hipError_t e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_full_combine_select, dim3(a.Hq * a.B), dim3(kCombineThreads), 0, stream,
+  hipLaunchKernelGGL(decode_full_combine_select, dim3(2 * a.Hq * a.B), dim3(kCombineThreads), 0, stream,
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
                      a.ctx_lens,

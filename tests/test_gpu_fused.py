@@ -92,6 +92,15 @@ def test_fused_fp32_group1_and_flags():
     check_fused(wl2, flags=0, k_top=100)
 
 
+def test_fused_two_sequences_two_kv_heads():
+    """Four streams (not a multiple of the eight XCDs): the row numbering of the
+    combine and selection work-groups must stay inside the batch."""
+    wl = synth.make_workload("fused_b2", seed=37, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[20000, 9000], kv_capacity=20000, p=0.05)
+    check_fused(wl, want_scores=True)
+    check_fused(wl, k_top=256, n_recent=32)
+
+
 def test_fused_empty_and_tiny_contexts():
     wl = synth.make_workload("fused_empty", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
                              ctx_lens=[0, 1, 1100], kv_capacity=2048, p=0.05)
