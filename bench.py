@@ -342,7 +342,7 @@ def main():
         "sparse_union_rows": int(union_rows),
         "roofline": {"kernel": ("ssa_decode_full (decode_full_kernel + combine)" if args.unfused else
                                 "ssa_decode_full_select (decode_full_kernel with candidate lists + "
-                                "combine_select + rescore/select of flagged rows)"),
+                                "combine_select + fallback for flagged rows)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if args.unfused else measured_traffic(),
