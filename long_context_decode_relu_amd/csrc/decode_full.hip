@@ -920,9 +920,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
 // ---------------------------------------------------------------------------
 // Selection from the candidate lists (the fused full layer + selection).
 // The lists of row (b, h) are those of its stream's slots, in slot order. If
-// they hold every key above the top-k cut the cut is exact among them;
-// otherwise (fewer than k candidates in a long row, or a cut bin too large
-// for LDS) the row is flagged and selected from rescored scores.
+// they hold every key above the top-k cut the cut is exact among them (radix
+// passes over the candidates held in registers); otherwise (fewer than k
+// candidates in a long row, or more entries than the work-group holds) the
+// row is flagged and selected from rescored scores.
 // ---------------------------------------------------------------------------
 
 // Entries a thread of the row's work-group gathers into registers: rows whose
@@ -1037,61 +1038,142 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
   }
 #pragma unroll
   for (int u = 0; u < kGatherPer; ++u) cnd[u] = cnd[u] && idx[u] < pool;
-  // the candidates to LDS in order; when there are more than kCap, only
-  // those from the cut bin of a kBits1-bit histogram up
-  auto place = [&](uint32_t d0) {
+  // the cut over the candidates held in registers: v* is the k-th largest
+  // key, i* the largest index selected among keys equal to v*. The count and
+  // the keys' range come first (one reduction); the radix digits start below
+  // the bits every candidate shares, and once the cut bin holds at most 64
+  // keys one wave ranks them directly.
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  int c;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  {
     int local = 0;
 #pragma unroll
-    for (int u = 0; u < kGatherPer; ++u) local += (cnd[u] && (key[u] >> (32 - kBits1)) >= d0) ? 1 : 0;
-    int total;
-    int pos = block_scan_excl(local, sh.scan, &total);
-    if (total <= kCap) {
-#pragma unroll
-      for (int u = 0; u < kGatherPer; ++u) {
-        if (cnd[u] && (key[u] >> (32 - kBits1)) >= d0) {
-          sh.ckey[pos] = key[u];
-          sh.cidx[pos] = idx[u];
-          ++pos;
-        }
+    for (int u = 0; u < kGatherPer; ++u) {
+      if (cnd[u]) {
+        ++local;
+        kmin = min(kmin, key[u]);
+        kmax = max(kmax, key[u]);
       }
     }
-    __syncthreads();
-    return total;
-  };
-  int c = place(0u);
-  if (c > kCap) {
-    for (int i = tid; i < kBins; i += kSelThreads) sh.hist[i] = 0;
-    __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kGatherPer; ++u) hist_add(sh.hist, key[u] >> (32 - kBits1), cnd[u]);
+    for (int off = 32; off >= 1; off >>= 1) {
+      local += __shfl_xor(local, off, kWave);
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+    }
+    if (lane == 0) {
+      sh.scan[wave] = local;
+      sh.ckey[wave] = kmin;
+      sh.ckey[kSelWaves + wave] = kmax;
+    }
+    if (tid == 0) sh.ccount = 0;
     __syncthreads();
-    int above;
-    const int d1 = threshold_bin(sh.hist, kBins, k, sh, &above);
-    c = place((uint32_t)d1);
+    c = 0;
+    kmin = 0xffffffffu;
+    kmax = 0u;
+    for (int w = 0; w < kSelWaves; ++w) {
+      c += sh.scan[w];
+      kmin = min(kmin, sh.ckey[w]);
+      kmax = max(kmax, sh.ckey[kSelWaves + w]);
+    }
+    __syncthreads();  // sh.ckey is reused below
   }
-  if (c < k || c > kCap) {  // the lists do not hold the whole top k, or it does not fit in LDS
+  if (c < k) {  // the lists do not hold the whole top k
     if (tid == 0) *flag = 1;
     return;
   }
-  uint32_t vstar;
-  int istar;
-  finish_in_lds(sh, c, 0u, 0, k, &vstar, &istar);
-  // the selected candidates below the recent window, in order, then the window
-  const int per2 = ceil_div(c, kSelThreads);
-  const int a0 = tid * per2, a1 = min(c, a0 + per2);
-  int local = 0;
-  for (int i = a0; i < a1; ++i) {
-    const uint32_t kk = sh.ckey[i];
-    const int ii = sh.cidx[i];
-    local += (ii < r0 && (kk > vstar || (kk == vstar && ii <= istar))) ? 1 : 0;
+  // keys whose first L bits equal P
+  auto in_bin = [](uint32_t x, int L, uint32_t P) {
+    return L == 0 || (L >= 32 ? x == P : (x >> (32 - L)) == P);
+  };
+  int L = kmin == kmax ? 32 : __clz(kmin ^ kmax);  // bits every candidate shares
+  uint32_t vstar = L == 0 ? 0u : (L >= 32 ? kmin : kmin >> (32 - L));
+  int need = k, eq = c;
+  int istar = INT_MAX;
+  bool done = false;
+  while (true) {
+    if (eq <= kWave) {
+      // the cut bin's keys to LDS, ranked by wave 0 (key descending, index
+      // ascending); the need-th is the last one selected
+#pragma unroll
+      for (int u = 0; u < kGatherPer; ++u) {
+        if (cnd[u] && in_bin(key[u], L, vstar)) {
+          const int at = atomicAdd(&sh.ccount, 1);
+          sh.ckey[at] = key[u];
+          sh.cidx[at] = idx[u];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const bool has = lane < eq;
+        const uint32_t kl = has ? sh.ckey[lane] : 0u;
+        const int il = has ? sh.cidx[lane] : INT_MAX;
+        int rank = 0;
+        for (int q = 0; q < eq; ++q) {
+          const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, q);
+          const int iq = __builtin_amdgcn_readlane(il, q);
+          rank += (kq > kl || (kq == kl && iq < il)) ? 1 : 0;
+        }
+        if (has && rank == need - 1) {
+          sh.bcast[0] = (int)kl;
+          sh.bcast[1] = il;
+        }
+      }
+      __syncthreads();
+      vstar = (uint32_t)sh.bcast[0];
+      istar = sh.bcast[1];
+      done = true;
+      break;
+    }
+    if (L >= 32) break;  // more than 64 equal keys: the tie pass below
+    const int D = min(11, 32 - L), nb = 1 << D;
+    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kGatherPer; ++u)
+      hist_add(sh.hist, (key[u] >> (32 - L - D)) & (nb - 1), cnd[u] && in_bin(key[u], L, vstar));
+    __syncthreads();
+    int above;
+    const int d = cut_bin(sh.hist, nb, need, sh, &above, &eq);
+    need -= above;
+    vstar = (vstar << D) | (uint32_t)d;
+    L += D;
   }
+  if (!done && need < eq) {
+    // the `need` smallest indices among the keys equal to v*: the largest
+    // complements
+    uint32_t Q = 0;
+    for (int M = 0; M < 32;) {
+      const int D = min(11, 32 - M), nb = 1 << D;
+      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kGatherPer; ++u) {
+        const uint32_t ci = ~(uint32_t)idx[u];
+        hist_add(sh.hist, (ci >> (32 - M - D)) & (nb - 1),
+                 cnd[u] && key[u] == vstar && (M == 0 || (ci >> (32 - M)) == Q));
+      }
+      __syncthreads();
+      int above, in_b;
+      const int d = cut_bin(sh.hist, nb, need, sh, &above, &in_b);
+      need -= above;
+      Q = (Q << D) | (uint32_t)d;
+      M += D;
+    }
+    istar = (int)~Q;
+  }
+  // the selected candidates below the recent window, in list (key) order,
+  // then the window
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u)
+    local += (cnd[u] && idx[u] < r0 && (key[u] > vstar || (key[u] == vstar && idx[u] <= istar))) ? 1 : 0;
   int nsel;
   int pos = block_scan_excl(local, sh.scan, &nsel);
-  for (int i = a0; i < a1; ++i) {
-    const uint32_t kk = sh.ckey[i];
-    const int ii = sh.cidx[i];
-    if (ii < r0 && (kk > vstar || (kk == vstar && ii <= istar))) out[pos++] = ii;
-  }
+#pragma unroll
+  for (int u = 0; u < kGatherPer; ++u)
+    if (cnd[u] && idx[u] < r0 && (key[u] > vstar || (key[u] == vstar && idx[u] <= istar))) out[pos++] = idx[u];
   const int total = nsel + (n - r0);
   for (int p = nsel + tid; p < stride; p += kSelThreads) out[p] = p < total ? r0 + (p - nsel) : -1;
   if (tid == 0) {

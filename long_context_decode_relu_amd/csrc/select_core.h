@@ -137,6 +137,51 @@ __device__ int threshold_bin(const uint32_t* hist, int nb, int need, SelShared& 
 // Resolve the cut among the candidates held in LDS. All of them share the top
 // `known` bits of their key (value `prefix`); `need` of them must be taken.
 // Returns v* and i* through *vstar / *istar.
+// The bin of hist[0 .. nb) holding the need-th largest item (bins counted
+// from the top), with the count in the bins above it and the bin's own count
+// in sh.bcast[0..2]. Each thread sums a run of bins, the runs are scanned
+// within each wave and across the waves' totals, and the one thread whose run
+// holds the item finds the bin: two barriers. Callers pass a barrier before
+// writing the histogram again.
+__device__ int cut_bin(const uint32_t* hist, int nb, int need, SelShared& sh, int* above,
+                       int* in_bin) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int per = ceil_div(nb, kSelThreads);
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = nb - 1 - (tid * per + i);
+    if (b >= 0) local += (int)hist[b];
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) sh.scan[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sh.scan[w];
+  int run = before + incl - local;  // items in the bins above this thread's run
+  if (run < need && run + local >= need) {
+    for (int i = 0; i < per; ++i) {
+      const int b = nb - 1 - (tid * per + i);
+      const int c = (int)hist[b];
+      if (run + c >= need) {
+        sh.bcast[0] = b;
+        sh.bcast[1] = run;
+        sh.bcast[2] = c;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  *above = sh.bcast[1];
+  *in_bin = sh.bcast[2];
+  return sh.bcast[0];
+}
+
 __device__ void finish_in_lds(SelShared& sh, int c, uint32_t prefix, int known, int need,
                               uint32_t* vstar, int* istar) {
   const int tid = threadIdx.x;

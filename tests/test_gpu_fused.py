@@ -101,6 +101,41 @@ def test_fused_two_sequences_two_kv_heads():
     check_fused(wl, k_top=256, n_recent=32)
 
 
+def test_fused_tied_top_scores():
+    """2000 copies of one high-scoring key row in each stream: more than 64 keys
+    share one score, so a cut inside the copies is resolved by index (lower
+    first) in the tie pass. Equality with the two calls; against the oracle,
+    equality outside the rounding band of the cut, and where the cut falls
+    inside the copies the selected ones are exactly the lowest-index copies."""
+    wl = synth.make_workload("fused_ties", seed=38, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[20000, 12000], kv_capacity=20000, p=0.05)
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    rng = np.random.default_rng(38)
+    dups = {}
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        for kvh in range(2):
+            s = ref["scores"][b][kvh * 8:(kvh + 1) * 8].sum(axis=0)
+            src = int(np.argmax(s))
+            dst = rng.choice(np.setdiff1d(np.arange(n - 200), [src]), 2000, replace=False)
+            wl.k[b, kvh, dst] = wl.k[b, kvh, src]
+            dups[(b, kvh)] = np.sort(np.concatenate([dst, [src]]))
+    sel, cnt, _ = check_fused(wl)
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    selection_vs_oracle(wl, ref["scores"], sel, cnt, score_bound(wl, 1.0), range(2))
+    inside = 0
+    for b in range(2):
+        r0 = int(wl.ctx_lens[b]) - 128
+        for h in range(16):
+            d = dups[(b, h // 8)]
+            d = d[d < r0]
+            got = np.intersect1d(sel[b, h, :cnt[b, h]], d)
+            if 0 < len(got) < len(d):
+                inside += 1
+                assert np.array_equal(got, d[:len(got)]), (b, h)
+    assert inside >= 8  # the tie pass ran for most heads
+
+
 def test_fused_empty_and_tiny_contexts():
     wl = synth.make_workload("fused_empty", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
                              ctx_lens=[0, 1, 1100], kv_capacity=2048, p=0.05)
