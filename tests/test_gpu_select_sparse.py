@@ -235,6 +235,25 @@ def test_sparse_union_extremes():
     check_sparse(wl, sels)
 
 
+def test_sparse_largest_stride():
+    """Selections of 4096 keys per head (the largest stride the entry point
+    accepts), heads of a group overlapping partly: unions up to 32K rows, a
+    context that is not a whole number of 8192-key segments."""
+    wl = synth.make_workload("spstride", seed=39, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[70001, 40000], kv_capacity=70001, recipe="planted", p=0.05)
+    rng = np.random.default_rng(39)
+    sels = []
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        shared = rng.choice(n, 2048, replace=False)
+        row = []
+        for h in range(16):
+            own = rng.choice(np.setdiff1d(np.arange(n), shared), 2048, replace=False)
+            row.append(np.sort(np.concatenate([shared, own])).astype(np.int64))
+        sels.append(row)
+    check_sparse(wl, sels, stride=4096)
+
+
 def test_block_step_sampled_full_size():
     """The batch-8 64K-128K workload end to end: full layer -> selection -> sparse layer.
 
