@@ -300,7 +300,8 @@ __device__ __forceinline__ float head_rms_factor(const float* qrow, int lane, fl
 // order: the key index and the group's G scores. A row (sequence, head)
 // then takes the keys of its stream's lists whose own score is positive.
 // Streams of at most kCandAll keys list every key instead, so that the exact
-// cut among the list always holds the top k.
+// cut among the list always holds the top k. List position p holds the key
+// index at cand_idx[p] and the G scores at cand_sc[p*G ..].
 constexpr int kCandAll = 8192;
 
 // First tile and tile count of the part of stream [s0, s1) that wave w of W
@@ -930,18 +931,172 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
 // lists hold more entries than kSelThreads * kGatherPer are flagged.
 constexpr int kGatherPer = 16;
 
+// Count, smallest and largest key of the candidates held in registers (the
+// first nr of P per thread; nr is uniform over the wave) over the work-group,
+// and whether `any` holds on some thread; clears the cut-bin counter. Two
+// barriers.
+template <int P>
+__device__ int cands_count_range(SelShared& sh, const uint32_t (&key)[P], const bool (&cnd)[P],
+                                 int nr, bool any, uint32_t* kmin_out, uint32_t* kmax_out,
+                                 bool* any_out) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  int local = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    if (u < nr && cnd[u]) {
+      ++local;
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    local += __shfl_xor(local, off, kWave);
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  }
+  const bool wany = __ballot(any) != 0;
+  if (lane == 0) {
+    sh.scan[wave] = local;
+    sh.scan[kSelWaves + wave] = wany ? 1 : 0;
+    sh.ckey[wave] = kmin;
+    sh.ckey[kSelWaves + wave] = kmax;
+  }
+  if (tid == 0) sh.ccount = 0;
+  __syncthreads();
+  // the waves' figures: lane l < 16 reads wave l's, then a reduction over 16 lanes
+  const int lw = lane & (kSelWaves - 1);
+  int c = sh.scan[lw], a = sh.scan[kSelWaves + lw];
+  kmin = sh.ckey[lw];
+  kmax = sh.ckey[kSelWaves + lw];
+#pragma unroll
+  for (int off = kSelWaves / 2; off >= 1; off >>= 1) {
+    c += __shfl_xor(c, off, kWave);
+    a |= __shfl_xor(a, off, kWave);
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  }
+  __syncthreads();  // sh.scan and sh.ckey are reused by the caller
+  // the same on every lane: scalar from here on
+  *kmin_out = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmin);
+  *kmax_out = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax);
+  *any_out = __builtin_amdgcn_readfirstlane(a) != 0;
+  return __builtin_amdgcn_readfirstlane(c);
+}
+
+// The cut over c >= k candidates held in registers (the first nr of P per
+// thread, keys in [kmin, kmax]): v* is the k-th largest key, i* the largest
+// index selected among keys equal to v* (ties go to the lower index). The
+// radix digits start below the bits every candidate shares; once the cut bin
+// holds at most 64 keys one wave ranks them directly, and more than 64 equal
+// keys are cut by index.
+template <int P>
+__device__ void cands_cut(SelShared& sh, const uint32_t (&key)[P], const int32_t (&idx)[P],
+                          const bool (&cnd)[P], int nr, int c, uint32_t kmin, uint32_t kmax, int k,
+                          uint32_t* vstar_out, int* istar_out) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  // keys whose first L bits equal P
+  auto in_bin = [](uint32_t x, int L, uint32_t Pf) {
+    return L == 0 || (L >= 32 ? x == Pf : (x >> (32 - L)) == Pf);
+  };
+  int L = kmin == kmax ? 32 : __clz(kmin ^ kmax);  // bits every candidate shares
+  uint32_t vstar = L == 0 ? 0u : (L >= 32 ? kmin : kmin >> (32 - L));
+  int need = k, eq = c;
+  int istar = INT_MAX;
+  bool done = false;
+  while (true) {
+    if (eq <= kWave) {
+      // the cut bin's keys to LDS, ranked by wave 0 (key descending, index
+      // ascending); the need-th is the last one selected
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        if (u < nr && cnd[u] && in_bin(key[u], L, vstar)) {
+          const int at = atomicAdd(&sh.ccount, 1);
+          sh.ckey[at] = key[u];
+          sh.cidx[at] = idx[u];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const bool has = lane < eq;
+        const uint32_t kl = has ? sh.ckey[lane] : 0u;
+        const int il = has ? sh.cidx[lane] : INT_MAX;
+        int rank = 0;
+        for (int q = 0; q < eq; ++q) {
+          const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, q);
+          const int iq = __builtin_amdgcn_readlane(il, q);
+          rank += (kq > kl || (kq == kl && iq < il)) ? 1 : 0;
+        }
+        if (has && rank == need - 1) {
+          sh.bcast[0] = (int)kl;
+          sh.bcast[1] = il;
+        }
+      }
+      __syncthreads();
+      vstar = (uint32_t)__builtin_amdgcn_readfirstlane(sh.bcast[0]);
+      istar = __builtin_amdgcn_readfirstlane(sh.bcast[1]);
+      done = true;
+      break;
+    }
+    if (L >= 32) break;  // more than 64 equal keys: the tie pass below
+    const int D = min(11, 32 - L), nb = 1 << D;
+    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+    __syncthreads();
+    // one atomic per key: the candidates' digits are spread out (equal keys
+    // only serialise on their bin)
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+      if (u < nr && cnd[u] && in_bin(key[u], L, vstar))
+        atomicAdd(&sh.hist[(key[u] >> (32 - L - D)) & (nb - 1)], 1u);
+    __syncthreads();
+    int above, in_b;
+    const int d = __builtin_amdgcn_readfirstlane(cut_bin(sh.hist, nb, need, sh, &above, &in_b));
+    eq = __builtin_amdgcn_readfirstlane(in_b);
+    need -= __builtin_amdgcn_readfirstlane(above);
+    vstar = (vstar << D) | (uint32_t)d;
+    L += D;
+  }
+  if (!done && need < eq) {
+    // the `need` smallest indices among the keys equal to v*: the largest
+    // complements
+    uint32_t Q = 0;
+    for (int M = 0; M < 32;) {
+      const int D = min(11, 32 - M), nb = 1 << D;
+      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const uint32_t ci = ~(uint32_t)idx[u];
+        if (u < nr)
+          hist_add(sh.hist, (ci >> (32 - M - D)) & (nb - 1),
+                   cnd[u] && key[u] == vstar && (M == 0 || (ci >> (32 - M)) == Q));
+      }
+      __syncthreads();
+      int above, in_b;
+      const int d = __builtin_amdgcn_readfirstlane(cut_bin(sh.hist, nb, need, sh, &above, &in_b));
+      need -= __builtin_amdgcn_readfirstlane(above);
+      Q = (Q << D) | (uint32_t)d;
+      M += D;
+    }
+    istar = (int)~Q;
+  }
+  *vstar_out = vstar;
+  *istar_out = istar;
+}
+
 // Selects row (b, h) into out[0..stride) and *count, or sets *flag. The
 // row's candidates are the entries of its stream's slot lists, in slot order
-// (ascending key index), whose score for head jh is positive (every entry
-// when the stream lists all its keys), restricted to the pool.
-__device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ cand_idx,
-                                  const float* __restrict__ cand_sc,
+// (ascending key index), whose score for head jh (cand_sc[p * qs] for
+// position p, with cand_sc pointing at the head's first score) is positive
+// (every entry when the stream lists all its keys), restricted to the pool.
+__device__ __forceinline__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ cand_idx,
+                                  const float* __restrict__ cand_sc, int qs,
                                   const int32_t* __restrict__ cand_cnt,
-                                  const int* __restrict__ tile_pre, int S, int G, int jh, int j,
+                                  const int* __restrict__ tile_pre, int S, int j,
                                   int Wl, int n, int k_top, int n_recent, int disjoint,
                                   int32_t* __restrict__ out, int stride,
-                                  int32_t* __restrict__ count, int32_t* __restrict__ flag,
-                                  int pre_cnt) {
+                                  int32_t* __restrict__ count, int32_t* __restrict__ flag) {
   const int tid = threadIdx.x;
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
@@ -969,16 +1124,12 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
   {
     const int per = ceil_div(np, kSelThreads);
     int local = 0;
-    if (per == 1) {
-      local = tid < np ? pre_cnt : 0;
-    } else {
-      for (int q = tid * per; q < min(np, tid * per + per); ++q) local += cand_cnt[p0 + q];
-    }
+    for (int q = tid * per; q < min(np, tid * per + per); ++q) local += cand_cnt[p0 + q];
     int total;
     int run = block_scan_excl(local, sh.scan, &total);
     for (int q = tid * per; q < min(np, tid * per + per); ++q) {
       offs[q] = (uint32_t)run;
-      run += per == 1 ? pre_cnt : cand_cnt[p0 + q];
+      run += cand_cnt[p0 + q];
       int first, nt;
       slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
       base[q] = (uint32_t)(first * kTileKeys);
@@ -1026,143 +1177,26 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
       sc[u] = 0.f;
       idx[u] = 0;
       if (e0 + u < e1) {
-        sc[u] = cand_sc[at[u] * G + jh];
+        sc[u] = cand_sc[at[u] * qs];
         idx[u] = cand_idx[at[u]];
       }
     }
 #pragma unroll
     for (int u = 0; u < kGatherPer; ++u) {
       key[u] = ordered_key(sc[u]);
-      cnd[u] = e0 + u < e1 && (all || sc[u] > 0.f);
+      cnd[u] = e0 + u < e1 && (all || sc[u] > 0.f) && idx[u] < pool;
     }
   }
-#pragma unroll
-  for (int u = 0; u < kGatherPer; ++u) cnd[u] = cnd[u] && idx[u] < pool;
-  // the cut over the candidates held in registers: v* is the k-th largest
-  // key, i* the largest index selected among keys equal to v*. The count and
-  // the keys' range come first (one reduction); the radix digits start below
-  // the bits every candidate shares, and once the cut bin holds at most 64
-  // keys one wave ranks them directly.
-  const int lane = tid & (kWave - 1), wave = tid >> 6;
-  int c;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  {
-    int local = 0;
-#pragma unroll
-    for (int u = 0; u < kGatherPer; ++u) {
-      if (cnd[u]) {
-        ++local;
-        kmin = min(kmin, key[u]);
-        kmax = max(kmax, key[u]);
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      local += __shfl_xor(local, off, kWave);
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-    }
-    if (lane == 0) {
-      sh.scan[wave] = local;
-      sh.ckey[wave] = kmin;
-      sh.ckey[kSelWaves + wave] = kmax;
-    }
-    if (tid == 0) sh.ccount = 0;
-    __syncthreads();
-    c = 0;
-    kmin = 0xffffffffu;
-    kmax = 0u;
-    for (int w = 0; w < kSelWaves; ++w) {
-      c += sh.scan[w];
-      kmin = min(kmin, sh.ckey[w]);
-      kmax = max(kmax, sh.ckey[kSelWaves + w]);
-    }
-    __syncthreads();  // sh.ckey is reused below
-  }
+  uint32_t kmin, kmax;
+  bool unused;
+  const int c = cands_count_range(sh, key, cnd, per, false, &kmin, &kmax, &unused);
   if (c < k) {  // the lists do not hold the whole top k
     if (tid == 0) *flag = 1;
     return;
   }
-  // keys whose first L bits equal P
-  auto in_bin = [](uint32_t x, int L, uint32_t P) {
-    return L == 0 || (L >= 32 ? x == P : (x >> (32 - L)) == P);
-  };
-  int L = kmin == kmax ? 32 : __clz(kmin ^ kmax);  // bits every candidate shares
-  uint32_t vstar = L == 0 ? 0u : (L >= 32 ? kmin : kmin >> (32 - L));
-  int need = k, eq = c;
-  int istar = INT_MAX;
-  bool done = false;
-  while (true) {
-    if (eq <= kWave) {
-      // the cut bin's keys to LDS, ranked by wave 0 (key descending, index
-      // ascending); the need-th is the last one selected
-#pragma unroll
-      for (int u = 0; u < kGatherPer; ++u) {
-        if (cnd[u] && in_bin(key[u], L, vstar)) {
-          const int at = atomicAdd(&sh.ccount, 1);
-          sh.ckey[at] = key[u];
-          sh.cidx[at] = idx[u];
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        const bool has = lane < eq;
-        const uint32_t kl = has ? sh.ckey[lane] : 0u;
-        const int il = has ? sh.cidx[lane] : INT_MAX;
-        int rank = 0;
-        for (int q = 0; q < eq; ++q) {
-          const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, q);
-          const int iq = __builtin_amdgcn_readlane(il, q);
-          rank += (kq > kl || (kq == kl && iq < il)) ? 1 : 0;
-        }
-        if (has && rank == need - 1) {
-          sh.bcast[0] = (int)kl;
-          sh.bcast[1] = il;
-        }
-      }
-      __syncthreads();
-      vstar = (uint32_t)sh.bcast[0];
-      istar = sh.bcast[1];
-      done = true;
-      break;
-    }
-    if (L >= 32) break;  // more than 64 equal keys: the tie pass below
-    const int D = min(11, 32 - L), nb = 1 << D;
-    for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kGatherPer; ++u)
-      hist_add(sh.hist, (key[u] >> (32 - L - D)) & (nb - 1), cnd[u] && in_bin(key[u], L, vstar));
-    __syncthreads();
-    int above;
-    const int d = cut_bin(sh.hist, nb, need, sh, &above, &eq);
-    need -= above;
-    vstar = (vstar << D) | (uint32_t)d;
-    L += D;
-  }
-  if (!done && need < eq) {
-    // the `need` smallest indices among the keys equal to v*: the largest
-    // complements
-    uint32_t Q = 0;
-    for (int M = 0; M < 32;) {
-      const int D = min(11, 32 - M), nb = 1 << D;
-      for (int i = tid; i < nb; i += kSelThreads) sh.hist[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kGatherPer; ++u) {
-        const uint32_t ci = ~(uint32_t)idx[u];
-        hist_add(sh.hist, (ci >> (32 - M - D)) & (nb - 1),
-                 cnd[u] && key[u] == vstar && (M == 0 || (ci >> (32 - M)) == Q));
-      }
-      __syncthreads();
-      int above, in_b;
-      const int d = cut_bin(sh.hist, nb, need, sh, &above, &in_b);
-      need -= above;
-      Q = (Q << D) | (uint32_t)d;
-      M += D;
-    }
-    istar = (int)~Q;
-  }
+  uint32_t vstar;
+  int istar;
+  cands_cut(sh, key, idx, cnd, per, c, kmin, kmax, k, &vstar, &istar);
   // the selected candidates below the recent window, in list (key) order,
   // then the window
   int local = 0;
@@ -1180,6 +1214,134 @@ __device__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ can
     *count = total;
     *flag = 0;
   }
+}
+
+// Rounds of the fast selection path: wave w takes slots w, w + 16, ... one
+// per round, so rows of up to 16*16 slots fit.
+constexpr int kFastRounds = 16;
+
+// The common case of select_from_cands, one global round trip shorter: a
+// stream of lists of survivors only, of at most kSelWaves*kFastRounds slots,
+// none holding more than 64 entries. In round u wave w loads the count of
+// slot q = w + 16u and, in the same round trip, the slot's first 64 list
+// positions, one per lane (every slot owns at least one tile of positions;
+// those past the count are ignored). The selected entries are then written in
+// (slot, position) order, which is key order: ranks within a slot from a
+// ballot, the slots' places from one scan of their totals. Returns false,
+// having written nothing, when the row does not fit; select_from_cands then
+// gives the same selection from the same lists.
+__device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __restrict__ cand_idx,
+                            const float* __restrict__ cand_sc, int qs,
+                            const int32_t* __restrict__ cand_cnt,
+                            int T, int s0, int s1, int j, int Wl, int n, int k_top, int n_recent,
+                            int disjoint, int32_t* __restrict__ out, int stride,
+                            int32_t* __restrict__ count, int32_t* __restrict__ flag) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int k = min(k_top, pool);
+  const int r0 = max(0, n - n_recent);
+  if (k >= pool || n <= kCandAll || s1 <= s0) return false;
+  const int W = min(Wl, T);
+  const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+  const int np = p1 - p0;
+  if (np > kSelWaves * kFastRounds) return false;
+  const int nr = ceil_div(max(0, np - wave), kSelWaves);  // this wave's rounds (uniform)
+  int32_t idx[kFastRounds];
+  uint32_t key[kFastRounds];
+  bool cnd[kFastRounds];
+  bool over = false;
+  {
+    // lane u (mod 16) finds round u's slot: its first position and its count
+    // (rounds past the last slot re-read the last slot and are masked below)
+    const int qv = min(wave + kSelWaves * (lane & (kFastRounds - 1)), np - 1);
+    int fv, ntv;
+    slot_tiles(s0, s1, p0 + qv - j, W, T, &fv, &ntv);
+    const int cntv = cand_cnt[p0 + qv];
+    float sc[kFastRounds];
+#pragma unroll
+    for (int u = 0; u < kFastRounds; ++u) {
+      idx[u] = 0;
+      sc[u] = 0.f;
+      if (u < nr) {
+        const size_t at = (size_t)__builtin_amdgcn_readlane(fv, u) * kTileKeys + lane;
+        idx[u] = cand_idx[at];
+        sc[u] = cand_sc[at * qs];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFastRounds; ++u) {
+      const int cnt = __builtin_amdgcn_readlane(cntv, u);
+      const bool live = u < nr;
+      over = over || (live && cnt > kWave);
+      key[u] = ordered_key(sc[u]);
+      cnd[u] = live && lane < cnt && sc[u] > 0.f && idx[u] < pool;
+    }
+  }
+  uint32_t kmin, kmax;
+  bool any_over;
+  const int c = cands_count_range(sh, key, cnd, nr, over, &kmin, &kmax, &any_over);
+  if (any_over) return false;
+  if (c < k) {  // the lists do not hold the whole top k
+    if (tid == 0) *flag = 1;
+    return true;
+  }
+  uint32_t vstar;
+  int istar;
+  cands_cut(sh, key, idx, cnd, nr, c, kmin, kmax, k, &vstar, &istar);
+  // rank of each selected entry within its slot, and the slots' totals (in
+  // sh.bits, free here), then their exclusive scan by wave 0
+  int rank[kFastRounds];
+  bool sel[kFastRounds];
+#pragma unroll
+  for (int u = 0; u < kFastRounds; ++u) {
+    sel[u] = false;
+    rank[u] = 0;
+    if (u < nr) {
+      sel[u] = cnd[u] && idx[u] < r0 && (key[u] > vstar || (key[u] == vstar && idx[u] <= istar));
+      const uint64_t m = __ballot(sel[u]);
+      rank[u] = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (lane == 0) sh.bits[wave + kSelWaves * u] = (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kPer = kSelWaves * kFastRounds / kWave;
+    uint32_t v[kPer];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = lane * kPer + i;
+      v[i] = q < np ? sh.bits[q] : 0u;
+      local += v[i];
+    }
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    uint32_t run = incl - local;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int q = lane * kPer + i;
+      if (q < np) sh.bits[q] = run;
+      run += v[i];
+    }
+    if (lane == kWave - 1) sh.bcast[3] = (int)incl;
+  }
+  __syncthreads();
+  const int nsel = sh.bcast[3];
+#pragma unroll
+  for (int u = 0; u < kFastRounds; ++u)
+    if (u < nr && sel[u]) out[sh.bits[wave + kSelWaves * u] + rank[u]] = idx[u];
+  const int total = nsel + (n - r0);
+  for (int p = nsel + tid; p < stride; p += kSelThreads) out[p] = p < total ? r0 + (p - nsel) : -1;
+  if (tid == 0) {
+    *count = total;
+    *flag = 0;
+  }
+  return true;
 }
 
 // The combine of each (sequence, query head) and its selection, on separate
@@ -1207,23 +1369,17 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
   const int j = b * Hkv + kvh;
-  // the entry count of this thread's slot of the row's stream (loaded before
-  // the offsets are needed)
-  int pre_cnt = 0;
-  {
-    const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
-    const int W = min(Wl, T);
-    if (s1 > s0) {
-      const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
-      if ((int)threadIdx.x < p1 - p0) pre_cnt = cand_cnt[p0 + threadIdx.x];
-    }
-  }
   const int row = b * Hq + h;
   const int stride = k_top + n_recent;
   const int n = live_keys(ctx_lens, b, max_ctx);
-  select_from_cands(sh, cand_idx, cand_sc, cand_cnt, tile_pre, S, G, jh, j, Wl, n, k_top,
-                    n_recent, disjoint, sel_idx + (size_t)row * stride, stride, sel_count + row,
-                    row_flag + row, pre_cnt);
+  const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
+  const float* hsc = cand_sc + jh;  // the row's scores: every G-th float
+  const int qs = G;
+  int32_t* const o = sel_idx + (size_t)row * stride;
+  if (!select_fast(sh, cand_idx, hsc, qs, cand_cnt, T, s0, s1, j, Wl, n, k_top, n_recent, disjoint,
+                   o, stride, sel_count + row, row_flag + row))
+    select_from_cands(sh, cand_idx, hsc, qs, cand_cnt, tile_pre, S, j, Wl, n, k_top, n_recent,
+                      disjoint, o, stride, sel_count + row, row_flag + row);
   // a flagged row joins the fallback list (fb[0] rows at fb[1 ..], their
   // done counters at fb[1 + rows + row]); thread 0 wrote the flag
   if (threadIdx.x == 0 && row_flag[row]) {
