@@ -578,8 +578,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     // pass; no store is outstanding at the wait for the next tile.
     Stream st = cur;                   // stream of tile t
     bool has_prev = false;
-    // value row of key 0 of tile t-1; before the first tile, that of tile t0
-    // (a live row: the loads of step 2 read it even with no survivors)
+    // value row of key 0 of tile t-1 (before the first tile there are no
+    // survivors, so it is not read)
     const uint8_t* p_v0 = reinterpret_cast<const uint8_t*>(v) +
                           ((size_t)cur.j * Nmax + (size_t)(t0 - cur.s0) * kTileKeys) * kRowBytes;
     float* p_sc0 = nullptr;            // score of key 0 of tile t-1, first head (null: none)
@@ -640,20 +640,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       if constexpr (CAND) {
         if (p_e >= 0) list_store(p_li, p_ls, p_e, p_key, p_s);
       }
-      // 3. the first kVS survivors of tile t-1 (raw bf16 pairs): always kVS
-      //    loads, the spare ones repeating a row already being loaded
+      // 3. the first kVS survivors of tile t-1 (raw bf16 pairs), one load
+      //    each (the wait below leaves only the 16 tile loads issued after
+      //    them outstanding, however many there are)
       uint64_t m = p_mask;
       VRows vr;
       int nv = 0;
-      const uint8_t* vrow = p_v0;
       unroll_seq(std::make_integer_sequence<int, kVS>{}, [&](auto uu) {
         constexpr int u = decltype(uu)::value;
         if (m) {
-          vrow = p_v0 + (size_t)__builtin_ctzll(m) * kRowBytes;
+          const uint8_t* vrow = p_v0 + (size_t)__builtin_ctzll(m) * kRowBytes;
           m &= m - 1;
           nv = u + 1;
+          vr.r[u] = vload(vrow, (uint32_t)lane * 4);
         }
-        vr.r[u] = vload(vrow, (uint32_t)lane * 4);
       });
       // 4. tile t+1 -> LDS (16 loads)
       if (t + 1 < t1) {
