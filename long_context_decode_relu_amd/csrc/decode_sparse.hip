@@ -45,6 +45,7 @@ constexpr int kRows = kWave;                      // rows per batch: one per lan
 constexpr int kTileBytes = kRows * kHeadDim * 2;  // bf16 rows of a batch
 constexpr int kWaitVm0 = 0x0F70;                  // s_waitcnt vmcnt(0)
 constexpr int kListEnt = 8;  // list entries per head and thread: strides up to 4096
+constexpr int kListEntMin = 3;  // entries every launch loads: strides up to 1536
 static_assert(kSegWords <= kSpThreads, "one bitmap word per thread at most");
 
 template <int G, bool BF16, bool NORMQ, bool NORMK>
@@ -71,31 +72,51 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
 
   const int sg = blockIdx.x, j = sg / nseg, g = sg - j * nseg;
   const int b = j / Hkv, kvh = j - b * Hkv;
-  const int n = max(0, min(ctx_lens[b], nlim));
-  const int c0 = g * kSegKeys, c1 = min(n, c0 + kSegKeys);
-  if (c0 >= c1) return;  // the combine reads only the segments that exist
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave >> 1, wv = wave & 1;
   const size_t hrow0 = (size_t)b * Hq + (size_t)kvh * G;
   const size_t row0 = (size_t)j * Nmax;
 
-  // one round of loads: every list entry of this thread (-1: none) and the
-  // query head of this wave
+  // one round of loads: every list entry of this thread, loaded with the
+  // counts (positions are clamped into the stride, stride >= 1, and those
+  // past a count become -1 afterwards), and the query head of this wave. The
+  // first kListEntMin entries per thread cover strides up to 1536; longer
+  // strides load the rest behind one uniform branch.
+  const int ne = ceil_div(stride, kSpThreads);
   int ent[G][kListEnt];
+  int cnt[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int cnt = max(0, min(sel_count[hrow0 + h], stride));
+    cnt[h] = sel_count[hrow0 + h];
     const int32_t* list = sel_idx + (hrow0 + h) * stride;
 #pragma unroll
-    for (int e = 0; e < kListEnt; ++e) {
-      const int i = tid + e * kSpThreads;
-      ent[h][e] = i < cnt ? list[i] : -1;
+    for (int e = 0; e < kListEntMin; ++e) ent[h][e] = list[min(tid + e * kSpThreads, stride - 1)];
+#pragma unroll
+    for (int e = kListEntMin; e < kListEnt; ++e) ent[h][e] = -1;
+  }
+  if (ne > kListEntMin) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int32_t* list = sel_idx + (hrow0 + h) * stride;
+#pragma unroll
+      for (int e = kListEntMin; e < kListEnt; ++e) ent[h][e] = list[min(tid + e * kSpThreads, stride - 1)];
     }
   }
   const int hq = min(wave, G - 1);
   const float q0 = q[(hrow0 + hq) * kHeadDim + 2 * lane];
   const float q1 = q[(hrow0 + hq) * kHeadDim + 2 * lane + 1];
+  // (the loads above are in flight while the context length is read)
+  const int n = max(0, min(ctx_lens[b], nlim));
+  const int c0 = g * kSegKeys, c1 = min(n, c0 + kSegKeys);
+  if (c0 >= c1) return;  // the combine reads only the segments that exist
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int c = max(0, min(cnt[h], stride));
+#pragma unroll
+    for (int e = 0; e < kListEnt; ++e)
+      if (tid + e * kSpThreads >= c) ent[h][e] = -1;
+  }
 
   for (int i = tid; i < G * kSegWords; i += kSpThreads) (&s_bm[0][0])[i] = 0u;
   // the queries in LDS, normalised and scaled by scale * log2(e) (the softmax
@@ -115,7 +136,7 @@ __global__ __launch_bounds__(kSpThreads) void sparse_kernel(
 #pragma unroll
     for (int e = 0; e < kListEnt; ++e) {
       const int x = ent[h][e];
-      if (x >= c0 && x < c1) atomicOr(&s_bm[h][(x - c0) >> 5], 1u << (x & 31));
+      if (e < ne && x >= c0 && x < c1) atomicOr(&s_bm[h][(x - c0) >> 5], 1u << (x & 31));
     }
   }
   __syncthreads();
