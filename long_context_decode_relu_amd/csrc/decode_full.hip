@@ -200,13 +200,52 @@ template <class A>
 __device__ __forceinline__ void qwait(f32x16& r, A& acc, float& x) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r), "+v"(acc), "+v"(x));
 }
+// The same for two loads in flight (two steps per wait).
+template <class A>
+__device__ __forceinline__ void qwait2(f32x16& r, f32x16& r2, A& acc, float& x) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(r), "+s"(r2), "+v"(acc), "+v"(x));
+}
 
 // acc[h] = sum_d q[h][d] k[d] for the G query heads of one KV head, q[h] the
 // raw query rows (qrow + h*128). Step i = (chunk c of 16 dims, head h), in
-// the order c-major; NORMK also accumulates sum_d k[d]^2.
+// the order c-major; NORMK also accumulates sum_d k[d]^2. With G even the
+// steps go in pairs: one wait covers the two loads of a pair, and the next
+// pair's two loads are in flight during its 32 FMAs (each wait waits for all
+// scalar loads, so one load per step would leave only 16 FMAs to cover it).
 template <int G, bool BF16, bool NORMK>
 __device__ __forceinline__ void score_row(const KeyRow<BF16>& kr, const float* qrow,
                                           typename Acc<G>::T& acc, float& ksq) {
+  if constexpr (G % 2 == 0) {
+    f32x16 qa, qa2, qb, qb2;
+    qload<0>(qa, qrow, acc, ksq);
+    qload<kHeadDim * 4>(qa2, qrow, acc, ksq);
+    unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      float e[16];
+      kr.chunk16(c, e);
+      if constexpr (NORMK) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) ksq = fmaf(e[t], e[t], ksq);
+      }
+      unroll_seq(std::make_integer_sequence<int, G / 2>{}, [&](auto hh) {
+        constexpr int h = 2 * decltype(hh)::value;
+        constexpr int i = c * G + h;
+        qwait2(qa, qa2, acc, ksq);
+        if constexpr (i + 2 < 8 * G) {
+          constexpr int c2 = (i + 2) / G, h2 = (i + 2) % G;
+          qload<h2 * kHeadDim * 4 + c2 * 64>(qb, qrow, acc, ksq);
+          qload<(h2 + 1) * kHeadDim * 4 + c2 * 64>(qb2, qrow, acc, ksq);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[h] = fmaf(qa[t], e[t], acc[h]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) acc[h + 1] = fmaf(qa2[t], e[t], acc[h + 1]);
+        qa = qb;
+        qa2 = qb2;
+      });
+    });
+    return;
+  }
   f32x16 qa, qb;
   qload<0>(qa, qrow, acc, ksq);
   unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto cc) {
