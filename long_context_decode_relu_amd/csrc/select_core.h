@@ -489,7 +489,7 @@ __device__ void emit_selection(SelShared& sh, const float* s, int n, int pool, u
 
 // Exact selection of one row from its full scores s[0 .. n): the top k_top of
 // the pool by (score, lower index first) plus the recent window.
-__device__ void select_row_exact(SelShared& sh, const float* s, int n, int k_top, int n_recent,
+__device__ __forceinline__ void select_row_exact(SelShared& sh, const float* s, int n, int k_top, int n_recent,
                                  int disjoint, int32_t* __restrict__ out, int stride,
                                  int32_t* __restrict__ count) {
   const int tid = threadIdx.x;
