@@ -668,11 +668,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       const int base = (t - st.s0) * kTileKeys;
       const bool valid = base + lane < st.n;
 
-      // 1. tile t has landed; LDS -> registers, after which it may be refilled
+      // 1. tile t has landed; LDS -> registers (waited for before step 4,
+      //    which refills the tile; steps 2 and 3 touch no LDS)
       wait_vm<0>();
       KeyRow<true> kr;
       tile_read_bf16(my_tile, lane, kr);
-      wait_lgkm0();
 
       // 2. score stores (or candidate-list entry) of tile t-1
       if (has_prev && p_sc0) store_scores();
@@ -694,7 +694,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
           vr.r[u] = vload(vrow, (uint32_t)lane * 4);
         }
       });
-      // 4. tile t+1 -> LDS (16 loads)
+      // 4. tile t+1 -> LDS (16 loads), once the reads of tile t are done
+      wait_lgkm0();
       if (t + 1 < t1) {
         const Stream nx = t + 1 < st.s1 ? st : stream_after(st, t + 1);
         issue_tile(&nx, t + 1, nullptr);
