@@ -60,6 +60,15 @@ def test_fused_single_sequence_lists():
     check_fused(synth.single_decode(n=32768), want_scores=True)
 
 
+def test_fused_batched_full_size():
+    """The batch-8 64K-128K workload in the launch configuration the benchmark
+    times (up to 164 slots per stream, so the selection takes its one-round-trip
+    path over up to 11 rounds per wave): the fused outputs equal the two calls
+    bit for bit; the two-call path is compared with the oracle at this size in
+    test_gpu_decode_full.py and test_gpu_select_sparse.py."""
+    check_fused(synth.batched_decode())
+
+
 def test_fused_ragged_batch_mixed_paths():
     """Short rows (every key listed), a ragged tail, and long rows, in one batch."""
     wl = synth.make_workload("fused_ragged", seed=31, batch=5, n_q_heads=16, n_kv_heads=2,
