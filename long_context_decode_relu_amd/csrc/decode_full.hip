@@ -1130,13 +1130,15 @@ __device__ void cands_cut(SelShared& sh, const uint32_t (&key)[P], const int32_t
 // (ascending key index), whose score for head jh (cand_sc[p * qs] for
 // position p, with cand_sc pointing at the head's first score) is positive
 // (every entry when the stream lists all its keys), restricted to the pool.
-__device__ __forceinline__ void select_from_cands(SelShared& sh, const int32_t* __restrict__ cand_idx,
-                                  const float* __restrict__ cand_sc, int qs,
-                                  const int32_t* __restrict__ cand_cnt,
-                                  const int* __restrict__ tile_pre, int S, int j,
-                                  int Wl, int n, int k_top, int n_recent, int disjoint,
-                                  int32_t* __restrict__ out, int stride,
-                                  int32_t* __restrict__ count, int32_t* __restrict__ flag) {
+__device__ __forceinline__ void select_from_cands(SelShared& sh,
+                                                  const int32_t* __restrict__ cand_idx,
+                                                  const float* __restrict__ cand_sc, int qs,
+                                                  const int32_t* __restrict__ cand_cnt,
+                                                  const int* __restrict__ tile_pre, int S, int j,
+                                                  int Wl, int n, int k_top, int n_recent,
+                                                  int disjoint, int32_t* __restrict__ out,
+                                                  int stride, int32_t* __restrict__ count,
+                                                  int32_t* __restrict__ flag) {
   const int tid = threadIdx.x;
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
@@ -1267,15 +1269,17 @@ constexpr int kFastRounds = 16;
 // positions, one per lane (every slot owns at least one tile of positions;
 // those past the count are ignored). The selected entries are then written in
 // (slot, position) order, which is key order: ranks within a slot from a
-// ballot, the slots' places from one scan of their totals. Returns false,
-// having written nothing, when the row does not fit; select_from_cands then
-// gives the same selection from the same lists.
+// ballot, the slots' places from one scan of their totals. Scores are read as
+// in select_from_cands (cand_sc[p * qs]). Returns false, having written
+// nothing, when the row does not fit; select_from_cands then gives the same
+// selection from the same lists.
 __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __restrict__ cand_idx,
-                            const float* __restrict__ cand_sc, int qs,
-                            const int32_t* __restrict__ cand_cnt,
-                            int T, int s0, int s1, int j, int Wl, int n, int k_top, int n_recent,
-                            int disjoint, int32_t* __restrict__ out, int stride,
-                            int32_t* __restrict__ count, int32_t* __restrict__ flag) {
+                                            const float* __restrict__ cand_sc, int qs,
+                                            const int32_t* __restrict__ cand_cnt, int T, int s0,
+                                            int s1, int j, int Wl, int n, int k_top, int n_recent,
+                                            int disjoint, int32_t* __restrict__ out, int stride,
+                                            int32_t* __restrict__ count,
+                                            int32_t* __restrict__ flag) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pool = disjoint ? max(0, n - n_recent) : n;
@@ -1293,7 +1297,8 @@ __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __rest
   bool over = false;
   {
     // lane u (mod 16) finds round u's slot: its first position and its count
-    // (rounds past the last slot re-read the last slot and are masked below)
+    // (lanes of rounds past this wave's last slot take the last slot; those
+    // rounds load nothing)
     const int qv = min(wave + kSelWaves * (lane & (kFastRounds - 1)), np - 1);
     int fv, ntv;
     slot_tiles(s0, s1, p0 + qv - j, W, T, &fv, &ntv);
