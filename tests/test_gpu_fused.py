@@ -69,6 +69,19 @@ def test_fused_batched_full_size():
     check_fused(synth.batched_decode())
 
 
+@pytest.mark.parametrize("n", [65536, 65792])
+def test_fused_slot_count_boundary(n):
+    """One sequence, 8 query heads over 2 KV heads (4 per group, so the
+    interleaved scores have stride 4). The launch gives each wave about four
+    64-key tiles: a 65536-key stream has 256 slots per list, the most the
+    selection's one-round-trip path takes, and a 65792-key stream a few more,
+    so that path declines and the general one selects. Both equal the two
+    calls bit for bit."""
+    wl = synth.make_workload(f"fused_slots_{n}", seed=39, batch=1, n_q_heads=8, n_kv_heads=2,
+                             ctx_lens=[n], kv_capacity=n, p=0.05)
+    check_fused(wl)
+
+
 def test_fused_ragged_batch_mixed_paths():
     """Short rows (every key listed), a ragged tail, and long rows, in one batch."""
     wl = synth.make_workload("fused_ragged", seed=31, batch=5, n_q_heads=16, n_kv_heads=2,
