@@ -180,3 +180,23 @@ def test_fused_block_step_vs_oracle():
     _, same = selection_vs_oracle(sub, ref["scores"], sel[seqs], cnt[seqs], bounds,
                                   range(len(seqs)))
     assert same >= 0.75 * len(seqs) * 16
+
+
+def test_fused_and_sparse_deterministic():
+    """Five runs of the fused call and a sparse layer on the batch-8 workload
+    give the same bits: every sum runs in a fixed order, and the selection's
+    LDS atomics only count or place keys that are then ranked."""
+    wl = synth.batched_decode()
+    cache = ssa.cache_from_workload(wl, DEV)
+    q = torch.from_numpy(wl.q).to(DEV)
+    qs = torch.from_numpy(wl.q_sparse[0]).to(DEV)
+    runs = []
+    for _ in range(5):
+        out, sel, cnt, _, nnz, vrows = ssa.ssa_decode_full_select(q, cache, want_stats=True)
+        osp = ssa.ssa_decode_sparse(qs, cache, sel, cnt)
+        torch.cuda.synchronize()
+        runs.append([out.cpu().numpy().view(np.uint32), sel.cpu().numpy(), cnt.cpu().numpy(),
+                     nnz.cpu().numpy(), vrows.cpu().numpy(), osp.cpu().numpy().view(np.uint32)])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert np.array_equal(a, b), "not deterministic"
