@@ -116,14 +116,30 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}))
 
 
+def host_info() -> dict:
+    """Host cores this process may run on, the CPU model and the BLAS thread count."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    return {"cores": cores, "cpu_model": model, "blas_threads": int(blas)}
+
+
 def cpu_baseline(wl, reps: int = 3) -> dict:
     """The CPU oracle, as it stands, on the whole batch: full layer, selection, one sparse layer."""
     from oracle import ssa_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    info = host_info()
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
@@ -137,7 +153,10 @@ def cpu_baseline(wl, reps: int = 3) -> dict:
     sparse_rows = sum(len(functools.reduce(np.union1d, sel[b][kvh * g:(kvh + 1) * g]))
                       for b in range(wl.batch) for kvh in range(wl.n_kv_heads))
     kv_total = kv["k"] + kv["v"] + 2 * wl.head_dim * 2 * sparse_rows
-    return {"value": round(kv_total / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+    # the oracle is NumPy: its matrix products use the BLAS threads, the rest one core
+    return {"value": round(kv_total / dt / 1e9, 3), "unit": "GB/s", "cores": info["blas_threads"],
+            "host_cores": info["cores"], "cpu_model": info["cpu_model"],
+            "blas_threads": info["blas_threads"],
             "kind": "oracle", "query_tok_per_s": round(wl.batch / dt, 3), "seconds_per_step": round(dt, 3),
             "sample": f"the whole batch ({wl.batch} sequences, {int(wl.ctx_lens.sum())} keys per KV head): "
                       f"full layer, selection and one sparse layer in float64 NumPy; median of {reps} passes"}

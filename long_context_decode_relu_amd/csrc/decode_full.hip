@@ -545,13 +545,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     // Copy tile t of stream st into the wave's LDS tile; rows past the live
     // ones are replaced by the last live row (read, never used). Every call
     // issues exactly 16 loads (the waits below count them); with st ==
-    // nullptr they re-read the first 1 KB of `again` (a tile already read,
-    // so cached), which only keeps that count fixed on a wave's last tile.
+    // nullptr they re-read the first row of `again` (the first key of a tile
+    // already read, always live and cached), which only keeps that count
+    // fixed on a wave's last tile.
     auto issue_tile = [&](const Stream* st, int t, const uint8_t* again) {
       if (!st) {
         unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
           constexpr int i = decltype(ii)::value;
-          dma16<i * 1024>(again, (uint32_t)lane * 16, tile_m0);
+          dma16<i * 1024>(again, (uint32_t)(lane & 15) * 16, tile_m0);
         });
         return;
       }

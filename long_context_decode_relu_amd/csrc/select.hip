@@ -129,7 +129,7 @@ static_assert(kColThreads == kSmpThreads, "the sample runs on the collect work-g
 
 __global__ __launch_bounds__(kColThreads) void select_collect(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, int segs, int cap, int32_t* __restrict__ cseg,
+    int max_ctx, int k_top, int n_recent, int disjoint, int segs, int cap, int32_t* __restrict__ cseg,
     uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
   __shared__ uint32_t lkey[kColLocal];
   __shared__ int32_t lidx[kColLocal];
@@ -139,7 +139,8 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int row = blockIdx.y, seg = blockIdx.x;
   const int b = row / Hq;
-  const int n = min(ctx_lens[b], Nmax);
+  // the live keys, clamped as every kernel of the library clamps them
+  const int n = max(0, min(ctx_lens[b], max_ctx));
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
   const int lo = seg * kColSeg;
@@ -217,14 +218,15 @@ __global__ __launch_bounds__(kColThreads) void select_collect(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void select_finish(
     const float* __restrict__ scores, const int32_t* __restrict__ ctx_lens, int Hq, int Nmax,
-    int k_top, int n_recent, int disjoint, int segs, int cap, const int32_t* __restrict__ cseg,
+    int max_ctx, int k_top, int n_recent, int disjoint, int segs, int cap, const int32_t* __restrict__ cseg,
     const uint32_t* __restrict__ ckey, const int32_t* __restrict__ cidx,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int stride) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int b = row / Hq;
-  const int n = min(ctx_lens[b], Nmax);
+  // the live keys, clamped as every kernel of the library clamps them
+  const int n = max(0, min(ctx_lens[b], max_ctx));
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int k = min(k_top, pool);
   const float* s = scores + (size_t)row * Nmax;
@@ -337,10 +339,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   int32_t* cidx = reinterpret_cast<int32_t*>(ws + l.idx);
   const int disjoint = (a.flags & SSA_SELECT_DISJOINT) ? 1 : 0;
   hipLaunchKernelGGL(select_collect, dim3(l.segs, rows), dim3(kColThreads), 0, stream, a.scores,
-                     a.ctx_lens, a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt,
-                     ckey, cidx);
+                     a.ctx_lens, a.Hq, a.Nmax, a.max_ctx, a.k_top, a.n_recent, disjoint, l.segs,
+                     l.cap, cnt, ckey, cidx);
   hipLaunchKernelGGL(select_finish, dim3(rows), dim3(kSelThreads), 0, stream, a.scores, a.ctx_lens,
-                     a.Hq, a.Nmax, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt, ckey, cidx,
+                     a.Hq, a.Nmax, a.max_ctx, a.k_top, a.n_recent, disjoint, l.segs, l.cap, cnt,
+                     ckey, cidx,
                      a.sel_idx, a.sel_count, a.k_top + a.n_recent);
   return hipGetLastError();
 }

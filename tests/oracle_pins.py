@@ -103,6 +103,61 @@ def pin_golden_prefill():
     _close(out[0, 0], _arr(pf["out"]), what="prefill golden")
 
 
+def pin_golden_sparse_norm_k():
+    """Sparse layer with SSA_NORM_K: each selected key row is RMS-normalised before
+    the score (hand-worked, keys stored at RMS 2, 1/2 and 3); without the flag the
+    rows enter as stored."""
+    g = _golden()
+    sp = g["sparse_layer_norm_k"]
+    K = np.array(sp["keys_unnormalised"], dtype=np.float32)[None, None]
+    V = np.array([[_num(a) for a in r] for r in g["values"]], dtype=np.float32)[None, None]
+    q = np.array(sp["q"], dtype=np.float32)[None, None]
+    out = O.decode_sparse(q, K, V, [[sp["sel"]]], scale=sp["scale"], eps=g["eps"],
+                          flags=O.SSA_NORM_Q | O.SSA_NORM_K)
+    _close(out[0, 0], _arr(sp["out_norm_k"]), what="sparse norm_k golden")
+    out = O.decode_sparse(q, K, V, [[sp["sel"]]], scale=sp["scale"], eps=g["eps"],
+                          flags=O.SSA_NORM_Q)
+    _close(out[0, 0], _arr(sp["out_stored"]), what="sparse stored-keys golden")
+
+
+def pin_golden_prefill_raw_q():
+    """Prefill with flags = 0 takes the query as given (hand-worked)."""
+    g = _golden()
+    pf = g["prefill_raw_q"]
+    K = synth.to_bf16_bits(np.array(g["keys"], dtype=np.float32))[None, None]
+    V = synth.to_bf16_bits(np.array([[_num(a) for a in r] for r in g["values"]],
+                                    dtype=np.float32))[None, None]
+    q = synth.to_bf16_bits(np.array(pf["q"], dtype=np.float32))[None, None]
+    out = O.prefill_full(q, K, V, [pf["q_pos0"]], scale=pf["scale"], c=pf["c"], eps=g["eps"],
+                         flags=pf["flags"])
+    _close(out[0, 0], _arr(pf["out"]), what="prefill raw q golden")
+
+
+def pin_golden_select_all_flags():
+    """select_all passes its flags to every row (hand-worked union and disjoint sets)."""
+    g = _golden()["select"]
+    a = g["all_rows"]
+    s = np.array(g["scores"], dtype=np.float64)
+    rows = [np.stack([s, s])]
+    for flags, want in ((0, a["sel_union"]), (O.SSA_SELECT_DISJOINT, a["sel_disjoint"])):
+        got = O.select_all(rows, [len(s)], a["k_top"], a["n_recent"], flags=flags)
+        assert [list(x) for x in got[0]] == [want, want], (flags, got)
+
+
+def pin_sparse_norm_k_scale_invariance():
+    """SSA_NORM_K in the sparse layer: keys scaled per row by any positive factor give
+    the output of the stored (RMS 1) keys without the flag (eps = 0)."""
+    wl = _iid(seed=43)
+    rng = np.random.default_rng(3)
+    scaled = (wl.k * rng.uniform(0.2, 5.0, size=wl.k.shape[:3] + (1,))).astype(np.float32)
+    sel = [[np.arange(h, 300, 7) for h in range(wl.n_q_heads)] for _ in range(wl.batch)]
+    o1 = O.decode_sparse(wl.q, wl.k, wl.v, sel, eps=0.0)
+    o2 = O.decode_sparse(wl.q, scaled, wl.v, sel, eps=0.0, flags=O.SSA_NORM_Q | O.SSA_NORM_K)
+    _close(o1, o2, rtol=1e-6, atol=1e-6, what="sparse norm k")
+    o3 = O.decode_sparse(wl.q, scaled, wl.v, sel, eps=0.0, flags=O.SSA_NORM_Q)
+    assert not np.allclose(o1, o3, rtol=1e-3)
+
+
 # --------------------------------------------------------------------------
 # exact zero rule, closed forms, invariants
 # --------------------------------------------------------------------------

@@ -19,6 +19,8 @@ _orig_softmax = O.softmax_attend
 _orig_prefill = O.prefill_full
 _orig_decode = O.decode_full
 _orig_widen = O.widen
+_orig_sparse = O.decode_sparse
+_orig_select_all = O.select_all
 
 
 def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
@@ -103,6 +105,28 @@ def _prefill_variant(kind):
     return prefill
 
 
+def _sparse_variant(kind):
+    def sparse(q, k, v, selections, scale=None, eps=1e-6, flags=O.SSA_NORM_Q):
+        if kind == "norm_k_ignored":
+            flags = flags & ~O.SSA_NORM_K
+        if kind == "norm_k_l2" and flags & O.SSA_NORM_K:
+            kk = O.widen(k)
+            k = kk / np.linalg.norm(kk, axis=-1, keepdims=True)
+            flags = flags & ~O.SSA_NORM_K
+        return _orig_sparse(q, k, v, selections, scale=scale, eps=eps, flags=flags)
+    return sparse
+
+
+def _prefill_always_normalises(q, k, v, q_pos0, scale=1.0, c=1.0, eps=1e-6, flags=O.SSA_NORM_Q,
+                               rows=None):
+    return _orig_prefill(q, k, v, q_pos0, scale=scale, c=c, eps=eps, flags=flags | O.SSA_NORM_Q,
+                         rows=rows)
+
+
+def _select_all_flags_dropped(scores, ctx_lens, k_top=1024, n_recent=128, flags=0):
+    return _orig_select_all(scores, ctx_lens, k_top, n_recent, 0)
+
+
 def _decode_vrows_all_heads(*a, **kw):
     r = _orig_decode(*a, **kw)
     r["vrows"] = r["nnz"].reshape(r["vrows"].shape[0], r["vrows"].shape[1], -1).min(axis=2)
@@ -137,6 +161,10 @@ MUTANTS = {
     "prefill_excludes_self": ("prefill_full", _prefill_variant("excludes_self")),
     "prefill_ignores_pos0": ("prefill_full", _prefill_variant("ignores_pos0")),
     "vrows_all_heads": ("decode_full", _decode_vrows_all_heads),
+    "sparse_norm_k_ignored": ("decode_sparse", _sparse_variant("norm_k_ignored")),
+    "sparse_norm_k_l2": ("decode_sparse", _sparse_variant("norm_k_l2")),
+    "prefill_raw_q_normalised": ("prefill_full", _prefill_always_normalises),
+    "select_all_flags_dropped": ("select_all", _select_all_flags_dropped),
     "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
                                           if np.asarray(x).dtype != np.uint16
                                           else np.asarray(x).astype(np.float64) / 256.0)),
