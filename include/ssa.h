@@ -173,6 +173,30 @@ ssa_status ssa_decode_sparse(const ssa_shape* shape, const float* q, const void*
                              const int32_t* sel_count, int32_t sel_stride, float scale, float eps,
                              uint32_t flags, float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch the library keeps for ssa_decode_sparse_static. */
+#define SSA_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* ssa_decode_sparse without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc). The softmax partials go to
+ * a fixed device array of SSA_STATIC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends; the call itself allocates and
+ * frees nothing (the caller still passes every input and `out`). Results are
+ * those of ssa_decode_sparse on the same arguments. Calls whose partials need
+ * more than SSA_STATIC_SCRATCH_BYTES, that is
+ *   ssa_workspace_bytes(SSA_OP_DECODE_SPARSE, shape, sel_stride)
+ *     = 4 * 130 * batch * n_q_heads * ceil(max_ctx_len / 8192) bytes (rounded up)
+ * > SSA_STATIC_SCRATCH_BYTES, return SSA_ERR_WORKSPACE and launch nothing.
+ * Every call on one GPU shares that GPU's array: two calls that may overlap on
+ * one GPU (on different streams, or from different threads) race and must be
+ * ordered by the caller. The first call on each device looks the array's
+ * address up once (hipGetSymbolAddress). */
+ssa_status ssa_decode_sparse_static(const ssa_shape* shape, const float* q, const void* k,
+                                    const void* v, const int32_t* ctx_lens,
+                                    const int32_t* sel_idx, const int32_t* sel_count,
+                                    int32_t sel_stride, float scale, float eps, uint32_t flags,
+                                    float* out, void* stream);
+
 /* Causal ReLU^2 prefill of a chunk of Tq prompt queries ("KV bridge, KV reuse,
  * and prefill"; weights as in ssa_decode_full).
  *

@@ -77,6 +77,43 @@ ssa_status from_hip(hipError_t e) {
 
 }  // namespace
 
+namespace {
+
+// Checks shared by ssa_decode_sparse and ssa_decode_sparse_static; fills a.
+ssa_status sparse_args(const ssa_shape* s, const float* q, const void* k, const void* v,
+                       const int32_t* ctx_lens, const int32_t* sel_idx, const int32_t* sel_count,
+                       int32_t sel_stride, float scale, float eps, uint32_t flags, float* out,
+                       DecodeSparseArgs* a) {
+  ssa_status st = check_shape(s, true);
+  if (st != SSA_OK) return st;
+  if (sel_stride < 1 || sel_stride > kMaxSel) return SSA_ERR_SHAPE;
+  if (s->batch == 0) return SSA_OK;
+  if (!q || !k || !v || !ctx_lens || !sel_idx || !sel_count || !out) return SSA_ERR_NULL;
+  if (!finite(scale) || !finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
+  if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  a->B = s->batch;
+  a->Hq = s->n_q_heads;
+  a->Hkv = s->n_kv_heads;
+  a->Nmax = s->kv_capacity;
+  a->max_ctx = s->max_ctx_len;
+  a->kv_bf16 = s->kv_dtype == SSA_BF16;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->ctx_lens = ctx_lens;
+  a->sel_idx = sel_idx;
+  a->sel_count = sel_count;
+  a->sel_stride = sel_stride;
+  a->scale = scale;
+  a->eps = eps;
+  a->flags = flags;
+  a->out = out;
+  a->ws = nullptr;
+  return SSA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t ssa_abi_version(void) { return SSA_ABI_VERSION; }
@@ -231,36 +268,30 @@ ssa_status ssa_decode_sparse(const ssa_shape* s, const float* q, const void* k, 
                              const int32_t* ctx_lens, const int32_t* sel_idx,
                              const int32_t* sel_count, int32_t sel_stride, float scale, float eps,
                              uint32_t flags, float* out, void* ws, size_t ws_bytes, void* stream) {
-  ssa_status st = check_shape(s, true);
-  if (st != SSA_OK) return st;
-  if (sel_stride < 1 || sel_stride > kMaxSel) return SSA_ERR_SHAPE;
-  if (s->batch == 0) return SSA_OK;
-  if (!q || !k || !v || !ctx_lens || !sel_idx || !sel_count || !out) return SSA_ERR_NULL;
-  if (!finite(scale) || !finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
-  if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  DecodeSparseArgs a;
+  const ssa_status st = sparse_args(s, q, k, v, ctx_lens, sel_idx, sel_count, sel_stride, scale,
+                                    eps, flags, out, &a);
+  if (st != SSA_OK || s->batch == 0) return st;
   const size_t need = decode_sparse_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads,
                                              s->max_ctx_len, sel_stride);
   if (need && (!ws || ws_bytes < need)) return SSA_ERR_WORKSPACE;
-  DecodeSparseArgs a;
-  a.B = s->batch;
-  a.Hq = s->n_q_heads;
-  a.Hkv = s->n_kv_heads;
-  a.Nmax = s->kv_capacity;
-  a.max_ctx = s->max_ctx_len;
-  a.kv_bf16 = s->kv_dtype == SSA_BF16;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.ctx_lens = ctx_lens;
-  a.sel_idx = sel_idx;
-  a.sel_count = sel_count;
-  a.sel_stride = sel_stride;
-  a.scale = scale;
-  a.eps = eps;
-  a.flags = flags;
-  a.out = out;
   a.ws = ws;
   return from_hip(launch_decode_sparse(a, static_cast<hipStream_t>(stream)));
+}
+
+ssa_status ssa_decode_sparse_static(const ssa_shape* s, const float* q, const void* k,
+                                    const void* v, const int32_t* ctx_lens,
+                                    const int32_t* sel_idx, const int32_t* sel_count,
+                                    int32_t sel_stride, float scale, float eps, uint32_t flags,
+                                    float* out, void* stream) {
+  DecodeSparseArgs a;
+  const ssa_status st = sparse_args(s, q, k, v, ctx_lens, sel_idx, sel_count, sel_stride, scale,
+                                    eps, flags, out, &a);
+  if (st != SSA_OK || s->batch == 0) return st;
+  if (decode_sparse_ws_bytes(s->batch, s->n_q_heads, s->n_kv_heads, s->max_ctx_len, sel_stride) >
+      SSA_STATIC_SCRATCH_BYTES)
+    return SSA_ERR_WORKSPACE;
+  return from_hip(launch_decode_sparse_static(a, static_cast<hipStream_t>(stream)));
 }
 
 ssa_status ssa_prefill_full(const ssa_shape* s, const void* q, int32_t n_query,

@@ -27,6 +27,8 @@
 // Every sum runs in a fixed order, so the result does not depend on timing.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -466,6 +468,48 @@ void launch_g(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_
 }
 
 }  // namespace
+
+// Device-resident scratch of ssa_decode_sparse_static, for callers that cannot
+// allocate: the per-(stream, segment, head) softmax partials live here instead
+// of in a caller-provided workspace. Every GPU that runs the library holds its
+// own copy until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): its device address
+// is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[SSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device id, null until looked up
+}  // namespace
+
+// The device address of `scratch` on the current device.
+static hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_sparse_static(const DecodeSparseArgs& a, hipStream_t stream) {
+  if (decode_sparse_ws_bytes(a.B, a.Hq, a.Hkv, a.max_ctx, a.sel_stride) > SSA_STATIC_SCRATCH_BYTES)
+    return hipErrorInvalidValue;
+  void* ptr = nullptr;
+  const hipError_t e = static_scratch(&ptr);
+  if (e != hipSuccess) return e;
+  DecodeSparseArgs b = a;
+  b.ws = ptr;
+  return launch_decode_sparse(b, stream);
+}
 
 size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int) {
   return sp_layout(B, Hq, Hkv, max_ctx).total;

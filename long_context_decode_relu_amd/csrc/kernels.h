@@ -71,6 +71,9 @@ struct DecodeSparseArgs {
 };
 size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int stride);
 hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream);
+// The same with the library's own device scratch in place of a.ws (a.ws is
+// ignored); hipErrorInvalidValue when the partials would not fit in it.
+hipError_t launch_decode_sparse_static(const DecodeSparseArgs& a, hipStream_t stream);
 
 struct PrefillArgs {
   int B, Hq, Hkv, Nmax, max_ctx, Tq;

@@ -41,7 +41,11 @@ SSA_OP_PREFILL_FULL = 3
 SSA_OP_DECODE_FULL_SELECT = 4
 
 EXPORTED = ("ssa_abi_version", "ssa_status_string", "ssa_workspace_bytes", "ssa_decode_full",
-            "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse", "ssa_prefill_full")
+            "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse",
+            "ssa_decode_sparse_static", "ssa_prefill_full")
+
+# bytes of device scratch the library holds for ssa_decode_sparse_static
+SSA_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class SsaError(RuntimeError):
@@ -85,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.ssa_select_topk_recent.argtypes = [SP, P, P, I32, I32, U32, P, P, P, SZ, P]
         L.ssa_decode_sparse.restype = I32
         L.ssa_decode_sparse.argtypes = [SP, P, P, P, P, P, P, I32, F, F, U32, P, P, SZ, P]
+        L.ssa_decode_sparse_static.restype = I32
+        L.ssa_decode_sparse_static.argtypes = [SP, P, P, P, P, P, P, I32, F, F, U32, P, P]
         L.ssa_prefill_full.restype = I32
         L.ssa_prefill_full.argtypes = [SP, P, I32, P, P, P, P, F, F, F, U32, P, P, SZ, P]
         _lib = L
@@ -258,6 +264,36 @@ def ssa_decode_sparse(q: torch.Tensor, cache: Cache, sel_idx: torch.Tensor, sel_
                                  _ptr(cache.ctx_lens), _ptr(sel_idx), _ptr(sel_count), stride, scale,
                                  eps, flags, _ptr(out), _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssa_decode_sparse")
+    return out
+
+
+def ssa_decode_sparse_static(q: torch.Tensor, cache: Cache, sel_idx: torch.Tensor,
+                             sel_count: torch.Tensor, out: torch.Tensor, *,
+                             scale: float | None = None, eps: float = 1e-6,
+                             flags: int = SSA_NORM_Q) -> torch.Tensor:
+    """ssa_decode_sparse with the library's own device scratch: allocates nothing.
+
+    The caller passes ``out`` [B, Hq, D] float32 (contiguous, on the GPU). Calls on
+    one GPU share the scratch, so calls that may overlap must be ordered.
+    """
+    _need(q.is_cuda and q.dtype == torch.float32 and q.dim() == 3 and q.is_contiguous(),
+          "q must be contiguous float32 [B, Hq, D]")
+    B, Hq, D = q.shape
+    _need(sel_idx.dtype == torch.int32 and sel_idx.dim() == 3 and sel_idx.shape[:2] == (B, Hq)
+          and sel_idx.is_contiguous(), "sel_idx must be int32 [B, Hq, stride]")
+    _need(sel_count.dtype == torch.int32 and sel_count.shape == (B, Hq) and sel_count.is_contiguous(),
+          "sel_count must be int32 [B, Hq]")
+    _need(out.is_cuda and out.dtype == torch.float32 and out.shape == (B, Hq, D) and out.is_contiguous(),
+          "out must be contiguous float32 [B, Hq, D]")
+    cache.check()
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    shp = cache.shape(Hq)
+    st = lib().ssa_decode_sparse_static(ctypes.byref(shp), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                        _ptr(cache.ctx_lens), _ptr(sel_idx), _ptr(sel_count),
+                                        sel_idx.shape[2], scale, eps, flags, _ptr(out),
+                                        _stream(q.device))
+    _check(st, "ssa_decode_sparse_static")
     return out
 
 
