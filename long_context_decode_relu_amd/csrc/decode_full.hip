@@ -52,7 +52,8 @@ constexpr int kMaxStreams = 1024;       // (sequence, KV head) streams per call
 constexpr int kTileKeys = kWave;        // one key per lane
 constexpr int kTileBytesBf16 = kTileKeys * kHeadDim * 2;
 constexpr int kMaxG = 8;                // query heads per KV head, at most
-constexpr int kVS = 16;                 // survivor V rows of a tile loaded ahead
+constexpr int kVS = 16;                 // pending value rows loaded ahead per tile
+constexpr int kDenseTile = 24;          // a tile with more candidates is scored in place
 constexpr int kXcds = 8;                // accelerator dies of an MI355X
 constexpr int kMaxWaves = 8192;         // upper bound on the waves of a launch
 
@@ -114,13 +115,25 @@ struct TileOffsets {
 // lds + LOFF + 16 L. Issued from asm so that the compiler does not wait for it
 // before unrelated LDS accesses; the kernel waits for it explicitly. M0 is
 // formed inside the asm (so that the compiler keeps no per-load copy of it)
-// and needs one wait state before the load that reads it.
+// and needs one wait state before the load that reads it. The loads carry the
+// non-temporal hint: every key is read once per call, and streaming past the
+// caches this way measured 13% faster than plain loads on this path.
 template <int LOFF>
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
                : "v"(voff), "s"(base), "s"(lds), "n"(LOFF)
                : "memory", "scc");
+}
+
+// The same with a per-lane source address: lane L's 16 bytes at src land at
+// LDS byte lds + LOFF + 16 L.
+template <int LOFF>
+__device__ __forceinline__ void dma16_lane(const uint8_t* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:0"
+               :
+               : "v"(src + 0), "s"(lds + LOFF)
+               : "memory");
 }
 
 // Wait until at most N vector-memory operations are outstanding.
@@ -135,6 +148,13 @@ struct VRows {
   uint32_t r[kVS];
 };
 static_assert(kVS == 16, "vwait16 passes sixteen value registers");
+// A pointer the wave holds in scalar registers (the same on every lane).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ uint32_t vload(const uint8_t* row, uint32_t off) {
   uint32_t x;
   asm volatile("global_load_dword %0, %1, %2" : "=v"(x) : "v"(off), "s"(row) : "memory");
@@ -272,6 +292,181 @@ __device__ __forceinline__ void score_row(const KeyRow<BF16>& kr, const float* q
 }
 
 // ---------------------------------------------------------------------------
+// The filter pass. Most keys of a long context get a negative score from
+// every head of the group; they need neither their value row nor an exact
+// score. The filter scores every key cheaply against one query for the whole
+// group and sends on only the keys that may score above zero for some head
+// ("candidates"); those are scored exactly (score_row, the float32 FMA chain
+// above), and only they can be survivors.
+//
+// Per group (sequence, KV head), with sigma a power of two putting the
+// group's largest query magnitude in [1, 2) and q'_h = sigma q_h:
+//   q_bar = the mean of the q'_h, and b = q_bar rounded to bf16 pairs;
+//   A = b . k by a chain of v_dot2c_f32_bf16 (two bf16 products added into a
+//       float32 per instruction) over the key's stored bf16 pairs.
+// For every head h, with acc_h the exact score's FMA chain (unscaled query),
+//   sigma acc_h = q'_h . k + e1,   q'_h . k = q_bar . k + (q'_h - q_bar) . k,
+//   q_bar . k = A + (q_bar - b) . k + e2,
+// |e1| <= 128 u |q'_h|_2 |k|_2 (u = 2^-24; float32 FMA chain of 128 terms),
+// |e2| <= 256 u |b|_2 |k|_2: measured on gfx950, one v_dot2c_f32_bf16 is
+// within 2^-22 of the largest magnitude among its three terms (it aligns them
+// to the largest exponent and truncates), so the 64-step chain is within
+// 64 * 2^-22 sum_d |b_d k_d|. With Cauchy-Schwarz on every term,
+//   |sigma acc_h - A| <= R |k|_2,
+//   R = max_h (|q_bar - b|_2 + |q'_h - q_bar|_2 + 2^-12 (|q_bar|_2 + |q'_h|_2)) * 1.001
+// (2^-12 = 4096 u: ten times the two chain bounds). A key with
+// sign(scale) A < -R |k|_2 therefore has, for every head, an exact dot
+// product of the sign that makes its score at most zero: all its weights are
+// exactly zero. |k|_2^2 is itself a dot2 chain (k . k, within 256 u of the
+// exact sum and below it), enlarged by 1.001. When the group's queries are
+// too far apart for the bound to drop any key (R >= |b|_2) the group is
+// scored exactly, key by key.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+constexpr float kKsqSafe = 1.001f;   // |k|_2^2 <= ksq * kKsqSafe
+constexpr float kKsqTiny = 1e-30f;   // and never less than this (keys of subnormal size)
+
+// acc[h] = b_h . k for G filter queries (head h's 64 bf16 pairs at qh + 64 h,
+// taken by scalar loads, 16 pairs per load, as score_row does) and ksq = k . k,
+// all by dot2 chains in pair order. The kernel uses one query per group.
+template <int G>
+__device__ __forceinline__ void filter_row(const KeyRow<true>& kr, const float* qh,
+                                           typename Acc<G>::T& acc, float& ksq) {
+  auto kd = [&](auto cc, auto tt) -> uint32_t {
+    constexpr int c = decltype(cc)::value, t = decltype(tt)::value;
+    return kr.c[4 * c + t / 4][t % 4];
+  };
+  constexpr int kHeadBytes = kHeadDim * 2;  // 64 pairs of one head
+  if constexpr (G % 2 == 0) {
+    f32x16 qa, qa2, qb, qb2;
+    qload<0>(qa, qh, acc, ksq);
+    qload<kHeadBytes>(qa2, qh, acc, ksq);
+    unroll_seq(std::make_integer_sequence<int, 4>{}, [&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto tt) {
+        const uint32_t x = kd(cc, tt);
+        ksq = dot2(x, x, ksq);
+      });
+      unroll_seq(std::make_integer_sequence<int, G / 2>{}, [&](auto hh) {
+        constexpr int h = 2 * decltype(hh)::value;
+        constexpr int i = c * G + h;
+        qwait2(qa, qa2, acc, ksq);
+        if constexpr (i + 2 < 4 * G) {
+          constexpr int c2 = (i + 2) / G, h2 = (i + 2) % G;
+          qload<h2 * kHeadBytes + c2 * 64>(qb, qh, acc, ksq);
+          qload<(h2 + 1) * kHeadBytes + c2 * 64>(qb2, qh, acc, ksq);
+        }
+        unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto tt) {
+          constexpr int t = decltype(tt)::value;
+          acc[h] = dot2(__float_as_uint(qa[t]), kd(cc, tt), acc[h]);
+        });
+        unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto tt) {
+          constexpr int t = decltype(tt)::value;
+          acc[h + 1] = dot2(__float_as_uint(qa2[t]), kd(cc, tt), acc[h + 1]);
+        });
+        qa = qb;
+        qa2 = qb2;
+      });
+    });
+    return;
+  }
+  f32x16 qa, qb;
+  qload<0>(qa, qh, acc, ksq);
+  unroll_seq(std::make_integer_sequence<int, 4>{}, [&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto tt) {
+      const uint32_t x = kd(cc, tt);
+      ksq = dot2(x, x, ksq);
+    });
+    unroll_seq(std::make_integer_sequence<int, G>{}, [&](auto hh) {
+      constexpr int h = decltype(hh)::value;
+      constexpr int i = c * G + h;
+      qwait(qa, acc, ksq);
+      if constexpr (i + 1 < 4 * G) {
+        constexpr int c2 = (i + 1) / G, h2 = (i + 1) % G;
+        qload<h2 * kHeadBytes + c2 * 64>(qb, qh, acc, ksq);
+      }
+      unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto tt) {
+        constexpr int t = decltype(tt)::value;
+        acc[h] = dot2(__float_as_uint(qa[t]), kd(cc, tt), acc[h]);
+      });
+      qa = qb;
+    });
+  });
+}
+
+// The filter's inputs per group (sequence, KV head), one wave per group: the
+// group's scaled mean query rounded to bf16 pairs (qhi, 64 words) and
+// sign(scale) / R (invc). A group whose queries are not all finite, are all
+// zero, or whose bound cannot drop any key, and any zero scale, get NaN: the
+// group is then scored exactly, key by key.
+template <int G>
+__global__ __launch_bounds__(256) void decode_full_qprep(const float* __restrict__ q, int groups,
+                                                         float scale, uint32_t* __restrict__ qhi,
+                                                         float* __restrict__ invc) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (grp >= groups) return;
+  const float* qg = q + (size_t)grp * G * kHeadDim + 2 * lane;
+  float x[G][2];
+  float amax = 0.f;
+  float bad = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    x[h][0] = qg[h * kHeadDim];
+    x[h][1] = qg[h * kHeadDim + 1];
+    amax = fmaxf(amax, fmaxf(fabsf(x[h][0]), fabsf(x[h][1])));
+    bad = (isfinite(x[h][0]) && isfinite(x[h][1])) ? bad : 1.f;
+  }
+  amax = wave_max_dpp(amax);
+  bad = wave_max_dpp(bad);
+  int e = 0;
+  frexpf(amax, &e);  // amax = f 2^e, f in [0.5, 1)
+  const float sigma = amax > 0.f ? ldexpf(1.f, min(126, max(-126, 1 - e))) : 1.f;
+  // q_bar: the mean of the scaled heads (scaling by sigma and dividing by G,
+  // a power of two, are exact; the bound holds for the vector computed here)
+  float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m0 += sigma * x[h][0];
+    m1 += sigma * x[h][1];
+  }
+  m0 *= 1.f / G;
+  m1 *= 1.f / G;
+  const bool ok = bad == 0.f;
+  const uint32_t b0 = ok ? f32_to_bf16_bits(m0) : 0u, b1 = ok ? f32_to_bf16_bits(m1) : 0u;
+  qhi[(size_t)grp * 64 + lane] = b0 | (b1 << 16);
+  const float bb0 = __uint_as_float(b0 << 16), bb1 = __uint_as_float(b1 << 16);
+  const float r0 = m0 - bb0, r1 = m1 - bb1;  // exact
+  // norms in float32: their rounding (a few hundred u at most) is far inside
+  // the factor 1.001 below
+  const float nr = sqrtf(wave_sum_dpp(r0 * r0 + r1 * r1));        // |q_bar - b|
+  const float nm = sqrtf(wave_sum_dpp(m0 * m0 + m1 * m1));        // |q_bar|
+  const float nb = sqrtf(wave_sum_dpp(bb0 * bb0 + bb1 * bb1));    // |b|
+  float R = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float y0 = sigma * x[h][0], y1 = sigma * x[h][1];
+    const float d0 = y0 - m0, d1 = y1 - m1;
+    const float nd = sqrtf(wave_sum_dpp(d0 * d0 + d1 * d1));      // |q'_h - q_bar|
+    const float ny = sqrtf(wave_sum_dpp(y0 * y0 + y1 * y1));      // |q'_h|
+    R = fmaxf(R, nr + nd + 0x1p-12f * (nm + ny));
+  }
+  R *= 1.001f;
+  if (lane == 0) {
+    const bool usable = ok && amax > 0.f && scale != 0.f && R > 0.f && R < nb;
+    invc[grp] = usable ? (scale > 0.f ? 1.f : -1.f) / R : __builtin_nanf("");
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Work split: stream-K over 64-key tiles. Stream j = b*Hkv + kvh holds
 // ceil(n_b / 64) tiles; the streams laid end to end form T tiles, and wave w
 // of W takes tiles [w*T/W, (w+1)*T/W) (W is capped at T, so every working
@@ -360,10 +555,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
     int* __restrict__ tile_pre_out, int32_t* __restrict__ cand_idx, float* __restrict__ cand_sc,
     int32_t* __restrict__ cand_cnt, int32_t* __restrict__ fb_count,
+    const float* __restrict__ qhi, const float* __restrict__ invc,
     int B, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps, int normq,
     int cus_per_xcd) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
+  // per wave: weights and keys of the pending value rows (a ring of 64), and
+  // the queue of candidate keys waiting for their exact scores
   __shared__ __attribute__((aligned(16))) float s_w[BF16 ? kWaves * kTileKeys * kMaxG : 4];
+  __shared__ int s_pk[BF16 ? kWaves * kTileKeys : 1];
+  __shared__ int s_qk[BF16 ? kWaves * kTileKeys : 1];
   __shared__ int s_tpre[kMaxStreams + 1];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -405,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   struct Stream {
     int j, b, kvh, n, s0, s1;
   };
-  auto stream_info = [&](int j) {
+  auto stream_info = [&](int j) __attribute__((always_inline)) {
     Stream st;
     st.j = j;
     st.b = j / Hkv;
@@ -416,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     return st;
   };
   // the stream holding tile t: the largest j with s_tpre[j] <= t (never an empty stream)
-  auto stream_of = [&](int t) {
+  auto stream_of = [&](int t) __attribute__((always_inline)) {
     int lo = 0, hi = S;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -425,13 +625,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     return stream_info(lo);
   };
   // the stream holding tile t >= st.s1
-  auto stream_after = [&](const Stream& st, int t) {
+  auto stream_after = [&](const Stream& st, int t) __attribute__((always_inline)) {
     int j = st.j + 1;
     while (__builtin_amdgcn_readfirstlane(s_tpre[j + 1]) <= t) ++j;
     return stream_info(j);
   };
   constexpr size_t kRowBytes = kHeadDim * (BF16 ? 2 : 4);
-  auto qrow_of = [&](const Stream& st) {
+  auto qrow_of = [&](const Stream& st) __attribute__((always_inline)) {
     return q + ((size_t)st.b * Hq + (size_t)st.kvh * G) * kHeadDim;
   };
 
@@ -455,14 +655,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   int ccount = 0;              // entries listed in the current slot
   int32_t* lidx = nullptr;     // the current slot's list: key indices
   float* lsc = nullptr;        //   and the group's scores, G per entry
-  auto reset = [&]() {
+  auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < G; ++h) { num[h][0] = num[h][1] = 0.f; den[h] = 0.f; nnz[h] = 0; }
     vrows = 0;
     ccount = 0;
   };
   // the candidate list of slot (st, this wave)
-  auto open_slot = [&](const Stream& st) {
+  auto open_slot = [&](const Stream& st) __attribute__((always_inline)) {
     if constexpr (CAND) {
       int first, nt;
       slot_tiles(st.s0, st.s1, w, W, T, &first, &nt);
@@ -472,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   };
   // Entry of this lane's key among the keys of mask m listed next in the
   // current slot (-1 unless `mine`); advances the slot's count.
-  auto list_entry = [&](uint64_t m, bool mine) {
+  auto list_entry = [&](uint64_t m, bool mine) __attribute__((always_inline)) {
     int e = -1;
     if constexpr (CAND) {
       if (m) {
@@ -498,13 +698,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       d[0] = sv[0];
     }
   };
-  auto flush = [&](const Stream& st) {
+  auto flush = [&](const Stream& st) __attribute__((always_inline)) {
     const int64_t slot = (int64_t)st.j + w;
     float* pn = part_num + slot * (G * kHeadDim);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       *reinterpret_cast<f32x2*>(pn + h * kHeadDim + 2 * lane) = f32x2{num[h][0], num[h][1]};
-      const float d = wave_sum(den[h]);
+      // (the bf16 path adds every weight to den in every lane, in key order)
+      const float d = BF16 ? den[h] : wave_sum(den[h]);
       const int z = wave_sum_i(nnz[h]);
       if (lane == 0) {
         part_den[slot * G + h] = d;
@@ -538,7 +739,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
 
   if constexpr (BF16) {
     uint8_t* const my_tile = s_tile + wave * kTileBytesBf16;
-    float* const my_w = s_w + wave * kTileKeys * kMaxG;
+    float* const my_w = s_w + wave * kTileKeys * kMaxG;  // pending weights (ring slot r at my_w + 8 r)
+    int* const my_pk = s_pk + wave * kTileKeys;           // pending keys (ring)
+    int* const my_qk = s_qk + wave * kTileKeys;           // candidate queue
     const uint32_t tile_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)my_tile);
     const TileOffsets toff(lane);
 
@@ -548,7 +751,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     // nullptr they re-read the first row of `again` (the first key of a tile
     // already read, always live and cached), which only keeps that count
     // fixed on a wave's last tile.
-    auto issue_tile = [&](const Stream* st, int t, const uint8_t* again) {
+    auto issue_tile = [&](const Stream* st, int t, const uint8_t* again) __attribute__((always_inline)) {
       if (!st) {
         unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
           constexpr int i = decltype(ii)::value;
@@ -574,14 +777,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
         });
       }
     };
-    auto tile_src = [&](const Stream& st, int t) {
+    auto tile_src = [&](const Stream& st, int t) __attribute__((always_inline)) {
       return reinterpret_cast<const uint8_t*>(k) +
              ((size_t)st.j * Nmax + (size_t)(t - st.s0) * kTileKeys) * kRowBytes;
     };
+    auto vbase_of = [&](const Stream& st) __attribute__((always_inline)) {
+      return reinterpret_cast<const uint8_t*>(v) + (size_t)st.j * Nmax * kRowBytes;
+    };
 
-    // num[h] += w_h(survivor of rank r) * (this lane's two dims of value row vraw)
-    auto v_add = [&](int r, uint32_t vraw) {
-      const float* ws = my_w + r * kMaxG;
+    // ---- Pending value rows: the survivors of the current stream whose
+    // value rows are still to be added, in key order (a FIFO ring of 64 in
+    // LDS: key and weights). Every survivor passes through it, whichever way
+    // its exact scores were found, so num and den are summed in key order and
+    // the result does not depend on how the keys were scored.
+    int ph = 0, pn = 0;                  // ring head and count (uniform)
+    const uint8_t* vbase = nullptr;      // value rows of the current stream
+
+    // num[h] += w_h * (this lane's two dims of the value row vraw), den[h] += w_h,
+    // for the pending entry in ring slot `slot`
+    auto v_add = [&](int slot, uint32_t vraw) __attribute__((always_inline)) {
+      const float* ws = my_w + slot * kMaxG;
       float wv[G];
       if constexpr (G >= 4) {
 #pragma unroll
@@ -599,153 +814,45 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       for (int h = 0; h < G; ++h) {
         num[h][0] = fmaf(wv[h], vx, num[h][0]);
         num[h][1] = fmaf(wv[h], vy, num[h][1]);
+        den[h] += wv[h];
       }
     };
-
-    Stream cur = stream_of(t0);
-    float fac[G];
-    issue_tile(&cur, t0, nullptr);
-    load_fac(cur, fac);
-    open_slot(cur);
-
-    // Pipelined over the wave's tiles. Iteration t waits for tile t, reads
-    // it from LDS, issues the score stores (or candidate-list entries) of
-    // tile t-1, the V rows of its survivors and the copy of tile t+1, in that
-    // order, scores tile t, then waits only for the stores and the V rows
-    // (the vector-memory counter completes in issue order, so the tile copy
-    // behind them stays in flight) and adds the rows. The tile copy therefore
-    // has a whole iteration to arrive, the stores and V rows a whole scoring
-    // pass; no store is outstanding at the wait for the next tile.
-    Stream st = cur;                   // stream of tile t
-    bool has_prev = false;
-    // value row of key 0 of tile t-1 (before the first tile there are no
-    // survivors, so it is not read)
-    const uint8_t* p_v0 = reinterpret_cast<const uint8_t*>(v) +
-                          ((size_t)cur.j * Nmax + (size_t)(t0 - cur.s0) * kTileKeys) * kRowBytes;
-    float* p_sc0 = nullptr;            // score of key 0 of tile t-1, first head (null: none)
-    bool p_valid = false;
-    uint64_t p_mask = 0;               // tile t-1's survivors
-    float p_s[G];
-    // tile t-1's candidate-list entry of this lane (-1: none) and its list;
-    // stored with the score stores, so that the wait for the stores is the
-    // one after the scoring pass rather than the one for the next tile
-    int p_e = -1, p_key = 0;
-    int32_t* p_li = nullptr;
-    float* p_ls = nullptr;
-
-    // V rows of tile t-1's survivors still in `m`, the first of rank r0,
-    // four at a time (the compiler waits for these loads itself)
-    auto v_rows_sync = [&](uint64_t m, int r0) {
-      int r = r0;
-      while (m) {
-        uint32_t vv[4];
-        int cnt = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1;
-            vv[u] = reinterpret_cast<const uint32_t*>(p_v0 + (size_t)j * kRowBytes)[lane];
-            cnt = u + 1;
+    // add the `cnt` oldest pending rows now, up to NB loads in flight at once
+    auto drain = [&]<int NB>(std::integral_constant<int, NB>, int cnt) __attribute__((always_inline)) {
+      while (cnt > 0) {
+        const int nb = min(cnt, NB);
+        const int key_l = my_pk[(ph + (lane & (NB - 1))) & (kTileKeys - 1)];
+        uint32_t vv[NB];
+        unroll_seq(std::make_integer_sequence<int, NB>{}, [&](auto uu) {
+          constexpr int u = decltype(uu)::value;
+          vv[u] = 0u;
+          if (u < nb) {
+            const int key = __builtin_amdgcn_readlane(key_l, u);
+            vv[u] = reinterpret_cast<const uint32_t*>(vbase + (size_t)key * kRowBytes)[lane];
           }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (u < cnt) v_add(r + u, vv[u]);
-        r += cnt;
+        });
+        unroll_seq(std::make_integer_sequence<int, NB>{}, [&](auto uu) {
+          constexpr int u = decltype(uu)::value;
+          if (u < nb) v_add((ph + u) & (kTileKeys - 1), vv[u]);
+        });
+        ph = (ph + nb) & (kTileKeys - 1);
+        pn -= nb;
+        cnt -= nb;
       }
     };
-    auto store_scores = [&]() {
-      float* sp = p_sc0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (p_valid) sp[lane] = p_s[h];  // lane 0 is always valid: G stores issue
-        sp += Nmax;
-      }
-    };
-
-    for (int t = t0; t < t1; ++t) {
-      if (t >= st.s1) st = stream_after(st, t);
-      const int base = (t - st.s0) * kTileKeys;
-      const bool valid = base + lane < st.n;
-
-      // 1. tile t has landed; LDS -> registers (waited for before step 4,
-      //    which refills the tile; steps 2 and 3 touch no LDS)
-      wait_vm<0>();
-      KeyRow<true> kr;
-      tile_read_bf16(my_tile, lane, kr);
-
-      // 2. score stores (or candidate-list entry) of tile t-1
-      if (has_prev && p_sc0) store_scores();
-      if constexpr (CAND) {
-        if (p_e >= 0) list_store(p_li, p_ls, p_e, p_key, p_s);
-      }
-      // 3. the first kVS survivors of tile t-1 (raw bf16 pairs), one load
-      //    each (the wait below leaves only the 16 tile loads issued after
-      //    them outstanding, however many there are)
-      uint64_t m = p_mask;
-      VRows vr;
-      int nv = 0;
-      unroll_seq(std::make_integer_sequence<int, kVS>{}, [&](auto uu) {
-        constexpr int u = decltype(uu)::value;
-        if (m) {
-          const uint8_t* vrow = p_v0 + (size_t)__builtin_ctzll(m) * kRowBytes;
-          m &= m - 1;
-          nv = u + 1;
-          vr.r[u] = vload(vrow, (uint32_t)lane * 4);
-        }
-      });
-      // 4. tile t+1 -> LDS (16 loads), once the reads of tile t are done
-      wait_lgkm0();
-      if (t + 1 < t1) {
-        const Stream nx = t + 1 < st.s1 ? st : stream_after(st, t + 1);
-        issue_tile(&nx, t + 1, nullptr);
-      } else {
-        issue_tile(nullptr, 0, tile_src(st, t));
-      }
-
-      // 5. scores of tile t
-#pragma unroll
-      for (int h = 0; h < Acc<G>::kN; ++h) acc[h] = 0.f;
-      ksq = 0.f;
-      score_row<G, true, NORMK>(kr, qrow_of(st), acc, ksq);
-      float kf = 1.f;
-      if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
-
-      // 6. the stores and the V rows are done; the tile copy (the last 16
-      //    loads) may still be in flight
-      vwait16(vr);
-
-      // 7. tile t-1's V rows, into the accumulators of its stream
-#pragma unroll
-      for (int u = 0; u < kVS; ++u)
-        if (u < nv) v_add(u, vr.r[u]);
-      if (m) v_rows_sync(m, kVS);
-
-      // 8. entering the next non-empty stream: tile t-1 closed the last one
-      if (st.j != cur.j) {
-        flush(cur);
-        reset();
-        cur = st;
-        load_fac(cur, fac);
-        open_slot(cur);
-      }
-
-      // 9. weights of tile t; survivors list theirs by rank
-      float wt[G];
-      const bool any = weigh(fac, kf, valid, p_s, wt);
-      p_mask = __ballot(any);
-      if constexpr (CAND) {
-        const bool all = st.n <= kCandAll;
-        p_e = list_entry(all ? __ballot(valid) : p_mask, all ? valid : any);
-        p_key = base + lane;
-        p_li = lidx;
-        p_ls = lsc;
-      }
-      if (any) {
-        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(p_mask >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)p_mask, 0));
-        float* ws = my_w + r * kMaxG;
+    auto drain16 = [&](int cnt) __attribute__((always_inline)) { drain(std::integral_constant<int, 16>{}, cnt); };
+    // the keys of the lanes with `surv` (weights wt) join the ring
+    auto append = [&](bool surv, int key, const float (&wt)[G]) {
+      const uint64_t m = __ballot(surv);
+      const int c = __popcll(m);
+      if (c == 0) return;
+      if (pn + c > kTileKeys) drain16(pn + c - kTileKeys);
+      if (surv) {
+        const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const int slot = (ph + pn + r) & (kTileKeys - 1);
+        my_pk[slot] = key;
+        float* ws = my_w + slot * kMaxG;
         if constexpr (G >= 4) {
 #pragma unroll
           for (int p = 0; p < G / 4; ++p)
@@ -755,20 +862,270 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
           *reinterpret_cast<f32x2*>(ws) = f32x2{wt[0], G == 2 ? wt[G - 1] : 0.f};
         }
       }
-      vrows += __popcll(p_mask);
-      p_v0 = reinterpret_cast<const uint8_t*>(v) + ((size_t)st.j * Nmax + base) * kRowBytes;
-      p_sc0 = scores ? scores + ((size_t)st.b * Hq + (size_t)st.kvh * G) * Nmax + base : nullptr;
-      p_valid = valid;
-      has_prev = true;
-    }
-    // the last tile's score stores (or list entry) and V rows
-    if (has_prev) {
+      pn += c;
+    };
+
+    // ---- Exact scores: the float32 FMA chain of score_row on key row kr_
+    // against stream s's queries (dot products a, key sum of squares ks),
+    // then the scores sv, weights wt and positive-score mask posm (bit h) with
+    // the query factors fac. True when some head keeps the key.
+    auto exact_acc = [&](const KeyRow<true>& kr_, const Stream& s, typename Acc<G>::T& a, float& ks) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < Acc<G>::kN; ++h) a[h] = 0.f;
+      ks = 0.f;
+      score_row<G, true, NORMK>(kr_, qrow_of(s), a, ks);
+    };
+    auto weights = [&](const typename Acc<G>::T& a, float ks, const float (&fac)[G], bool valid,
+                       float (&sv)[G], float (&wt)[G], uint32_t& posm) {
+      float kf = 1.f;
+      if constexpr (NORMK) kf = 1.f / sqrtf(ks * (1.0f / kHeadDim) + eps);
+      bool any = false;
+      posm = 0u;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sv[h] = NORMK ? a[h] * fac[h] * kf : a[h] * fac[h];
+        const bool pos = valid && sv[h] > 0.f;
+        wt[h] = pos ? sv[h] * sv[h] : 0.f;
+        posm |= pos ? (1u << h) : 0u;
+        any |= pos;
+      }
+      return any;
+    };
+    auto count_pos = [&](uint32_t posm) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) nnz[h] += (posm >> h) & 1u;
+    };
+
+    Stream cur = stream_of(t0);
+    float fac[G];
+    issue_tile(&cur, t0, nullptr);
+    load_fac(cur, fac);
+    open_slot(cur);
+    vbase = vbase_of(cur);
+
+    // ---- The candidate queue: keys of the current stream that the filter
+    // could not rule out, in key order; their rows are read again (they were
+    // streamed moments ago) and scored exactly 64 at a time, one per lane.
+    int qn = 0;
+    bool kq_in_lds = false;  // the queued keys' rows wait in the LDS tile (a wave's last tile)
+    // copy the rows of the queued keys (lane L: key L of the queue) into the
+    // wave's LDS tile, piece j of row L at byte 1024 j + 16 L: 16 loads, like a tile copy
+    auto copy_queue_rows = [&]() __attribute__((always_inline)) {
+      const int key = my_qk[lane < qn ? lane : 0];
+      const uint8_t* row =
+          reinterpret_cast<const uint8_t*>(k) + ((size_t)cur.j * Nmax + key) * kRowBytes;
+      unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        dma16_lane<j * 1024>(row + 16 * j, tile_m0);
+      });
+    };
+    // the queued keys' exact scores; their rows come from the LDS tile (a
+    // wave's last tile) or are read again now
+    auto flush_queue = [&]() __attribute__((always_inline)) {
+      if (qn == 0) return;
+      const bool live = lane < qn;
+      const int key = my_qk[live ? lane : 0];
+      KeyRow<true> kq;
+      if (kq_in_lds) {
+        wait_vm<0>();
+        const uint8_t* r = my_tile + 16 * lane;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) kq.c[j] = *reinterpret_cast<const u32x4*>(r + 1024 * j);
+        kq_in_lds = false;
+      } else {
+        const u32x4* src = reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint8_t*>(k) + ((size_t)cur.j * Nmax + key) * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) kq.c[j] = src[j];
+      }
+      typename Acc<G>::T a;
+      float ks;
+      exact_acc(kq, cur, a, ks);
+      float sv[G], wt[G];
+      uint32_t posm;
+      const bool any = weights(a, ks, fac, live, sv, wt, posm);
+      count_pos(posm);
+      const uint64_t m = __ballot(any);
+      vrows += __popcll(m);
+      if constexpr (CAND) {
+        const int e = list_entry(m, any);
+        if (e >= 0) list_store(lidx, lsc, e, key, sv);
+      }
+      append(any, key, wt);
+      qn = 0;
+    };
+
+    // Filter inputs of the stream of tile t: whether it is scored exactly key
+    // by key (scores are written, every key is listed, or the filter has no
+    // usable query), its filter queries and sign(scale) / C_h.
+    Stream st = cur;                   // stream of tile t
+    bool st_exact = true;
+    float inv = 0.f;                   // sign(scale) / R of the group
+    const float* qh_st = nullptr;
+    auto load_filter = [&](const Stream& s) __attribute__((always_inline)) {
+      st_exact = qhi == nullptr || scores != nullptr || (CAND && s.n <= kCandAll);
+      if (!st_exact) {
+        inv = invc[s.j];
+        st_exact = !(inv == inv);
+        qh_st = qhi + (size_t)s.j * (kHeadDim / 2);
+      }
+    };
+    load_filter(st);
+    bool dense = false;                // the next tile is scored in place without the filter
+
+    // scores / list entry of the last tile scored in place, stored with the
+    // next tile's loads so that their wait is the one after its scoring pass
+    bool p_have = false;
+    float p_s[G];
+    bool p_valid = false;
+    float* p_sc0 = nullptr;            // score of key 0, first head (null: no scores)
+    int p_e = -1, p_key = 0;
+    int32_t* p_li = nullptr;
+    float* p_ls = nullptr;
+    auto store_scores = [&]() __attribute__((always_inline)) {
+      float* sp = p_sc0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (p_valid) sp[lane] = p_s[h];
+        sp += Nmax;
+      }
+    };
+    auto deferred_stores = [&]() __attribute__((always_inline)) {
+      if (!p_have) return;
       if (p_sc0) store_scores();
       if constexpr (CAND) {
         if (p_e >= 0) list_store(p_li, p_ls, p_e, p_key, p_s);
       }
-      v_rows_sync(p_mask, 0);
+      p_have = false;
+    };
+
+    // Per tile t: wait for it, read it from LDS, issue the deferred stores,
+    // the value rows of the oldest pending survivors (up to 16) and the copy
+    // of tile t+1, in that order; score tile t (exactly, or by the filter);
+    // then wait only for the stores and value rows (the vector-memory counter
+    // completes in issue order, so the tile copy behind them stays in flight)
+    // and add the rows; then settle tile t's keys.
+    for (int t = t0; t < t1; ++t) {
+      if (t >= st.s1) {
+        st = stream_after(st, t);
+        load_filter(st);
+        dense = false;
+      }
+      const int base = (t - st.s0) * kTileKeys;
+      const bool valid = base + lane < st.n;
+
+      // 1. tile t has landed; LDS -> registers
+      wait_vm<0>();
+      KeyRow<true> kr;
+      tile_read_bf16(my_tile, lane, kr);
+
+      // 2. deferred stores of the last tile scored in place
+      deferred_stores();
+      // 3. the oldest pending value rows, one load each (the wait below
+      //    leaves only the 16 tile loads issued after them outstanding)
+      const int nv = min(pn, kVS);
+      VRows vr;
+      if (nv > 0) {
+        const int key_l = my_pk[(ph + (lane & (kVS - 1))) & (kTileKeys - 1)];
+        unroll_seq(std::make_integer_sequence<int, kVS>{}, [&](auto uu) {
+          constexpr int u = decltype(uu)::value;
+          if (u < nv) {
+            const int key = __builtin_amdgcn_readlane(key_l, u);
+            vr.r[u] = vload(uniform_ptr(vbase + (size_t)key * kRowBytes), (uint32_t)lane * 4);
+          }
+        });
+      }
+      // 4. tile t+1 -> LDS (16 loads), once the reads of tile t are done
+      const bool last = t + 1 == t1;
+      wait_lgkm0();
+      if (!last) {
+        const Stream nx = t + 1 < st.s1 ? st : stream_after(st, t + 1);
+        issue_tile(&nx, t + 1, nullptr);
+      } else if (qn > 0) {
+        // the wave's last tile: the queued keys' rows come into the free LDS
+        // tile (16 loads, like a tile copy) while this tile is scored
+        copy_queue_rows();
+        kq_in_lds = true;
+      } else {
+        issue_tile(nullptr, 0, tile_src(st, t));
+      }
+
+      // 5. tile t: exact dot products in place, or the filter; a tile with
+      //    many candidates (on the last tile: any) is scored in place at once
+      typename Acc<G>::T ta;
+      float tks = 0.f;
+      bool inplace = st_exact || dense;
+      uint64_t cmask = 0;
+      if (inplace) {
+        exact_acc(kr, st, ta, tks);
+      } else {
+        typename Acc<1>::T fa = {0.f, 0.f};
+        filter_row<1>(kr, qh_st, fa, tks);
+        const float m = fa[0] * inv;
+        const bool drop = m < 0.f && m > -INFINITY && m * m > fmaf(tks, kKsqSafe, kKsqTiny);
+        cmask = __ballot(valid && !drop);
+        if (__popcll(cmask) > (last ? 0 : kDenseTile)) {
+          inplace = true;
+          exact_acc(kr, st, ta, tks);
+        }
+      }
+
+      // 6. the pending value rows are in (the tile copy may still be in flight)
+      vwait16(vr);
+      unroll_seq(std::make_integer_sequence<int, kVS>{}, [&](auto uu) {
+        constexpr int u = decltype(uu)::value;
+        if (u < nv) v_add((ph + u) & (kTileKeys - 1), vr.r[u]);
+      });
+      ph = (ph + nv) & (kTileKeys - 1);
+      pn -= nv;
+
+      // 7. entering the next non-empty stream: the last one is finished
+      if (st.j != cur.j) {
+        flush_queue();
+        drain16(pn);
+        flush(cur);
+        reset();
+        cur = st;
+        load_fac(cur, fac);
+        open_slot(cur);
+        vbase = vbase_of(cur);
+      }
+
+      // 8. tile t's keys
+      if (inplace) {
+        flush_queue();  // older candidates first: everything stays in key order
+        float wt[G];
+        uint32_t posm;
+        const bool any = weights(ta, tks, fac, valid, p_s, wt, posm);
+        count_pos(posm);
+        const uint64_t m = __ballot(any);
+        vrows += __popcll(m);
+        dense = !st_exact && __popcll(m) > kDenseTile;
+        if constexpr (CAND) {
+          const bool all = st.n <= kCandAll;
+          p_e = list_entry(all ? __ballot(valid) : m, all ? valid : any);
+          p_key = base + lane;
+          p_li = lidx;
+          p_ls = lsc;
+        }
+        p_sc0 = scores ? scores + ((size_t)st.b * Hq + (size_t)st.kvh * G) * Nmax + base : nullptr;
+        p_valid = valid;
+        p_have = true;
+        append(any, base + lane, wt);
+      } else if (cmask) {
+        const int c = __popcll(cmask);
+        if (qn + c > kTileKeys) flush_queue();
+        if ((cmask >> lane) & 1)
+          my_qk[qn + __builtin_amdgcn_mbcnt_hi((uint32_t)(cmask >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)cmask, 0))] =
+              base + lane;
+        qn += c;
+      }
     }
+    // the last tile's deferred stores, the queue and the pending rows
+    deferred_stores();
+    flush_queue();
+    drain(std::integral_constant<int, kTileKeys>{}, pn);
     flush(cur);
     wait_vm<0>();
   } else {
@@ -1515,7 +1872,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_full_fallback(
 }
 
 struct WsLayout {
-  size_t num, den, nnz, vrows, tile_pre, total;
+  size_t num, den, nnz, vrows, tile_pre, qhi, invc, total;
   // the fused selection: candidate lists and counts, row flags, rescored rows
   size_t cand_idx, cand_sc, cand_cnt, flag, fb, rescored, total_sel;
 };
@@ -1532,6 +1889,8 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   l.nnz = o; o += align_up(slots * G * sizeof(int32_t), 256);
   l.vrows = o; o += align_up(slots * sizeof(int32_t), 256);
   l.tile_pre = o; o += align_up((S + 1) * sizeof(int), 256);
+  l.qhi = o; o += align_up(S * (kHeadDim / 2) * sizeof(uint32_t), 256);
+  l.invc = o; o += align_up(S * sizeof(float), 256);
   l.total = o;
   const size_t tiles = (size_t)B * Hkv * (size_t)ceil_div(max_ctx, kTileKeys);
   l.cand_idx = o; o += align_up(tiles * kTileKeys * sizeof(int32_t), 256);
@@ -1557,6 +1916,8 @@ struct Launch {
   float* cand_sc;
   int32_t* cand_cnt;
   int32_t* fb;  // fallback rows: count, list, per-row done counters
+  const float* qhi;  // the filter's queries (null: every key scored exactly)
+  const float* invc;
   int B, Hq, Hkv, Nmax, max_ctx;
   float scale, eps;
   int normq;
@@ -1603,7 +1964,7 @@ hipError_t launch_full(const DecodeFullArgs& a, const Launch& L, hipStream_t str
     *grid_out = (int)grid;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, L.q, L.k, L.v, L.ctx_lens,
                        L.scores, L.num, L.den, L.nnz, L.vrows, L.tile_pre, L.cand_idx, L.cand_sc,
-                       L.cand_cnt, L.fb, L.B,
+                       L.cand_cnt, L.fb, L.qhi, L.invc, L.B,
                        L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale, L.eps, L.normq, cus_per_xcd);
     return hipGetLastError();
   });
@@ -1626,6 +1987,10 @@ Launch make_launch(const DecodeFullArgs& a, const WsLayout& l, bool cand) {
   L.cand_sc = cand ? reinterpret_cast<float*>(ws + l.cand_sc) : nullptr;
   L.cand_cnt = cand ? reinterpret_cast<int32_t*>(ws + l.cand_cnt) : nullptr;
   L.fb = cand ? reinterpret_cast<int32_t*>(ws + l.fb) : nullptr;
+  // the filter serves bf16 caches when no full scores are written
+  const bool filter = a.kv_bf16 && a.scores == nullptr;
+  L.qhi = filter ? reinterpret_cast<const float*>(ws + l.qhi) : nullptr;
+  L.invc = filter ? reinterpret_cast<const float*>(ws + l.invc) : nullptr;
   L.B = a.B;
   L.Hq = a.Hq;
   L.Hkv = a.Hkv;
@@ -1653,9 +2018,32 @@ size_t decode_full_select_ws_bytes(int B, int Hq, int Hkv, int max_ctx) {
   return ws_layout(B, Hq, Hkv, max_ctx).total_sel;
 }
 
+// The filter's query inputs, when the main kernel uses the filter.
+hipError_t launch_qprep(const DecodeFullArgs& a, const WsLayout& l, const Launch& L,
+                        hipStream_t stream) {
+  if (!L.qhi) return hipSuccess;
+  char* ws = static_cast<char*>(a.ws);
+  const int groups = a.B * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(ceil_div(groups, 4)), dim3(256), 0, stream, a.q, groups, a.scale,
+                       reinterpret_cast<uint32_t*>(ws + l.qhi), reinterpret_cast<float*>(ws + l.invc));
+  };
+  switch (G) {
+    case 1: go(decode_full_qprep<1>); break;
+    case 2: go(decode_full_qprep<2>); break;
+    case 4: go(decode_full_qprep<4>); break;
+    case 8: go(decode_full_qprep<8>); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
   const Launch L = make_launch(a, l, false);
+  hipError_t e0 = launch_qprep(a, l, L, stream);
+  if (e0 != hipSuccess) return e0;
   int grid = 0;
   hipError_t e = launch_full<false>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
@@ -1674,7 +2062,9 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   float* rescored = reinterpret_cast<float*>(ws + l.rescored);
   const int disjoint = (s.sel_flags & SSA_SELECT_DISJOINT) ? 1 : 0;
   int grid = 0;
-  hipError_t e = launch_full<true>(a, L, stream, &grid);
+  hipError_t e = launch_qprep(a, l, L, stream);
+  if (e != hipSuccess) return e;
+  e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_full_combine_select, dim3(2 * a.Hq * a.B), dim3(kCombineThreads), 0, stream,
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
