@@ -54,6 +54,15 @@ def parse():
                    help="use this context length for every sequence instead of U[64K,128K]")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain device copy of known size (counter calibration)")
+    p.add_argument("--no-legs", action="store_true",
+                   help="skip the other workloads (the headline line then holds no 'legs')")
+    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block",
+                   help="comma-separated workloads measured after the headline: "
+                        "tiny, single, fixed128k, sweep, block")
+    p.add_argument("--leg-steps", type=int, default=20)
+    p.add_argument("--workload", default=None,
+                   help="measure only this workload (tiny, single, fixed128k, sweep, block) and "
+                        "print its JSON object")
     return p.parse_args()
 
 
@@ -165,6 +174,125 @@ def cpu_baseline(wl, reps: int = 3) -> dict:
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def bench_leg(wl, *, n_sparse: int, steps: int, warmup: int = 3, rotate_bytes: int = 768 << 20,
+              k_top: int = 1024, n_recent: int = 128) -> dict:
+    """One decode step of a workload: ssa_decode_full_select, then n_sparse sparse layers
+    reusing its cache and selection. Cache copies are rotated until they exceed the
+    Infinity Cache several times over, so reads come from HBM.
+
+    Bytes counted (algorithmic): every live key once, the value rows of keys some
+    head kept, the selections written; per sparse layer the union of the group's
+    selected rows (K and V). GB/s is that over the measured time.
+    """
+    import torch
+    from long_context_decode_relu_amd import ssa
+    dev = torch.device("cuda:0")
+    kvb = 2 if wl.kv_dtype == "bf16" else 4
+    cache_bytes = 2 * wl.k.nbytes
+    copies = max(1, min(64, -(-rotate_bytes // max(1, cache_bytes))))
+    caches = [ssa.cache_from_workload(wl, dev) for _ in range(copies)]
+    q = torch.from_numpy(wl.q).to(dev)
+    qs = [torch.from_numpy(wl.q_sparse[l % wl.q_sparse.shape[0]]).to(dev) for l in range(n_sparse)]
+    B, Hq, D = q.shape
+    shp = caches[0].shape(Hq)
+    ws_fs = ssa.workspace(ssa.SSA_OP_DECODE_FULL_SELECT, shp, 0, dev)
+    ws_sp = ssa.workspace(ssa.SSA_OP_DECODE_SPARSE, shp, k_top + n_recent, dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(n_sparse)]
+
+    def step(i, ev=None):
+        c = caches[i % copies]
+        if ev is not None:
+            ev[0].record()
+        _, sel, cnt, _, _, _ = ssa.ssa_decode_full_select(q, c, out=out, ws=ws_fs, k_top=k_top,
+                                                          n_recent=n_recent)
+        if ev is not None:
+            ev[1].record()
+        for l in range(n_sparse):
+            ssa.ssa_decode_sparse(qs[l], c, sel, cnt, out=outs[l], ws=ws_sp)
+        if ev is not None:
+            ev[2].record()
+        return sel, cnt
+
+    # statistics once, untimed: value rows fetched and rows each sparse layer gathers
+    _, _, nnz, vrows = ssa.ssa_decode_full(q, caches[0], want_stats=True)
+    sel, cnt = step(0)
+    torch.cuda.synchronize()
+    vrows_np, nnz_np = vrows.cpu().numpy(), nnz.cpu().numpy()
+    sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    g = Hq // wl.n_kv_heads
+    union_rows = 0
+    for b in range(B):
+        for kvh in range(wl.n_kv_heads):
+            u = set()
+            for h in range(kvh * g, (kvh + 1) * g):
+                u.update(sel_np[b, h, :cnt_np[b, h]].tolist())
+            union_rows += len(u)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    full_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    n = wl.ctx_lens.astype(np.int64)
+    k_bytes = int(wl.n_kv_heads * D * kvb * n.sum())
+    v_bytes = int(D * kvb * int(vrows_np.sum()))
+    sel_out = 4 * B * Hq * (k_top + n_recent + 1)
+    full_alg = k_bytes + v_bytes + 2 * B * Hq * D * 4 + sel_out
+    sparse_alg = n_sparse * 2 * D * kvb * union_rows
+    kv_read = k_bytes + v_bytes + sparse_alg
+    gbs = kv_read / (ms_step * 1e-3) / 1e9
+    full_gbs = full_alg / (full_ms * 1e-3) / 1e9
+    res = {
+        "workload": wl.name, "batch": B, "ctx_lens_sum": int(n.sum()), "kv_dtype": wl.kv_dtype,
+        "n_sparse_layers": n_sparse, "copies_rotated": copies,
+        "ms_per_step": round(ms_step, 4), "kv_bytes_read_per_step": kv_read,
+        "gb_s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "query_tok_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_full_select": {"avg_ms": round(full_ms, 4), "alg_bytes": full_alg,
+                               "gb_s": round(full_gbs, 1), "frac": round(full_gbs / HBM_PEAK_GBS, 4)},
+        "sparse_layers": {"avg_ms": round(sp_ms, 4), "alg_bytes": sparse_alg,
+                          "gb_s": round(sparse_alg / (sp_ms * 1e-3) / 1e9, 1) if n_sparse else None},
+        "vskip": {"v_rows_fetched": int(vrows_np.sum()), "v_rows_dense": int(wl.n_kv_heads * n.sum()),
+                  "v_traffic_saved": round(1 - v_bytes / (wl.n_kv_heads * D * kvb * n.sum()), 4),
+                  "measured_zero_weight_fraction": round(1 - float(nnz_np.sum()) / (Hq * float(n.sum())), 4)},
+    }
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_legs(names, steps: int) -> dict:
+    """The other workloads, one step each (see bench_leg)."""
+    from long_context_decode_relu_amd import synth
+    legs = {}
+    for name in names:
+        t0 = time.perf_counter()
+        if name == "tiny":
+            legs[name] = bench_leg(synth.tiny_decode(), n_sparse=1, steps=steps)
+        elif name == "single":
+            legs[name] = bench_leg(synth.single_decode(), n_sparse=1, steps=steps)
+        elif name == "fixed128k":
+            legs[name] = bench_leg(synth.batched_decode(fixed_len=131072), n_sparse=1, steps=steps)
+        elif name == "sweep":
+            legs[name] = {f"p{p}": bench_leg(synth.sweep_decode(p), n_sparse=1, steps=steps)
+                          for p in synth.SWEEP_FRACTIONS}
+        elif name == "block":
+            legs[name] = bench_leg(synth.block_step(), n_sparse=3, steps=steps)
+        else:
+            raise ValueError(f"unknown workload {name}")
+        log(f"[bench] leg {name} done in {time.perf_counter() - t0:.1f}s")
+    return legs
+
+
 def bench_prefill(reps: int, warmup: int = 3) -> dict:
     """Chunked ReLU^2 prefill: 2048 queries at the end of a 64K cache (B1, 16/2 heads, bf16).
 
@@ -214,6 +342,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill(args.prefill_reps)}), flush=True)
+        return
+    if args.workload:
+        print(json.dumps(bench_legs([args.workload], args.leg_steps)), flush=True)
         return
 
     import torch
@@ -373,6 +504,10 @@ def main():
                      "traffic": None if args.unfused else measured_traffic(),
                      "alg_bytes_per_launch": full_alg, "avg_launch_ms": round(full_avg_ms, 4)},
     }
+    if not args.no_legs:
+        del caches
+        torch.cuda.empty_cache()
+        res["legs"] = bench_legs([x for x in args.legs.split(",") if x], args.leg_steps)
     if not args.no_prefill:
         log("[bench] prefill ...")
         res["prefill"] = bench_prefill(args.prefill_reps)

@@ -537,6 +537,13 @@ __device__ __forceinline__ float head_rms_factor(const float* qrow, int lane, fl
 // cut among the list always holds the top k. List position p holds the key
 // index at cand_idx[p] and the G scores at cand_sc[p*G ..].
 constexpr int kCandAll = 8192;
+// Entries a thread of a row's selection work-group gathers into registers:
+// rows whose lists hold more entries than kSelThreads * kGatherPer are
+// selected from rescored scores instead.
+constexpr int kGatherPer = 16;
+// Rounds of the fast selection path: wave w takes slots w, w + 16, ... one
+// per round, so rows of up to 16*16 slots fit.
+constexpr int kFastRounds = 16;
 
 // First tile and tile count of the part of stream [s0, s1) that wave w of W
 // (over T tiles) takes: the candidate list of that (stream, wave) slot has
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part_num,
     float* __restrict__ part_den, int32_t* __restrict__ part_nnz, int32_t* __restrict__ part_vrows,
     int* __restrict__ tile_pre_out, int32_t* __restrict__ cand_idx, float* __restrict__ cand_sc,
-    int32_t* __restrict__ cand_cnt, int32_t* __restrict__ fb_count,
+    int32_t* __restrict__ cand_cnt,
     const float* __restrict__ qhi, const float* __restrict__ invc,
     int B, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps, int normq,
     int cus_per_xcd) {
@@ -574,8 +581,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   __syncthreads();
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= S; i += kThreads) tile_pre_out[i] = s_tpre[i];
-    // the list of rows the selection falls back on starts empty
-    if (fb_count && threadIdx.x == 0) *fb_count = 0;
   }
 
   const int T = s_tpre[S];
@@ -1325,9 +1330,6 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
 // row is flagged and selected from rescored scores.
 // ---------------------------------------------------------------------------
 
-// Entries a thread of the row's work-group gathers into registers: rows whose
-// lists hold more entries than kSelThreads * kGatherPer are flagged.
-constexpr int kGatherPer = 16;
 
 // Count, smallest and largest key of the candidates held in registers (the
 // first nr of P per thread; nr is uniform over the wave) over the work-group,
@@ -1616,9 +1618,6 @@ __device__ __forceinline__ void select_from_cands(SelShared& sh,
   }
 }
 
-// Rounds of the fast selection path: wave w takes slots w, w + 16, ... one
-// per round, so rows of up to 16*16 slots fit.
-constexpr int kFastRounds = 16;
 
 // The common case of select_from_cands, one global round trip shorter: a
 // stream of lists of survivors only, of at most kSelWaves*kFastRounds slots,
@@ -1758,8 +1757,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_sc,
     const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ ctx_lens, int max_ctx,
     int k_top, int n_recent, int disjoint,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count, int32_t* __restrict__ row_flag,
-    int32_t* __restrict__ fb) {
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
+    const int32_t* __restrict__ row_flag, int32_t* __restrict__ sel_fail,
+    const float* __restrict__ rs) {
   __shared__ SelShared sh;
   const int rows = S / Hkv * Hq;
   if ((int)blockIdx.x < rows) {
@@ -1779,102 +1779,177 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   const float* hsc = cand_sc + jh;  // the row's scores: every G-th float
   const int qs = G;
   int32_t* const o = sel_idx + (size_t)row * stride;
-  if (!select_fast(sh, cand_idx, hsc, qs, cand_cnt, T, s0, s1, j, Wl, n, k_top, n_recent, disjoint,
-                   o, stride, sel_count + row, row_flag + row))
-    select_from_cands(sh, cand_idx, hsc, qs, cand_cnt, tile_pre, S, j, Wl, n, k_top, n_recent,
-                      disjoint, o, stride, sel_count + row, row_flag + row);
-  // a flagged row joins the fallback list (fb[0] rows at fb[1 ..], their
-  // done counters at fb[1 + rows + row]); thread 0 wrote the flag
-  if (threadIdx.x == 0 && row_flag[row]) {
-    fb[1 + rows + row] = 0;
-    fb[1 + atomicAdd(fb, 1)] = row;
+  if (row_flag[row]) {  // rescored: the exact selection from the row's scores
+    select_row_exact(sh, rs + (size_t)row * max_ctx, n, k_top, n_recent, disjoint, o, stride,
+                     sel_count + row);
+    return;
   }
+  int32_t* const fail = sel_fail + row;
+  if (!select_fast(sh, cand_idx, hsc, qs, cand_cnt, T, s0, s1, j, Wl, n, k_top, n_recent, disjoint,
+                   o, stride, sel_count + row, fail))
+    select_from_cands(sh, cand_idx, hsc, qs, cand_cnt, tile_pre, S, j, Wl, n, k_top, n_recent,
+                      disjoint, o, stride, sel_count + row, fail);
+  // the full-layer kernel flags every row these tests reject; should one be
+  // rejected anyway its count is -1 (an empty selection), never stale
+  __syncthreads();
+  if (threadIdx.x == 0 && *fail) sel_count[row] = -1;
 }
 
-// The rows whose candidate lists did not decide the selection (listed by
-// the combine), rescored and selected exactly. Work item (f, s) scores slice s
-// of the keys of listed row f exactly as the full-layer kernel does (same
-// widening, same FMA order over the dimensions, same query factor) into the
-// row's buffer of `max_ctx` floats; the work-group that completes the last
-// slice of a row (a counter per row, zeroed by the combine) selects it from
-// the buffer. The items run on a persistent grid; with no listed row every
-// work-group exits after one load.
-constexpr int kFallbackBlocks = 128;
-constexpr int kFallbackSlices = 16;
+// Rows whose candidate lists cannot decide their selection, rescored. For
+// each stream (sequence, KV head) the work-group decides which of the G rows
+// the combine's list selection would reject: fewer listed keys with a positive
+// score than k, or more list entries or slots than that selection holds. It
+// writes row_flag for every row and, for flagged rows, rescores slice s of the
+// stream's 64-key tiles: each wave copies its tiles into LDS as the full-layer
+// kernel does and scores every key exactly as it does (score_row: same
+// widening, FMA order and query factors) into the row's buffer of `max_ctx`
+// floats. The combine then selects flagged rows from the buffers. Work items
+// (stream, slice) are numbered stream first, so a work-group of the persistent
+// grid usually keeps one stream and decides it once.
+constexpr int kFallbackBlocks = 256;
+constexpr int kFallbackSlices = 64;
 
 template <int G, bool BF16, bool NORMK>
-__global__ __launch_bounds__(kSelThreads) void decode_full_fallback(
+__global__ __launch_bounds__(kThreads) void decode_full_rescore(
     const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
-    int32_t* __restrict__ fb, int Hq, int Hkv, int Nmax, int max_ctx, float scale, float eps,
-    int normq, int k_top, int n_recent, int disjoint, int rows, float* __restrict__ rs,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count) {
-  const int nf = fb[0];
-  if (nf == 0) return;
-  __shared__ SelShared sh;
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int stride = k_top + n_recent;
-  for (int it = blockIdx.x; it < nf * kFallbackSlices; it += gridDim.x) {
-    const int f = it / kFallbackSlices, sl = it - f * kFallbackSlices;
-    const int row = fb[1 + f];
-    const int b = row / Hq, h = row - b * Hq;
-    const int kvh = h / G, jh = h - kvh * G;
-    const int n = live_keys(ctx_lens, b, max_ctx);
-    const float* qrow = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
-    float fac = scale;
-    if (normq) fac = __shfl(head_rms_factor<G>(qrow, lane, scale, eps), jh * (kWave / G), kWave);
-    const float* qh = qrow + jh * kHeadDim;
-    const int per = ceil_div(n, kFallbackSlices);
-    const int i1 = min(n, sl * per + per);
-    for (int i = sl * per + tid; i < i1; i += kSelThreads) {
-      const size_t r = ((size_t)b * Hkv + kvh) * Nmax + i;
-      float acc = 0.f, ksq = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < 8; ++c) {
-        float e[16];
-        if constexpr (BF16) {
-          const u32x4* kp = reinterpret_cast<const u32x4*>(k) + r * 16 + 2 * c;
-          KeyRow<true> one;
-          one.c[0] = kp[0];
-          one.c[1] = kp[1];
-          one.chunk16(0, e);
+    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
+    const int* __restrict__ tile_pre, int S, int W, int k_top, int n_recent, int disjoint,
+    int32_t* __restrict__ row_flag, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
+    float eps, int normq, float* __restrict__ rs) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
+  __shared__ int s_red[kWaves][2 + G];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint8_t* const my_tile = s_tile + wave * kTileBytesBf16;
+  const uint32_t tile_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)my_tile);
+  constexpr size_t kRowBytes = kHeadDim * (BF16 ? 2 : 4);
+  const TileOffsets toff(lane);
+  const int T = tile_pre[S];
+  int jd = -1;     // the stream decided last
+  uint32_t fm = 0; // its flagged rows, one bit per head
+  for (int it = blockIdx.x; it < S * kFallbackSlices; it += gridDim.x) {
+    const int j = it % S, sl = it / S;
+    const int b = j / Hkv, kvh = j - b * Hkv;
+    const int row0 = b * Hq + kvh * G;  // the group's first row
+    const int n = __builtin_amdgcn_readfirstlane(live_keys(ctx_lens, b, max_ctx));
+    if (j != jd) {
+      jd = j;
+      const int s0 = tile_pre[j], s1 = tile_pre[j + 1];
+      const int p0 = s1 > s0 ? j + wave_of_tile(s0, W, T) : 0;
+      const int p1 = s1 > s0 ? j + wave_of_tile(s1 - 1, W, T) + 1 : 0;
+      int E = 0, emax = 0;
+      int nz[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) nz[h] = 0;
+      for (int p = p0 + tid; p < p1; p += kThreads) {
+        const int cc = cand_cnt[p];
+        E += cc;
+        emax = max(emax, cc);
+#pragma unroll
+        for (int h = 0; h < G; ++h) nz[h] += part_nnz[(size_t)p * G + h];
+      }
+      E = wave_sum_i(E);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, kWave));
+#pragma unroll
+      for (int h = 0; h < G; ++h) nz[h] = wave_sum_i(nz[h]);
+      __syncthreads();  // the previous decision's reads are done
+      if (lane == 0) {
+        s_red[wave][0] = E;
+        s_red[wave][1] = emax;
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_red[wave][2 + h] = nz[h];
+      }
+      __syncthreads();
+      E = 0;
+      emax = 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) nz[h] = 0;
+#pragma unroll
+      for (int x = 0; x < kWaves; ++x) {
+        E += s_red[x][0];
+        emax = max(emax, s_red[x][1]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) nz[h] += s_red[x][2 + h];
+      }
+      const int pool = disjoint ? max(0, n - n_recent) : n;
+      const int kk = min(k_top, pool);
+      // keys of the recent window are not in the pool of a disjoint selection
+      const int outside = disjoint ? min(n_recent, n) : 0;
+      // the fast path takes up to 16*16 slots of survivor lists of at most 64
+      // entries; otherwise the general path, which holds 2 np + 1 slot words
+      // and kSelThreads * kGatherPer entries
+      const int np = p1 - p0;
+      const bool fast = n > kCandAll && np <= kSelWaves * kFastRounds && emax <= kWave;
+      const bool too_big = !fast && (2 * np + 1 > kSegWords || E > kSelThreads * kGatherPer);
+      fm = 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int c = n <= kCandAll ? pool : nz[h] - outside;
+        if (kk < pool && (too_big || c < kk)) fm |= 1u << h;
+      }
+      fm = __builtin_amdgcn_readfirstlane(fm);
+    }
+    if (sl == 0 && tid < G) row_flag[row0 + tid] = (fm >> tid) & 1u;
+    if (fm == 0) continue;
+    const float* qrow = q + (size_t)row0 * kHeadDim;
+    float fac[G];
+    {
+      const float fh = normq ? head_rms_factor<G>(qrow, lane, scale, eps) : scale;
+#pragma unroll
+      for (int h = 0; h < G; ++h) fac[h] = __shfl(fh, h * (kWave / G), kWave);
+    }
+    const int nt = ceil_div(n, kTileKeys);
+    const int per = ceil_div(nt, kFallbackSlices);
+    const int e1 = min(nt, sl * per + per);
+    for (int t = sl * per + wave; t < e1; t += kWaves) {
+      const int base = t * kTileKeys;
+      const int nvalid = min(kTileKeys, n - base);
+      const bool valid = lane < nvalid;
+      typename Acc<G>::T acc;
+#pragma unroll
+      for (int h = 0; h < Acc<G>::kN; ++h) acc[h] = 0.f;
+      float ksq = 0.f;
+      if constexpr (BF16) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(k) + ((size_t)j * Nmax + base) * kRowBytes;
+        if (nvalid == kTileKeys) {
+          unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            dma16<i * 1024>(src + (i >> 2) * 4096, toff.off[i & 3], tile_m0);
+          });
         } else {
-          const f32x4* kp = reinterpret_cast<const f32x4*>(k) + r * 32 + 4 * c;
-          KeyRow<false> one;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) one.c[p] = kp[p];
-          one.chunk16(0, e);
+          unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            const int kt = 4 * i + (lane >> 4);
+            const int row = min(kt, nvalid - 1);
+            dma16<i * 1024>(src, (uint32_t)(row * 256 + (((lane & 15) ^ (kt & 15)) << 4)), tile_m0);
+          });
         }
-        if constexpr (NORMK) {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) ksq = fmaf(e[t], e[t], ksq);
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) acc = fmaf(qh[16 * c + t], e[t], acc);
+        wait_vm<0>();
+        KeyRow<true> kr;
+        tile_read_bf16(my_tile, lane, kr);
+        wait_lgkm0();
+        score_row<G, true, NORMK>(kr, qrow, acc, ksq);
+      } else {
+        KeyRow<false> kr;
+        row_load_f32(k, (size_t)j * Nmax + base + min(lane, nvalid - 1), kr);
+        score_row<G, false, NORMK>(kr, qrow, acc, ksq);
       }
       float kf = 1.f;
       if constexpr (NORMK) kf = 1.f / sqrtf(ksq * (1.0f / kHeadDim) + eps);
-      rs[(size_t)row * max_ctx + i] = NORMK ? acc * fac * kf : acc * fac;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (((fm >> h) & 1u) && valid)
+          rs[(size_t)(row0 + h) * max_ctx + base + lane] = NORMK ? acc[h] * fac[h] * kf : acc[h] * fac[h];
     }
-    // the slice's scores are visible device-wide before it is counted; the
-    // work-group that counts the row's last slice reads them all
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&fb[1 + rows + row], 1) == kFallbackSlices - 1;
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      select_row_exact(sh, rs + (size_t)row * max_ctx, n, k_top, n_recent, disjoint,
-                       sel_idx + (size_t)row * stride, stride, sel_count + row);
-    }
-    __syncthreads();
   }
 }
 
 struct WsLayout {
   size_t num, den, nnz, vrows, tile_pre, qhi, invc, total;
   // the fused selection: candidate lists and counts, row flags, rescored rows
-  size_t cand_idx, cand_sc, cand_cnt, flag, fb, rescored, total_sel;
+  size_t cand_idx, cand_sc, cand_cnt, flag, fail, rescored, total_sel;
 };
 
 WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
@@ -1897,7 +1972,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   l.cand_sc = o; o += align_up(tiles * kTileKeys * G * sizeof(float), 256);
   l.cand_cnt = o; o += align_up(slots * sizeof(int32_t), 256);
   l.flag = o; o += align_up(rows * sizeof(int32_t), 256);
-  l.fb = o; o += align_up((1 + 2 * rows) * sizeof(int32_t), 256);
+  l.fail = o; o += align_up(rows * sizeof(int32_t), 256);
   l.rescored = o; o += align_up(rows * (size_t)max_ctx * sizeof(float), 256);
   l.total_sel = o;
   return l;
@@ -1915,7 +1990,6 @@ struct Launch {
   int32_t* cand_idx;
   float* cand_sc;
   int32_t* cand_cnt;
-  int32_t* fb;  // fallback rows: count, list, per-row done counters
   const float* qhi;  // the filter's queries (null: every key scored exactly)
   const float* invc;
   int B, Hq, Hkv, Nmax, max_ctx;
@@ -1964,8 +2038,8 @@ hipError_t launch_full(const DecodeFullArgs& a, const Launch& L, hipStream_t str
     *grid_out = (int)grid;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, L.q, L.k, L.v, L.ctx_lens,
                        L.scores, L.num, L.den, L.nnz, L.vrows, L.tile_pre, L.cand_idx, L.cand_sc,
-                       L.cand_cnt, L.fb, L.qhi, L.invc, L.B,
-                       L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale, L.eps, L.normq, cus_per_xcd);
+                       L.cand_cnt, L.qhi, L.invc, L.B, L.Hq, L.Hkv, L.Nmax, L.max_ctx, L.scale,
+                       L.eps, L.normq, cus_per_xcd);
     return hipGetLastError();
   });
 }
@@ -1986,7 +2060,6 @@ Launch make_launch(const DecodeFullArgs& a, const WsLayout& l, bool cand) {
   L.cand_idx = cand ? reinterpret_cast<int32_t*>(ws + l.cand_idx) : nullptr;
   L.cand_sc = cand ? reinterpret_cast<float*>(ws + l.cand_sc) : nullptr;
   L.cand_cnt = cand ? reinterpret_cast<int32_t*>(ws + l.cand_cnt) : nullptr;
-  L.fb = cand ? reinterpret_cast<int32_t*>(ws + l.fb) : nullptr;
   // the filter serves bf16 caches when no full scores are written
   const bool filter = a.kv_bf16 && a.scores == nullptr;
   L.qhi = filter ? reinterpret_cast<const float*>(ws + l.qhi) : nullptr;
@@ -2026,8 +2099,9 @@ hipError_t launch_qprep(const DecodeFullArgs& a, const WsLayout& l, const Launch
   const int groups = a.B * a.Hkv;
   const int G = a.Hq / a.Hkv;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(ceil_div(groups, 4)), dim3(256), 0, stream, a.q, groups, a.scale,
-                       reinterpret_cast<uint32_t*>(ws + l.qhi), reinterpret_cast<float*>(ws + l.invc));
+    hipLaunchKernelGGL(kern, dim3(std::max(1, ceil_div(groups, 4))), dim3(256), 0, stream, a.q,
+                       groups, a.scale, reinterpret_cast<uint32_t*>(ws + l.qhi),
+                       reinterpret_cast<float*>(ws + l.invc));
   };
   switch (G) {
     case 1: go(decode_full_qprep<1>); break;
@@ -2058,30 +2132,33 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   const WsLayout l = ws_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
   const Launch L = make_launch(a, l, true);
   char* ws = static_cast<char*>(a.ws);
-  int32_t* flag = reinterpret_cast<int32_t*>(ws + l.flag);
   float* rescored = reinterpret_cast<float*>(ws + l.rescored);
+  int32_t* row_flag = reinterpret_cast<int32_t*>(ws + l.flag);
+  int32_t* fail = reinterpret_cast<int32_t*>(ws + l.fail);
   const int disjoint = (s.sel_flags & SSA_SELECT_DISJOINT) ? 1 : 0;
   int grid = 0;
+  // 1. filter inputs; 2. the full layer with its candidate lists; 3. per
+  // stream, the rows the lists cannot select flagged and rescored; 4. combine
+  // and selection, one work-group per row
   hipError_t e = launch_qprep(a, l, L, stream);
   if (e != hipSuccess) return e;
   e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
+  const int G = a.Hq / a.Hkv;
+  e = dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
+    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kThreads), 0,
+                       stream, a.q, a.k, a.ctx_lens, L.cand_cnt, L.nnz, L.tile_pre, a.B * a.Hkv,
+                       grid * kWaves, s.k_top, s.n_recent, disjoint, row_flag, a.Hq, a.Hkv,
+                       a.Nmax, a.max_ctx, a.scale, a.eps, L.normq, rescored);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_full_combine_select, dim3(2 * a.Hq * a.B), dim3(kCombineThreads), 0, stream,
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
-                     a.ctx_lens,
-                     a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count, flag, L.fb);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.max_ctx == 0) return e;
-  // rows whose lists did not hold the top k: rescored, then selected exactly
-  const int G = a.Hq / a.Hkv;
-  return dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
-    hipLaunchKernelGGL((decode_full_fallback<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kSelThreads),
-                       0, stream, a.q, a.k, a.ctx_lens, L.fb, a.Hq, a.Hkv, a.Nmax, a.max_ctx,
-                       a.scale, a.eps, L.normq, s.k_top, s.n_recent, disjoint, a.B * a.Hq,
-                       rescored, s.sel_idx, s.sel_count);
-    return hipGetLastError();
-  });
+                     a.ctx_lens, a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count,
+                     row_flag, fail, rescored);
+  return hipGetLastError();
 }
 
 }  // namespace ssa
