@@ -182,10 +182,12 @@ ssa_status ssa_decode_sparse(const ssa_shape* shape, const float* q, const void*
  * a fixed device array of SSA_STATIC_SCRATCH_BYTES that the library holds on
  * each GPU it runs on until the process ends; the call itself allocates and
  * frees nothing (the caller still passes every input and `out`). Results are
- * those of ssa_decode_sparse on the same arguments. Calls whose partials need
- * more than SSA_STATIC_SCRATCH_BYTES, that is
+ * those of ssa_decode_sparse on the same arguments. Calls whose workspace would
+ * exceed SSA_STATIC_SCRATCH_BYTES, that is
  *   ssa_workspace_bytes(SSA_OP_DECODE_SPARSE, shape, sel_stride)
- *     = 4 * 130 * batch * n_q_heads * ceil(max_ctx_len / 8192) bytes (rounded up)
+ *     = about batch * n_kv_heads * (8 G sel_stride + 2080 G C) bytes,
+ *   G = n_q_heads / n_kv_heads, C = ceil(min(G sel_stride, max_ctx_len) / 256)
+ *   (the union rows of each KV group and one softmax partial per 256 of them)
  * > SSA_STATIC_SCRATCH_BYTES, return SSA_ERR_WORKSPACE and launch nothing.
  * Every call on one GPU shares that GPU's array: two calls that may overlap on
  * one GPU (on different streams, or from different threads) race and must be

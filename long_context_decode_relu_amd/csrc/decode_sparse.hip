@@ -6,24 +6,32 @@
 // selected key gets some weight). No position encoding is applied.
 //
 // The G query heads that share a KV head usually select many of the same
-// rows, so each row is read once for all of them. Two kernels per call:
-//   sparse   one work-group (eight waves) per (sequence, KV head, segment of
-//            8192 keys). It loads the G heads' selection lists, marks the
-//            segment's keys in per-head LDS bitmaps and ranks their union
-//            (block scan of the word popcounts). The union's rows then go in
-//            batches of 64 to four pairs of waves, batch i to pair i mod 4,
-//            so that a dense part of the selection (the recent window every
-//            head selects) is read by the four pairs at once. A pair gathers
-//            its batch's K and V rows HBM -> LDS by direct-to-LDS loads (K
-//            pieces XOR-permuted so that each lane reads its own row without
-//            bank conflicts); with one row per lane each wave scores the rows
-//            against half of the heads (queries from LDS), updates their
-//            softmax statistics, and accumulates half of the value dims for
-//            all heads. The softmax runs in base 2 (log2(e) folded into the
-//            query). The four pairs' states are merged in pair order into one
-//            (max, sum, weighted values) partial per head and segment.
-//   combine  merges the segments of each (sequence, head) by log-sum-exp in
-//            segment order.
+// rows, so each row is read once for all of them: the work is laid out over
+// the union of the group's selections, in fixed chunks of that union, so that
+// a dense selection (a short context whose heads select most of its keys, the
+// recent window) costs no more per work-group than a sparse one. Three
+// kernels per call:
+//   union    one work-group per (sequence, KV head, segment of 8192 keys).
+//            It finds each head's entries of the segment in its ascending list
+//            (two rounds of 64 probes), marks them in per-head LDS bitmaps,
+//            ranks their union (block scan of word popcounts) and writes each
+//            union row as (key, head bits) in key order, to a per-stream
+//            buffer of G * stride slots at the segment's offset: the number of
+//            list entries below the segment. The segments' runs follow one
+//            another; whatever the lists hold, every run stays in the buffer.
+//   gather   one work-group (eight waves) per (stream, chunk of 256 union
+//            rows). Each wave finds its 32 rows from the segments' counts and
+//            offsets (a wave scan), copies their K rows HBM -> LDS by
+//            direct-to-LDS loads (16-byte pieces XOR-permuted so that a lane
+//            reads its own row without bank conflicts) and their V rows into
+//            registers (a lane holds two value dims of every row). Two lanes
+//            score a row against the G heads, half of the dims each; each wave
+//            forms the softmax state of its rows per head (max, sum, weighted
+//            values, in base 2 with log2(e) folded into the query), and the
+//            eight waves' states are merged in wave order into the chunk's
+//            partial.
+//   combine  merges the chunks of each (sequence, head) by log-sum-exp in
+//            chunk order.
 // Every sum runs in a fixed order, so the result does not depend on timing.
 #include <algorithm>
 #include <cmath>
@@ -38,365 +46,434 @@ namespace ssa {
 
 namespace {
 
-constexpr int kSegKeys = 8192;                    // keys per work-group
+constexpr int kSegKeys = 8192;                    // keys per union work-group
 constexpr int kSegWords = kSegKeys / 32;          // bitmap words per head
-constexpr int kSpWaves = 8;
-constexpr int kSpThreads = kSpWaves * kWave;
-constexpr int kPairs = kSpWaves / 2;
-constexpr int kRows = kWave;                      // rows per batch: one per lane
-constexpr int kTileBytes = kRows * kHeadDim * 2;  // bf16 rows of a batch
+constexpr int kUThreads = 256;                    // union work-group
+constexpr int kUWaves = kUThreads / kWave;
+static_assert(kSegWords == kUThreads, "one bitmap word per thread");
+constexpr int kGWaves = 8;                        // gather work-group
+constexpr int kGThreads = kGWaves * kWave;
+constexpr int kWRows = kWave / 2;                 // rows per wave: two lanes per row
+constexpr int kChunk = kGWaves * kWRows;          // union rows per gather work-group
+constexpr int kKTileBf16 = kWRows * kHeadDim * 2; // one wave's bf16 K rows
 constexpr int kWaitVm0 = 0x0F70;                  // s_waitcnt vmcnt(0)
-constexpr int kListEnt = 8;  // list entries per head and thread: strides up to 4096
-constexpr int kListEntMin = 3;  // entries every launch loads: strides up to 1536
-static_assert(kSegWords <= kSpThreads, "one bitmap word per thread at most");
+constexpr int kMaxStride = kWave * kWave;         // two rounds of 64 probes
 
-template <int G, bool BF16, bool NORMQ, bool NORMK>
-__global__ __launch_bounds__(kSpThreads) void sparse_kernel(
-    const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+// Numbers of entries below x0 and below x1 in list[0 .. cnt) (ascending;
+// cnt <= 4096), by two rounds of 64 probes; every lane gets both.
+__device__ __forceinline__ int2 list_bounds(const int32_t* list, int cnt, int x0, int x1, int lane) {
+  if (cnt <= 0) return int2{0, 0};
+  const int step = ceil_div(cnt, kWave);  // <= 64
+  const int v = list[min(cnt, (lane + 1) * step) - 1];
+  const int b0 = min(cnt, (int)__popcll(__ballot(v < x0)) * step);
+  const int b1 = min(cnt, (int)__popcll(__ballot(v < x1)) * step);
+  const int p0 = b0 + lane, p1 = b1 + lane;
+  const bool in0 = lane < step && p0 < cnt && list[min(p0, cnt - 1)] < x0;
+  const bool in1 = lane < step && p1 < cnt && list[min(p1, cnt - 1)] < x1;
+  const int lo = b0 + (int)__popcll(__ballot(in0));
+  return int2{lo, max(lo, b1 + (int)__popcll(__ballot(in1)))};
+}
+
+template <int G>
+__global__ __launch_bounds__(kUThreads) void sparse_union(
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ sel_idx,
-    const int32_t* __restrict__ sel_count, int stride, int Hq, int Hkv, int Nmax, int nlim,
-    int nseg, float scale, float eps, float* __restrict__ part_m, float* __restrict__ part_l,
-    float* __restrict__ part_acc) {
-  constexpr int HW = G > 1 ? G / 2 : 1;  // heads scored by each wave of a pair
-  constexpr int GP = G < 4 ? 4 : G;
+    const int32_t* __restrict__ sel_count, int stride, int Hq, int Hkv, int nlim, int nseg,
+    int cap, int2* __restrict__ urow, int32_t* __restrict__ ucnt, int32_t* __restrict__ uoff) {
+  constexpr int HPW = (G + kUWaves - 1) / kUWaves;  // heads per wave
   __shared__ uint32_t s_bm[G][kSegWords];
-  __shared__ uint32_t s_u[kSegWords];
-  __shared__ int s_pre[kSegWords + 1];
-  __shared__ int s_wsum[kSpWaves];
-  __shared__ __attribute__((aligned(16))) float s_q[G][kHeadDim];
-  __shared__ __attribute__((aligned(16))) float s_p[kPairs][kRows][GP];
-  __shared__ __attribute__((aligned(16))) float s_sc[kPairs][GP];
-  __shared__ float s_mm[kPairs][G];
-  __shared__ float s_ll[kPairs][G];
-  // K rows of each pair's batch (bf16); at the end, the pairs' value sums
-  __shared__ __attribute__((aligned(16))) uint8_t s_ktile[BF16 ? kPairs * kTileBytes : kPairs * G * kHeadDim * 4];
-  __shared__ __attribute__((aligned(16))) uint8_t s_vtile[BF16 ? kPairs * kTileBytes : 16];
+  __shared__ int s_wsum[kUWaves];
+  __shared__ int s_lo[G];
 
   const int sg = blockIdx.x, j = sg / nseg, g = sg - j * nseg;
   const int b = j / Hkv, kvh = j - b * Hkv;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave >> 1, wv = wave & 1;
   const size_t hrow0 = (size_t)b * Hq + (size_t)kvh * G;
-  const size_t row0 = (size_t)j * Nmax;
-
-  // one round of loads: every list entry of this thread, loaded with the
-  // counts (positions are clamped into the stride, stride >= 1, and those
-  // past a count become -1 afterwards), and the query head of this wave. The
-  // first kListEntMin entries per thread cover strides up to 1536; longer
-  // strides load the rest behind one uniform branch.
-  const int ne = ceil_div(stride, kSpThreads);
-  int ent[G][kListEnt];
-  int cnt[G];
+  int cnt[HPW];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    cnt[h] = sel_count[hrow0 + h];
-    const int32_t* list = sel_idx + (hrow0 + h) * stride;
-#pragma unroll
-    for (int e = 0; e < kListEntMin; ++e) ent[h][e] = list[min(tid + e * kSpThreads, stride - 1)];
-#pragma unroll
-    for (int e = kListEntMin; e < kListEnt; ++e) ent[h][e] = -1;
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + i * kUWaves;
+    cnt[i] = h < G ? max(0, min(sel_count[hrow0 + h], stride)) : 0;
   }
-  if (ne > kListEntMin) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int32_t* list = sel_idx + (hrow0 + h) * stride;
-#pragma unroll
-      for (int e = kListEntMin; e < kListEnt; ++e) ent[h][e] = list[min(tid + e * kSpThreads, stride - 1)];
-    }
-  }
-  const int hq = min(wave, G - 1);
-  const float q0 = q[(hrow0 + hq) * kHeadDim + 2 * lane];
-  const float q1 = q[(hrow0 + hq) * kHeadDim + 2 * lane + 1];
-  // (the loads above are in flight while the context length is read)
   const int n = max(0, min(ctx_lens[b], nlim));
   const int c0 = g * kSegKeys, c1 = min(n, c0 + kSegKeys);
-  if (c0 >= c1) return;  // the combine reads only the segments that exist
+  if (c0 >= c1) return;  // the gather reads only the segments that exist
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) s_bm[h][tid] = 0u;
+  __syncthreads();
+  // each wave marks its heads' entries in [c0, c1): with ascending lists they
+  // sit at positions [lo, hi) of the list; lo entries lie below the segment
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + i * kUWaves;
+    if (h >= G) break;
+    const int32_t* list = sel_idx + (hrow0 + h) * stride;
+    const int2 lh = list_bounds(list, cnt[i], c0, c1, lane);
+    // eight coalesced loads per lane in flight per round
+    for (int p0 = lh.x; p0 < lh.y; p0 += 8 * kWave) {
+      int xs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = p0 + e * kWave + lane;
+        xs[e] = p < lh.y ? list[p] : -1;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (xs[e] >= c0 && xs[e] < c1) atomicOr(&s_bm[h][(xs[e] - c0) >> 5], 1u << (xs[e] & 31));
+    }
+    if (lane == 0) s_lo[h] = lh.x;
+  }
+  __syncthreads();
+  // union words (one per thread), their row counts and the exclusive prefix
+  // (block scan)
+  uint32_t hw[G];
+  uint32_t x = 0u;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int c = max(0, min(cnt[h], stride));
-#pragma unroll
-    for (int e = 0; e < kListEnt; ++e)
-      if (tid + e * kSpThreads >= c) ent[h][e] = -1;
+    hw[h] = s_bm[h][tid];
+    x |= hw[h];
   }
+  const int pc = __popc(x);
+  int incl = pc;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0, off = 0;
+#pragma unroll
+  for (int w = 0; w < kUWaves; ++w) {
+    const int sw = s_wsum[w];
+    before += w < wave ? sw : 0;
+    total += sw;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) off += s_lo[h];
+  // this word's rows, in key order, at the segment's offset plus their rank
+  int2* const dst = urow + (size_t)j * cap + off + (before + incl - pc);
+  int r = 0;
+  while (x) {
+    const int bit = __builtin_ctz(x);
+    x &= x - 1u;
+    int m = 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) m |= (int)((hw[h] >> bit) & 1u) << h;
+    dst[r++] = int2{c0 + tid * 32 + bit, m};
+  }
+  if (tid == 0) {
+    ucnt[(size_t)j * nseg + g] = total;
+    uoff[(size_t)j * nseg + g] = off;
+  }
+}
 
-  for (int i = tid; i < G * kSegWords; i += kSpThreads) (&s_bm[0][0])[i] = 0u;
+template <int G, bool BF16, bool NORMQ, bool NORMK>
+__global__ __launch_bounds__(kGThreads) void sparse_gather(
+    const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int Nmax, int nlim, int nseg, int cap,
+    int C, float scale, float eps, const int2* __restrict__ urow, const int32_t* __restrict__ ucnt,
+    const int32_t* __restrict__ uoff, int32_t* __restrict__ nch, float* __restrict__ part_m,
+    float* __restrict__ part_l, float* __restrict__ part_acc) {
+  constexpr int GP = G < 4 ? 4 : G;
+  constexpr int kAccBytes = kGWaves * G * kHeadDim * 4;
+  constexpr int kTileAll = BF16 ? kGWaves * kKTileBf16 : 0;
+  // the waves' K rows (bf16); at the end, the waves' value sums
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kTileAll > kAccBytes ? kTileAll : kAccBytes];
+  __shared__ __attribute__((aligned(16))) float s_q[G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_p[kGWaves][kWRows][GP];
+  __shared__ float s_mm[kGWaves][G];
+  __shared__ float s_ll[kGWaves][G];
+
+  // chunk-major order: the streams' first chunks, which always hold rows,
+  // are dispatched before later chunks, which may hold none
+  const int S = gridDim.x / C;
+  const int c = blockIdx.x / S, j = blockIdx.x - c * S;
+  const int b = j / Hkv, kvh = j - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ri = lane & (kWRows - 1), half = lane >> 5;  // this lane's row and half of it
+  const size_t hrow0 = (size_t)b * Hq + (size_t)kvh * G;
+  const size_t row0 = (size_t)j * Nmax;
+  // the first 64 segments' counts and offsets are loaded with the context
+  // length (those past the live segments are ignored)
+  const int ua = lane < nseg ? ucnt[(size_t)j * nseg + lane] : 0;
+  const int oa = lane < nseg ? uoff[(size_t)j * nseg + lane] : 0;
+  const int n = max(0, min(ctx_lens[b], nlim));
+  const int nsl = min(nseg, ceil_div(n, kSegKeys));
+
   // the queries in LDS, normalised and scaled by scale * log2(e) (the softmax
-  // runs in base 2: exp(t - m) = exp2(t2 - m2), t2 = t log2 e); wave w < G
-  // prepares head w
-  {
+  // runs in base 2: exp(t - m) = exp2(t2 - m2), t2 = t log2 e)
+  for (int h = wave; h < G; h += kGWaves) {
+    const float q0 = q[(hrow0 + h) * kHeadDim + 2 * lane];
+    const float q1 = q[(hrow0 + h) * kHeadDim + 2 * lane + 1];
     float f = scale * 1.4426950408889634f;
     if constexpr (NORMQ) f = f / sqrtf(wave_sum_dpp(q0 * q0 + q1 * q1) * (1.0f / kHeadDim) + eps);
-    if (wave < G) {
-      s_q[wave][2 * lane] = q0 * f;
-      s_q[wave][2 * lane + 1] = q1 * f;
-    }
+    s_q[h][2 * lane] = q0 * f;
+    s_q[h][2 * lane + 1] = q1 * f;
   }
-  __syncthreads();
+
+  // The chunk's rows are union ranks [r0, r0 + kChunk) of the stream; row r
+  // belongs to the first segment whose inclusive count prefix exceeds r and
+  // sits at that segment's offset plus its rank within the segment. Every
+  // wave scans the segments' counts itself (64 per round).
+  const int r0 = c * kChunk;
+  const int r = r0 + wave * kWRows + ri;  // this lane's row
+  int carry = 0, rslot = -1;  // this row's slot in the union buffer
+  for (int g0 = 0; g0 < nsl; g0 += kWave) {
+    const int g = g0 + lane;
+    int u = g0 == 0 ? ua : (g < nsl ? ucnt[(size_t)j * nseg + g] : 0);
+    const int o = g0 == 0 ? oa : (g < nsl ? uoff[(size_t)j * nseg + g] : 0);
+    u = g < nsl ? u : 0;
+    int incl = u;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
+    }
+    incl += carry;
+    const int tot = __shfl(incl, kWave - 1, kWave);
+    // segments of this round whose inclusive prefix is <= r (every lane runs
+    // the shuffles; rows past this round's total take nothing from it)
+    int pos = 0;
+#pragma unroll
+    for (int st = kWave / 2; st >= 1; st >>= 1) {
+      const int t = __shfl(incl, pos + st - 1, kWave);
+      if (t <= r) pos += st;
+    }
+    const int ip = __shfl(incl, pos, kWave), up = __shfl(u, pos, kWave);
+    const int op = __shfl(o, pos, kWave);
+    if (rslot < 0 && r < tot) rslot = op + (r - (ip - up));
+    carry = tot;
+  }
+  const int U = carry;
+  if (c == 0 && tid == 0) nch[j] = ceil_div(U, kChunk);
+  if (r0 >= U) return;  // the combine reads only the chunks that exist
+  const int nrow = min(kChunk, U - r0);
+  __syncthreads();  // every head's query is in LDS
+
+  // this lane's row (rows past the chunk repeat the wave's last row, with no
+  // heads); a wave with no rows keeps an empty state
+  const int nb = nrow - kWRows * wave;  // rows of this wave (uniform)
+  float m_w[G], l_w[G], acc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int e = 0; e < kListEnt; ++e) {
-      const int x = ent[h][e];
-      if (e < ne && x >= c0 && x < c1) atomicOr(&s_bm[h][(x - c0) >> 5], 1u << (x & 31));
-    }
+    m_w[h] = -INFINITY;
+    l_w[h] = 0.f;
+    acc[h][0] = acc[h][1] = 0.f;
   }
-  __syncthreads();
-  // union words, their row counts and the exclusive prefix (block scan)
-  {
-    uint32_t x = 0u;
-    if (tid < kSegWords) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) x |= s_bm[h][tid];
-      s_u[tid] = x;
-    }
-    const int pc = __popc(x);
-    int incl = pc;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int t = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += t;
-    }
-    if (lane == kWave - 1) s_wsum[wave] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kSpWaves; ++w) {
-      const int sw = s_wsum[w];
-      before += w < wave ? sw : 0;
-      total += sw;
-    }
-    if (tid < kSegWords) s_pre[tid] = before + incl - pc;
-    if (tid == 0) s_pre[kSegWords] = total;
-  }
-  __syncthreads();
-  const int nu = s_pre[kSegWords];
-  const int nbs = ceil_div(nu, kRows);
-
-  // softmax state of this pair: this wave's heads (max in base-2 units, sum)
-  // and this lane's value dim of every head
-  float m_run[HW], l_run[HW], acc[G];
-#pragma unroll
-  for (int i = 0; i < HW; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
-#pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = 0.f;
-  const int vdim = kWave * wv + lane;
-  uint8_t* const ktile = s_ktile + pair * (BF16 ? kTileBytes : 0);
-  uint8_t* const vtile = s_vtile + pair * (BF16 ? kTileBytes : 0);
-
-  for (int r = 0; r < ceil_div(nbs, kPairs); ++r) {
-    const int bq = r * kPairs + pair;
-    const bool active = bq < nbs;  // uniform across the pair
+  if (nb > 0) {
     int key = 0, hb = 0;
-    float vv[BF16 ? 1 : kRows];
-    if (active) {
-      // this lane's row: its word (the last whose prefix is <= the row), its
-      // bit (the row's rank within the word) and its head bits; lanes past
-      // the batch repeat its last row, with no heads
-      const int nb = min(kRows, nu - bq * kRows);
-      const int row = bq * kRows + min(lane, nb - 1);
-      int lo = 0, hi = kSegWords - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= row) lo = mid; else hi = mid - 1;
-      }
-      uint32_t w = s_u[lo];
-      int kth = row - s_pre[lo], bit = 0;
+    if (ri < nb) {
+      const int2 e = urow[(size_t)j * cap + rslot];
+      key = min(max(e.x, 0), n - 1);  // (always in range; kept inside the cache regardless)
+      hb = e.y;
+    }
+    key = ri < nb ? key : __shfl(key, nb - 1, kWave);
+    // V rows -> registers: lane L holds value dims 2L, 2L + 1 of every row
+    uint32_t vb[BF16 ? kWRows : 1];
+    f32x2 vf[BF16 ? 1 : kWRows];
+    uint8_t* const ktile = s_k + (BF16 ? wave * kKTileBf16 : 0);
+    if constexpr (BF16) {
+      // K rows -> LDS: load i moves rows 4i .. 4i+3 (lane L: row 4i + L/16,
+      // 16-byte piece L % 16); piece p of row r lands in slot p ^ (r & 15).
+      // Through plain pointers: the direct-to-LDS builtin called on the
+      // __shared__ arrays themselves makes the host pass drop the kernel's
+      // stub.
+      const uint8_t* kb8 = static_cast<const uint8_t*>(k);
 #pragma unroll
-      for (int half = 16; half > 0; half >>= 1) {
-        const uint32_t low = w & ((1u << half) - 1u);
-        const int c = __popc(low);
-        if (kth >= c) { kth -= c; bit += half; w >>= half; } else { w = low; }
+      for (int i = 0; i < kWRows / 4; ++i) {
+        const int rr = 4 * i + (lane >> 4);
+        const size_t src = (row0 + __shfl(key, rr, kWave)) * (kHeadDim * 2);
+        __builtin_amdgcn_global_load_lds(kb8 + src + (((lane & 15) ^ (rr & 15)) << 4),
+                                         ktile + i * 1024, 16, 0, 0);
       }
-      key = c0 + lo * 32 + bit;
-      if (lane < nb) {
+      const uint32_t* vb32 = static_cast<const uint32_t*>(v);
 #pragma unroll
-        for (int h = 0; h < G; ++h) hb |= (int)((s_bm[h][lo] >> bit) & 1u) << h;
-      }
-      if constexpr (BF16) {
-        // K and V rows -> LDS, each wave of the pair half of them: load i
-        // moves rows 4i .. 4i+3 (lane L: row 4i + L/16, 16-byte piece L % 16).
-        // K piece c of row r lands in slot c ^ (r & 15); V rows keep their
-        // layout. Through plain pointers: the direct-to-LDS builtin called on
-        // the __shared__ arrays themselves makes the host pass drop this
-        // kernel's stub.
-        const uint8_t* kb8 = static_cast<const uint8_t*>(k);
-        const uint8_t* vb8 = static_cast<const uint8_t*>(v);
+      for (int rr = 0; rr < kWRows; ++rr)
+        vb[rr] = vb32[(row0 + __builtin_amdgcn_readlane(key, rr)) * (kHeadDim / 2) + lane];
+    } else {
+      const f32x2* vf2 = static_cast<const f32x2*>(v);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = wv * 8 + u;
-          const int rr = 4 * i + (lane >> 4);
-          const size_t src = (row0 + __shfl(key, rr, kWave)) * (kHeadDim * 2);
-          __builtin_amdgcn_global_load_lds(kb8 + src + (((lane & 15) ^ (rr & 15)) << 4),
-                                           ktile + i * 1024, 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb8 + src + ((lane & 15) << 4), vtile + i * 1024, 16, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < kRows; ++rr)
-          vv[rr] = reinterpret_cast<const float*>(v)[(row0 + __builtin_amdgcn_readlane(key, rr)) * kHeadDim + vdim];
-      }
+      for (int rr = 0; rr < kWRows; ++rr)
+        vf[rr] = vf2[(row0 + __builtin_amdgcn_readlane(key, rr)) * (kHeadDim / 2) + lane];
     }
     if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();  // every pair's K and V rows are in LDS
 
-    if (active) {
-      // scores of this lane's row against this wave's heads
-      float t[HW];
+    // scores of this lane's row against the G heads: each of its two lanes
+    // takes half of the dims, then the halves are added
+    float t[G];
 #pragma unroll
-      for (int i = 0; i < HW; ++i) t[i] = 0.f;
-      float ss = 0.f;
-      if constexpr (BF16) {
-        const uint8_t* myrow = ktile + lane * (kHeadDim * 2);
+    for (int h = 0; h < G; ++h) t[h] = 0.f;
+    float ss = 0.f;
+    if constexpr (BF16) {
+      const uint8_t* myrow = ktile + ri * (kHeadDim * 2);
 #pragma unroll 2
-        for (int c = 0; c < 16; ++c) {
-          const u32x4 pc = *reinterpret_cast<const u32x4*>(myrow + ((c ^ (lane & 15)) << 4));
-          float x[8];
+      for (int i = 0; i < 8; ++i) {
+        const int cc = 8 * half + i;
+        const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((cc ^ (ri & 15)) << 4));
+        float xx[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) { x[2 * e] = bf16_lo(pc[e]); x[2 * e + 1] = bf16_hi(pc[e]); }
-          if constexpr (NORMK) {
+        for (int e = 0; e < 4; ++e) { xx[2 * e] = bf16_lo(pcs[e]); xx[2 * e + 1] = bf16_hi(pcs[e]); }
+        if constexpr (NORMK) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-          }
-#pragma unroll
-          for (int i = 0; i < HW; ++i) {
-            const int h = min(wv * HW + i, G - 1);
-            const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c]);
-            const f32x4 qb4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * c + 4]);
-            t[i] = fmaf(qa4[0], x[0], t[i]);
-            t[i] = fmaf(qa4[1], x[1], t[i]);
-            t[i] = fmaf(qa4[2], x[2], t[i]);
-            t[i] = fmaf(qa4[3], x[3], t[i]);
-            t[i] = fmaf(qb4[0], x[4], t[i]);
-            t[i] = fmaf(qb4[1], x[5], t[i]);
-            t[i] = fmaf(qb4[2], x[6], t[i]);
-            t[i] = fmaf(qb4[3], x[7], t[i]);
-          }
+          for (int e = 0; e < 8; ++e) ss = fmaf(xx[e], xx[e], ss);
         }
-      } else {
-        const f32x4* kr = reinterpret_cast<const f32x4*>(k) + (row0 + key) * (kHeadDim / 4);
-#pragma unroll 2
-        for (int c = 0; c < kHeadDim / 4; ++c) {
-          const f32x4 x = kr[c];
-          if constexpr (NORMK) ss = fmaf(x[0], x[0], fmaf(x[1], x[1], fmaf(x[2], x[2], fmaf(x[3], x[3], ss))));
 #pragma unroll
-          for (int i = 0; i < HW; ++i) {
-            const int h = min(wv * HW + i, G - 1);
-            const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][4 * c]);
-            t[i] = fmaf(qa4[0], x[0], fmaf(qa4[1], x[1], fmaf(qa4[2], x[2], fmaf(qa4[3], x[3], t[i]))));
-          }
+        for (int h = 0; h < G; ++h) {
+          const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * cc]);
+          const f32x4 qb4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * cc + 4]);
+          t[h] = fmaf(qa4[0], xx[0], t[h]);
+          t[h] = fmaf(qa4[1], xx[1], t[h]);
+          t[h] = fmaf(qa4[2], xx[2], t[h]);
+          t[h] = fmaf(qa4[3], xx[3], t[h]);
+          t[h] = fmaf(qb4[0], xx[4], t[h]);
+          t[h] = fmaf(qb4[1], xx[5], t[h]);
+          t[h] = fmaf(qb4[2], xx[6], t[h]);
+          t[h] = fmaf(qb4[3], xx[7], t[h]);
         }
       }
-      float kf = 1.f;
-      if constexpr (NORMK) kf = 1.f / sqrtf(ss * (1.0f / kHeadDim) + eps);
-      // this wave's heads: batch maximum, rescale factor, row weights
+    } else {
+      const f32x4* kr = reinterpret_cast<const f32x4*>(k) + (row0 + key) * (kHeadDim / 4) + 16 * half;
+#pragma unroll 2
+      for (int i = 0; i < 16; ++i) {
+        const int cc = 16 * half + i;
+        const f32x4 xx = kr[i];
+        if constexpr (NORMK) ss = fmaf(xx[0], xx[0], fmaf(xx[1], xx[1], fmaf(xx[2], xx[2], fmaf(xx[3], xx[3], ss))));
 #pragma unroll
-      for (int i = 0; i < HW; ++i) {
-        const int h = wv * HW + i;
-        if (h >= G) break;
-        const bool on = (hb >> h) & 1;
-        const float th = on ? t[i] * kf : -INFINITY;
-        const float bm = wave_max_dpp(th);
-        float pr = 0.f, sc = 1.f;
-        if (bm != -INFINITY) {  // some row of the batch is selected by head h
-          const float mn = fmaxf(m_run[i], bm);
-          sc = exp2f(m_run[i] - mn);  // 0 while m_run is still -inf
-          pr = on ? exp2f(th - mn) : 0.f;
-          l_run[i] = fmaf(l_run[i], sc, wave_sum_dpp(pr));
-          m_run[i] = mn;
+        for (int h = 0; h < G; ++h) {
+          const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][4 * cc]);
+          t[h] = fmaf(qa4[0], xx[0], fmaf(qa4[1], xx[1], fmaf(qa4[2], xx[2], fmaf(qa4[3], xx[3], t[h]))));
         }
-        s_p[pair][lane][h] = pr;
-        if (lane == 0) s_sc[pair][h] = sc;
       }
     }
-    __syncthreads();  // every head's weights and rescale factor are in LDS
-    if (active) {
-      // acc[h] (this lane's dim) = acc[h] * sc[h] + sum_r p[r][h] v[r]
+    // (lower half first, so both lanes of a row hold the same sum)
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] *= s_sc[pair][h];
+    for (int h = 0; h < G; ++h) {
+      const float o = __shfl_xor(t[h], kWRows, kWave);
+      t[h] = half ? o + t[h] : t[h] + o;
+    }
+    float kf = 1.f;
+    if constexpr (NORMK) {
+      const float o = __shfl_xor(ss, kWRows, kWave);
+      ss = half ? o + ss : ss + o;
+      kf = 1.f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    }
+    // per head: the wave's maximum over its rows of the head, their weights
+    // relative to it and their sum (over the lower half's lanes)
 #pragma unroll
-      for (int rr = 0; rr < kRows; ++rr) {
-        float vr;
-        if constexpr (BF16)
-          vr = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(vtile + rr * (kHeadDim * 2))[vdim] << 16);
-        else
-          vr = vv[rr];
-        float pj[G];
-        if constexpr (G >= 4) {
+    for (int h = 0; h < G; ++h) {
+      const bool on = (hb >> h) & 1;
+      const float th = on ? t[h] * kf : -INFINITY;
+      const float mw = wave_max_dpp(th);
+      const float pr = on ? exp2f(th - mw) : 0.f;
+      m_w[h] = mw;
+      l_w[h] = wave_sum_dpp(half ? 0.f : pr);
+      if (!half) s_p[wave][ri][h] = pr;
+    }
+    // acc[h] (this lane's two dims) = sum over the wave's rows of p[r][h] v[r].
+    // A row outside head h's selection never enters its sum: where a value
+    // row is not finite the products with zero weights are skipped (a wave
+    // whose rows are all finite takes the plain loop)
+    bool fin = true;
 #pragma unroll
-          for (int h = 0; h < G; h += 4) {
-            const f32x4 pq = *reinterpret_cast<const f32x4*>(&s_p[pair][rr][h]);
+    for (int rr = 0; rr < kWRows; ++rr) {
+      if constexpr (BF16)  // exponent bits of neither bf16 all ones
+        fin = fin && (vb[rr] & 0x7f80u) != 0x7f80u && (vb[rr] & 0x7f800000u) != 0x7f800000u;
+      else fin = fin && isfinite(vf[rr][0]) && isfinite(vf[rr][1]);
+    }
+    const bool all_fin = __ballot(!fin) == 0;
+    auto accumulate = [&](auto guarded) __attribute__((always_inline)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pj[h + e] = pq[e];
-          }
+      for (int rr = 0; rr < kWRows; ++rr) {
+        float v0, v1;
+        if constexpr (BF16) {
+          v0 = bf16_lo(vb[rr]);
+          v1 = bf16_hi(vb[rr]);
         } else {
+          v0 = vf[rr][0];
+          v1 = vf[rr][1];
+        }
+        float pj[GP];
 #pragma unroll
-          for (int h = 0; h < G; ++h) pj[h] = s_p[pair][rr][h];
+        for (int h = 0; h < GP; h += 4) {
+          const f32x4 pq = *reinterpret_cast<const f32x4*>(&s_p[wave][rr][h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pj[h + e] = pq[e];
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = fmaf(pj[h], vr, acc[h]);
+        for (int h = 0; h < G; ++h) {
+          if constexpr (decltype(guarded)::value) {
+            acc[h][0] = pj[h] != 0.f ? fmaf(pj[h], v0, acc[h][0]) : acc[h][0];
+            acc[h][1] = pj[h] != 0.f ? fmaf(pj[h], v1, acc[h][1]) : acc[h][1];
+          } else {
+            acc[h][0] = fmaf(pj[h], v0, acc[h][0]);
+            acc[h][1] = fmaf(pj[h], v1, acc[h][1]);
+          }
+        }
       }
-    }
-    __syncthreads();  // the next round overwrites the rows and the weights
+    };
+    if (all_fin) accumulate(std::false_type{});
+    else accumulate(std::true_type{});
   }
 
-  // merge the pairs' states in pair order into the segment's partial
-  float* const s_acc = reinterpret_cast<float*>(s_ktile);  // [pair][head][dim]
+  // merge the waves' states in wave order into the chunk's partial
+  __syncthreads();  // every wave is done with its K rows (s_acc aliases them)
+  float* const s_acc = reinterpret_cast<float*>(s_k);  // [wave][head][dim]
 #pragma unroll
-  for (int h = 0; h < G; ++h) s_acc[(pair * G + h) * kHeadDim + vdim] = acc[h];
-#pragma unroll
-  for (int i = 0; i < HW; ++i) {
-    const int h = wv * HW + i;
-    if (h < G && lane == 0) {
-      s_mm[pair][h] = m_run[i];
-      s_ll[pair][h] = l_run[i];
+  for (int h = 0; h < G; ++h) {
+    *reinterpret_cast<f32x2*>(&s_acc[(wave * G + h) * kHeadDim + 2 * lane]) = f32x2{acc[h][0], acc[h][1]};
+    if (lane == 0) {
+      s_mm[wave][h] = m_w[h];
+      s_ll[wave][h] = l_w[h];
     }
   }
   __syncthreads();
-  const size_t slot = (size_t)j * nseg + g;
-  for (int e = tid; e < G * kHeadDim; e += kSpThreads) {
+  const size_t slot = (size_t)j * C + c;
+  for (int e = tid; e < G * kHeadDim; e += kGThreads) {
     const int h = e / kHeadDim, d = e - h * kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int p = 0; p < kPairs; ++p) M = fmaxf(M, s_mm[p][h]);
+    for (int w = 0; w < kGWaves; ++w) M = fmaxf(M, s_mm[w][h]);
     float a = 0.f, ls = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int p = 0; p < kPairs; ++p) {
-        const float mp = s_mm[p][h];
+      for (int w = 0; w < kGWaves; ++w) {
+        const float mp = s_mm[w][h];
         const float f = mp == -INFINITY ? 0.f : exp2f(mp - M);
-        a = fmaf(f, s_acc[(p * G + h) * kHeadDim + d], a);
-        ls = fmaf(f, s_ll[p][h], ls);
+        a = fmaf(f, s_acc[(w * G + h) * kHeadDim + d], a);
+        ls = fmaf(f, s_ll[w][h], ls);
       }
     }
     part_acc[(slot * G + h) * kHeadDim + d] = a;
     if (d == 0) {
-      part_m[slot * G + h] = M;  // -inf: head h selects no key of the segment
+      part_m[slot * G + h] = M;  // -inf: head h selects no row of the chunk
       part_l[slot * G + h] = ls;
     }
   }
 }
 
-// out[b][h] = sum_g 2^(m_g - M) acc_g / sum_g 2^(m_g - M) l_g over the
-// segments g of the sequence, in segment order (the maxima are in base-2
-// units); 0 for an empty selection. The segment maxima are staged in LDS so
-// that the loads of all segments are in flight together.
+// out[b][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c over the chunks
+// c of the stream, in chunk order (the maxima are in base-2 units); 0 for an
+// empty selection. The chunk maxima are staged in LDS so that the loads of all
+// chunks are in flight together.
 constexpr int kCmbChunk = 256;
 
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
-    const float* __restrict__ part_acc, const int32_t* __restrict__ ctx_lens, int Hq, int Hkv,
-    int nlim, int nseg, float* __restrict__ out) {
+    const float* __restrict__ part_acc, const int32_t* __restrict__ nch, int Hq, int Hkv, int C,
+    float* __restrict__ out) {
   __shared__ float s_mm[kCmbChunk];
   __shared__ float s_ll[kCmbChunk];
   __shared__ float s_red[kHeadDim];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
-  const int n = max(0, min(ctx_lens[b], nlim));
-  const int pb = min(ceil_div(n, kSegKeys), nseg);
-  const size_t s0 = ((size_t)b * Hkv + kvh) * nseg;
-  // global maximum over the segments
+  const int j = b * Hkv + kvh;
+  const int pb = min(nch[j], C);
+  const size_t s0 = (size_t)j * C;
+  // global maximum over the chunks
   float M = -INFINITY;
   for (int p = d; p < pb; p += kHeadDim) M = fmaxf(M, part_m[(s0 + p) * G + jh]);
   s_red[d] = M;
@@ -428,31 +505,51 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(
   out[((size_t)b * Hq + h) * kHeadDim + d] = ls > 0.f ? a / ls : 0.f;
 }
 
-// Workspace: one (max, sum, weighted values) partial per (stream, segment, head).
+// Workspace: the union rows (G * stride slots per stream), the segments'
+// counts and offsets, the chunk count per stream, and one (max, sum, weighted
+// values) partial per (stream, chunk, head).
 struct SpLayout {
-  size_t m, l, acc, total;
-  int nseg;
+  size_t urow, ucnt, uoff, nch, m, l, acc, total;
+  int nseg, cap, C;
 };
 
-SpLayout sp_layout(int B, int Hq, int Hkv, int max_ctx) {
+SpLayout sp_layout(int B, int Hq, int Hkv, int max_ctx, int stride) {
   SpLayout s;
-  s.nseg = ceil_div(max_ctx, kSegKeys);
-  const size_t slots = (size_t)B * Hkv * s.nseg;
   const int G = Hkv > 0 ? Hq / Hkv : 0;
-  s.m = 0;
-  s.l = align_up(slots * G * sizeof(float), 256);
-  s.acc = s.l + align_up(slots * G * sizeof(float), 256);
-  s.total = s.acc + align_up(slots * G * kHeadDim * sizeof(float), 256);
+  const size_t S = (size_t)B * Hkv;
+  s.nseg = ceil_div(max_ctx, kSegKeys);
+  s.cap = G * stride;
+  // a stream's union holds at most min(G * stride, max_ctx) rows
+  s.C = std::max(1, ceil_div(std::min(s.cap, max_ctx), kChunk));
+  size_t o = 0;
+  s.urow = o; o += align_up(S * s.cap * sizeof(int2), 256);
+  s.ucnt = o; o += align_up(S * s.nseg * sizeof(int32_t), 256);
+  s.uoff = o; o += align_up(S * s.nseg * sizeof(int32_t), 256);
+  s.nch = o; o += align_up(S * sizeof(int32_t), 256);
+  const size_t slots = S * s.C * G;
+  s.m = o; o += align_up(slots * sizeof(float), 256);
+  s.l = o; o += align_up(slots * sizeof(float), 256);
+  s.acc = o; o += align_up(slots * kHeadDim * sizeof(float), 256);
+  s.total = o;
   return s;
 }
 
 template <int G, bool BF16, bool NORMQ, bool NORMK>
 void launch_t(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_t stream) {
-  hipLaunchKernelGGL((sparse_kernel<G, BF16, NORMQ, NORMK>), dim3(a.B * a.Hkv * s.nseg),
-                     dim3(kSpThreads), 0, stream, a.q, a.k, a.v, a.ctx_lens, a.sel_idx,
-                     a.sel_count, a.sel_stride, a.Hq, a.Hkv, a.Nmax, std::min(a.Nmax, a.max_ctx),
-                     s.nseg, a.scale, a.eps, reinterpret_cast<float*>(ws + s.m),
-                     reinterpret_cast<float*>(ws + s.l), reinterpret_cast<float*>(ws + s.acc));
+  const int S = a.B * a.Hkv;
+  const int nlim = std::min(a.Nmax, a.max_ctx);
+  int2* urow = reinterpret_cast<int2*>(ws + s.urow);
+  int32_t* ucnt = reinterpret_cast<int32_t*>(ws + s.ucnt);
+  int32_t* uoff = reinterpret_cast<int32_t*>(ws + s.uoff);
+  if (s.nseg > 0)
+    hipLaunchKernelGGL((sparse_union<G>), dim3(S * s.nseg), dim3(kUThreads), 0, stream, a.ctx_lens,
+                       a.sel_idx, a.sel_count, a.sel_stride, a.Hq, a.Hkv, nlim, s.nseg, s.cap, urow,
+                       ucnt, uoff);
+  hipLaunchKernelGGL((sparse_gather<G, BF16, NORMQ, NORMK>), dim3(S * s.C), dim3(kGThreads), 0,
+                     stream, a.q, a.k, a.v, a.ctx_lens, a.Hq, a.Hkv, a.Nmax, nlim, s.nseg, s.cap,
+                     s.C, a.scale, a.eps, urow, ucnt, uoff, reinterpret_cast<int32_t*>(ws + s.nch),
+                     reinterpret_cast<float*>(ws + s.m), reinterpret_cast<float*>(ws + s.l),
+                     reinterpret_cast<float*>(ws + s.acc));
 }
 
 template <int G>
@@ -470,8 +567,8 @@ void launch_g(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_
 }  // namespace
 
 // Device-resident scratch of ssa_decode_sparse_static, for callers that cannot
-// allocate: the per-(stream, segment, head) softmax partials live here instead
-// of in a caller-provided workspace. Every GPU that runs the library holds its
+// allocate: the union rows and the per-(stream, chunk, head) softmax partials
+// live here instead of in a caller-provided workspace. Every GPU that runs the library holds its
 // own copy until the process ends. Host code never passes the array's name to a
 // kernel (on the host it is only a stand-in for the symbol): its device address
 // is looked up once per device with hipGetSymbolAddress and kept.
@@ -511,30 +608,28 @@ hipError_t launch_decode_sparse_static(const DecodeSparseArgs& a, hipStream_t st
   return launch_decode_sparse(b, stream);
 }
 
-size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int) {
-  return sp_layout(B, Hq, Hkv, max_ctx).total;
+size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int stride) {
+  return sp_layout(B, Hq, Hkv, max_ctx, stride).total;
 }
 
 hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream) {
-  if (a.sel_stride > kListEnt * kSpThreads) return hipErrorInvalidValue;
+  if (a.sel_stride > kMaxStride) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
-  const SpLayout s = sp_layout(a.B, a.Hq, a.Hkv, a.max_ctx);
+  const SpLayout s = sp_layout(a.B, a.Hq, a.Hkv, a.max_ctx, a.sel_stride);
   char* ws = static_cast<char*>(a.ws);
-  if (s.nseg > 0) {
-    switch (G) {
-      case 1: launch_g<1>(a, s, ws, stream); break;
-      case 2: launch_g<2>(a, s, ws, stream); break;
-      case 4: launch_g<4>(a, s, ws, stream); break;
-      case 8: launch_g<8>(a, s, ws, stream); break;
-      default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  switch (G) {
+    case 1: launch_g<1>(a, s, ws, stream); break;
+    case 2: launch_g<2>(a, s, ws, stream); break;
+    case 4: launch_g<4>(a, s, ws, stream); break;
+    case 8: launch_g<8>(a, s, ws, stream); break;
+    default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sparse_combine, dim3(a.Hq, a.B), dim3(kHeadDim), 0, stream,
                      reinterpret_cast<float*>(ws + s.m), reinterpret_cast<float*>(ws + s.l),
-                     reinterpret_cast<float*>(ws + s.acc), a.ctx_lens, a.Hq, a.Hkv,
-                     std::min(a.Nmax, a.max_ctx), s.nseg, a.out);
+                     reinterpret_cast<float*>(ws + s.acc), reinterpret_cast<int32_t*>(ws + s.nch),
+                     a.Hq, a.Hkv, s.C, a.out);
   return hipGetLastError();
 }
 

@@ -255,6 +255,40 @@ def test_sparse_largest_stride():
     check_sparse(wl, sels, stride=4096)
 
 
+def test_sparse_segment_gaps_and_chunk_edges():
+    """Unions laid out over 32768-key segments and 256-row chunks: a segment
+    with no selected key between two that have some, runs of 257 and 300 rows
+    so that chunk boundaries fall inside segments, a lone key in the last
+    (partial) segment, heads with an empty selection and one whose count is
+    -1 (the fused call's mark of a failed row), which select nothing."""
+    wl = synth.make_workload("spgaps", seed=41, batch=2, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[100000, 33000], kv_capacity=100000, recipe="planted", p=0.05)
+    rng = np.random.default_rng(41)
+    sels = []
+    for b in range(2):
+        n = int(wl.ctx_lens[b])
+        row = []
+        for h in range(16):
+            if b == 0:
+                a = np.sort(rng.choice(32768, 257, replace=False))            # segment 0
+                c = 65536 + np.sort(rng.choice(32768, 300, replace=False))    # segment 2
+                s = np.concatenate([a, c, [n - 1]]) if h % 8 < 4 else c[: 37 * (h % 8) * (h != 15)]
+            else:
+                s = np.sort(rng.choice(n, 700 + 29 * h, replace=False)) if h not in (3, 12) else []
+            row.append(np.asarray(s, dtype=np.int64))
+        sels.append(row)
+    qs = wl.q_sparse[0]
+    cache = ssa.cache_from_workload(wl, DEV)
+    si, sc = sel_tensors(sels, 2, 16, 1152)
+    sc[1, 12] = -1
+    out = ssa.ssa_decode_sparse(torch.from_numpy(qs).to(DEV), cache, si, sc)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref = O.decode_sparse(qs, wl.k, wl.v, sels)
+    assert_rows_close(out, ref, TOL_BF16, wl.name)
+    assert np.all(out[1, 3] == 0.0) and np.all(out[1, 12] == 0.0) and np.all(out[0, 15] == 0.0)
+
+
 def test_block_step_sampled_full_size():
     """The batch-8 64K-128K workload end to end: full layer -> selection -> sparse layer.
 

@@ -60,10 +60,11 @@ def test_static_matches_workspace_call_twice_shrinking():
 
 
 def test_static_refuses_partials_beyond_the_scratch():
-    # 32 sequences x 16 heads x 64 segments of 8192 keys: 4 * 130 * 32 * 16 * 64 bytes
-    # = 17 MB of partials, more than the 16 MiB scratch; nothing is launched, so
-    # the cache only has to exist (one row per sequence) for the call to be judged
-    B, Hq, Hkv = 32, 16, 2
+    # 64 sequences x 2 KV groups of 8 heads, stride 1152: 128 groups x (8 x 9216
+    # union slots of 8 bytes + 36 chunks x 8 heads x 130 floats) = 28.6 MB of
+    # workspace, more than the 16 MiB scratch; nothing is launched, so the cache
+    # only has to exist (one row per sequence) for the call to be judged
+    B, Hq, Hkv = 64, 16, 2
     k = torch.zeros((B, Hkv, 1, 128), dtype=torch.bfloat16, device=DEV)
     cache = ssa.Cache(k=k, v=k, ctx_lens=torch.ones(B, dtype=torch.int32, device=DEV),
                       max_ctx_len=1)
