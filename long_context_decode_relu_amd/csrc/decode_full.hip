@@ -1795,29 +1795,105 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   if (threadIdx.x == 0 && *fail) sel_count[row] = -1;
 }
 
-// Rows whose candidate lists cannot decide their selection, rescored. For
-// each stream (sequence, KV head) the work-group decides which of the G rows
-// the combine's list selection would reject: fewer listed keys with a positive
-// score than k, or more list entries or slots than that selection holds. It
-// writes row_flag for every row and, for flagged rows, rescores slice s of the
-// stream's 64-key tiles: each wave copies its tiles into LDS as the full-layer
-// kernel does and scores every key exactly as it does (score_row: same
-// widening, FMA order and query factors) into the row's buffer of `max_ctx`
-// floats. The combine then selects flagged rows from the buffers. Work items
-// (stream, slice) are numbered stream first, so a work-group of the persistent
-// grid usually keeps one stream and decides it once.
+// Rows whose candidate lists cannot decide their selection: one wave per
+// stream (sequence, KV head) decides which of its G rows the combine's list
+// selection would reject, by the tests that selection makes: fewer listed
+// keys with a positive score than k, or more list entries or slots than it
+// holds. It writes row_flag for the G rows and the stream's mask (one bit per
+// head) for the rescoring kernel.
+__global__ __launch_bounds__(256) void decode_full_decide(
+    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
+    const int* __restrict__ tile_pre, const int32_t* __restrict__ ctx_lens, int S, int W, int G,
+    int Hq, int Hkv, int max_ctx, int k_top, int n_recent, int disjoint,
+    int32_t* __restrict__ row_flag, int32_t* __restrict__ fmask) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= S) return;
+  const int b = j / Hkv, kvh = j - b * Hkv;
+  const int n = live_keys(ctx_lens, b, max_ctx);
+  const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
+  const int p0 = s1 > s0 ? j + wave_of_tile(s0, W, T) : 0;
+  const int p1 = s1 > s0 ? j + wave_of_tile(s1 - 1, W, T) + 1 : 0;
+  int E = 0, emax = 0;
+  int nz[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // two slots per lane in one round of loads (more slots loop)
+  for (int pb = p0; pb < p1; pb += 2 * kWave) {
+    int cc[2];
+    int4 za[2], zb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p = pb + u * kWave + lane;
+      const bool in = p < p1;
+      cc[u] = in ? cand_cnt[p] : 0;
+      za[u] = zb[u] = int4{0, 0, 0, 0};
+      if (in) {
+        if (G == 8) {
+          za[u] = reinterpret_cast<const int4*>(part_nnz)[(size_t)p * 2];
+          zb[u] = reinterpret_cast<const int4*>(part_nnz)[(size_t)p * 2 + 1];
+        } else if (G == 4) {
+          za[u] = reinterpret_cast<const int4*>(part_nnz)[p];
+        } else {
+          za[u].x = part_nnz[(size_t)p * G];
+          if (G == 2) za[u].y = part_nnz[(size_t)p * G + 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      E += cc[u];
+      emax = max(emax, cc[u]);
+      nz[0] += za[u].x; nz[1] += za[u].y; nz[2] += za[u].z; nz[3] += za[u].w;
+      nz[4] += zb[u].x; nz[5] += zb[u].y; nz[6] += zb[u].z; nz[7] += zb[u].w;
+    }
+  }
+  E = wave_sum_i(E);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, kWave));
+  const int pool = disjoint ? max(0, n - n_recent) : n;
+  const int kk = min(k_top, pool);
+  // keys of the recent window are not in the pool of a disjoint selection
+  const int outside = disjoint ? min(n_recent, n) : 0;
+  // the fast path takes up to 16*16 slots of survivor lists of at most 64
+  // entries; otherwise the general path, which holds 2 np + 1 slot words and
+  // kSelThreads * kGatherPer entries
+  const int np = p1 - p0;
+  const bool fast = n > kCandAll && np <= kSelWaves * kFastRounds && emax <= kWave;
+  const bool too_big = !fast && (2 * np + 1 > kSegWords || E > kSelThreads * kGatherPer);
+  uint32_t fm = 0;
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    if (h >= G) break;
+    const int c = n <= kCandAll ? pool : wave_sum_i(nz[h]) - outside;
+    const bool f = kk < pool && (too_big || c < kk);
+    fm |= f ? 1u << h : 0u;
+    if (lane == 0) row_flag[b * Hq + kvh * G + h] = f ? 1 : 0;
+  }
+  if (lane == 0) fmask[j] = (int32_t)fm;
+}
+
+// The flagged rows rescored. Every work-group reads the streams' masks,
+// keeps a bitmap of the streams with a flagged row in LDS, and takes its share
+// of the work items (flagged stream, slice of its 64-key tiles): each wave
+// copies its tiles into LDS as the full-layer kernel does and scores every key
+// exactly as it does (score_row: same widening, FMA order and query factors)
+// into the flagged rows' buffers of `max_ctx` floats. The combine then
+// selects those rows from the buffers. With nothing flagged every work-group
+// exits after one load.
 constexpr int kFallbackBlocks = 256;
 constexpr int kFallbackSlices = 64;
 
 template <int G, bool BF16, bool NORMK>
 __global__ __launch_bounds__(kThreads) void decode_full_rescore(
     const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
-    const int* __restrict__ tile_pre, int S, int W, int k_top, int n_recent, int disjoint,
-    int32_t* __restrict__ row_flag, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
+    const int32_t* __restrict__ fmask, int S, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
     float eps, int normq, float* __restrict__ rs) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
-  __shared__ int s_red[kWaves][2 + G];
+  __shared__ int s_red[kWaves];
+  __shared__ int s_carry;
+  extern __shared__ uint32_t s_dyn[];  // bitmap of streams with a flagged row, then its word prefix
+  const int nw = ceil_div(S, 32);
+  uint32_t* const s_fw = s_dyn;
+  int* const s_fpre = reinterpret_cast<int*>(s_dyn + nw);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1825,74 +1901,56 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
   const uint32_t tile_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)my_tile);
   constexpr size_t kRowBytes = kHeadDim * (BF16 ? 2 : 4);
   const TileOffsets toff(lane);
-  const int T = tile_pre[S];
-  int jd = -1;     // the stream decided last
-  uint32_t fm = 0; // its flagged rows, one bit per head
-  for (int it = blockIdx.x; it < S * kFallbackSlices; it += gridDim.x) {
-    const int j = it % S, sl = it / S;
+  for (int i = tid; i < nw; i += kThreads) s_fw[i] = 0u;
+  __syncthreads();
+  int any = 0;
+  for (int j = tid; j < S; j += kThreads)
+    if (fmask[j]) {
+      atomicOr(&s_fw[j >> 5], 1u << (j & 31));
+      any = 1;
+    }
+  if (!__syncthreads_or(any)) return;  // nothing flagged
+  // exclusive prefix of the bitmap words' counts (block scan, kThreads at a time)
+  if (tid == 0) s_carry = 0;
+  for (int w0 = 0; w0 < nw; w0 += kThreads) {
+    __syncthreads();
+    const int i = w0 + tid;
+    const int c = i < nw ? __popc(s_fw[i]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
+    }
+    if (lane == kWave - 1) s_red[wave] = incl;
+    __syncthreads();
+    int before = s_carry, total = s_carry;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      before += x < wave ? s_red[x] : 0;
+      total += s_red[x];
+    }
+    if (i < nw) s_fpre[i] = before + incl - c;
+    __syncthreads();
+    if (tid == 0) s_carry = total;
+  }
+  __syncthreads();
+  const int F = s_carry;  // streams with a flagged row
+  for (int it = blockIdx.x; it < F * kFallbackSlices; it += gridDim.x) {
+    const int f = it / kFallbackSlices, sl = it - f * kFallbackSlices;
+    // the f-th flagged stream: its bitmap word, then its bit within the word
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_fpre[mid] <= f) lo = mid; else hi = mid - 1;
+    }
+    uint32_t x = s_fw[lo];
+    for (int r = f - s_fpre[lo]; r > 0; --r) x &= x - 1u;
+    const int j = __builtin_amdgcn_readfirstlane(lo * 32 + __builtin_ctz(x));
+    const uint32_t fm = (uint32_t)__builtin_amdgcn_readfirstlane(fmask[j]);
     const int b = j / Hkv, kvh = j - b * Hkv;
     const int row0 = b * Hq + kvh * G;  // the group's first row
     const int n = __builtin_amdgcn_readfirstlane(live_keys(ctx_lens, b, max_ctx));
-    if (j != jd) {
-      jd = j;
-      const int s0 = tile_pre[j], s1 = tile_pre[j + 1];
-      const int p0 = s1 > s0 ? j + wave_of_tile(s0, W, T) : 0;
-      const int p1 = s1 > s0 ? j + wave_of_tile(s1 - 1, W, T) + 1 : 0;
-      int E = 0, emax = 0;
-      int nz[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) nz[h] = 0;
-      for (int p = p0 + tid; p < p1; p += kThreads) {
-        const int cc = cand_cnt[p];
-        E += cc;
-        emax = max(emax, cc);
-#pragma unroll
-        for (int h = 0; h < G; ++h) nz[h] += part_nnz[(size_t)p * G + h];
-      }
-      E = wave_sum_i(E);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, kWave));
-#pragma unroll
-      for (int h = 0; h < G; ++h) nz[h] = wave_sum_i(nz[h]);
-      __syncthreads();  // the previous decision's reads are done
-      if (lane == 0) {
-        s_red[wave][0] = E;
-        s_red[wave][1] = emax;
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_red[wave][2 + h] = nz[h];
-      }
-      __syncthreads();
-      E = 0;
-      emax = 0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) nz[h] = 0;
-#pragma unroll
-      for (int x = 0; x < kWaves; ++x) {
-        E += s_red[x][0];
-        emax = max(emax, s_red[x][1]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) nz[h] += s_red[x][2 + h];
-      }
-      const int pool = disjoint ? max(0, n - n_recent) : n;
-      const int kk = min(k_top, pool);
-      // keys of the recent window are not in the pool of a disjoint selection
-      const int outside = disjoint ? min(n_recent, n) : 0;
-      // the fast path takes up to 16*16 slots of survivor lists of at most 64
-      // entries; otherwise the general path, which holds 2 np + 1 slot words
-      // and kSelThreads * kGatherPer entries
-      const int np = p1 - p0;
-      const bool fast = n > kCandAll && np <= kSelWaves * kFastRounds && emax <= kWave;
-      const bool too_big = !fast && (2 * np + 1 > kSegWords || E > kSelThreads * kGatherPer);
-      fm = 0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int c = n <= kCandAll ? pool : nz[h] - outside;
-        if (kk < pool && (too_big || c < kk)) fm |= 1u << h;
-      }
-      fm = __builtin_amdgcn_readfirstlane(fm);
-    }
-    if (sl == 0 && tid < G) row_flag[row0 + tid] = (fm >> tid) & 1u;
-    if (fm == 0) continue;
     const float* qrow = q + (size_t)row0 * kHeadDim;
     float fac[G];
     {
@@ -1949,7 +2007,7 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
 struct WsLayout {
   size_t num, den, nnz, vrows, tile_pre, qhi, invc, total;
   // the fused selection: candidate lists and counts, row flags, rescored rows
-  size_t cand_idx, cand_sc, cand_cnt, flag, fail, rescored, total_sel;
+  size_t cand_idx, cand_sc, cand_cnt, flag, fail, fmask, rescored, total_sel;
 };
 
 WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
@@ -1973,6 +2031,7 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   l.cand_cnt = o; o += align_up(slots * sizeof(int32_t), 256);
   l.flag = o; o += align_up(rows * sizeof(int32_t), 256);
   l.fail = o; o += align_up(rows * sizeof(int32_t), 256);
+  l.fmask = o; o += align_up(S * sizeof(int32_t), 256);
   l.rescored = o; o += align_up(rows * (size_t)max_ctx * sizeof(float), 256);
   l.total_sel = o;
   return l;
@@ -2138,18 +2197,26 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   const int disjoint = (s.sel_flags & SSA_SELECT_DISJOINT) ? 1 : 0;
   int grid = 0;
   // 1. filter inputs; 2. the full layer with its candidate lists; 3. per
-  // stream, the rows the lists cannot select flagged and rescored; 4. combine
-  // and selection, one work-group per row
+  // stream, the rows the lists cannot select flagged; 4. those rows rescored;
+  // 5. combine and selection, one work-group per row
   hipError_t e = launch_qprep(a, l, L, stream);
   if (e != hipSuccess) return e;
   e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
+  const int S = a.B * a.Hkv;
+  int32_t* fmask = reinterpret_cast<int32_t*>(ws + l.fmask);
+  hipLaunchKernelGGL(decode_full_decide, dim3(ceil_div(S, 4)), dim3(256), 0, stream, L.cand_cnt,
+                     L.nnz, L.tile_pre, a.ctx_lens, S, grid * kWaves, G, a.Hq, a.Hkv, a.max_ctx,
+                     s.k_top, s.n_recent, disjoint, row_flag, fmask);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the rescoring kernel's LDS bitmap of streams and its word prefix
+  const size_t dyn = 2 * (size_t)ceil_div(S, 32) * sizeof(uint32_t);
   e = dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
-    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kThreads), 0,
-                       stream, a.q, a.k, a.ctx_lens, L.cand_cnt, L.nnz, L.tile_pre, a.B * a.Hkv,
-                       grid * kWaves, s.k_top, s.n_recent, disjoint, row_flag, a.Hq, a.Hkv,
-                       a.Nmax, a.max_ctx, a.scale, a.eps, L.normq, rescored);
+    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kThreads), dyn,
+                       stream, a.q, a.k, a.ctx_lens, fmask, S, a.Hq, a.Hkv, a.Nmax, a.max_ctx,
+                       a.scale, a.eps, L.normq, rescored);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
