@@ -199,6 +199,27 @@ ssa_status ssa_decode_sparse_static(const ssa_shape* shape, const float* q, cons
                                     int32_t sel_stride, float scale, float eps, uint32_t flags,
                                     float* out, void* stream);
 
+/* Cache write: the keys and values of new tokens into the full-layer cache
+ * ("Sevren Sparse Attention learns to be sparse": the score uses the
+ * RMS-normalised key, and normalising a key needs that key alone, so it is
+ * done once as the key enters the cache; "KV bridge, KV reuse, and prefill":
+ * the cache grows by one row per token).
+ *
+ *   k_new, v_new [B, Hkv, T, D] float32 (T = n_tokens >= 0); pos0 [B] device int32.
+ *   Token t of sequence b goes to cache row r = pos0[b] + t of every KV head:
+ *     k[b,kvh,r] = round(k_new[b,kvh,t] / sqrt(mean(k_new[b,kvh,t]^2) + eps))   (SSA_NORM_K)
+ *                  round(k_new[b,kvh,t])                                        (flags = 0)
+ *     v[b,kvh,r] = round(v_new[b,kvh,t])
+ *   round() is the cache's storage type: float32 as computed, bf16 to nearest
+ *   with ties to even. Rows r outside [0, kv_capacity) are not written. No
+ *   other cache row is touched, and ctx_lens is not changed: the caller
+ *   advances it. With SSA_NORM_K the stored keys are the "stored normalised"
+ *   keys the decode entry points expect when SSA_NORM_K is not passed to them.
+ * Only SSA_NORM_K is accepted in flags. Requires eps >= 0. No workspace. */
+ssa_status ssa_cache_write(const ssa_shape* shape, const float* k_new, const float* v_new,
+                           int32_t n_tokens, const int32_t* pos0, float eps, uint32_t flags,
+                           void* k, void* v, void* stream);
+
 /* Causal ReLU^2 prefill of a chunk of Tq prompt queries ("KV bridge, KV reuse,
  * and prefill"; weights as in ssa_decode_full).
  *

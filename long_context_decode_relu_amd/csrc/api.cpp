@@ -330,4 +330,31 @@ ssa_status ssa_prefill_full(const ssa_shape* s, const void* q, int32_t n_query,
   return from_hip(launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+ssa_status ssa_cache_write(const ssa_shape* s, const float* k_new, const float* v_new,
+                           int32_t n_tokens, const int32_t* pos0, float eps, uint32_t flags,
+                           void* k, void* v, void* stream) {
+  const ssa_status st = check_shape(s, false);
+  if (st != SSA_OK) return st;
+  if (n_tokens < 0) return SSA_ERR_SHAPE;
+  if (!finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
+  if (flags & ~(uint32_t)(SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  if (s->batch == 0 || n_tokens == 0) return SSA_OK;
+  if (!k_new || !v_new || !pos0 || !k || !v) return SSA_ERR_NULL;
+  if ((int64_t)s->batch * s->n_kv_heads * n_tokens > (int64_t)1 << 30) return SSA_ERR_SHAPE;
+  CacheWriteArgs a;
+  a.B = s->batch;
+  a.Hkv = s->n_kv_heads;
+  a.Nmax = s->kv_capacity;
+  a.T = n_tokens;
+  a.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos0 = pos0;
+  a.eps = eps;
+  a.flags = flags;
+  a.k = k;
+  a.v = v;
+  return from_hip(launch_cache_write(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -75,6 +75,18 @@ hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream);
 // ignored); hipErrorInvalidValue when the partials would not fit in it.
 hipError_t launch_decode_sparse_static(const DecodeSparseArgs& a, hipStream_t stream);
 
+struct CacheWriteArgs {
+  int B, Hkv, Nmax, T, kv_bf16;
+  const float* k_new;  // [B, Hkv, T, D]
+  const float* v_new;
+  const int32_t* pos0;  // [B]: token t of sequence b goes to row pos0[b] + t
+  float eps;
+  uint32_t flags;
+  void* k;
+  void* v;
+};
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+
 struct PrefillArgs {
   int B, Hq, Hkv, Nmax, max_ctx, Tq;
   const void* q;

@@ -42,7 +42,7 @@ SSA_OP_DECODE_FULL_SELECT = 4
 
 EXPORTED = ("ssa_abi_version", "ssa_status_string", "ssa_workspace_bytes", "ssa_decode_full",
             "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse",
-            "ssa_decode_sparse_static", "ssa_prefill_full")
+            "ssa_decode_sparse_static", "ssa_prefill_full", "ssa_cache_write")
 
 # bytes of device scratch the library holds for ssa_decode_sparse_static
 SSA_STATIC_SCRATCH_BYTES = 16 << 20
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.ssa_decode_sparse_static.argtypes = [SP, P, P, P, P, P, P, I32, F, F, U32, P, P]
         L.ssa_prefill_full.restype = I32
         L.ssa_prefill_full.argtypes = [SP, P, I32, P, P, P, P, F, F, F, U32, P, P, SZ, P]
+        L.ssa_cache_write.restype = I32
+        L.ssa_cache_write.argtypes = [SP, P, P, I32, P, F, U32, P, P, P]
         _lib = L
     return _lib
 
@@ -295,6 +297,28 @@ def ssa_decode_sparse_static(q: torch.Tensor, cache: Cache, sel_idx: torch.Tenso
                                         _stream(q.device))
     _check(st, "ssa_decode_sparse_static")
     return out
+
+
+def ssa_cache_write(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch.Tensor, *,
+                    eps: float = 1e-6, flags: int = SSA_NORM_K) -> None:
+    """Write the new tokens' keys and values into ``cache`` (in place).
+
+    k_new, v_new [B, Hkv, T, D] float32; token t of sequence b goes to row pos0[b] + t.
+    With SSA_NORM_K (default) each key is RMS-normalised as it is stored. ctx_lens is
+    not changed.
+    """
+    cache.check()
+    _need(k_new.is_cuda and k_new.dtype == torch.float32 and k_new.dim() == 4 and k_new.is_contiguous(),
+          "k_new must be contiguous float32 [B, Hkv, T, D]")
+    _need(v_new.shape == k_new.shape and v_new.dtype == torch.float32 and v_new.is_contiguous(),
+          "v_new must match k_new")
+    B, Hkv, T, D = k_new.shape
+    _need((B, Hkv, D) == (cache.k.shape[0], cache.k.shape[1], cache.k.shape[3]), "k_new does not match the cache")
+    _need(pos0.dtype == torch.int32 and pos0.shape == (B,) and pos0.is_contiguous(), "pos0 must be int32 [B]")
+    shp = cache.shape(Hkv)
+    st = lib().ssa_cache_write(ctypes.byref(shp), _ptr(k_new), _ptr(v_new), T, _ptr(pos0), eps, flags,
+                               _ptr(cache.k), _ptr(cache.v), _stream(k_new.device))
+    _check(st, "ssa_cache_write")
 
 
 def ssa_prefill_full(q: torch.Tensor, q_pos0: torch.Tensor, cache: Cache, *, scale: float = 1.0,

@@ -266,3 +266,52 @@ def prefill_full(q, k, v, q_pos0, scale: float = 1.0, c: float = 1.0,
         qt = rms_normalize(q[b, h, t], eps) if flags & SSA_NORM_Q else q[b, h, t]
         out[b, h, t] = relu2_attend(qt, keys, v[b, kvh, :last], scale, c)[0]
     return out
+
+
+# --------------------------------------------------------------------------
+# cache write: keys normalised as they enter the cache, rounded to storage
+# --------------------------------------------------------------------------
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to bf16, to nearest with ties to an even last bit,
+    and return the bf16 bit patterns (uint16).
+
+    bf16 keeps the sign, the 8 exponent bits and 7 stored significand bits of
+    an IEEE binary32: 8 significant bits for normal numbers, so a value in
+    [2^(e-1), 2^e) is rounded to a multiple of 2^(e-8); below the normal range
+    the step stays 2^-133. Values that round past the largest finite bf16 go
+    to infinity. Done in one rounding from float64 (no detour through float32).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)  # a = m 2^e, 0.5 <= m < 1 (e = 0 for a = 0)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    with np.errstate(invalid="ignore"):
+        r = np.rint(a / q) * q  # rint: halfway cases to even
+    r = np.where(r > BF16_MAX, np.inf, r)
+    y = np.copysign(r, x).astype(np.float32)
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: int = SSA_NORM_K):
+    """The cache rows that storing new tokens writes.
+
+    "Sevren Sparse Attention learns to be sparse": the score takes the
+    RMS-normalised key; normalising a key depends on that key alone, so it is
+    done once, as the key is stored (flag SSA_NORM_K; without it the key is
+    stored as given). Values are stored as given. Each stored value is the
+    exact result rounded once to the storage type.
+
+    k_new, v_new [..., D] float32. Returns a dict with ``k_exact`` (the keys
+    before rounding, float64) and the stored rows ``k`` and ``v``: bf16 bit
+    patterns (uint16) for kv_dtype "bf16", float32 values for "f32".
+    """
+    k = widen(np.asarray(k_new, dtype=np.float32))
+    v = widen(np.asarray(v_new, dtype=np.float32))
+    kx = rms_normalize(k, eps) if flags & SSA_NORM_K else k
+    if kv_dtype == "bf16":
+        return {"k_exact": kx, "k": round_bf16(kx), "v": round_bf16(v)}
+    return {"k_exact": kx, "k": kx.astype(np.float32), "v": v.astype(np.float32)}

@@ -477,4 +477,73 @@ def pin_prefill_causal():
         _close(out[:, :, t], r["out"], rtol=1e-12, atol=1e-14, what=f"prefill vs decode t={t}")
 
 
+# --------------------------------------------------------------------------
+# cache write
+# --------------------------------------------------------------------------
+
+def pin_round_bf16_definition():
+    """Rounding into bf16 (binary32 with 8 significant bits), to nearest with
+    ties to the even neighbour, on values whose result the definition fixes by
+    hand: exact values, halfway cases, just above halfway, the sign, the
+    subnormal step 2^-133, overflow past the largest finite value, and 0.1
+    (0.1 / 2^-11 = 204.8, so 205 * 2^-11)."""
+    cases = [(1.0, 0x3F80), (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+             (1 + 2.0 ** -8 + 2.0 ** -40, 0x3F81), (-(1 + 2.0 ** -8), 0xBF80),
+             (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002), (2.0 ** -133, 0x0001),
+             (0.1, 0x3DCD), (3.4e38, 0x7F80), ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),
+             ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F), (-0.0, 0x8000), (0.0, 0x0000)]
+    got = O.round_bf16(np.array([c[0] for c in cases]))
+    for (x, want), g in zip(cases, got):
+        assert int(g) == want, f"round_bf16({x!r}) = {int(g):#06x}, want {want:#06x}"
+
+
+def _bf16_from_f32_bits(x32):
+    """Round-to-nearest-even of float32 values to bf16 by integer arithmetic on
+    their bits (valid for finite float32 inputs: one rounding from the exact
+    value)."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_cache_write_golden():
+    """The page's normalisation on the hand-worked keys: the unnormalised rows
+    (keys scaled by 2, 1/2 and 3) are stored as the RMS-1 keys, which bf16
+    holds exactly; values are stored as given."""
+    g = _golden()
+    ku = _arr(g["sparse_layer_norm_k"]["keys_unnormalised"])
+    keys = _arr(g["keys"])
+    vals = _arr(g["values"])
+    r = O.cache_write(ku.astype(np.float32), np.nan_to_num(vals).astype(np.float32), "bf16",
+                      eps=0.0, flags=O.SSA_NORM_K)
+    _close(r["k_exact"], keys, what="normalised keys")
+    assert np.array_equal(r["k"], _bf16_from_f32_bits(keys.astype(np.float32))), "stored keys"
+    assert np.array_equal(r["v"], _bf16_from_f32_bits(np.nan_to_num(vals).astype(np.float32))), "stored values"
+    r0 = O.cache_write(ku.astype(np.float32), np.nan_to_num(vals).astype(np.float32), "bf16", eps=0.0,
+                       flags=0)
+    _close(r0["k_exact"], ku, what="keys stored as given without SSA_NORM_K")
+
+
+def pin_cache_write_invariants():
+    """On seeded rows of very different sizes: the stored key's mean square is
+    ms / (ms + eps) (closed form of x / sqrt(ms + eps)); with eps = 0 a
+    positive rescaling of the input leaves it unchanged; values are stored as
+    given, rounded once (checked against integer rounding of the float32
+    bits); float32 storage keeps the values."""
+    rng = np.random.default_rng(91)
+    k = (rng.standard_normal((6, 128)) * np.array([1e-3, 0.5, 1, 3, 1e2, 1e3])[:, None]).astype(np.float32)
+    v = rng.standard_normal((6, 128)).astype(np.float32)
+    eps = 1e-6
+    r = O.cache_write(k, v, "bf16", eps=eps, flags=O.SSA_NORM_K)
+    ms = np.mean(k.astype(np.float64) ** 2, axis=-1)
+    _close(np.mean(r["k_exact"] ** 2, axis=-1), ms / (ms + eps), rtol=1e-12, what="mean square")
+    r1 = O.cache_write(k, v, "bf16", eps=0.0)
+    r2 = O.cache_write((k.astype(np.float64) * 4.0).astype(np.float32), v, "bf16", eps=0.0)
+    _close(r1["k_exact"], r2["k_exact"], rtol=1e-12, what="scale invariance")
+    assert np.array_equal(r["v"], _bf16_from_f32_bits(v)), "values rounded once"
+    assert np.array_equal(r["k"], O.round_bf16(r["k_exact"])), "keys rounded"
+    rf = O.cache_write(k, v, "f32", eps=eps)
+    assert np.array_equal(rf["v"], v), "float32 values kept"
+    _close(rf["k"], r["k_exact"], rtol=2.0 ** -23, what="float32 keys")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -21,6 +21,7 @@ _orig_decode = O.decode_full
 _orig_widen = O.widen
 _orig_sparse = O.decode_sparse
 _orig_select_all = O.select_all
+_orig_cache_write = O.cache_write
 
 
 def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
@@ -133,6 +134,34 @@ def _decode_vrows_all_heads(*a, **kw):
     return r
 
 
+def _round_bf16_variant(kind):
+    def rnd(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        _, e = np.frexp(a)
+        q = np.ldexp(1.0, np.maximum(e - 8, -133))
+        if kind == "truncate":
+            r = np.floor(a / q) * q
+        else:  # halfway cases away from zero
+            r = np.floor(a / q + 0.5) * q
+        r = np.where(r > O.BF16_MAX, np.inf, r)
+        y = np.copysign(r, x).astype(np.float32)
+        return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return rnd
+
+
+def _cache_write_variant(kind):
+    def cw(k_new, v_new, kv_dtype="bf16", eps=1e-6, flags=O.SSA_NORM_K):
+        if kind == "flags_ignored":
+            flags = 0
+        r = _orig_cache_write(k_new, v_new, kv_dtype, eps, flags)
+        if kind == "values_normalised":
+            vx = O.rms_normalize(O.widen(np.asarray(v_new, np.float32)), eps)
+            r["v"] = O.round_bf16(vx) if kv_dtype == "bf16" else vx.astype(np.float32)
+        return r
+    return cw
+
+
 MUTANTS = {
     "weight_not_squared": ("relu2_attend", _attend_with(weights=lambda s: np.where(s > 0, s, 0.0))),
     "no_relu": ("relu2_attend", _attend_with(weights=lambda s: s * s)),
@@ -165,6 +194,10 @@ MUTANTS = {
     "sparse_norm_k_l2": ("decode_sparse", _sparse_variant("norm_k_l2")),
     "prefill_raw_q_normalised": ("prefill_full", _prefill_always_normalises),
     "select_all_flags_dropped": ("select_all", _select_all_flags_dropped),
+    "round_bf16_truncate": ("round_bf16", _round_bf16_variant("truncate")),
+    "round_bf16_half_away": ("round_bf16", _round_bf16_variant("half_away")),
+    "cache_write_flags_ignored": ("cache_write", _cache_write_variant("flags_ignored")),
+    "cache_write_values_normalised": ("cache_write", _cache_write_variant("values_normalised")),
     "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
                                           if np.asarray(x).dtype != np.uint16
                                           else np.asarray(x).astype(np.float64) / 256.0)),
