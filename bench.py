@@ -56,9 +56,10 @@ def parse():
                    help="only run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-legs", action="store_true",
                    help="skip the other workloads (the headline line then holds no 'legs')")
-    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block",
+    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block,fp8",
                    help="comma-separated workloads measured after the headline: "
-                        "tiny, single, fixed128k, sweep, block")
+                        "tiny, single, fixed128k, sweep, block, fp8 (the headline batch "
+                        "with an 8-bit cache)")
     p.add_argument("--leg-steps", type=int, default=20)
     p.add_argument("--workload", default=None,
                    help="measure only this workload (tiny, single, fixed128k, sweep, block) and "
@@ -74,7 +75,7 @@ def alg_bytes_full(wl, vrows: np.ndarray, with_scores: bool = True) -> dict:
     raw scores written (fp32, one per query head and key).
     """
     D = wl.head_dim
-    kvb = 2 if wl.kv_dtype == "bf16" else 4
+    kvb = {"bf16": 2, "fp8": 1}.get(wl.kv_dtype, 4)
     n = wl.ctx_lens.astype(np.int64)
     k_bytes = int(wl.n_kv_heads * D * kvb * n.sum())
     v_bytes = int(D * kvb * int(vrows.sum()))
@@ -187,7 +188,7 @@ def bench_leg(wl, *, n_sparse: int, steps: int, warmup: int = 3, rotate_bytes: i
     import torch
     from long_context_decode_relu_amd import ssa
     dev = torch.device("cuda:0")
-    kvb = 2 if wl.kv_dtype == "bf16" else 4
+    kvb = {"bf16": 2, "fp8": 1}.get(wl.kv_dtype, 4)
     cache_bytes = 2 * wl.k.nbytes
     copies = max(1, min(64, -(-rotate_bytes // max(1, cache_bytes))))
     caches = [ssa.cache_from_workload(wl, dev) for _ in range(copies)]
@@ -287,6 +288,8 @@ def bench_legs(names, steps: int) -> dict:
                           for p in synth.SWEEP_FRACTIONS}
         elif name == "block":
             legs[name] = bench_leg(synth.block_step(), n_sparse=3, steps=steps)
+        elif name == "fp8":
+            legs[name] = bench_leg(synth.batched_decode(kv_dtype="fp8"), n_sparse=1, steps=steps)
         else:
             raise ValueError(f"unknown workload {name}")
         log(f"[bench] leg {name} done in {time.perf_counter() - t0:.1f}s")

@@ -22,9 +22,19 @@
  * Conventions shared by every entry point
  *   Layout   All tensors are dense and row-major.
  *            queries  q   [B, Hq, D]        float32 (decode), bf16 (prefill: [B, Hq, Tq, D])
- *            cache    k,v [B, Hkv, Nmax, D] kv_dtype (SSA_F32 or SSA_BF16), Nmax = kv_capacity
+ *            cache    k,v [B, Hkv, Nmax, D] kv_dtype, Nmax = kv_capacity
  *            outputs  out [B, Hq, D] / [B, Hq, Tq, D] float32
  *            Query head h uses KV head h / (Hq / Hkv) (grouped-query attention).
+ *   8-bit    SSA_FP8_E4M3 ("KV bridge, KV reuse, and prefill": the full
+ *            caches kept in 8-bit precision): one byte per element in the
+ *            OCP E4M3FN layout (sign, 4 exponent bits with bias 7, 3
+ *            significand bits; S.1111.111 is NaN; largest magnitude 448).
+ *            k holds the keys' codes as they are used (keys are stored
+ *            normalised, so they lie within +-sqrt(D)); v holds the codes of
+ *            v / v_scale[b, kvh] and, right after the B*Hkv*Nmax*D code
+ *            bytes, the float32 scales v_scale [B, Hkv]: a value is
+ *            v_scale[b, kvh] * e4m3(code). ssa_prefill_full does not take
+ *            8-bit caches.
  *            D must be 128. Hq / Hkv must be 1, 2, 4 or 8.
  *   Memory   Every pointer except `shape` is a DEVICE pointer owned by the
  *            caller. The library allocates nothing, frees nothing and keeps
@@ -66,7 +76,7 @@ typedef enum {
   SSA_ERR_HIP = 6          /* the HIP runtime reported an error */
 } ssa_status;
 
-typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype;
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1, SSA_FP8_E4M3 = 2 } ssa_dtype;
 
 enum {
   SSA_NORM_Q = 1,          /* RMS-normalise each query row in the kernel */
@@ -211,7 +221,10 @@ ssa_status ssa_decode_sparse_static(const ssa_shape* shape, const float* q, cons
  *                  round(k_new[b,kvh,t])                                        (flags = 0)
  *     v[b,kvh,r] = round(v_new[b,kvh,t])
  *   round() is the cache's storage type: float32 as computed, bf16 to nearest
- *   with ties to even. Rows r outside [0, kv_capacity) are not written. No
+ *   with ties to even, SSA_FP8_E4M3 to the nearest code with ties to an even
+ *   significand and magnitudes past 448 saturated (values divided by the
+ *   v_scale already stored after the value codes; the call does not change
+ *   the scales). Rows r outside [0, kv_capacity) are not written. No
  *   other cache row is touched, and ctx_lens is not changed: the caller
  *   advances it. With SSA_NORM_K the stored keys are the "stored normalised"
  *   keys the decode entry points expect when SSA_NORM_K is not passed to them.

@@ -48,7 +48,8 @@ namespace {
 
 ssa_status check_shape(const ssa_shape* s, bool need_group) {
   if (!s) return SSA_ERR_NULL;
-  if (s->kv_dtype != SSA_F32 && s->kv_dtype != SSA_BF16) return SSA_ERR_DTYPE;
+  if (s->kv_dtype != SSA_F32 && s->kv_dtype != SSA_BF16 && s->kv_dtype != SSA_FP8_E4M3)
+    return SSA_ERR_DTYPE;
   if (s->batch < 0 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 1 ||
       s->kv_capacity < 0 || s->max_ctx_len < 0 || s->max_ctx_len > kMaxCtx ||
       s->max_ctx_len > s->kv_capacity)
@@ -97,6 +98,7 @@ ssa_status sparse_args(const ssa_shape* s, const float* q, const void* k, const 
   a->Nmax = s->kv_capacity;
   a->max_ctx = s->max_ctx_len;
   a->kv_bf16 = s->kv_dtype == SSA_BF16;
+  a->kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
   a->q = q;
   a->k = k;
   a->v = v;
@@ -172,6 +174,7 @@ ssa_status ssa_decode_full(const ssa_shape* s, const float* q, const void* k, co
   a.Nmax = s->kv_capacity;
   a.max_ctx = s->max_ctx_len;
   a.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -215,6 +218,7 @@ ssa_status ssa_decode_full_select(const ssa_shape* s, const float* q, const void
   a.full.Nmax = s->kv_capacity;
   a.full.max_ctx = s->max_ctx_len;
   a.full.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.full.kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
   a.full.q = q;
   a.full.k = k;
   a.full.v = v;
@@ -347,6 +351,7 @@ ssa_status ssa_cache_write(const ssa_shape* s, const float* k_new, const float* 
   a.Nmax = s->kv_capacity;
   a.T = n_tokens;
   a.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
   a.k_new = k_new;
   a.v_new = v_new;
   a.pos0 = pos0;

@@ -147,7 +147,7 @@ __device__ __forceinline__ void wait_vm() {
 struct VRows {
   uint32_t r[kVS];
 };
-static_assert(kVS == 16, "vwait16 passes sixteen value registers");
+static_assert(kVS == 16, "vwait passes sixteen value registers");
 // A pointer the wave holds in scalar registers (the same on every lane).
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   const uint64_t x = reinterpret_cast<uint64_t>(p);
@@ -160,15 +160,22 @@ __device__ __forceinline__ uint32_t vload(const uint8_t* row, uint32_t off) {
   asm volatile("global_load_dword %0, %1, %2" : "=v"(x) : "v"(off), "s"(row) : "memory");
   return x;
 }
-// Wait until at most 16 vector-memory operations (the 16 loads of the tile
+// The same for a 2-byte piece (two 8-bit codes), zero-extended.
+__device__ __forceinline__ uint32_t vload16(const uint8_t* row, uint32_t off) {
+  uint32_t x;
+  asm volatile("global_load_ushort %0, %1, %2" : "=v"(x) : "v"(off), "s"(row) : "memory");
+  return x;
+}
+// Wait until at most N vector-memory operations (the N loads of the tile
 // copy, issued after the value rows) are outstanding.
-__device__ __forceinline__ void vwait16(VRows& v) {
-  asm volatile("s_waitcnt vmcnt(16)"
+template <int N>
+__device__ __forceinline__ void vwait(VRows& v) {
+  asm volatile("s_waitcnt vmcnt(%16)"
                : "+v"(v.r[0]), "+v"(v.r[1]), "+v"(v.r[2]), "+v"(v.r[3]), "+v"(v.r[4]),
                  "+v"(v.r[5]), "+v"(v.r[6]), "+v"(v.r[7]), "+v"(v.r[8]), "+v"(v.r[9]),
                  "+v"(v.r[10]), "+v"(v.r[11]), "+v"(v.r[12]), "+v"(v.r[13]), "+v"(v.r[14]),
                  "+v"(v.r[15])
-               :
+               : "n"(N)
                : "memory");
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -179,6 +186,41 @@ __device__ __forceinline__ void tile_read_bf16(const uint8_t* lds_tile, int lane
   const int x = lane & 15;
 #pragma unroll
   for (int j = 0; j < 16; ++j) kr.c[j] = *reinterpret_cast<const u32x4*>(row + ((j ^ x) << 4));
+}
+
+// 8-bit tile (E4M3FN codes, 128 bytes per key): LDS byte k*128 + p*16 holds
+// piece p ^ (k & 7) of tile row k. Load i (of 8) moves rows 8i..8i+7: lane L
+// fetches row 8i + L/8, stored position L % 8, so each load reads 1 KB of
+// contiguous HBM and the lane's source offset within the kilobyte does not
+// depend on i.
+__device__ __forceinline__ uint32_t fp8_tile_offset(int lane) {
+  const int kq = lane >> 3, p = lane & 7;
+  return (uint32_t)(kq * 128 + ((p ^ kq) << 4));
+}
+// Four E4M3FN codes -> two bf16 pairs (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true);
+  __builtin_memcpy(&lo, &a, 4);
+  __builtin_memcpy(&hi, &b, 4);
+}
+// Sixteen codes (one 16-byte piece) -> eight bf16 pairs.
+__device__ __forceinline__ void fp8_piece_to_bf16(const u32x4 c, u32x4& o0, u32x4& o1) {
+  uint32_t x[8];
+  fp8x4_to_bf16(c.x, x[0], x[1]);
+  fp8x4_to_bf16(c.y, x[2], x[3]);
+  fp8x4_to_bf16(c.z, x[4], x[5]);
+  fp8x4_to_bf16(c.w, x[6], x[7]);
+  o0 = u32x4{x[0], x[1], x[2], x[3]};
+  o1 = u32x4{x[4], x[5], x[6], x[7]};
+}
+// This lane's row of an 8-bit LDS tile, as the bf16 key row of the same values.
+__device__ __forceinline__ void tile_read_fp8(const uint8_t* lds_tile, int lane, KeyRow<true>& kr) {
+  const uint8_t* row = lds_tile + lane * 128;
+  const int x = lane & 7;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    fp8_piece_to_bf16(*reinterpret_cast<const u32x4*>(row + ((j ^ x) << 4)), kr.c[2 * j], kr.c[2 * j + 1]);
 }
 
 __device__ __forceinline__ void row_load_f32(const void* k, size_t row, KeyRow<false>& kr) {
@@ -555,7 +597,7 @@ __device__ __forceinline__ void slot_tiles(int s0, int s1, int w, int W, int T, 
   *nt = min(s1, t1) - *first;
 }
 
-template <int G, bool BF16, bool NORMK, bool CAND>
+template <int G, bool BF16, bool NORMK, bool CAND, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ ctx_lens, float* __restrict__ scores, float* __restrict__ part_num,
@@ -635,7 +677,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     while (__builtin_amdgcn_readfirstlane(s_tpre[j + 1]) <= t) ++j;
     return stream_info(j);
   };
-  constexpr size_t kRowBytes = kHeadDim * (BF16 ? 2 : 4);
+  // bytes per key row; 8-bit rows go through the bf16 machinery, converted
+  // as they leave LDS
+  constexpr size_t kRowBytes = kHeadDim * (FP8 ? 1 : BF16 ? 2 : 4);
+  constexpr int kTileLoads = FP8 ? 8 : 16;  // 1 KB loads per tile copy
   auto qrow_of = [&](const Stream& st) __attribute__((always_inline)) {
     return q + ((size_t)st.b * Hq + (size_t)st.kvh * G) * kHeadDim;
   };
@@ -752,15 +797,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
 
     // Copy tile t of stream st into the wave's LDS tile; rows past the live
     // ones are replaced by the last live row (read, never used). Every call
-    // issues exactly 16 loads (the waits below count them); with st ==
+    // issues exactly kTileLoads loads (the waits below count them); with st ==
     // nullptr they re-read the first row of `again` (the first key of a tile
     // already read, always live and cached), which only keeps that count
     // fixed on a wave's last tile.
+    const uint32_t f8off = fp8_tile_offset(lane);
     auto issue_tile = [&](const Stream* st, int t, const uint8_t* again) __attribute__((always_inline)) {
       if (!st) {
-        unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
+        unroll_seq(std::make_integer_sequence<int, kTileLoads>{}, [&](auto ii) {
           constexpr int i = decltype(ii)::value;
-          dma16<i * 1024>(again, (uint32_t)(lane & 15) * 16, tile_m0);
+          dma16<i * 1024>(again, (uint32_t)(lane & (FP8 ? 7 : 15)) * 16, tile_m0);
         });
         return;
       }
@@ -768,7 +814,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       const int nvalid = min(kTileKeys, st->n - kb);
       const uint8_t* src =
           reinterpret_cast<const uint8_t*>(k) + ((size_t)st->j * Nmax + kb) * kRowBytes;
-      if (nvalid == kTileKeys) {
+      if constexpr (FP8) {
+        if (nvalid == kTileKeys) {
+          unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            dma16<i * 1024>(src + i * 1024, f8off, tile_m0);
+          });
+        } else {
+          unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            const int kt = 8 * i + (lane >> 3);
+            const int row = min(kt, nvalid - 1);
+            dma16<i * 1024>(src, (uint32_t)(row * 128 + (((lane & 7) ^ (kt & 7)) << 4)), tile_m0);
+          });
+        }
+      } else if (nvalid == kTileKeys) {
         unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
           constexpr int i = decltype(ii)::value;
           dma16<i * 1024>(src + (i >> 2) * 4096, toff.off[i & 3], tile_m0);
@@ -781,6 +841,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
           dma16<i * 1024>(src, (uint32_t)(row * 256 + (((lane & 15) ^ (kt & 15)) << 4)), tile_m0);
         });
       }
+    };
+    // this lane's key row of the wave's LDS tile
+    auto tile_read = [&](KeyRow<true>& kr_) __attribute__((always_inline)) {
+      if constexpr (FP8) tile_read_fp8(my_tile, lane, kr_);
+      else tile_read_bf16(my_tile, lane, kr_);
     };
     auto tile_src = [&](const Stream& st, int t) __attribute__((always_inline)) {
       return reinterpret_cast<const uint8_t*>(k) +
@@ -814,7 +879,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
         wv[0] = x.x;
         if constexpr (G == 2) wv[1] = x.y;
       }
-      const float vx = bf16_lo(vraw), vy = bf16_hi(vraw);
+      float vx, vy;
+      if constexpr (FP8) {
+        const f32x2 vf = __builtin_amdgcn_cvt_pk_f32_fp8((int)vraw, false);
+        vx = vf[0];
+        vy = vf[1];
+      } else {
+        vx = bf16_lo(vraw);
+        vy = bf16_hi(vraw);
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         num[h][0] = fmaf(wv[h], vx, num[h][0]);
@@ -833,7 +906,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
           vv[u] = 0u;
           if (u < nb) {
             const int key = __builtin_amdgcn_readlane(key_l, u);
-            vv[u] = reinterpret_cast<const uint32_t*>(vbase + (size_t)key * kRowBytes)[lane];
+            if constexpr (FP8)
+              vv[u] = reinterpret_cast<const uint16_t*>(vbase + (size_t)key * kRowBytes)[lane];
+            else
+              vv[u] = reinterpret_cast<const uint32_t*>(vbase + (size_t)key * kRowBytes)[lane];
           }
         });
         unroll_seq(std::make_integer_sequence<int, NB>{}, [&](auto uu) {
@@ -914,12 +990,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
     int qn = 0;
     bool kq_in_lds = false;  // the queued keys' rows wait in the LDS tile (a wave's last tile)
     // copy the rows of the queued keys (lane L: key L of the queue) into the
-    // wave's LDS tile, piece j of row L at byte 1024 j + 16 L: 16 loads, like a tile copy
+    // wave's LDS tile, piece j of row L at byte 1024 j + 16 L: kTileLoads
+    // loads, like a tile copy
     auto copy_queue_rows = [&]() __attribute__((always_inline)) {
       const int key = my_qk[lane < qn ? lane : 0];
       const uint8_t* row =
           reinterpret_cast<const uint8_t*>(k) + ((size_t)cur.j * Nmax + key) * kRowBytes;
-      unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto jj) {
+      unroll_seq(std::make_integer_sequence<int, kTileLoads>{}, [&](auto jj) {
         constexpr int j = decltype(jj)::value;
         dma16_lane<j * 1024>(row + 16 * j, tile_m0);
       });
@@ -934,14 +1011,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       if (kq_in_lds) {
         wait_vm<0>();
         const uint8_t* r = my_tile + 16 * lane;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) kq.c[j] = *reinterpret_cast<const u32x4*>(r + 1024 * j);
+          for (int j = 0; j < 8; ++j)
+            fp8_piece_to_bf16(*reinterpret_cast<const u32x4*>(r + 1024 * j), kq.c[2 * j], kq.c[2 * j + 1]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) kq.c[j] = *reinterpret_cast<const u32x4*>(r + 1024 * j);
+        }
         kq_in_lds = false;
       } else {
         const u32x4* src = reinterpret_cast<const u32x4*>(
             reinterpret_cast<const uint8_t*>(k) + ((size_t)cur.j * Nmax + key) * kRowBytes);
+        if constexpr (FP8) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) kq.c[j] = src[j];
+          for (int j = 0; j < 8; ++j) fp8_piece_to_bf16(src[j], kq.c[2 * j], kq.c[2 * j + 1]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) kq.c[j] = src[j];
+        }
       }
       typename Acc<G>::T a;
       float ks;
@@ -1022,12 +1110,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       // 1. tile t has landed; LDS -> registers
       wait_vm<0>();
       KeyRow<true> kr;
-      tile_read_bf16(my_tile, lane, kr);
+      tile_read(kr);
 
       // 2. deferred stores of the last tile scored in place
       deferred_stores();
       // 3. the oldest pending value rows, one load each (the wait below
-      //    leaves only the 16 tile loads issued after them outstanding)
+      //    leaves only the tile loads issued after them outstanding)
       const int nv = min(pn, kVS);
       VRows vr;
       if (nv > 0) {
@@ -1036,11 +1124,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
           constexpr int u = decltype(uu)::value;
           if (u < nv) {
             const int key = __builtin_amdgcn_readlane(key_l, u);
-            vr.r[u] = vload(uniform_ptr(vbase + (size_t)key * kRowBytes), (uint32_t)lane * 4);
+            if constexpr (FP8)
+              vr.r[u] = vload16(uniform_ptr(vbase + (size_t)key * kRowBytes), (uint32_t)lane * 2);
+            else
+              vr.r[u] = vload(uniform_ptr(vbase + (size_t)key * kRowBytes), (uint32_t)lane * 4);
           }
         });
       }
-      // 4. tile t+1 -> LDS (16 loads), once the reads of tile t are done
+      // 4. tile t+1 -> LDS (kTileLoads loads), once the reads of tile t are done
       const bool last = t + 1 == t1;
       wait_lgkm0();
       if (!last) {
@@ -1048,7 +1139,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
         issue_tile(&nx, t + 1, nullptr);
       } else if (qn > 0) {
         // the wave's last tile: the queued keys' rows come into the free LDS
-        // tile (16 loads, like a tile copy) while this tile is scored
+        // tile (kTileLoads loads, like a tile copy) while this tile is scored
         copy_queue_rows();
         kq_in_lds = true;
       } else {
@@ -1076,7 +1167,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       }
 
       // 6. the pending value rows are in (the tile copy may still be in flight)
-      vwait16(vr);
+      vwait<kTileLoads>(vr);
       unroll_seq(std::make_integer_sequence<int, kVS>{}, [&](auto uu) {
         constexpr int u = decltype(uu)::value;
         if (u < nv) v_add((ph + u) & (kTileKeys - 1), vr.r[u]);
@@ -1240,7 +1331,8 @@ __device__ void combine_row(
     int blk, const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
-    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
+    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows,
+    const float* __restrict__ vsc) {
   __shared__ float s_num[kCombineGroups][kHeadDim];
   __shared__ float s_den[kCombineWaves];
   __shared__ int s_cnt[kCombineWaves][2];
@@ -1296,7 +1388,9 @@ __device__ void combine_row(
 #pragma unroll
     for (int w2 = 0; w2 < kCombineWaves; ++w2) td += s_den[w2];
     const float denom = c + td;
-    out[((size_t)b * Hq + h) * kHeadDim + d] = denom == 0.f ? 0.f : tn / denom;
+    // (8-bit caches: the value rows were summed in units of the head's scale)
+    const float o = denom == 0.f ? 0.f : tn / denom;
+    out[((size_t)b * Hq + h) * kHeadDim + d] = vsc ? o * vsc[j] : o;
     if (d == 0 && nnz) {
       int z = 0;
 #pragma unroll
@@ -1316,9 +1410,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
     const float* __restrict__ part_num, const float* __restrict__ part_den,
     const int32_t* __restrict__ part_nnz, const int32_t* __restrict__ part_vrows,
     const int* __restrict__ tile_pre, int S, int Hq, int Hkv, int Wl, float c,
-    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows) {
+    float* __restrict__ out, int32_t* __restrict__ nnz, int32_t* __restrict__ vrows,
+    const float* __restrict__ vsc) {
   combine_row(blockIdx.x, part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c, out,
-              nnz, vrows);
+              nnz, vrows, vsc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1759,12 +1854,12 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     int k_top, int n_recent, int disjoint,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_count,
     const int32_t* __restrict__ row_flag, int32_t* __restrict__ sel_fail,
-    const float* __restrict__ rs) {
+    const float* __restrict__ rs, const float* __restrict__ vsc) {
   __shared__ SelShared sh;
   const int rows = S / Hkv * Hq;
   if ((int)blockIdx.x < rows) {
     combine_row(blockIdx.x, part_num, part_den, part_nnz, part_vrows, tile_pre, S, Hq, Hkv, Wl, c,
-                out, nnz, vrows);
+                out, nnz, vrows, vsc);
     return;
   }
   int b, h;
@@ -1882,7 +1977,7 @@ __global__ __launch_bounds__(256) void decode_full_decide(
 constexpr int kFallbackBlocks = 256;
 constexpr int kFallbackSlices = 64;
 
-template <int G, bool BF16, bool NORMK>
+template <int G, bool BF16, bool NORMK, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_full_rescore(
     const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ fmask, int S, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
@@ -1899,7 +1994,8 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint8_t* const my_tile = s_tile + wave * kTileBytesBf16;
   const uint32_t tile_m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)my_tile);
-  constexpr size_t kRowBytes = kHeadDim * (BF16 ? 2 : 4);
+  constexpr size_t kRowBytes = kHeadDim * (FP8 ? 1 : BF16 ? 2 : 4);
+  const uint32_t f8off = fp8_tile_offset(lane);
   const TileOffsets toff(lane);
   for (int i = tid; i < nw; i += kThreads) s_fw[i] = 0u;
   __syncthreads();
@@ -1971,7 +2067,21 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
       float ksq = 0.f;
       if constexpr (BF16) {
         const uint8_t* src = reinterpret_cast<const uint8_t*>(k) + ((size_t)j * Nmax + base) * kRowBytes;
-        if (nvalid == kTileKeys) {
+        if constexpr (FP8) {
+          if (nvalid == kTileKeys) {
+            unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto ii) {
+              constexpr int i = decltype(ii)::value;
+              dma16<i * 1024>(src + i * 1024, f8off, tile_m0);
+            });
+          } else {
+            unroll_seq(std::make_integer_sequence<int, 8>{}, [&](auto ii) {
+              constexpr int i = decltype(ii)::value;
+              const int kt = 8 * i + (lane >> 3);
+              const int row = min(kt, nvalid - 1);
+              dma16<i * 1024>(src, (uint32_t)(row * 128 + (((lane & 7) ^ (kt & 7)) << 4)), tile_m0);
+            });
+          }
+        } else if (nvalid == kTileKeys) {
           unroll_seq(std::make_integer_sequence<int, 16>{}, [&](auto ii) {
             constexpr int i = decltype(ii)::value;
             dma16<i * 1024>(src + (i >> 2) * 4096, toff.off[i & 3], tile_m0);
@@ -1986,7 +2096,8 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
         }
         wait_vm<0>();
         KeyRow<true> kr;
-        tile_read_bf16(my_tile, lane, kr);
+        if constexpr (FP8) tile_read_fp8(my_tile, lane, kr);
+        else tile_read_bf16(my_tile, lane, kr);
         wait_lgkm0();
         score_row<G, true, NORMK>(kr, qrow, acc, ksq);
       } else {
@@ -2051,18 +2162,26 @@ struct Launch {
   int32_t* cand_cnt;
   const float* qhi;  // the filter's queries (null: every key scored exactly)
   const float* invc;
+  const float* vsc;  // 8-bit caches: the value scales [B, Hkv] (null otherwise)
   int B, Hq, Hkv, Nmax, max_ctx;
   float scale, eps;
   int normq;
 };
 
-// f.template operator()<G, BF16, NORMK>() for the runtime choice
+// Calls f.template operator()<g, bf16, nk, fp8>() for the group size and
+// storage type (kvt: 0 float32, 1 bf16, 2 8-bit; 8-bit rows take the bf16
+// path, converted as they leave LDS).
+int kvt_of(const DecodeFullArgs& a) { return a.kv_fp8 ? 2 : a.kv_bf16 ? 1 : 0; }
+
 template <class F>
-hipError_t dispatch(int G, bool bf16, bool normk, F&& f) {
+hipError_t dispatch(int G, int kvt, bool normk, F&& f) {
   auto by_g = [&](auto gc) -> hipError_t {
     constexpr int g = decltype(gc)::value;
-    if (bf16) return normk ? f.template operator()<g, true, true>() : f.template operator()<g, true, false>();
-    return normk ? f.template operator()<g, false, true>() : f.template operator()<g, false, false>();
+    if (kvt == 2)
+      return normk ? f.template operator()<g, true, true, true>() : f.template operator()<g, true, false, true>();
+    if (kvt == 1)
+      return normk ? f.template operator()<g, true, true, false>() : f.template operator()<g, true, false, false>();
+    return normk ? f.template operator()<g, false, true, false>() : f.template operator()<g, false, false, false>();
   };
   switch (G) {
     case 1: return by_g(std::integral_constant<int, 1>{});
@@ -2082,8 +2201,8 @@ hipError_t launch_full(const DecodeFullArgs& a, const Launch& L, hipStream_t str
   const bool normk = a.flags & SSA_NORM_K;
   const int64_t tiles_bound = decode_full_tiles_bound(a.B, a.Hkv, a.max_ctx);
   const int cus_per_xcd = device_cu_count() % kXcds == 0 ? device_cu_count() / kXcds : 0;
-  return dispatch(G, a.kv_bf16, normk, [&]<int g, bool bf16, bool nk>() -> hipError_t {
-    auto kern = decode_full_kernel<g, bf16, nk, CAND>;
+  return dispatch(G, kvt_of(a), normk, [&]<int g, bool bf16, bool nk, bool f8>() -> hipError_t {
+    auto kern = decode_full_kernel<g, bf16, nk, CAND, f8>;
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
         per_cu < 1)
@@ -2119,8 +2238,12 @@ Launch make_launch(const DecodeFullArgs& a, const WsLayout& l, bool cand) {
   L.cand_idx = cand ? reinterpret_cast<int32_t*>(ws + l.cand_idx) : nullptr;
   L.cand_sc = cand ? reinterpret_cast<float*>(ws + l.cand_sc) : nullptr;
   L.cand_cnt = cand ? reinterpret_cast<int32_t*>(ws + l.cand_cnt) : nullptr;
-  // the filter serves bf16 caches when no full scores are written
-  const bool filter = a.kv_bf16 && a.scores == nullptr;
+  // the filter serves bf16 and 8-bit caches when no full scores are written
+  const bool filter = (a.kv_bf16 || a.kv_fp8) && a.scores == nullptr;
+  // 8-bit caches: the value scales follow the B*Hkv*Nmax*D value codes
+  L.vsc = a.kv_fp8 ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v) +
+                                                    (size_t)a.B * a.Hkv * a.Nmax * kHeadDim)
+                   : nullptr;
   L.qhi = filter ? reinterpret_cast<const float*>(ws + l.qhi) : nullptr;
   L.invc = filter ? reinterpret_cast<const float*>(ws + l.invc) : nullptr;
   L.B = a.B;
@@ -2182,7 +2305,7 @@ hipError_t launch_decode_full(const DecodeFullArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_full_combine, dim3(a.Hq * a.B), dim3(kCombineThreads), 0,
                      stream, L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
-                     grid * kWaves, a.c, a.out, a.nnz, a.vrows);
+                     grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.vsc);
   return hipGetLastError();
 }
 
@@ -2213,8 +2336,8 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   if (e != hipSuccess) return e;
   // the rescoring kernel's LDS bitmap of streams and its word prefix
   const size_t dyn = 2 * (size_t)ceil_div(S, 32) * sizeof(uint32_t);
-  e = dispatch(G, a.kv_bf16, a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk>() -> hipError_t {
-    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk>), dim3(kFallbackBlocks), dim3(kThreads), dyn,
+  e = dispatch(G, kvt_of(a), a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk, bool f8>() -> hipError_t {
+    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk, f8>), dim3(kFallbackBlocks), dim3(kThreads), dyn,
                        stream, a.q, a.k, a.ctx_lens, fmask, S, a.Hq, a.Hkv, a.Nmax, a.max_ctx,
                        a.scale, a.eps, L.normq, rescored);
     return hipGetLastError();
@@ -2224,7 +2347,7 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
                      L.num, L.den, L.nnz, L.vrows, L.tile_pre, a.B * a.Hkv, a.Hq, a.Hkv,
                      grid * kWaves, a.c, a.out, a.nnz, a.vrows, L.cand_idx, L.cand_sc, L.cand_cnt,
                      a.ctx_lens, a.max_ctx, s.k_top, s.n_recent, disjoint, s.sel_idx, s.sel_count,
-                     row_flag, fail, rescored);
+                     row_flag, fail, rescored, L.vsc);
   return hipGetLastError();
 }
 

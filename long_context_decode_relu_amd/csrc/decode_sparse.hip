@@ -169,13 +169,15 @@ __global__ __launch_bounds__(kUThreads) void sparse_union(
   }
 }
 
-template <int G, bool BF16, bool NORMQ, bool NORMK>
+// FP8 (with BF16): 8-bit rows (E4M3FN codes, one byte per dim) and value
+// scales vsc [B*Hkv] that multiply the chunk's value sums.
+template <int G, bool BF16, bool NORMQ, bool NORMK, bool FP8>
 __global__ __launch_bounds__(kGThreads) void sparse_gather(
     const float* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const int32_t* __restrict__ ctx_lens, int Hq, int Hkv, int Nmax, int nlim, int nseg, int cap,
     int C, float scale, float eps, const int2* __restrict__ urow, const int32_t* __restrict__ ucnt,
     const int32_t* __restrict__ uoff, int32_t* __restrict__ nch, float* __restrict__ part_m,
-    float* __restrict__ part_l, float* __restrict__ part_acc) {
+    float* __restrict__ part_l, float* __restrict__ part_acc, const float* __restrict__ vsc) {
   constexpr int GP = G < 4 ? 4 : G;
   constexpr int kAccBytes = kGWaves * G * kHeadDim * 4;
   constexpr int kTileAll = BF16 ? kGWaves * kKTileBf16 : 0;
@@ -275,7 +277,22 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     uint32_t vb[BF16 ? kWRows : 1];
     f32x2 vf[BF16 ? 1 : kWRows];
     uint8_t* const ktile = s_k + (BF16 ? wave * kKTileBf16 : 0);
-    if constexpr (BF16) {
+    if constexpr (FP8) {
+      // 8-bit K rows -> LDS: load i moves rows 8i .. 8i+7 (lane L: row 8i +
+      // L/8, 16-byte piece L % 8); piece p of row r lands in slot p ^ (r & 7)
+      const uint8_t* kb8 = static_cast<const uint8_t*>(k);
+#pragma unroll
+      for (int i = 0; i < kWRows / 8; ++i) {
+        const int rr = 8 * i + (lane >> 3);
+        const size_t src = (row0 + __shfl(key, rr, kWave)) * kHeadDim;
+        __builtin_amdgcn_global_load_lds(kb8 + src + (((lane & 7) ^ (rr & 7)) << 4),
+                                         ktile + i * 1024, 16, 0, 0);
+      }
+      const uint16_t* vb16 = static_cast<const uint16_t*>(v);
+#pragma unroll
+      for (int rr = 0; rr < kWRows; ++rr)
+        vb[rr] = vb16[(row0 + __builtin_amdgcn_readlane(key, rr)) * (kHeadDim / 2) + lane];
+    } else if constexpr (BF16) {
       // K rows -> LDS: load i moves rows 4i .. 4i+3 (lane L: row 4i + L/16,
       // 16-byte piece L % 16); piece p of row r lands in slot p ^ (r & 15).
       // Through plain pointers: the direct-to-LDS builtin called on the
@@ -307,7 +324,36 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
 #pragma unroll
     for (int h = 0; h < G; ++h) t[h] = 0.f;
     float ss = 0.f;
-    if constexpr (BF16) {
+    if constexpr (FP8) {
+      const uint8_t* myrow = ktile + ri * kHeadDim;
+#pragma unroll 2
+      for (int i = 0; i < 4; ++i) {
+        const int pc = 4 * half + i;  // 16 dims per piece
+        const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((pc ^ (ri & 7)) << 4));
+        float xx[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], false);
+          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], true);
+          xx[4 * e] = a[0]; xx[4 * e + 1] = a[1]; xx[4 * e + 2] = b[0]; xx[4 * e + 3] = b[1];
+        }
+        if constexpr (NORMK) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss = fmaf(xx[e], xx[e], ss);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 qa = *reinterpret_cast<const f32x4*>(&s_q[h][16 * pc + 4 * q4]);
+            t[h] = fmaf(qa[0], xx[4 * q4], t[h]);
+            t[h] = fmaf(qa[1], xx[4 * q4 + 1], t[h]);
+            t[h] = fmaf(qa[2], xx[4 * q4 + 2], t[h]);
+            t[h] = fmaf(qa[3], xx[4 * q4 + 3], t[h]);
+          }
+        }
+      }
+    } else if constexpr (BF16) {
       const uint8_t* myrow = ktile + ri * (kHeadDim * 2);
 #pragma unroll 2
       for (int i = 0; i < 8; ++i) {
@@ -379,7 +425,9 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     bool fin = true;
 #pragma unroll
     for (int rr = 0; rr < kWRows; ++rr) {
-      if constexpr (BF16)  // exponent bits of neither bf16 all ones
+      if constexpr (FP8)  // neither code is S.1111.111
+        fin = fin && (vb[rr] & 0x7fu) != 0x7fu && (vb[rr] & 0x7f00u) != 0x7f00u;
+      else if constexpr (BF16)  // exponent bits of neither bf16 all ones
         fin = fin && (vb[rr] & 0x7f80u) != 0x7f80u && (vb[rr] & 0x7f800000u) != 0x7f800000u;
       else fin = fin && isfinite(vf[rr][0]) && isfinite(vf[rr][1]);
     }
@@ -388,7 +436,11 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
 #pragma unroll
       for (int rr = 0; rr < kWRows; ++rr) {
         float v0, v1;
-        if constexpr (BF16) {
+        if constexpr (FP8) {
+          const f32x2 vf8 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vb[rr], false);
+          v0 = vf8[0];
+          v1 = vf8[1];
+        } else if constexpr (BF16) {
           v0 = bf16_lo(vb[rr]);
           v1 = bf16_hi(vb[rr]);
         } else {
@@ -446,7 +498,7 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
         ls = fmaf(f, s_ll[w][h], ls);
       }
     }
-    part_acc[(slot * G + h) * kHeadDim + d] = a;
+    part_acc[(slot * G + h) * kHeadDim + d] = FP8 ? a * vsc[j] : a;
     if (d == 0) {
       part_m[slot * G + h] = M;  // -inf: head h selects no row of the chunk
       part_l[slot * G + h] = ls;
@@ -534,7 +586,7 @@ SpLayout sp_layout(int B, int Hq, int Hkv, int max_ctx, int stride) {
   return s;
 }
 
-template <int G, bool BF16, bool NORMQ, bool NORMK>
+template <int G, bool BF16, bool NORMQ, bool NORMK, bool FP8 = false>
 void launch_t(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_t stream) {
   const int S = a.B * a.Hkv;
   const int nlim = std::min(a.Nmax, a.max_ctx);
@@ -545,17 +597,24 @@ void launch_t(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_
     hipLaunchKernelGGL((sparse_union<G>), dim3(S * s.nseg), dim3(kUThreads), 0, stream, a.ctx_lens,
                        a.sel_idx, a.sel_count, a.sel_stride, a.Hq, a.Hkv, nlim, s.nseg, s.cap, urow,
                        ucnt, uoff);
-  hipLaunchKernelGGL((sparse_gather<G, BF16, NORMQ, NORMK>), dim3(S * s.C), dim3(kGThreads), 0,
+  // 8-bit caches: the value scales follow the B*Hkv*Nmax*D value codes
+  const float* vsc = FP8 ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.v) +
+                                                          (size_t)a.B * a.Hkv * a.Nmax * kHeadDim)
+                         : nullptr;
+  hipLaunchKernelGGL((sparse_gather<G, BF16, NORMQ, NORMK, FP8>), dim3(S * s.C), dim3(kGThreads), 0,
                      stream, a.q, a.k, a.v, a.ctx_lens, a.Hq, a.Hkv, a.Nmax, nlim, s.nseg, s.cap,
                      s.C, a.scale, a.eps, urow, ucnt, uoff, reinterpret_cast<int32_t*>(ws + s.nch),
                      reinterpret_cast<float*>(ws + s.m), reinterpret_cast<float*>(ws + s.l),
-                     reinterpret_cast<float*>(ws + s.acc));
+                     reinterpret_cast<float*>(ws + s.acc), vsc);
 }
 
 template <int G>
 void launch_g(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_t stream) {
   const bool bf = a.kv_bf16, nq = a.flags & SSA_NORM_Q, nk = a.flags & SSA_NORM_K;
-  if (bf) {
+  if (a.kv_fp8) {
+    if (nq) nk ? launch_t<G, true, true, true, true>(a, s, ws, stream) : launch_t<G, true, true, false, true>(a, s, ws, stream);
+    else nk ? launch_t<G, true, false, true, true>(a, s, ws, stream) : launch_t<G, true, false, false, true>(a, s, ws, stream);
+  } else if (bf) {
     if (nq) nk ? launch_t<G, true, true, true>(a, s, ws, stream) : launch_t<G, true, true, false>(a, s, ws, stream);
     else nk ? launch_t<G, true, false, true>(a, s, ws, stream) : launch_t<G, true, false, false>(a, s, ws, stream);
   } else {

@@ -12,7 +12,7 @@ namespace ssa {
 int decode_full_chunk(int batch, int n_kv_heads, int max_ctx_len);
 
 struct DecodeFullArgs {
-  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;
+  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16, kv_fp8;
   const float* q;
   const void* k;
   const void* v;
@@ -56,7 +56,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 // The exact selection of the rows with row_flag[row] != 0 only (no workspace).
 
 struct DecodeSparseArgs {
-  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16;
+  int B, Hq, Hkv, Nmax, max_ctx, kv_bf16, kv_fp8;
   const float* q;
   const void* k;
   const void* v;
@@ -76,7 +76,7 @@ hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream);
 hipError_t launch_decode_sparse_static(const DecodeSparseArgs& a, hipStream_t stream);
 
 struct CacheWriteArgs {
-  int B, Hkv, Nmax, T, kv_bf16;
+  int B, Hkv, Nmax, T, kv_bf16, kv_fp8;
   const float* k_new;  // [B, Hkv, T, D]
   const float* v_new;
   const int32_t* pos0;  // [B]: token t of sequence b goes to row pos0[b] + t

@@ -29,6 +29,7 @@ SSA_ERR_HIP = 6
 
 SSA_F32 = 0
 SSA_BF16 = 1
+SSA_FP8_E4M3 = 2
 
 SSA_NORM_Q = 1
 SSA_NORM_K = 2
@@ -117,6 +118,8 @@ def _stream(device: torch.device) -> int:
 
 
 def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.uint8:
+        return SSA_FP8_E4M3
     if t.dtype == torch.bfloat16:
         return SSA_BF16
     if t.dtype == torch.float32:
@@ -131,11 +134,16 @@ def _need(cond: bool, msg: str) -> None:
 
 @dataclass
 class Cache:
-    """A full layer's KV cache: k, v [B, Hkv, Nmax, D] and ctx_lens [B] on one GPU."""
+    """A full layer's KV cache: k, v [B, Hkv, Nmax, D] and ctx_lens [B] on one GPU.
+
+    8-bit caches (uint8 E4M3FN codes) also carry v_scale [B, Hkv] float32, which
+    must sit right after v's codes in memory (make one with ``fp8_cache``).
+    """
     k: torch.Tensor
     v: torch.Tensor
     ctx_lens: torch.Tensor
     max_ctx_len: int
+    v_scale: torch.Tensor | None = None
 
     def shape(self, n_q_heads: int) -> ssa_shape:
         B, Hkv, Nmax, D = self.k.shape
@@ -148,6 +156,11 @@ class Cache:
         _need(k.is_contiguous() and v.is_contiguous(), "k, v must be contiguous")
         _need(c.dtype == torch.int32 and c.shape == (k.shape[0],) and c.is_contiguous(),
               "ctx_lens must be int32 [B]")
+        if k.dtype == torch.uint8:
+            s = self.v_scale
+            _need(s is not None and s.dtype == torch.float32 and s.shape == k.shape[:2]
+                  and s.data_ptr() == v.data_ptr() + v.numel(),
+                  "an 8-bit cache needs v_scale [B, Hkv] float32 right after v's codes (fp8_cache)")
 
 
 def workspace(op: int, shape: ssa_shape, aux: int, device: torch.device) -> torch.Tensor:
@@ -356,7 +369,30 @@ def kv_tensor(arr, device) -> torch.Tensor:
     return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
 
 
+def fp8_cache(B: int, Hkv: int, Nmax: int, D: int, device, *, ctx_lens: torch.Tensor | None = None,
+              max_ctx_len: int = 0) -> Cache:
+    """An empty 8-bit cache: k and v codes [B, Hkv, Nmax, D] uint8 and v_scale [B, Hkv]
+    float32 (ones) laid out after v's codes, as the library expects."""
+    n = B * Hkv * Nmax * D
+    buf = torch.zeros(n + 4 * B * Hkv, dtype=torch.uint8, device=device)
+    v = buf[:n].view(B, Hkv, Nmax, D)
+    sc = buf[n:].view(torch.float32).view(B, Hkv)
+    sc.fill_(1.0)
+    k = torch.zeros((B, Hkv, Nmax, D), dtype=torch.uint8, device=device)
+    if ctx_lens is None:
+        ctx_lens = torch.zeros(B, dtype=torch.int32, device=device)
+    return Cache(k=k, v=v, ctx_lens=ctx_lens, max_ctx_len=max_ctx_len, v_scale=sc)
+
+
 def cache_from_workload(wl, device) -> Cache:
-    return Cache(k=kv_tensor(wl.k, device), v=kv_tensor(wl.v, device),
-                 ctx_lens=torch.from_numpy(wl.ctx_lens.astype("int32")).to(device),
-                 max_ctx_len=int(wl.ctx_lens.max()) if wl.batch else 0)
+    ctx = torch.from_numpy(wl.ctx_lens.astype("int32")).to(device)
+    mx = int(wl.ctx_lens.max()) if wl.batch else 0
+    if wl.kv_dtype == "fp8":
+        import numpy as np
+        B, Hkv, Nmax, D = wl.k.shape
+        c = fp8_cache(B, Hkv, Nmax, D, device, ctx_lens=ctx, max_ctx_len=mx)
+        c.k.copy_(torch.from_numpy(np.ascontiguousarray(wl.k)).to(device))
+        c.v.copy_(torch.from_numpy(np.ascontiguousarray(wl.v)).to(device))
+        c.v_scale.copy_(torch.from_numpy(np.asarray(wl.v_scale, dtype=np.float32)).to(device))
+        return c
+    return Cache(k=kv_tensor(wl.k, device), v=kv_tensor(wl.v, device), ctx_lens=ctx, max_ctx_len=mx)

@@ -21,7 +21,9 @@ and ~95% after training):
 * V rows are N(0, 1) per element.
 
 Stored keys/values are bf16 (round to nearest even, kept as uint16 bit
-patterns) or float32. Cache slots at or beyond a sequence's context length
+patterns), float32, or 8-bit E4M3FN codes (uint8; keys as stored, values
+divided by a per-(sequence, KV head) power-of-two scale, kept in
+``Workload.v_scale``). Cache slots at or beyond a sequence's context length
 hold NaN so that any read past the live keys shows up in the output.
 Queries are float32 and are NOT normalised (the attention path does that).
 """
@@ -36,6 +38,38 @@ import os
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
+# scale of the synthetic values in an 8-bit cache: N(0, 1) values divided by
+# 2^-5 stay far inside the format's largest magnitude (448, i.e. 14 here)
+FP8_V_SCALE = np.float32(2.0 ** -5)
+
+
+def _e4m3_table() -> np.ndarray:
+    """The 127 non-negative finite E4M3FN values, indexed by code (0x00..0x7E):
+    sign bit 0, exponent field e (bias 7), significand field m;
+    (1 + m/8) 2^(e-7) for e > 0, (m/8) 2^-6 for e = 0."""
+    out = np.empty(127, dtype=np.float64)
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        out[c] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+_E4M3 = _e4m3_table()
+
+
+def to_e4m3_bits(x) -> np.ndarray:
+    """Round float32 values to E4M3FN codes (uint8): the nearest value of the
+    table, halfway cases to the even code, magnitudes past 448 saturated."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x).astype(np.float64), _E4M3[-1])
+    hi = np.minimum(np.searchsorted(_E4M3, a, side="left"), 126)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code)
+    return np.where(np.isnan(x), E4M3_NAN, code).astype(np.uint8)
 
 
 def to_bf16_bits(x) -> np.ndarray:
@@ -80,13 +114,14 @@ class Workload:
     n_kv_heads: int
     head_dim: int
     kv_capacity: int
-    kv_dtype: str                 # "bf16" or "f32"
+    kv_dtype: str                 # "bf16", "f32" or "fp8"
     ctx_lens: np.ndarray          # [B] int32
     q: np.ndarray                 # [B, Hq, D] float32 (raw)
-    k: np.ndarray                 # [B, Hkv, Nmax, D] uint16 (bf16 bits) or float32
-    v: np.ndarray                 # same layout as k
+    k: np.ndarray                 # [B, Hkv, Nmax, D] uint16 (bf16 bits), float32 or uint8 (E4M3 codes)
+    v: np.ndarray                 # same layout as k (8-bit: codes of v / v_scale)
     q_sparse: np.ndarray          # [L, B, Hq, D] float32 (raw), one set per sparse layer
     planted_p: float | None = None
+    v_scale: np.ndarray | None = None  # [B, Hkv] float32, 8-bit caches only
     meta: dict = field(default_factory=dict)
 
     @property
@@ -95,6 +130,8 @@ class Workload:
 
 
 def _store(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    if kv_dtype == "fp8":
+        return to_e4m3_bits(x)
     return to_bf16_bits(x) if kv_dtype == "bf16" else np.ascontiguousarray(x, np.float32)
 
 
@@ -109,8 +146,9 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
         raise ValueError("context longer than the cache capacity")
     B, Hq, Hkv, D = batch, n_q_heads, n_kv_heads, head_dim
     g = Hq // Hkv
-    sdt = np.uint16 if kv_dtype == "bf16" else np.float32
-    fill = BF16_NAN if kv_dtype == "bf16" else np.float32(np.nan)
+    sdt = {"bf16": np.uint16, "fp8": np.uint8}.get(kv_dtype, np.float32)
+    fill = {"bf16": BF16_NAN, "fp8": E4M3_NAN}.get(kv_dtype, np.float32(np.nan))
+    vsc = FP8_V_SCALE if kv_dtype == "fp8" else np.float32(1.0)
     k = np.empty((B, Hkv, nmax, D), dtype=sdt)
     v = np.empty((B, Hkv, nmax, D), dtype=sdt)
     q = np.empty((B, Hq, D), dtype=np.float32)
@@ -141,7 +179,7 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
             else:
                 raise ValueError(recipe)
             k[b, kvh, :n] = _store(_rows_to_rms1(keys), kv_dtype)
-            v[b, kvh, :n] = _store(r.standard_normal((n, D), dtype=np.float32), kv_dtype)
+            v[b, kvh, :n] = _store(r.standard_normal((n, D), dtype=np.float32) / vsc, kv_dtype)
             if poison_tail:
                 k[b, kvh, n:] = fill
                 v[b, kvh, n:] = fill
@@ -159,6 +197,7 @@ def make_workload(name: str, *, seed: int, batch: int, n_q_heads: int, n_kv_head
     return Workload(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
                     kv_capacity=nmax, kv_dtype=kv_dtype, ctx_lens=ctx, q=q, k=k, v=v,
                     q_sparse=qs, planted_p=p if recipe == "planted" else None,
+                    v_scale=np.full((B, Hkv), vsc, dtype=np.float32) if kv_dtype == "fp8" else None,
                     meta={"seed": seed, "recipe": recipe})
 
 
@@ -185,16 +224,18 @@ def batched_ctx_lens(seed: int = 3, batch: int = 8, lo: int = 65536, hi: int = 1
 
 def batched_decode(seed: int = 3, batch: int = 8, lo: int = 65536, hi: int = 131072,
                    kv_capacity: int = 131072, p: float = 0.05, fixed_len: int | None = None,
-                   n_sparse_layers: int = 1) -> Workload:
-    """Batch 8, contexts uniform in [64K, 128K], 16 q / 2 KV heads, bf16, planted 95%."""
+                   n_sparse_layers: int = 1, kv_dtype: str = "bf16") -> Workload:
+    """Batch 8, contexts uniform in [64K, 128K], 16 q / 2 KV heads, bf16 (or another
+    storage type), planted 95%."""
     if fixed_len is not None:
         ctx = np.full(batch, fixed_len, dtype=np.int32)
     else:
         ctx = batched_ctx_lens(seed, batch, lo, hi)
-    return make_workload("batched_decode_b8_64k_128k" if fixed_len is None else
-                         f"batched_decode_b{batch}_fixed{fixed_len}",
-                         seed=seed, batch=batch, n_q_heads=16, n_kv_heads=2, ctx_lens=ctx,
-                         kv_capacity=kv_capacity, p=p, n_sparse_layers=n_sparse_layers)
+    name = "batched_decode_b8_64k_128k" if fixed_len is None else f"batched_decode_b{batch}_fixed{fixed_len}"
+    if kv_dtype != "bf16":
+        name += "_" + kv_dtype
+    return make_workload(name, seed=seed, batch=batch, n_q_heads=16, n_kv_heads=2, ctx_lens=ctx,
+                         kv_capacity=kv_capacity, kv_dtype=kv_dtype, p=p, n_sparse_layers=n_sparse_layers)
 
 
 SWEEP_FRACTIONS = (0.5, 0.2, 0.05, 0.01, 0.002)

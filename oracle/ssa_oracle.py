@@ -60,13 +60,32 @@ SSA_SELECT_DISJOINT = 4
 # exact widening of stored values
 # --------------------------------------------------------------------------
 
+def e4m3_value(code) -> np.ndarray:
+    """The value of 8-bit floating-point codes in the OCP E4M3FN layout, exactly.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the
+    significand field m: e > 0 gives (1 + m/8) 2^(e-7), e = 0 gives
+    (m/8) 2^-6; the all-ones pattern S.1111.111 is NaN and there is no
+    infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(code).astype(np.int64)
+    sgn = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((e == 15) & (m == 7.0), np.nan, sgn * mag)
+
+
 def widen(x) -> np.ndarray:
     """Return the stored values of ``x`` exactly as float64.
 
     uint16 arrays are bf16 bit patterns: the 16 bits are the upper half of an
-    IEEE binary32, so shifting them up and reinterpreting is exact.
+    IEEE binary32, so shifting them up and reinterpreting is exact. uint8
+    arrays are 8-bit float codes (E4M3FN, see e4m3_value).
     """
     a = np.asarray(x)
+    if a.dtype == np.uint8:
+        return e4m3_value(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     if a.dtype in (np.float16, np.float32, np.float64):
@@ -296,7 +315,34 @@ def round_bf16(x) -> np.ndarray:
     return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: int = SSA_NORM_K):
+E4M3_MAX = 448.0
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Round float64 values to 8-bit E4M3FN codes (uint8): to nearest with ties
+    to an even significand, magnitudes beyond the largest finite value 448
+    saturated to +-448, NaN to the NaN code of its sign. The format has 4
+    significant bits for normal numbers (a value in [2^(e-1), 2^e) is rounded
+    to a multiple of 2^(e-4)) and the subnormal step 2^-9.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    q = np.ldexp(1.0, np.maximum(e - 4, -9))
+    with np.errstate(invalid="ignore"):
+        r = np.minimum(np.rint(a / q) * q, E4M3_MAX)
+    # encode the rounded magnitude: normal values (1 + m/8) 2^(E-7), subnormal m 2^-9
+    _, er = np.frexp(r)               # r = f 2^er, 0.5 <= f < 1
+    normal = r >= 2.0 ** -6
+    E = np.where(normal, er + 6, 0)   # exponent field: r in [2^(E-7), 2^(E-6))
+    m = np.where(normal, np.rint(r / np.ldexp(1.0, er - 4)) - 8, np.rint(r / 2.0 ** -9))
+    code = (E.astype(np.int64) << 3) | np.nan_to_num(m).astype(np.int64)
+    code = np.where(np.isnan(x), 0x7F, code) | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: int = SSA_NORM_K,
+                v_scale=None):
     """The cache rows that storing new tokens writes.
 
     "Sevren Sparse Attention learns to be sparse": the score takes the
@@ -314,4 +360,12 @@ def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: 
     kx = rms_normalize(k, eps) if flags & SSA_NORM_K else k
     if kv_dtype == "bf16":
         return {"k_exact": kx, "k": round_bf16(kx), "v": round_bf16(v)}
+    if kv_dtype == "fp8":
+        # 8-bit cache: keys as E4M3 codes (stored normalised they stay within
+        # +-sqrt(D), far inside the format's range); values divided by the
+        # KV head's scale (v_scale[..., None], broadcast over the leading
+        # axes), the quotient taken in float32 as the kernel forms it
+        s = np.asarray(v_scale, dtype=np.float32)[..., None, None]
+        vq = (np.asarray(v_new, dtype=np.float32) / s).astype(np.float64)
+        return {"k_exact": kx, "k": round_e4m3(kx), "v": round_e4m3(vq), "v_exact": vq}
     return {"k_exact": kx, "k": kx.astype(np.float32), "v": v.astype(np.float32)}

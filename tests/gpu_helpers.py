@@ -17,7 +17,7 @@ TOL_F32 = 1e-5
 
 
 def tol_for(wl) -> float:
-    return TOL_BF16 if wl.kv_dtype == "bf16" else TOL_F32
+    return TOL_F32 if wl.kv_dtype == "f32" else TOL_BF16
 
 
 def assert_rows_close(got: np.ndarray, ref: np.ndarray, tol: float, what: str = "") -> None:
@@ -73,10 +73,18 @@ def run_decode_full(wl, scale=1.0, c=1.0, eps=1e-6, flags=ssa.SSA_NORM_Q, cache=
             "vrows": vrows.cpu().numpy()}
 
 
+def oracle_v(wl):
+    """The value rows as the oracle takes them: the stored rows, or for an
+    8-bit cache their decoded codes times the KV head's scale."""
+    if wl.kv_dtype == "fp8":
+        return O.widen(wl.v) * wl.v_scale.astype(np.float64)[:, :, None, None]
+    return wl.v
+
+
 def check_decode_full(wl, scale=1.0, c=1.0, eps=1e-6, flags=ssa.SSA_NORM_Q, tol=None):
     """Run both sides on one workload and check out, scores, nnz and vrows."""
     got = run_decode_full(wl, scale, c, eps, flags)
-    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens, scale=scale, c=c, eps=eps, flags=flags)
+    ref = O.decode_full(wl.q, wl.k, oracle_v(wl), wl.ctx_lens, scale=scale, c=c, eps=eps, flags=flags)
     assert_rows_close(got["out"], ref["out"], tol or tol_for(wl), wl.name)
     bounds = score_bound(wl, scale, eps, flags)
     g = wl.n_q_heads // wl.n_kv_heads

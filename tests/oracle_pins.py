@@ -546,4 +546,61 @@ def pin_cache_write_invariants():
     _close(rf["k"], r["k_exact"], rtol=2.0 ** -23, what="float32 keys")
 
 
+# --------------------------------------------------------------------------
+# 8-bit KV cache (E4M3FN codes)
+# --------------------------------------------------------------------------
+
+def pin_e4m3_definition():
+    """Code values fixed by the E4M3FN layout (sign, 4-bit exponent with bias 7,
+    3-bit significand; subnormals (m/8) 2^-6; S.1111.111 is NaN, no
+    infinity), worked by hand, plus the layout's invariants: 254 finite codes,
+    the non-negative codes increasing with their bits, and the sign bit
+    negating."""
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0,
+             0xFE: -448.0}
+    for c, want in cases.items():
+        got = float(O.e4m3_value(np.array([c], dtype=np.uint8))[0])
+        assert got == want, f"code {c:#04x}: {got} != {want}"
+    allv = O.widen(np.arange(256, dtype=np.uint8))
+    assert np.isnan(allv[0x7F]) and np.isnan(allv[0xFF]) and np.isfinite(allv).sum() == 254
+    assert np.all(np.diff(allv[:0x7F]) > 0), "non-negative codes must increase"
+    assert np.array_equal(allv[0x80:0xFF], -allv[:0x7F]), "sign bit"
+
+
+def pin_round_e4m3_definition():
+    """Rounding into E4M3FN codes: every finite code's value maps back to it;
+    halfway cases go to the even significand (1 + 1/16 -> 1, 1 + 3/16 -> 1.25,
+    1.5 * 2^-9 -> 2^-8, 0.5 * 2^-9 -> 0); just above halfway rounds up;
+    magnitudes past 448 (and infinity) saturate to +-448."""
+    codes = np.arange(256, dtype=np.uint8)
+    fin = np.isfinite(O.e4m3_value(codes))
+    assert np.array_equal(O.round_e4m3(O.e4m3_value(codes[fin])), codes[fin]), "round trip"
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (1.0625 + 2.0 ** -30, 0x39), (1.5 * 2.0 ** -9, 0x02),
+             (0.5 * 2.0 ** -9, 0x00), (464.0, 0x7E), (1000.0, 0x7E), (-1e9, 0xFE), (np.inf, 0x7E),
+             (-0.0, 0x80), (0.3, 0x2A)]  # 0.3 = 1.2 * 2^-2: nearer 1.25 (m = 2) than 1.125
+    got = O.round_e4m3(np.array([c[0] for c in cases]))
+    for (x, want), g in zip(cases, got):
+        assert int(g) == want, f"round_e4m3({x!r}) = {int(g):#04x}, want {want:#04x}"
+    assert np.isnan(O.e4m3_value(O.round_e4m3(np.array([np.nan]))))[0]
+
+
+def pin_cache_write_fp8_golden():
+    """The hand-worked keys stored as 8-bit codes: RMS-1 rows of +-1, 2 and 0 are
+    exact codes (1 = 0x38, 2 = 0x40); values are divided by the KV head's
+    scale before rounding (scale 1/4: 1 -> 4 = 0x48, 5 -> 20 = 1.25 * 2^4 =
+    0x5A, 25 -> 100 = 1.5625 * 2^6, halfway between 96 and 104: 96 = 0x6C)."""
+    g = _golden()
+    ku = _arr(g["sparse_layer_norm_k"]["keys_unnormalised"]).astype(np.float32)
+    vals = np.nan_to_num(_arr(g["values"])).astype(np.float32)
+    r = O.cache_write(ku, vals, "fp8", eps=0.0, v_scale=np.float32(0.25))
+    want_k = {1.0: 0x38, -1.0: 0xB8, 2.0: 0x40, 0.0: 0x00}
+    keys = _arr(g["keys"])
+    assert np.array_equal(r["k"], np.vectorize(lambda x: want_k[x])(keys).astype(np.uint8)), "key codes"
+    assert int(r["v"][3, 1]) == 0x5A and int(r["v"][4, 2]) == 0x6C and int(r["v"][0, 0]) == 0x48, "value codes"
+    want_v = vals.astype(np.float64).copy()
+    want_v[4, 2], want_v[4, 3] = 24.0, -24.0  # the halfway case
+    _close(O.widen(r["v"]) * 0.25, want_v, what="values decode back")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -22,6 +22,7 @@ _orig_widen = O.widen
 _orig_sparse = O.decode_sparse
 _orig_select_all = O.select_all
 _orig_cache_write = O.cache_write
+_orig_round_e4m3 = O.round_e4m3
 
 
 def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
@@ -150,6 +151,30 @@ def _round_bf16_variant(kind):
     return rnd
 
 
+def _e4m3_fnuz(code):
+    c = np.asarray(code).astype(np.int64)
+    sgn = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -7), np.ldexp(1.0 + m / 8.0, e - 8))
+    return np.where(c == 0x80, np.nan, sgn * mag)
+
+
+def _round_e4m3_variant(kind):
+    def rnd(x):
+        x = np.asarray(x, dtype=np.float64)
+        if kind == "no_saturation":
+            big = np.abs(x) > O.E4M3_MAX
+            out = _orig_round_e4m3(np.where(big, 0.0, x))
+            return np.where(big, np.uint8(0x7F) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8), out)
+        # truncation: round the magnitude down to the code below
+        vals = O.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+        a = np.minimum(np.abs(x), O.E4M3_MAX)
+        idx = np.searchsorted(vals, a, side="right") - 1
+        return (idx.astype(np.int64) | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+    return rnd
+
+
 def _cache_write_variant(kind):
     def cw(k_new, v_new, kv_dtype="bf16", eps=1e-6, flags=O.SSA_NORM_K):
         if kind == "flags_ignored":
@@ -198,6 +223,9 @@ MUTANTS = {
     "round_bf16_half_away": ("round_bf16", _round_bf16_variant("half_away")),
     "cache_write_flags_ignored": ("cache_write", _cache_write_variant("flags_ignored")),
     "cache_write_values_normalised": ("cache_write", _cache_write_variant("values_normalised")),
+    "e4m3_fnuz_layout": ("e4m3_value", _e4m3_fnuz),
+    "round_e4m3_no_saturation": ("round_e4m3", _round_e4m3_variant("no_saturation")),
+    "round_e4m3_truncate": ("round_e4m3", _round_e4m3_variant("truncate")),
     "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
                                           if np.asarray(x).dtype != np.uint16
                                           else np.asarray(x).astype(np.float64) / 256.0)),
