@@ -87,7 +87,7 @@ def alg_bytes_full(wl, vrows: np.ndarray, with_scores: bool = True) -> dict:
 
 PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_step_b8_64k_128k.txt")
 KERNEL_SRCS = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_decode_relu_amd", "csrc", f)
-               for f in ("decode_full.hip", "select_core.h", "select.hip")]
+               for f in ("decode_full.hip", "select_core.h", "select.hip", "common.h")]
 
 
 def measured_traffic():
@@ -500,8 +500,9 @@ def main():
                       1 - float(nnz_np.sum()) / (Hq * float(wl.ctx_lens.astype(np.int64).sum())), 4)},
         "sparse_union_rows": int(union_rows),
         "roofline": {"kernel": ("ssa_decode_full (decode_full_kernel + combine)" if args.unfused else
-                                "ssa_decode_full_select (decode_full_kernel with candidate lists + "
-                                "combine_select + fallback for flagged rows)"),
+                                "ssa_decode_full_select (filter inputs, decode_full_kernel with "
+                                "candidate lists, flagging and rescoring of the rows the lists "
+                                "cannot select, combine + selection)"),
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if args.unfused else measured_traffic(),
