@@ -24,6 +24,10 @@ Source: the web page "The Architecture of Embla 1" (sevren.ai blog):
     KV head gives the key a nonzero weight.
   * "KV bridge, KV reuse, and prefill" -- the prompt is pushed through the
     full layer to fill its cache (causal prefill).
+  * "ReLU² activation" -- the MLPs square the positive part of each
+    neuron; a neuron at zero contributes nothing, so its row of the down
+    projection is never read. Reading: a plain (ungated, bias-free) MLP
+    y = sum_i ReLU(w_up[i] . x)^2 w_down[i]; the page names no hidden size.
 
 The displayed SSA formula itself did not survive on the page: the constant in
 the denominator and the hat symbols are missing from the text. Readings taken
@@ -369,3 +373,39 @@ def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: 
         vq = (np.asarray(v_new, dtype=np.float32) / s).astype(np.float64)
         return {"k_exact": kx, "k": round_e4m3(kx), "v": round_e4m3(vq), "v_exact": vq}
     return {"k_exact": kx, "k": kx.astype(np.float32), "v": v.astype(np.float32)}
+
+
+# --------------------------------------------------------------------------
+# ReLU^2 MLP with dead-neuron row skip
+# --------------------------------------------------------------------------
+
+def mlp_relu2(x, w_up, w_down):
+    """A ReLU^2 MLP for T tokens ("ReLU² activation": negative values become
+    zero and positive values are squared; a zero neuron's row of the down
+    projection contributes nothing and is never read).
+
+    x [T, d]; w_up [d_ff, d] (row i: neuron i's input weights); w_down
+    [d_ff, d] (row i: neuron i's output row). For each token:
+    h = w_up x, a_i = h_i^2 for h_i > 0 else 0, y = sum over neurons with
+    h_i > 0 of a_i w_down[i]. Only those rows of w_down are touched.
+
+    Returns y [T, d], h [T, d_ff], fired [T] (neurons with h_i > 0) and
+    rows_read (neurons that fired for some token: the down rows a batch reads).
+    """
+    xx = widen(x)
+    wu = widen(w_up)
+    wd = np.asarray(w_down)
+    T, d = xx.shape
+    y = np.zeros((T, d))
+    h_all = np.zeros((T, wu.shape[0]))
+    fired = np.zeros(T, dtype=np.int64)
+    used = np.zeros(wu.shape[0], dtype=bool)
+    for t in range(T):
+        h = wu @ xx[t]
+        live = np.flatnonzero(h > 0.0)
+        if live.size:
+            y[t] = (h[live] * h[live]) @ widen(wd[live])
+        h_all[t] = h
+        fired[t] = live.size
+        used[live] = True
+    return {"y": y, "h": h_all, "fired": fired, "rows_read": int(used.sum())}

@@ -603,4 +603,132 @@ def pin_cache_write_fp8_golden():
     _close(O.widen(r["v"]) * 0.25, want_v, what="values decode back")
 
 
+# --------------------------------------------------------------------------
+# ReLU^2 MLP with dead-neuron row skip ("ReLU² activation")
+# --------------------------------------------------------------------------
+
+def _mlp_golden_inputs():
+    g = _golden()["mlp"]
+    return g, (_arr(g["x"]).astype(np.float32), _arr(g["w_up"]).astype(np.float32),
+               _arr(g["w_down"]).astype(np.float32))
+
+
+def pin_mlp_golden():
+    """The hand-worked MLP case: h, y, per-token fired counts and rows read.
+    Rows of neurons that never fire (one of them sits exactly at h = 0) are
+    NaN, so an oracle that reads them, or that fires at h = 0, returns NaN."""
+    g, (x, wu, wd) = _mlp_golden_inputs()
+    r = O.mlp_relu2(x, wu, wd)
+    _close(r["h"], _arr(g["h"]), what="mlp h")
+    _close(r["y"], _arr(g["y"]), what="mlp y")
+    assert list(r["fired"]) == g["fired"], f"fired {r['fired']}"
+    assert r["rows_read"] == g["rows_read"], f"rows_read {r['rows_read']}"
+
+
+def _mlp_int_case(seed, T=3, d=6, d_ff=9):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-3, 4, (T, d)).astype(np.float32)
+    wu = rng.integers(-2, 3, (d_ff, d)).astype(np.float32)
+    wd = rng.integers(-4, 5, (d_ff, d)).astype(np.float32)
+    return x, wu, wd
+
+
+def pin_mlp_bruteforce_exact():
+    """Tiny integer MLPs worked in exact integers with plain loops: for each
+    token and output column, add h^2 * w_down[i][c] over the neurons whose
+    integer pre-activation is positive; count them; the rows read are the
+    size of the union of the fired sets."""
+    hit_zero = False
+    for seed in range(6):
+        x, wu, wd = _mlp_int_case(seed)
+        T, d = x.shape
+        d_ff = wu.shape[0]
+        want = np.zeros((T, d))
+        union = set()
+        fired = []
+        for t in range(T):
+            n = 0
+            for i in range(d_ff):
+                h = sum(int(wu[i, j]) * int(x[t, j]) for j in range(d))
+                hit_zero |= h == 0
+                if h > 0:
+                    n += 1
+                    union.add(i)
+                    for c in range(d):
+                        want[t, c] += h * h * int(wd[i, c])
+            fired.append(n)
+        r = O.mlp_relu2(x, wu, wd)
+        _close(r["y"], want, rtol=0, atol=0, what=f"mlp brute force seed {seed}")
+        assert list(r["fired"]) == fired and r["rows_read"] == len(union), f"counts seed {seed}"
+    assert hit_zero, "the cases should include a neuron exactly at zero"
+
+
+def pin_mlp_sign_split():
+    """Negating the input flips the sign of every pre-activation, so each
+    neuron with h != 0 fires for exactly one of x and -x: y(x) + y(-x) is the
+    ungated quadratic form sum_i h_i^2 w_down[i] (a plain matrix product), and
+    fired(x) + fired(-x) counts the neurons with h != 0."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 32)).astype(np.float32)
+    wu = rng.standard_normal((48, 32)).astype(np.float32)
+    wd = rng.standard_normal((48, 32)).astype(np.float32)
+    rp = O.mlp_relu2(x, wu, wd)
+    rn = O.mlp_relu2(-x, wu, wd)
+    h = x.astype(np.float64) @ wu.astype(np.float64).T
+    _close(rp["y"] + rn["y"], (h * h) @ wd.astype(np.float64), rtol=1e-10, atol=1e-9,
+           what="sign split")
+    assert np.array_equal(rp["fired"] + rn["fired"], np.count_nonzero(h, axis=1)), "fired split"
+
+
+def pin_mlp_homogeneity():
+    """ReLU^2 is positively homogeneous of degree two: for a > 0, y(a x) =
+    a^2 y(x) with the same neurons firing (a power of two keeps it exact)."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 40)).astype(np.float32)
+    wu = rng.standard_normal((64, 40)).astype(np.float32)
+    wd = rng.standard_normal((64, 40)).astype(np.float32)
+    r1 = O.mlp_relu2(x, wu, wd)
+    r2 = O.mlp_relu2(x * np.float32(4.0), wu, wd)
+    _close(r2["y"], 16.0 * r1["y"], rtol=1e-12, atol=1e-9, what="degree-two homogeneity")
+    assert np.array_equal(r1["fired"], r2["fired"])
+
+
+def pin_mlp_neuron_permutation():
+    """Relabelling the neurons (the same permutation on the rows of w_up and
+    w_down) changes nothing; permuting only the rows of w_down does."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 24)).astype(np.float32)
+    wu = rng.standard_normal((30, 24)).astype(np.float32)
+    wd = rng.standard_normal((30, 24)).astype(np.float32)
+    p = rng.permutation(30)
+    r = O.mlp_relu2(x, wu, wd)
+    _close(O.mlp_relu2(x, wu[p], wd[p])["y"], r["y"], rtol=1e-12, atol=1e-10, what="relabel")
+    assert not np.allclose(O.mlp_relu2(x, wu, wd[p])["y"], r["y"]), "down rows must follow neurons"
+
+
+def pin_mlp_single_neuron_closed_form():
+    """One neuron: y = max(u . x, 0)^2 w, in closed form for both signs."""
+    u = np.array([[0.5, -1.0, 2.0]], dtype=np.float32)
+    w = np.array([[3.0, 0.0, -1.0]], dtype=np.float32)
+    x = np.array([[2.0, 1.0, 1.0], [-2.0, -1.0, -1.0]], dtype=np.float32)
+    r = O.mlp_relu2(x, u, w)  # u . x = (2, -2)
+    _close(r["y"], np.array([[12.0, 0.0, -4.0], [0.0, 0.0, 0.0]]), what="single neuron")
+    assert list(r["fired"]) == [1, 0] and r["rows_read"] == 1
+
+
+def pin_mlp_rows_read_union():
+    """On a seeded batch the rows read equal the size of the union of the
+    tokens' fired sets (Python sets over the signs of a plain matrix
+    product), not the largest or the last token's count."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((4, 16)).astype(np.float32)
+    wu = rng.standard_normal((200, 16)).astype(np.float32)
+    wd = np.zeros((200, 16), dtype=np.float32)
+    h = x.astype(np.float64) @ wu.astype(np.float64).T
+    sets = [set(np.flatnonzero(h[t] > 0).tolist()) for t in range(4)]
+    r = O.mlp_relu2(x, wu, wd)
+    assert r["rows_read"] == len(set().union(*sets)) > max(len(s) for s in sets)
+    assert list(r["fired"]) == [len(s) for s in sets]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -23,6 +23,7 @@ _orig_sparse = O.decode_sparse
 _orig_select_all = O.select_all
 _orig_cache_write = O.cache_write
 _orig_round_e4m3 = O.round_e4m3
+_orig_mlp = O.mlp_relu2
 
 
 def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
@@ -187,6 +188,37 @@ def _cache_write_variant(kind):
     return cw
 
 
+def _mlp_variant(kind):
+    def mlp(x, w_up, w_down):
+        xx = O.widen(x)
+        wu = O.widen(w_up)
+        wd = np.asarray(w_down)
+        T, d = xx.shape
+        y = np.zeros((T, d))
+        h_all = np.zeros((T, wu.shape[0]))
+        fired = np.zeros(T, dtype=np.int64)
+        used = np.zeros(wu.shape[0], dtype=bool)
+        for t in range(T):
+            h = wu @ xx[t]
+            if kind == "fires_at_zero":
+                live = np.flatnonzero(h >= 0.0)
+            elif kind == "abs_activation":
+                live = np.flatnonzero(h != 0.0)
+            else:
+                live = np.flatnonzero(h > 0.0)
+            a = h[live] if kind == "not_squared" else h[live] * h[live]
+            rows = live + 1 if kind == "down_row_off_by_one" else live
+            if live.size:
+                y[t] = a @ O.widen(wd[np.minimum(rows, wd.shape[0] - 1)])
+            h_all[t] = h
+            fired[t] = live.size
+            if kind == "rows_read_last_token":
+                used[:] = False
+            used[live] = True
+        return {"y": y, "h": h_all, "fired": fired, "rows_read": int(used.sum())}
+    return mlp
+
+
 MUTANTS = {
     "weight_not_squared": ("relu2_attend", _attend_with(weights=lambda s: np.where(s > 0, s, 0.0))),
     "no_relu": ("relu2_attend", _attend_with(weights=lambda s: s * s)),
@@ -226,6 +258,11 @@ MUTANTS = {
     "e4m3_fnuz_layout": ("e4m3_value", _e4m3_fnuz),
     "round_e4m3_no_saturation": ("round_e4m3", _round_e4m3_variant("no_saturation")),
     "round_e4m3_truncate": ("round_e4m3", _round_e4m3_variant("truncate")),
+    "mlp_not_squared": ("mlp_relu2", _mlp_variant("not_squared")),
+    "mlp_fires_at_zero": ("mlp_relu2", _mlp_variant("fires_at_zero")),
+    "mlp_abs_activation": ("mlp_relu2", _mlp_variant("abs_activation")),
+    "mlp_down_row_off_by_one": ("mlp_relu2", _mlp_variant("down_row_off_by_one")),
+    "mlp_rows_read_last_token": ("mlp_relu2", _mlp_variant("rows_read_last_token")),
     "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
                                           if np.asarray(x).dtype != np.uint16
                                           else np.asarray(x).astype(np.float64) / 256.0)),
