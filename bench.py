@@ -56,13 +56,13 @@ def parse():
                    help="only run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-legs", action="store_true",
                    help="skip the other workloads (the headline line then holds no 'legs')")
-    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block,fp8",
+    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block,fp8,mlp",
                    help="comma-separated workloads measured after the headline: "
                         "tiny, single, fixed128k, sweep, block, fp8 (the headline batch "
-                        "with an 8-bit cache)")
+                        "with an 8-bit cache), mlp (the ReLU^2 MLP row skip)")
     p.add_argument("--leg-steps", type=int, default=20)
     p.add_argument("--workload", default=None,
-                   help="measure only this workload (tiny, single, fixed128k, sweep, block) and "
+                   help="measure only this workload (tiny, single, fixed128k, sweep, block, fp8, mlp) and "
                         "print its JSON object")
     return p.parse_args()
 
@@ -290,10 +290,68 @@ def bench_legs(names, steps: int) -> dict:
             legs[name] = bench_leg(synth.block_step(), n_sparse=3, steps=steps)
         elif name == "fp8":
             legs[name] = bench_leg(synth.batched_decode(kv_dtype="fp8"), n_sparse=1, steps=steps)
+        elif name == "mlp":
+            legs[name] = bench_mlp(5 * steps)
         else:
             raise ValueError(f"unknown workload {name}")
         log(f"[bench] leg {name} done in {time.perf_counter() - t0:.1f}s")
     return legs
+
+
+def bench_mlp(steps: int, warmup: int = 3, rotate_bytes: int = 1 << 30) -> dict:
+    """ReLU^2 MLP at width 2048 with 8192 neurons ("ReLU² activation"), bf16 weights.
+
+    For 1 and 4 tokens with ~22% of neurons firing per token, and for 1 token
+    with every neuron firing (the dense read, same kernel), one ssa_mlp_relu2
+    call is timed with HIP events. Weight copies are rotated past 1 GiB so
+    they come from HBM. Algorithmic bytes: all of w_up, the rows of w_down of
+    neurons that fired for some token, x in and y out.
+    """
+    import torch
+    from long_context_decode_relu_amd import ssa, synth
+    dev = torch.device("cuda:0")
+
+    def one(T, rate, seed):
+        wl = synth.mlp_workload(seed=seed, n_tokens=T, fire_rate=rate)
+        d, d_ff = wl.d_model, wl.d_ff
+        wbytes = 2 * 2 * d * d_ff
+        copies = max(1, -(-rotate_bytes // wbytes))
+        wu0 = torch.from_numpy(wl.w_up.view(np.int16)).view(torch.bfloat16).to(dev)
+        wd0 = torch.from_numpy(wl.w_down.view(np.int16)).view(torch.bfloat16).to(dev)
+        ws_up = [wu0] + [wu0.clone() for _ in range(copies - 1)]
+        ws_dn = [wd0] + [wd0.clone() for _ in range(copies - 1)]
+        x = torch.from_numpy(wl.x).to(dev)
+        y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        ws = ssa.mlp_workspace(T, d, d_ff, dev)
+        fired = torch.zeros(T, dtype=torch.int32, device=dev)
+        rows = torch.zeros(1, dtype=torch.int32, device=dev)
+        ssa.ssa_mlp_relu2(x, wu0, wd0, y=y, ws=ws, fired=fired, rows_read=rows)
+        for i in range(warmup):
+            ssa.ssa_mlp_relu2(x, ws_up[i % copies], ws_dn[i % copies], y=y, ws=ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (e0, e1) in enumerate(evs):
+            e0.record()
+            ssa.ssa_mlp_relu2(x, ws_up[i % copies], ws_dn[i % copies], y=y, ws=ws)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        n_rows = int(rows.item())
+        alg = 2 * d * d_ff + 2 * d * n_rows + 2 * 4 * T * d
+        gbs = alg / (ms * 1e-3) / 1e9
+        res = {"tokens": T, "d_model": d, "d_ff": d_ff, "copies_rotated": copies,
+               "avg_ms": round(ms, 5), "alg_bytes": alg, "gb_s": round(gbs, 1),
+               "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_read": n_rows,
+               "fired_per_token": fired.cpu().tolist(),
+               "down_bytes_saved": round(1 - n_rows / d_ff, 4),
+               "tokens_per_s": round(T / (ms * 1e-3), 1)}
+        del ws_up, ws_dn
+        torch.cuda.empty_cache()
+        return res
+
+    return {"t1_fire0.22": one(1, 0.22, 31), "t4_fire0.22": one(4, 0.22, 32),
+            "t1_dense": one(1, 0.99999, 33)}
 
 
 def bench_prefill(reps: int, warmup: int = 3) -> dict:

@@ -253,6 +253,42 @@ ssa_status ssa_prefill_full(const ssa_shape* shape, const void* q, int32_t n_que
                             const void* v, float scale, float c, float eps, uint32_t flags,
                             float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* ReLU^2 MLP for a few decode tokens that reads the down projection only
+ * where a neuron fired ("ReLU² activation": negative values become zero,
+ * positive values are squared, and a zero neuron's row of the down
+ * projection contributes nothing, so it is never read).
+ *
+ * For each token t < n_tokens:
+ *   h[t]    = w_up x[t]                     (h_i = dot(w_up[i], x[t]), float32 accumulation)
+ *   a_i     = h_i^2 if h_i > 0, else 0      (neuron i fires when h_i > 0)
+ *   y[t]    = sum over fired i of a_i w_down[i]
+ * Row i of w_down is read only when neuron i fires for at least one of the
+ * n_tokens tokens.
+ *
+ * Layout (dense, row-major; device pointers owned by the caller):
+ *   x       [n_tokens, d_model]  float32
+ *   w_up    [d_ff, d_model]      bf16 (row i: neuron i's input weights)
+ *   w_down  [d_ff, d_model]      bf16 (row i: neuron i's output row, i.e. the
+ *                                transpose of the usual [d_model, d_ff] matrix)
+ *   y       [n_tokens, d_model]  float32, fully written
+ *   h         optional [n_tokens, d_ff] float32: the pre-activations
+ *   fired     optional [n_tokens] int32: neurons that fired per token
+ *   rows_read optional [1] int32: rows of w_down read (neurons that fired for
+ *             some token)
+ * Sizes: 0 <= n_tokens <= SSA_MLP_MAX_TOKENS (more: SSA_ERR_UNSUPPORTED;
+ * 0 does nothing), d_model a multiple of 8 in [8, SSA_MLP_MAX_WIDTH],
+ * 1 <= d_ff <= SSA_MLP_MAX_NEURONS (else SSA_ERR_SHAPE). x, w_up, w_down and
+ * ws must be 16-byte aligned (else SSA_ERR_SHAPE). Scratch: ws of at least
+ * ssa_mlp_relu2_workspace_bytes(n_tokens, d_model, d_ff) bytes. */
+#define SSA_MLP_MAX_TOKENS 8
+#define SSA_MLP_MAX_WIDTH 65536
+#define SSA_MLP_MAX_NEURONS (1 << 24)
+size_t ssa_mlp_relu2_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t d_ff);
+ssa_status ssa_mlp_relu2(int32_t n_tokens, int32_t d_model, int32_t d_ff, const float* x,
+                         const void* w_up, const void* w_down, float* y, float* h,
+                         int32_t* fired, int32_t* rows_read, void* ws, size_t ws_bytes,
+                         void* stream);
+
 const char* ssa_status_string(ssa_status status);
 int32_t ssa_abi_version(void);
 

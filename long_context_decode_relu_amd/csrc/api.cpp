@@ -362,4 +362,42 @@ ssa_status ssa_cache_write(const ssa_shape* s, const float* k_new, const float* 
   return from_hip(launch_cache_write(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssa_mlp_relu2_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t d_ff) {
+  if (n_tokens < 1 || n_tokens > SSA_MLP_MAX_TOKENS || d_model < 8 || d_model % 8 ||
+      d_model > SSA_MLP_MAX_WIDTH || d_ff < 1 || d_ff > SSA_MLP_MAX_NEURONS)
+    return 0;
+  return mlp_ws_bytes(n_tokens, d_model, d_ff);
+}
+
+ssa_status ssa_mlp_relu2(int32_t n_tokens, int32_t d_model, int32_t d_ff, const float* x,
+                         const void* w_up, const void* w_down, float* y, float* h,
+                         int32_t* fired, int32_t* rows_read, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (n_tokens < 0 || d_model < 8 || d_model % 8 || d_model > SSA_MLP_MAX_WIDTH || d_ff < 1 ||
+      d_ff > SSA_MLP_MAX_NEURONS)
+    return SSA_ERR_SHAPE;
+  if (n_tokens > SSA_MLP_MAX_TOKENS) return SSA_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return SSA_OK;
+  if (!x || !w_up || !w_down || !y) return SSA_ERR_NULL;
+  const size_t need = mlp_ws_bytes(n_tokens, d_model, d_ff);
+  if (!ws || ws_bytes < need) return SSA_ERR_WORKSPACE;
+  // 16-byte vector loads of x, the weights and the scratch
+  auto misaligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 != 0; };
+  if (misaligned(x) || misaligned(w_up) || misaligned(w_down) || misaligned(ws))
+    return SSA_ERR_SHAPE;
+  MlpArgs a;
+  a.T = n_tokens;
+  a.d = d_model;
+  a.d_ff = d_ff;
+  a.x = x;
+  a.w_up = w_up;
+  a.w_down = w_down;
+  a.y = y;
+  a.h = h;
+  a.fired = fired;
+  a.rows_read = rows_read;
+  a.ws = ws;
+  return from_hip(launch_mlp_relu2(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -87,6 +87,20 @@ struct CacheWriteArgs {
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 
+struct MlpArgs {
+  int T, d, d_ff;
+  const float* x;       // [T, d]
+  const void* w_up;     // [d_ff, d] bf16
+  const void* w_down;   // [d_ff, d] bf16, row i = neuron i's output row
+  float* y;             // [T, d]
+  float* h;             // optional [T, d_ff]
+  int32_t* fired;       // optional [T]
+  int32_t* rows_read;   // optional [1]
+  void* ws;
+};
+size_t mlp_ws_bytes(int T, int d_model, int d_ff);
+hipError_t launch_mlp_relu2(const MlpArgs& a, hipStream_t stream);
+
 struct PrefillArgs {
   int B, Hq, Hkv, Nmax, max_ctx, Tq;
   const void* q;

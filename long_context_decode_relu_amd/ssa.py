@@ -43,7 +43,13 @@ SSA_OP_DECODE_FULL_SELECT = 4
 
 EXPORTED = ("ssa_abi_version", "ssa_status_string", "ssa_workspace_bytes", "ssa_decode_full",
             "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse",
-            "ssa_decode_sparse_static", "ssa_prefill_full", "ssa_cache_write")
+            "ssa_decode_sparse_static", "ssa_prefill_full", "ssa_cache_write",
+            "ssa_mlp_relu2_workspace_bytes", "ssa_mlp_relu2")
+
+# limits of ssa_mlp_relu2
+SSA_MLP_MAX_TOKENS = 8
+SSA_MLP_MAX_WIDTH = 65536
+SSA_MLP_MAX_NEURONS = 1 << 24
 
 # bytes of device scratch the library holds for ssa_decode_sparse_static
 SSA_STATIC_SCRATCH_BYTES = 16 << 20
@@ -96,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.ssa_prefill_full.argtypes = [SP, P, I32, P, P, P, P, F, F, F, U32, P, P, SZ, P]
         L.ssa_cache_write.restype = I32
         L.ssa_cache_write.argtypes = [SP, P, P, I32, P, F, U32, P, P, P]
+        L.ssa_mlp_relu2_workspace_bytes.restype = SZ
+        L.ssa_mlp_relu2_workspace_bytes.argtypes = [I32, I32, I32]
+        L.ssa_mlp_relu2.restype = I32
+        L.ssa_mlp_relu2.argtypes = [I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
         _lib = L
     return _lib
 
@@ -354,6 +364,48 @@ def ssa_prefill_full(q: torch.Tensor, q_pos0: torch.Tensor, cache: Cache, *, sca
                                 _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssa_prefill_full")
     return out
+
+
+def mlp_workspace(n_tokens: int, d_model: int, d_ff: int, device) -> torch.Tensor:
+    n = lib().ssa_mlp_relu2_workspace_bytes(n_tokens, d_model, d_ff)
+    _need(n > 0, f"no MLP workspace for n_tokens={n_tokens} d_model={d_model} d_ff={d_ff}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ssa_mlp_relu2(x: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor, *,
+                  y: torch.Tensor | None = None, h: torch.Tensor | None = None,
+                  fired: torch.Tensor | None = None, rows_read: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None) -> torch.Tensor:
+    """ReLU^2 MLP that reads w_down rows only for neurons that fired.
+
+    x [T, d] float32; w_up, w_down [d_ff, d] bf16 (w_down row i = neuron i's output row).
+    Optional outputs h [T, d_ff] float32, fired [T] int32, rows_read [1] int32.
+    Returns y [T, d] float32.
+    """
+    _need(x.is_cuda and x.dtype == torch.float32 and x.dim() == 2 and x.is_contiguous(),
+          "x must be contiguous float32 [T, d]")
+    T, d = x.shape
+    _need(w_up.dtype == torch.bfloat16 and w_up.dim() == 2 and w_up.shape[1] == d and w_up.is_contiguous(),
+          "w_up must be contiguous bf16 [d_ff, d]")
+    d_ff = w_up.shape[0]
+    _need(w_down.dtype == torch.bfloat16 and w_down.shape == w_up.shape and w_down.is_contiguous(),
+          "w_down must be contiguous bf16 [d_ff, d]")
+    for t, shape, dt in ((h, (T, d_ff), torch.float32), (fired, (T,), torch.int32),
+                         (rows_read, (1,), torch.int32)):
+        _need(t is None or (t.shape == shape and t.dtype == dt and t.is_contiguous()),
+              f"optional output must be {dt} {shape}")
+    dev = x.device
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    _need(y.shape == (T, d) and y.dtype == torch.float32 and y.is_contiguous(), "y must be float32 [T, d]")
+    if T == 0:
+        return y
+    if ws is None:
+        ws = mlp_workspace(T, d, d_ff, dev)
+    st = lib().ssa_mlp_relu2(T, d, d_ff, _ptr(x), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(h),
+                             _ptr(fired), _ptr(rows_read), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "ssa_mlp_relu2")
+    return y
 
 
 # --------------------------------------------------------------------------

@@ -26,6 +26,20 @@ divided by a per-(sequence, KV head) power-of-two scale, kept in
 ``Workload.v_scale``). Cache slots at or beyond a sequence's context length
 hold NaN so that any read past the live keys shows up in the output.
 Queries are float32 and are NOT normalised (the attention path does that).
+
+MLP recipe (``mlp_workload``; no trained weights are available):
+
+* tokens x are N(1, 1) per element (a positive mean, so every token shares a
+  component along the all-ones direction);
+* each up-projection row is N(0, 1/d) per element plus a shift mu along the
+  all-ones direction, mu = z * sqrt(2) / d with z the standard normal
+  quantile of the target firing rate: a token's pre-activations are then
+  about N(mu * d, 2), positive for that fraction of the neurons (22% by
+  default, the rate that leaves about 78% of the down-projection rows
+  unread at one token). Tokens share half the variance of each neuron, so
+  the fired sets of a batch overlap more than independent draws would;
+* down-projection rows are N(0, 1/(rate * d_ff)) per element.
+Weights are stored as bf16 bits (uint16), tokens as float32.
 """
 
 from __future__ import annotations
@@ -312,3 +326,35 @@ def prefill_chunk(seed: int = 5, batch: int = 1, n_query: int = 2048, n_keys: in
                            n_kv_heads=Hkv, head_dim=D, n_query=n_query,
                            kv_capacity=wl.kv_capacity, q_pos0=pos0.astype(np.int32),
                            q=to_bf16_bits(q), k=wl.k, v=wl.v, ctx_lens=ctx)
+
+
+@dataclass
+class MlpWorkload:
+    name: str
+    n_tokens: int
+    d_model: int
+    d_ff: int
+    fire_rate: float
+    x: np.ndarray        # [T, d] float32
+    w_up: np.ndarray     # [d_ff, d] bf16 bits (uint16)
+    w_down: np.ndarray   # [d_ff, d] bf16 bits (uint16), row i = neuron i's output row
+
+
+def mlp_workload(seed: int = 7, n_tokens: int = 1, d_model: int = 2048, d_ff: int = 8192,
+                 fire_rate: float = 0.22, name: str | None = None) -> MlpWorkload:
+    """Seeded tokens and ReLU^2 MLP weights (recipe in the module docstring)."""
+    from statistics import NormalDist
+    d = d_model
+    mu = NormalDist().inv_cdf(fire_rate) * np.sqrt(2.0) / d
+    x = (1.0 + _rng(seed, 10).standard_normal((n_tokens, d))).astype(np.float32)
+    wu = np.empty((d_ff, d), dtype=np.uint16)
+    wd = np.empty((d_ff, d), dtype=np.uint16)
+    step = 4096
+    for i0 in range(0, d_ff, step):
+        n = min(step, d_ff - i0)
+        r = _rng(seed, 11, i0)
+        wu[i0:i0 + n] = to_bf16_bits((r.standard_normal((n, d)) / np.sqrt(d) + mu).astype(np.float32))
+        wd[i0:i0 + n] = to_bf16_bits((r.standard_normal((n, d)) / np.sqrt(fire_rate * d_ff)).astype(np.float32))
+    return MlpWorkload(name=name or f"mlp_relu2_t{n_tokens}_{d}x{d_ff}", n_tokens=n_tokens,
+                       d_model=d, d_ff=d_ff, fire_rate=fire_rate, x=x, w_up=wu, w_down=wd)
+

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(ssa.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_match_header():
@@ -125,3 +125,23 @@ def test_sparse_and_prefill_reject():
                               FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_SHAPE
     assert L.ssa_prefill_full(ctypes.byref(s), FAKE, 16, FAKE, FAKE, FAKE, FAKE, 1.0, -2.0, 1e-6, 1,
                               FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_SHAPE
+
+
+def test_mlp_rejects():
+    L = ssa.lib()
+    W = L.ssa_mlp_relu2_workspace_bytes
+    assert W(1, 2048, 8192) > 0
+    assert W(8, 2048, 8192) > W(1, 2048, 8192)
+    assert W(0, 2048, 8192) == 0 and W(9, 2048, 8192) == 0
+    assert W(1, 12, 64) == 0 and W(1, 2048, 0) == 0 and W(1, 1 << 17, 64) == 0
+    f = lambda T, d, dff, x=FAKE, ws_=FAKE, wb=1 << 40: L.ssa_mlp_relu2(
+        T, d, dff, x, FAKE, FAKE, FAKE, None, None, None, ws_, wb, None)
+    assert f(1, 12, 64) == ssa.SSA_ERR_SHAPE
+    assert f(1, 0, 64) == ssa.SSA_ERR_SHAPE
+    assert f(1, 2048, 0) == ssa.SSA_ERR_SHAPE
+    assert f(-1, 2048, 64) == ssa.SSA_ERR_SHAPE
+    assert f(9, 2048, 64) == ssa.SSA_ERR_UNSUPPORTED
+    assert f(1, 2048, 64, x=None) == ssa.SSA_ERR_NULL
+    assert f(1, 2048, 64, ws_=None) == ssa.SSA_ERR_WORKSPACE
+    assert f(1, 2048, 64, wb=W(1, 2048, 64) - 1) == ssa.SSA_ERR_WORKSPACE
+    assert f(0, 2048, 64, x=None) == ssa.SSA_OK  # no tokens: nothing to do
