@@ -24,6 +24,12 @@ Source: the web page "The Architecture of Embla 1" (sevren.ai blog):
     KV head gives the key a nonzero weight.
   * "KV bridge, KV reuse, and prefill" -- the prompt is pushed through the
     full layer to fill its cache (causal prefill).
+  * "Three kinds of attention" (window layers) -- the 128 most recent tokens
+    with an ordinary softmax; the only layers with a position encoding,
+    RoPE. Readings: RoPE as RoFormer defines it (pairs (2i, 2i+1), theta_i =
+    base^(-2i/D), base 10000; the (i, i + D/2) layout by flag); keys rotated
+    at their positions when stored; the query rotated at its position n - 1;
+    softmax scale 1/sqrt(D); no normalisation of q or k;
   * "ReLU² activation" -- the MLPs square the positive part of each
     neuron; a neuron at zero contributes nothing, so its row of the down
     projection is never read. Reading: a plain (ungated, bias-free) MLP
@@ -58,6 +64,8 @@ import numpy as np
 SSA_NORM_Q = 1
 SSA_NORM_K = 2
 SSA_SELECT_DISJOINT = 4
+SSA_ROPE = 8          # window decode: rotate the query at its position
+SSA_ROPE_HALF = 16    # RoPE pairs (i, i + D/2) instead of (2i, 2i + 1)
 
 
 # --------------------------------------------------------------------------
@@ -369,6 +377,93 @@ def cache_write(k_new, v_new, kv_dtype: str = "bf16", eps: float = 1e-6, flags: 
         # +-sqrt(D), far inside the format's range); values divided by the
         # KV head's scale (v_scale[..., None], broadcast over the leading
         # axes), the quotient taken in float32 as the kernel forms it
+        s = np.asarray(v_scale, dtype=np.float32)[..., None, None]
+        vq = (np.asarray(v_new, dtype=np.float32) / s).astype(np.float64)
+        return {"k_exact": kx, "k": round_e4m3(kx), "v": round_e4m3(vq), "v_exact": vq}
+    return {"k_exact": kx, "k": kx.astype(np.float32), "v": v.astype(np.float32)}
+
+
+# --------------------------------------------------------------------------
+# Sliding-window softmax decode with RoPE ("Three kinds of attention")
+# --------------------------------------------------------------------------
+
+def rope(x, pos, base: float = 10000.0, half: bool = False) -> np.ndarray:
+    """Rotary position encoding (RoFormer, Su et al. 2021): the pair
+    (x_a, x_b) number i turns by the angle pos * theta_i, theta_i =
+    base^(-2i/D), i < D/2: x_a' = x_a cos - x_b sin, x_b' = x_a sin + x_b cos.
+    Pairs are (2i, 2i + 1), RoFormer's layout, or (i, i + D/2) with half=True.
+
+    x [..., D]; pos broadcast against x[..., 0]. float64 throughout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    i = np.arange(D // 2, dtype=np.float64)
+    theta = float(base) ** (-2.0 * i / D)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    ia = np.arange(D // 2) if half else np.arange(0, D, 2)
+    ib = ia + D // 2 if half else ia + 1
+    xa, xb = x[..., ia], x[..., ib]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (D,)))
+    out[..., ia] = xa * c - xb * s
+    out[..., ib] = xa * s + xb * c
+    return out
+
+
+def decode_window(q, k, v, ctx_lens, window: int = 128, scale: float | None = None,
+                  rope_base: float = 10000.0, flags: int = SSA_ROPE) -> np.ndarray:
+    """Window-layer decode, one query token per sequence ("Three kinds of
+    attention": a window layer reads the 128 most recent tokens with an
+    ordinary softmax, so every key in the window gets some weight, and these
+    are the only layers that encode position, with RoPE).
+
+    q [B, Hq, D]; k, v [B, Hkv, Nmax, D] value arrays, keys stored already
+    rotated at their positions; position j lives in slot j mod Nmax (a ring
+    buffer when Nmax is the window, a plain cache when Nmax >= every length).
+    For sequence b with n = ctx_lens[b] the window is positions
+    max(0, n - window) .. n - 1, the query is the token at position n - 1
+    (rotated there with SSA_ROPE), and out = sum_j softmax_j(scale q . k_j) v_j
+    with scale 1/sqrt(D) by default. n <= 0 gives 0. Query head h reads KV
+    head h / (Hq / Hkv).
+    """
+    q = widen(q)
+    B, Hq, D = q.shape
+    Hkv, Nmax = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(ctx_lens[b])
+        if n <= 0:
+            continue
+        slots = np.arange(max(0, n - window), n) % Nmax
+        for h in range(Hq):
+            qv = q[b, h]
+            if flags & SSA_ROPE:
+                qv = rope(qv, n - 1, rope_base, half=bool(flags & SSA_ROPE_HALF))
+            out[b, h] = softmax_attend(qv, widen(k[b, h // g, slots]), widen(v[b, h // g, slots]), scale)
+    return out
+
+
+def cache_write_rope(k_new, v_new, pos, kv_dtype: str = "bf16", rope_base: float = 10000.0,
+                     flags: int = 0, v_scale=None):
+    """The rows a window layer stores for new tokens: each key rotated at its
+    own position ("Three kinds of attention": window layers encode position
+    with RoPE; a cached key keeps the rotation of the position it was made at),
+    then rounded once to the storage type; values rounded once as given
+    (8-bit: divided by the KV head's scale, the quotient taken in float32).
+
+    k_new, v_new [..., D] float32; pos [...] the rows' positions. Returns
+    ``k_exact`` (rotated keys, float64) and the stored ``k`` and ``v`` as in
+    cache_write.
+    """
+    kx = rope(widen(np.asarray(k_new, dtype=np.float32)), pos, rope_base,
+              half=bool(flags & SSA_ROPE_HALF))
+    v = widen(np.asarray(v_new, dtype=np.float32))
+    if kv_dtype == "bf16":
+        return {"k_exact": kx, "k": round_bf16(kx), "v": round_bf16(v)}
+    if kv_dtype == "fp8":
         s = np.asarray(v_scale, dtype=np.float32)[..., None, None]
         vq = (np.asarray(v_new, dtype=np.float32) / s).astype(np.float64)
         return {"k_exact": kx, "k": round_e4m3(kx), "v": round_e4m3(vq), "v_exact": vq}

@@ -39,8 +39,9 @@ def _num(s):
         return float(s)
     if s == "nan":
         return float("nan")
-    if "e" in s:  # closed form in Euler's number
-        return float(eval(s, {"__builtins__": {}}, {"e": math.e}))
+    if any(ch.isalpha() for ch in s):  # closed form in e, pi, cos, sin
+        return float(eval(s, {"__builtins__": {}},
+                          {"e": math.e, "pi": math.pi, "cos": math.cos, "sin": math.sin}))
     return float(Fraction(s))
 
 
@@ -601,6 +602,153 @@ def pin_cache_write_fp8_golden():
     want_v = vals.astype(np.float64).copy()
     want_v[4, 2], want_v[4, 3] = 24.0, -24.0  # the halfway case
     _close(O.widen(r["v"]) * 0.25, want_v, what="values decode back")
+
+
+# --------------------------------------------------------------------------
+# sliding-window softmax decode with RoPE ("Three kinds of attention")
+# --------------------------------------------------------------------------
+
+def pin_rope_golden():
+    """RoPE worked by hand at D = 4 for both pair layouts (theta_0 = 1 rad and,
+    with base 4/pi^2, theta_1 = pi/2: pins the exponent -2i/D)."""
+    g = _golden()["window"]["rope"]
+    x = np.array(g["x"], dtype=np.float64)
+    base = _num(g["base"])
+    _close(O.rope(x, g["pos"], base), _arr(g["interleaved"]), what="rope pairs (2i, 2i+1)")
+    _close(O.rope(x, g["pos"], base, half=True), _arr(g["half"]), what="rope pairs (i, i+D/2)")
+
+
+def _rope_complex(x, pos, base):
+    """RoPE on pairs (2i, 2i+1) as complex multiplication by exp(1j pos theta_i)."""
+    D = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * pos * base ** (-2.0 * np.arange(D // 2) / D))
+    out = np.empty(x.shape)
+    out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+def pin_rope_complex_and_invariants():
+    """Against complex multiplication (pairs as complex numbers, an independent
+    route to the rotation), at positions up to 2^30; the half layout is the
+    same rotation on permuted dimensions; norms are kept; position 0 is the
+    identity; the dot product of a rotated query and key depends only on the
+    difference of their positions."""
+    rng = np.random.default_rng(40)
+    D = 128
+    x = rng.standard_normal((6, D))
+    pos = np.array([0, 1, 7, 4095, 123457, 2 ** 30 - 3])
+    want = _rope_complex(x, pos[:, None], 10000.0)
+    _close(O.rope(x, pos, 10000.0), want, rtol=1e-9, atol=1e-9, what="rope vs complex")
+    perm = np.empty(D, dtype=np.int64)
+    perm[0::2], perm[1::2] = np.arange(D // 2), np.arange(D // 2) + D // 2
+    _close(O.rope(x[:, perm], pos, 10000.0)[:, np.argsort(perm)], O.rope(x, pos, 10000.0, half=True),
+           rtol=1e-12, atol=1e-12, what="half layout = permuted pairs")
+    _close(np.linalg.norm(O.rope(x, pos, 500.0), axis=1), np.linalg.norm(x, axis=1), rtol=1e-12,
+           what="rope keeps norms")
+    _close(O.rope(x, 0, 10000.0), x, rtol=0, atol=0, what="position 0")
+    q, k = x[0], x[1]
+    for half in (False, True):
+        d1 = O.rope(q, 1000, 10000.0, half) @ O.rope(k, 990, 10000.0, half)
+        d2 = O.rope(q, 50010, 10000.0, half) @ O.rope(k, 50000, 10000.0, half)
+        _close(d1, d2, rtol=1e-9, atol=1e-9, what="relative position")
+
+
+def _window_golden_case():
+    g = _golden()["window"]["decode"]
+    q = _arr(g["q"])[None]                    # [1, 1, 2]
+    k = _arr(g["keys_stored"])[None, None]    # [1, 1, 2, 2]
+    v = _arr(g["values"])[None, None]
+    return g, q, k, v, np.array([g["ctx"]])
+
+
+def pin_window_golden():
+    """The hand-worked D = 2 window case: the query turns at position n - 1,
+    keys are used as stored; window 2 and window 1; RoPE off."""
+    g, q, k, v, ctx = _window_golden_case()
+    _close(O.decode_window(q, k, v, ctx, window=2, scale=1.0)[0, 0], _arr(g["out_window2"]), what="window 2")
+    _close(O.decode_window(q, k, v, ctx, window=1, scale=1.0)[0, 0], _arr(g["out_window1"]), what="window 1")
+    _close(O.decode_window(q, k, v, ctx, window=2, scale=1.0, flags=0)[0, 0], _arr(g["out_no_rope"]),
+           what="no rope")
+
+
+def pin_window_equals_sdpa():
+    """On seeded GQA caches: the window output equals textbook softmax attention
+    (torch's scaled_dot_product_attention in float64 on the CPU) over the last
+    `window` keys, with the query rotated by complex multiplication at n - 1."""
+    import torch
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, N, D, W = 3, 8, 2, 300, 128, 128
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, N, D))
+    v = rng.standard_normal((B, Hkv, N, D))
+    ctx = np.array([300, 77, 129])
+    got = O.decode_window(q, k, v, ctx, window=W)
+    for b in range(B):
+        n = int(ctx[b])
+        lo = max(0, n - W)
+        for h in range(Hq):
+            qr = _rope_complex(q[b, h], n - 1, 10000.0)
+            kk = torch.from_numpy(k[b, h // (Hq // Hkv), lo:n])[None, None]
+            vv = torch.from_numpy(v[b, h // (Hq // Hkv), lo:n])[None, None]
+            want = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qr)[None, None, None], kk, vv)[0, 0, 0].numpy()
+            _close(got[b, h], want, rtol=1e-10, atol=1e-12, what=f"window sdpa b{b} h{h}")
+
+
+def pin_window_ring_equals_linear():
+    """A ring buffer of capacity `window` (position j in slot j mod window)
+    gives the same output as a plain cache; slots of a plain cache outside the
+    window hold NaN and are never read; an empty context gives 0."""
+    rng = np.random.default_rng(42)
+    D, W, n = 16, 8, 21
+    q = rng.standard_normal((1, 2, D))
+    lin_k = np.full((1, 1, 32, D), np.nan)
+    lin_v = np.full((1, 1, 32, D), np.nan)
+    lin_k[0, 0, n - W:n] = rng.standard_normal((W, D))
+    lin_v[0, 0, n - W:n] = rng.standard_normal((W, D))
+    ring_k = np.zeros((1, 1, W, D))
+    ring_v = np.zeros((1, 1, W, D))
+    for j in range(n - W, n):
+        ring_k[0, 0, j % W] = lin_k[0, 0, j]
+        ring_v[0, 0, j % W] = lin_v[0, 0, j]
+    a = O.decode_window(q, lin_k, lin_v, np.array([n]), window=W)
+    r = O.decode_window(q, ring_k, ring_v, np.array([n]), window=W)
+    assert np.all(np.isfinite(a)), "read outside the window"
+    _close(a, r, rtol=1e-13, atol=1e-13, what="ring vs linear")
+    assert np.all(O.decode_window(q, ring_k, ring_v, np.array([0]), window=W) == 0.0)
+
+
+def pin_window_shift_invariance():
+    """Relative positions only: moving the whole context by 1000 positions
+    (keys rotated at their new positions, the query at its new position)
+    leaves the output unchanged."""
+    rng = np.random.default_rng(43)
+    D, n, W = 64, 40, 32
+    q = rng.standard_normal((1, 1, D))
+    kr = rng.standard_normal((n, D))
+    v = rng.standard_normal((1, 1, n + 1000, D))
+    v[0, 0, 1000:] = v[0, 0, :n]
+    k0 = O.rope(kr, np.arange(n), 10000.0)[None, None]
+    k1 = np.zeros((1, 1, n + 1000, D))
+    k1[0, 0, 1000:] = O.rope(kr, np.arange(n) + 1000, 10000.0)
+    a = O.decode_window(q, k0, v[:, :, :n], np.array([n]), window=W)
+    b = O.decode_window(q, k1, v, np.array([n + 1000]), window=W)
+    _close(a, b, rtol=1e-9, atol=1e-9, what="shift invariance")
+
+
+def pin_cache_write_rope():
+    """Stored window keys are the keys rotated at their own positions (checked
+    against complex multiplication), rounded once; values rounded once."""
+    rng = np.random.default_rng(44)
+    k = rng.standard_normal((5, 128)).astype(np.float32)
+    v = rng.standard_normal((5, 128)).astype(np.float32)
+    pos = np.array([0, 3, 127, 65536, 2 ** 28 + 5])
+    r = O.cache_write_rope(k, v, pos, "bf16")
+    _close(r["k_exact"], _rope_complex(k.astype(np.float64), pos[:, None], 10000.0), rtol=1e-9,
+           atol=1e-9, what="rotated keys")
+    assert np.array_equal(r["k"], O.round_bf16(r["k_exact"]))
+    assert np.array_equal(r["v"], _bf16_from_f32_bits(v))
 
 
 # --------------------------------------------------------------------------

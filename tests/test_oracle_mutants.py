@@ -24,6 +24,8 @@ _orig_select_all = O.select_all
 _orig_cache_write = O.cache_write
 _orig_round_e4m3 = O.round_e4m3
 _orig_mlp = O.mlp_relu2
+_orig_rope = O.rope
+_orig_window = O.decode_window
 
 
 def _attend_with(weights=None, den_fn=None, c_override=None, values_from_keys=False):
@@ -219,6 +221,37 @@ def _mlp_variant(kind):
     return mlp
 
 
+def _rope_variant(kind):
+    def rope(x, pos, base=10000.0, half=False):
+        if kind == "negative_angle":
+            return _orig_rope(x, -np.asarray(pos, dtype=np.float64), base, half)
+        if kind == "half_ignored":
+            return _orig_rope(x, pos, base, False)
+        if kind == "theta_exponent":
+            x = np.asarray(x, dtype=np.float64)
+            D = x.shape[-1]
+            # theta_i = base^(-i/D): the same as base' = sqrt(base) at exponent -2i/D
+            return _orig_rope(x, pos, float(base) ** 0.5, half)
+        raise ValueError(kind)
+    return rope
+
+
+def _window_variant(kind):
+    def window_fn(q, k, v, ctx_lens, window=128, scale=None, rope_base=10000.0, flags=O.SSA_ROPE):
+        if kind == "extra_key":
+            return _orig_window(q, k, v, ctx_lens, window + 1, scale, rope_base, flags)
+        if kind == "unit_scale" and scale is None:
+            return _orig_window(q, k, v, ctx_lens, window, 1.0, rope_base, flags)
+        if kind == "query_at_n":
+            qq = O.widen(q).copy()
+            if flags & O.SSA_ROPE:
+                for b in range(qq.shape[0]):
+                    qq[b] = O.rope(qq[b], int(ctx_lens[b]), rope_base, bool(flags & O.SSA_ROPE_HALF))
+            return _orig_window(qq, k, v, ctx_lens, window, scale, rope_base, flags & ~O.SSA_ROPE)
+        return _orig_window(q, k, v, ctx_lens, window, scale, rope_base, flags)
+    return window_fn
+
+
 MUTANTS = {
     "weight_not_squared": ("relu2_attend", _attend_with(weights=lambda s: np.where(s > 0, s, 0.0))),
     "no_relu": ("relu2_attend", _attend_with(weights=lambda s: s * s)),
@@ -263,6 +296,12 @@ MUTANTS = {
     "mlp_abs_activation": ("mlp_relu2", _mlp_variant("abs_activation")),
     "mlp_down_row_off_by_one": ("mlp_relu2", _mlp_variant("down_row_off_by_one")),
     "mlp_rows_read_last_token": ("mlp_relu2", _mlp_variant("rows_read_last_token")),
+    "rope_negative_angle": ("rope", _rope_variant("negative_angle")),
+    "rope_half_ignored": ("rope", _rope_variant("half_ignored")),
+    "rope_theta_exponent": ("rope", _rope_variant("theta_exponent")),
+    "window_extra_key": ("decode_window", _window_variant("extra_key")),
+    "window_unit_scale": ("decode_window", _window_variant("unit_scale")),
+    "window_query_at_n": ("decode_window", _window_variant("query_at_n")),
     "bf16_low_half": ("widen", lambda x: (np.asarray(x).astype(np.float64)
                                           if np.asarray(x).dtype != np.uint16
                                           else np.asarray(x).astype(np.float64) / 256.0)),
