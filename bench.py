@@ -56,13 +56,15 @@ def parse():
                    help="only run a plain device copy of known size (counter calibration)")
     p.add_argument("--no-legs", action="store_true",
                    help="skip the other workloads (the headline line then holds no 'legs')")
-    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block,fp8,mlp",
+    p.add_argument("--legs", default="tiny,single,fixed128k,sweep,block,fp8,window,mlp",
                    help="comma-separated workloads measured after the headline: "
                         "tiny, single, fixed128k, sweep, block, fp8 (the headline batch "
-                        "with an 8-bit cache), mlp (the ReLU^2 MLP row skip)")
+                        "with an 8-bit cache), window (sliding-window layer with RoPE), "
+                        "mlp (the ReLU^2 MLP row skip)")
     p.add_argument("--leg-steps", type=int, default=20)
     p.add_argument("--workload", default=None,
-                   help="measure only this workload (tiny, single, fixed128k, sweep, block, fp8, mlp) and "
+                   help="measure only this workload (tiny, single, fixed128k, sweep, block, fp8, window, "
+                        "mlp) and "
                         "print its JSON object")
     return p.parse_args()
 
@@ -290,6 +292,8 @@ def bench_legs(names, steps: int) -> dict:
             legs[name] = bench_leg(synth.block_step(), n_sparse=3, steps=steps)
         elif name == "fp8":
             legs[name] = bench_leg(synth.batched_decode(kv_dtype="fp8"), n_sparse=1, steps=steps)
+        elif name == "window":
+            legs[name] = bench_window(5 * steps)
         elif name == "mlp":
             legs[name] = bench_mlp(5 * steps)
         else:
@@ -298,13 +302,112 @@ def bench_legs(names, steps: int) -> dict:
     return legs
 
 
+def graph_ms(fn, n: int) -> tuple[float, str]:
+    """Average device time of fn(0), ..., fn(n-1): captured once into a HIP
+    graph and replayed (so the host's launch rate does not pace small kernels),
+    timed with events around the replay on the current stream. Falls back to
+    events around eager calls if capture fails."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, "graph"
+    except Exception as ex:  # noqa: BLE001 - timing method only
+        log(f"[bench] graph capture failed ({ex}); timing eager calls")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, "events"
+
+
+def bench_window(steps: int, warmup: int = 3, rotate_bytes: int = 768 << 20) -> dict:
+    """Window layer decode ("Three kinds of attention"): 16 query / 2 KV heads, D 128,
+    bf16, a 128-row ring buffer per (sequence, KV head), contexts U[64K, 128K] (RoPE at
+    those positions). One step: ssa_cache_write_rope of the new token, then
+    ssa_decode_window, for batch 8 and for a serving batch of 256, timed in a HIP
+    graph replay (graph_ms). Ring copies are rotated past 768 MB so reads come
+    from HBM.
+
+    Algorithmic bytes: decode reads the window's K and V rows and q, writes out; the
+    write reads the new k, v (float32) and writes one row of each.
+    """
+    import torch
+    from long_context_decode_relu_amd import ssa, synth
+    dev = torch.device("cuda:0")
+
+    def one(B, seed):
+        ctx = synth.batched_ctx_lens(seed=seed, batch=B)
+        W, Hq, Hkv, D = 128, 16, 2, 128
+        wt = synth.window_tokens(seed=seed, ctx_lens=ctx - 1, n_q_heads=Hq, n_kv_heads=Hkv, window=W)
+        base = ssa.Cache(k=torch.empty((B, Hkv, W, D), dtype=torch.bfloat16, device=dev),
+                         v=torch.empty((B, Hkv, W, D), dtype=torch.bfloat16, device=dev),
+                         ctx_lens=torch.from_numpy(ctx.astype(np.int32)).to(dev), max_ctx_len=0)
+        # the previous 128 tokens (positions n-129 .. n-2), rotated and stored by the library
+        ssa.ssa_cache_write_rope(base, torch.from_numpy(wt.k_raw).to(dev), torch.from_numpy(wt.v_raw).to(dev),
+                                 torch.from_numpy(wt.pos[:, 0].astype(np.int32)).to(dev))
+        cache_bytes = 2 * base.k.numel() * 2
+        copies = max(1, min(1024, -(-rotate_bytes // cache_bytes)))
+        caches = [base] + [ssa.Cache(k=base.k.clone(), v=base.v.clone(), ctx_lens=base.ctx_lens, max_ctx_len=0)
+                           for _ in range(copies - 1)]
+        r = np.random.default_rng(seed)
+        q = torch.from_numpy(r.standard_normal((B, Hq, D)).astype(np.float32)).to(dev)
+        k_new = torch.from_numpy(r.standard_normal((B, Hkv, 1, D)).astype(np.float32)).to(dev)
+        v_new = torch.from_numpy(r.standard_normal((B, Hkv, 1, D)).astype(np.float32)).to(dev)
+        pos = (base.ctx_lens - 1).contiguous()
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+        def write(i):
+            ssa.ssa_cache_write_rope(caches[i % copies], k_new, v_new, pos)
+
+        def decode(i):
+            ssa.ssa_decode_window(q, caches[i % copies], window=W, out=out)
+
+        def step(i):
+            write(i)
+            decode(i)
+
+        for i in range(warmup):
+            step(i)
+        ms, how = graph_ms(step, steps)
+        w_ms, _ = graph_ms(write, steps)
+        d_ms, _ = graph_ms(decode, steps)
+        dec = B * Hkv * W * D * 2 * 2 + 2 * B * Hq * D * 4
+        wr = B * Hkv * D * (2 * 4 + 2 * 2)
+        gbs = dec / (d_ms * 1e-3) / 1e9
+        res = {"batch": B, "window": W, "ring_copies_rotated": copies, "timing": how,
+               "ms_per_step": round(ms, 5),
+               "query_tok_per_s": round(B / (ms * 1e-3), 1),
+               "decode_window": {"avg_ms": round(d_ms, 5), "alg_bytes": dec, "gb_s": round(gbs, 1),
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4)},
+               "cache_write_rope": {"avg_ms": round(w_ms, 5), "alg_bytes": wr}}
+        del caches
+        torch.cuda.empty_cache()
+        return res
+
+    return {"b8": one(8, 3), "b256": one(256, 13)}
+
+
 def bench_mlp(steps: int, warmup: int = 3, rotate_bytes: int = 1 << 30) -> dict:
     """ReLU^2 MLP at width 2048 with 8192 neurons ("ReLU² activation"), bf16 weights.
 
     For 1 and 4 tokens with ~22% of neurons firing per token, and for 1 token
-    with every neuron firing (the dense read, same kernel), one ssa_mlp_relu2
-    call is timed with HIP events. Weight copies are rotated past 1 GiB so
-    they come from HBM. Algorithmic bytes: all of w_up, the rows of w_down of
+    with every neuron firing (the dense read, same kernel), ssa_mlp_relu2 calls
+    are timed in a HIP graph replay (graph_ms). Weight copies are rotated past
+    1 GiB so they come from HBM. Algorithmic bytes: all of w_up, the rows of w_down of
     neurons that fired for some token, x in and y out.
     """
     import torch
@@ -326,21 +429,17 @@ def bench_mlp(steps: int, warmup: int = 3, rotate_bytes: int = 1 << 30) -> dict:
         fired = torch.zeros(T, dtype=torch.int32, device=dev)
         rows = torch.zeros(1, dtype=torch.int32, device=dev)
         ssa.ssa_mlp_relu2(x, wu0, wd0, y=y, ws=ws, fired=fired, rows_read=rows)
+
+        def call(i):
+            ssa.ssa_mlp_relu2(x, ws_up[i % copies], ws_dn[i % copies], y=y, ws=ws)
+
         for i in range(warmup):
-            ssa.ssa_mlp_relu2(x, ws_up[i % copies], ws_dn[i % copies], y=y, ws=ws)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for i, (e0, e1) in enumerate(evs):
-            e0.record()
-            ssa.ssa_mlp_relu2(x, ws_up[i % copies], ws_dn[i % copies], y=y, ws=ws)
-            e1.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+            call(i)
+        ms, how = graph_ms(call, steps)
         n_rows = int(rows.item())
         alg = 2 * d * d_ff + 2 * d * n_rows + 2 * 4 * T * d
         gbs = alg / (ms * 1e-3) / 1e9
-        res = {"tokens": T, "d_model": d, "d_ff": d_ff, "copies_rotated": copies,
+        res = {"tokens": T, "d_model": d, "d_ff": d_ff, "copies_rotated": copies, "timing": how,
                "avg_ms": round(ms, 5), "alg_bytes": alg, "gb_s": round(gbs, 1),
                "frac": round(gbs / HBM_PEAK_GBS, 4), "rows_read": n_rows,
                "fired_per_token": fired.cpu().tolist(),

@@ -81,7 +81,9 @@ typedef enum { SSA_F32 = 0, SSA_BF16 = 1, SSA_FP8_E4M3 = 2 } ssa_dtype;
 enum {
   SSA_NORM_Q = 1,          /* RMS-normalise each query row in the kernel */
   SSA_NORM_K = 2,          /* RMS-normalise each key row on the fly (else keys are stored normalised) */
-  SSA_SELECT_DISJOINT = 4  /* selection = recent window + top-k of the keys outside it */
+  SSA_SELECT_DISJOINT = 4, /* selection = recent window + top-k of the keys outside it */
+  SSA_ROPE = 8,            /* window decode: rotate the query at its position (RoPE) */
+  SSA_ROPE_HALF = 16       /* RoPE pairs dims (i, i + D/2) instead of (2i, 2i + 1) */
 };
 
 typedef struct {
@@ -252,6 +254,41 @@ ssa_status ssa_prefill_full(const ssa_shape* shape, const void* q, int32_t n_que
                             const int32_t* q_pos0, const int32_t* ctx_lens, const void* k,
                             const void* v, float scale, float c, float eps, uint32_t flags,
                             float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Sliding-window softmax decode with RoPE, one query token per sequence
+ * ("Three kinds of attention": a window layer reads the most recent tokens
+ * with an ordinary softmax, so every key of the window gets some weight, and
+ * window layers are the only ones that encode position, with RoPE).
+ *
+ * Position j of sequence b lives in cache row j mod kv_capacity: a cache of
+ * `window` rows is a ring buffer, a cache at least as long as every context a
+ * plain one. Keys are stored already rotated at their own positions (see
+ * ssa_cache_write_rope). For n = ctx_lens[b] > 0 and query head h (KV head
+ * kvh = h / (Hq/Hkv)):
+ *   positions  j = max(0, n - window) .. n - 1   (the query is token n - 1)
+ *   q_rot      = RoPE(q[b,h], n - 1) with SSA_ROPE, else q[b,h] as given
+ *   out[b,h]   = sum_j softmax_j(scale * dot(q_rot, k_j)) v_j
+ * n <= 0 gives out = 0. RoPE (RoFormer): pair i turns by pos * theta_i,
+ * theta_i = rope_base^(-2i/D); pairs (2i, 2i+1), or (i, i + D/2) with
+ * SSA_ROPE_HALF. The angle is formed in float64.
+ * Requires 1 <= window <= kv_capacity (else SSA_ERR_SHAPE; a smaller ring
+ * would have overwritten part of the window), scale finite, rope_base > 0
+ * finite, flags within SSA_ROPE | SSA_ROPE_HALF. shape->max_ctx_len is not
+ * used (contexts may exceed kv_capacity in a ring). No workspace. */
+ssa_status ssa_decode_window(const ssa_shape* shape, const float* q, const void* k, const void* v,
+                             const int32_t* ctx_lens, int32_t window, float scale, float rope_base,
+                             uint32_t flags, float* out, void* stream);
+
+/* Store T new tokens' keys and values for a window layer: the key of the
+ * token at position p = pos0[b] + t is rotated at p (RoPE as above, float64
+ * angle, float32 rotation) and both are rounded once to the cache type
+ * (8-bit: values divided by the KV head's scale), into row p mod kv_capacity.
+ * Tokens with p < 0 are not written. k_new, v_new [B, Hkv, T, D] float32.
+ * Requires n_tokens <= kv_capacity (else SSA_ERR_SHAPE: one call must not
+ * write a ring row twice), rope_base > 0 finite, flags within SSA_ROPE_HALF. */
+ssa_status ssa_cache_write_rope(const ssa_shape* shape, const float* k_new, const float* v_new,
+                                int32_t n_tokens, const int32_t* pos0, float rope_base,
+                                uint32_t flags, void* k, void* v, void* stream);
 
 /* ReLU^2 MLP for a few decode tokens that reads the down projection only
  * where a neuron fired ("ReLU² activation": negative values become zero,

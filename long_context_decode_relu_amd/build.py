@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
-SOURCES = ["api.cpp", "decode_full.hip", "select.hip", "decode_sparse.hip", "prefill.hip", "cache.hip", "mlp.hip"]
+SOURCES = ["api.cpp", "decode_full.hip", "select.hip", "decode_sparse.hip", "prefill.hip", "cache.hip", "mlp.hip", "window.hip"]
 ARCH = "gfx950"
 
 

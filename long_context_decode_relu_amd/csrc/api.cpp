@@ -362,6 +362,63 @@ ssa_status ssa_cache_write(const ssa_shape* s, const float* k_new, const float* 
   return from_hip(launch_cache_write(a, static_cast<hipStream_t>(stream)));
 }
 
+ssa_status ssa_decode_window(const ssa_shape* s, const float* q, const void* k, const void* v,
+                             const int32_t* ctx_lens, int32_t window, float scale, float rope_base,
+                             uint32_t flags, float* out, void* stream) {
+  const ssa_status st = check_shape(s, true);
+  if (st != SSA_OK) return st;
+  if (window < 1 || window > s->kv_capacity) return SSA_ERR_SHAPE;
+  if (!finite(scale) || !finite(rope_base) || !(rope_base > 0.0f)) return SSA_ERR_SHAPE;
+  if (flags & ~(uint32_t)(SSA_ROPE | SSA_ROPE_HALF)) return SSA_ERR_UNSUPPORTED;
+  if (s->batch == 0) return SSA_OK;
+  if (!q || !k || !v || !ctx_lens || !out) return SSA_ERR_NULL;
+  DecodeWindowArgs a;
+  a.B = s->batch;
+  a.Hq = s->n_q_heads;
+  a.Hkv = s->n_kv_heads;
+  a.Nmax = s->kv_capacity;
+  a.window = window;
+  a.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ctx_lens = ctx_lens;
+  a.scale = scale;
+  a.rope_base = rope_base;
+  a.flags = flags;
+  a.out = out;
+  return from_hip(launch_decode_window(a, static_cast<hipStream_t>(stream)));
+}
+
+ssa_status ssa_cache_write_rope(const ssa_shape* s, const float* k_new, const float* v_new,
+                                int32_t n_tokens, const int32_t* pos0, float rope_base,
+                                uint32_t flags, void* k, void* v, void* stream) {
+  const ssa_status st = check_shape(s, false);
+  if (st != SSA_OK) return st;
+  if (n_tokens < 0 || n_tokens > s->kv_capacity) return SSA_ERR_SHAPE;
+  if (!finite(rope_base) || !(rope_base > 0.0f)) return SSA_ERR_SHAPE;
+  if (flags & ~(uint32_t)SSA_ROPE_HALF) return SSA_ERR_UNSUPPORTED;
+  if (s->batch == 0 || n_tokens == 0) return SSA_OK;
+  if (!k_new || !v_new || !pos0 || !k || !v) return SSA_ERR_NULL;
+  if ((int64_t)s->batch * s->n_kv_heads * n_tokens > (int64_t)1 << 30) return SSA_ERR_SHAPE;
+  CacheWriteRopeArgs a;
+  a.B = s->batch;
+  a.Hkv = s->n_kv_heads;
+  a.Nmax = s->kv_capacity;
+  a.T = n_tokens;
+  a.kv_bf16 = s->kv_dtype == SSA_BF16;
+  a.kv_fp8 = s->kv_dtype == SSA_FP8_E4M3;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.pos0 = pos0;
+  a.rope_base = rope_base;
+  a.flags = flags;
+  a.k = k;
+  a.v = v;
+  return from_hip(launch_cache_write_rope(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t ssa_mlp_relu2_workspace_bytes(int32_t n_tokens, int32_t d_model, int32_t d_ff) {
   if (n_tokens < 1 || n_tokens > SSA_MLP_MAX_TOKENS || d_model < 8 || d_model % 8 ||
       d_model > SSA_MLP_MAX_WIDTH || d_ff < 1 || d_ff > SSA_MLP_MAX_NEURONS)

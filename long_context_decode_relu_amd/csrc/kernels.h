@@ -87,6 +87,32 @@ struct CacheWriteArgs {
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 
+struct DecodeWindowArgs {
+  int B, Hq, Hkv, Nmax, window;
+  bool kv_bf16, kv_fp8;
+  const float* q;            // [B, Hq, D]
+  const void* k;             // [B, Hkv, Nmax, D], position j in row j mod Nmax
+  const void* v;
+  const int32_t* ctx_lens;   // [B]
+  float scale, rope_base;
+  uint32_t flags;            // SSA_ROPE, SSA_ROPE_HALF
+  float* out;                // [B, Hq, D]
+};
+hipError_t launch_decode_window(const DecodeWindowArgs& a, hipStream_t stream);
+
+struct CacheWriteRopeArgs {
+  int B, Hkv, Nmax, T;
+  bool kv_bf16, kv_fp8;
+  const float* k_new;   // [B, Hkv, T, D]
+  const float* v_new;
+  const int32_t* pos0;  // [B]: token t of sequence b has position pos0[b] + t, row (pos0[b] + t) mod Nmax
+  float rope_base;
+  uint32_t flags;       // SSA_ROPE_HALF
+  void* k;
+  void* v;
+};
+hipError_t launch_cache_write_rope(const CacheWriteRopeArgs& a, hipStream_t stream);
+
 struct MlpArgs {
   int T, d, d_ff;
   const float* x;       // [T, d]

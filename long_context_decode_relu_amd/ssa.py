@@ -34,6 +34,8 @@ SSA_FP8_E4M3 = 2
 SSA_NORM_Q = 1
 SSA_NORM_K = 2
 SSA_SELECT_DISJOINT = 4
+SSA_ROPE = 8
+SSA_ROPE_HALF = 16
 
 SSA_OP_DECODE_FULL = 0
 SSA_OP_SELECT = 1
@@ -44,7 +46,8 @@ SSA_OP_DECODE_FULL_SELECT = 4
 EXPORTED = ("ssa_abi_version", "ssa_status_string", "ssa_workspace_bytes", "ssa_decode_full",
             "ssa_decode_full_select", "ssa_select_topk_recent", "ssa_decode_sparse",
             "ssa_decode_sparse_static", "ssa_prefill_full", "ssa_cache_write",
-            "ssa_mlp_relu2_workspace_bytes", "ssa_mlp_relu2")
+            "ssa_decode_window", "ssa_cache_write_rope", "ssa_mlp_relu2_workspace_bytes",
+            "ssa_mlp_relu2")
 
 # limits of ssa_mlp_relu2
 SSA_MLP_MAX_TOKENS = 8
@@ -102,6 +105,10 @@ def lib() -> ctypes.CDLL:
         L.ssa_prefill_full.argtypes = [SP, P, I32, P, P, P, P, F, F, F, U32, P, P, SZ, P]
         L.ssa_cache_write.restype = I32
         L.ssa_cache_write.argtypes = [SP, P, P, I32, P, F, U32, P, P, P]
+        L.ssa_decode_window.restype = I32
+        L.ssa_decode_window.argtypes = [SP, P, P, P, P, I32, F, F, U32, P, P]
+        L.ssa_cache_write_rope.restype = I32
+        L.ssa_cache_write_rope.argtypes = [SP, P, P, I32, P, F, U32, P, P, P]
         L.ssa_mlp_relu2_workspace_bytes.restype = SZ
         L.ssa_mlp_relu2_workspace_bytes.argtypes = [I32, I32, I32]
         L.ssa_mlp_relu2.restype = I32
@@ -364,6 +371,49 @@ def ssa_prefill_full(q: torch.Tensor, q_pos0: torch.Tensor, cache: Cache, *, sca
                                 _ptr(ws), ws.numel(), _stream(dev))
     _check(st, "ssa_prefill_full")
     return out
+
+
+def ssa_decode_window(q: torch.Tensor, cache: Cache, *, window: int = 128, scale: float | None = None,
+                      rope_base: float = 10000.0, flags: int = SSA_ROPE,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """Sliding-window softmax decode with RoPE. q [B, Hq, D] float32; position j of a
+    sequence lives in cache row j mod Nmax (a ring buffer when Nmax == window).
+    Returns out [B, Hq, D] float32."""
+    cache.check()
+    _need(q.is_cuda and q.dtype == torch.float32 and q.dim() == 3 and q.is_contiguous(),
+          "q must be contiguous float32 [B, Hq, D]")
+    B, Hq, D = q.shape
+    _need(B == cache.k.shape[0] and D == cache.k.shape[3], "q does not match the cache")
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    B_, Hkv, Nmax, _ = cache.k.shape
+    # contexts of a ring buffer run past its capacity: the window call ignores max_ctx_len
+    shp = ssa_shape(B, Hq, Hkv, D, Nmax, 0, _kv_dtype(cache.k))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    st = lib().ssa_decode_window(ctypes.byref(shp), _ptr(q), _ptr(cache.k), _ptr(cache.v),
+                                 _ptr(cache.ctx_lens), window, scale, rope_base, flags, _ptr(out),
+                                 _stream(q.device))
+    _check(st, "ssa_decode_window")
+    return out
+
+
+def ssa_cache_write_rope(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos0: torch.Tensor, *,
+                         rope_base: float = 10000.0, flags: int = 0) -> None:
+    """Store a window layer's new tokens (in place): keys rotated at their positions
+    pos0[b] + t, rows (pos0[b] + t) mod Nmax. k_new, v_new [B, Hkv, T, D] float32."""
+    cache.check()
+    _need(k_new.is_cuda and k_new.dtype == torch.float32 and k_new.dim() == 4 and k_new.is_contiguous(),
+          "k_new must be contiguous float32 [B, Hkv, T, D]")
+    _need(v_new.shape == k_new.shape and v_new.dtype == torch.float32 and v_new.is_contiguous(),
+          "v_new must match k_new")
+    B, Hkv, T, D = k_new.shape
+    _need((B, Hkv, D) == (cache.k.shape[0], cache.k.shape[1], cache.k.shape[3]), "k_new does not match the cache")
+    _need(pos0.dtype == torch.int32 and pos0.shape == (B,) and pos0.is_contiguous(), "pos0 must be int32 [B]")
+    shp = ssa_shape(B, Hkv, Hkv, D, cache.k.shape[2], 0, _kv_dtype(cache.k))
+    st = lib().ssa_cache_write_rope(ctypes.byref(shp), _ptr(k_new), _ptr(v_new), T, _ptr(pos0), rope_base,
+                                    flags, _ptr(cache.k), _ptr(cache.v), _stream(k_new.device))
+    _check(st, "ssa_cache_write_rope")
 
 
 def mlp_workspace(n_tokens: int, d_model: int, d_ff: int, device) -> torch.Tensor:

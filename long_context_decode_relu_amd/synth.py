@@ -27,6 +27,11 @@ divided by a per-(sequence, KV head) power-of-two scale, kept in
 hold NaN so that any read past the live keys shows up in the output.
 Queries are float32 and are NOT normalised (the attention path does that).
 
+Window recipe (``window_tokens``): for a sliding-window layer, raw (not yet
+rotated) keys, values and queries N(0, 1) per element for the last
+min(window, n) positions of each sequence, float32, with those positions;
+rotating and storing them is the cache write's job.
+
 MLP recipe (``mlp_workload``; no trained weights are available):
 
 * tokens x are N(1, 1) per element (a positive mean, so every token shares a
@@ -357,4 +362,42 @@ def mlp_workload(seed: int = 7, n_tokens: int = 1, d_model: int = 2048, d_ff: in
         wd[i0:i0 + n] = to_bf16_bits((r.standard_normal((n, d)) / np.sqrt(fire_rate * d_ff)).astype(np.float32))
     return MlpWorkload(name=name or f"mlp_relu2_t{n_tokens}_{d}x{d_ff}", n_tokens=n_tokens,
                        d_model=d, d_ff=d_ff, fire_rate=fire_rate, x=x, w_up=wu, w_down=wd)
+
+
+@dataclass
+class WindowTokens:
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    window: int
+    ctx_lens: np.ndarray   # [B] int32
+    q: np.ndarray          # [B, Hq, D] float32 (the token at position n - 1)
+    k_raw: np.ndarray      # [B, Hkv, W, D] float32, row r = position pos[b, r]
+    v_raw: np.ndarray      # [B, Hkv, W, D] float32
+    pos: np.ndarray        # [B, W] int64 positions; -1 past min(window, n)
+
+
+def window_tokens(seed: int = 9, ctx_lens=(131072,), n_q_heads: int = 16, n_kv_heads: int = 2,
+                  window: int = 128, name: str | None = None) -> WindowTokens:
+    """The last min(window, n) tokens of each sequence for a window layer (recipe in the
+    module docstring). Rows past a short sequence's count hold NaN and position -1."""
+    ctx = np.asarray(ctx_lens, dtype=np.int32)
+    B, D = len(ctx), 128
+    k = np.full((B, n_kv_heads, window, D), np.nan, dtype=np.float32)
+    v = np.full((B, n_kv_heads, window, D), np.nan, dtype=np.float32)
+    pos = np.full((B, window), -1, dtype=np.int64)
+    q = np.empty((B, n_q_heads, D), dtype=np.float32)
+    for b in range(B):
+        r = _rng(seed, 20, b)
+        n = int(ctx[b])
+        m = min(window, max(n, 0))
+        pos[b, :m] = np.arange(n - m, n)
+        k[b, :, :m] = r.standard_normal((n_kv_heads, m, D))
+        v[b, :, :m] = r.standard_normal((n_kv_heads, m, D))
+        q[b] = r.standard_normal((n_q_heads, D))
+    return WindowTokens(name=name or f"window{window}_b{B}", batch=B, n_q_heads=n_q_heads,
+                        n_kv_heads=n_kv_heads, head_dim=D, window=window, ctx_lens=ctx, q=q,
+                        k_raw=k, v_raw=v, pos=pos)
 

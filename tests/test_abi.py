@@ -145,3 +145,23 @@ def test_mlp_rejects():
     assert f(1, 2048, 64, ws_=None) == ssa.SSA_ERR_WORKSPACE
     assert f(1, 2048, 64, wb=W(1, 2048, 64) - 1) == ssa.SSA_ERR_WORKSPACE
     assert f(0, 2048, 64, x=None) == ssa.SSA_OK  # no tokens: nothing to do
+
+
+def test_window_rejects():
+    L = ssa.lib()
+    s = shape(kv_capacity=128, max_ctx_len=0)
+    f = lambda s_, w, fl=ssa.SSA_ROPE, q=FAKE, base=10000.0: L.ssa_decode_window(
+        ctypes.byref(s_), q, FAKE, FAKE, FAKE, w, 0.088, base, fl, FAKE, None)
+    assert f(s, 129) == ssa.SSA_ERR_SHAPE
+    assert f(s, 0) == ssa.SSA_ERR_SHAPE
+    assert f(s, 128, base=0.0) == ssa.SSA_ERR_SHAPE
+    assert f(s, 128, fl=ssa.SSA_NORM_Q) == ssa.SSA_ERR_UNSUPPORTED
+    assert f(s, 128, q=None) == ssa.SSA_ERR_NULL
+    assert f(shape(kv_capacity=128, max_ctx_len=0, n_q_heads=24), 128) == ssa.SSA_ERR_UNSUPPORTED
+    assert f(shape(batch=0, kv_capacity=128, max_ctx_len=0), 128) == ssa.SSA_OK
+    g = lambda s_, T, fl=0: L.ssa_cache_write_rope(ctypes.byref(s_), FAKE, FAKE, T, FAKE, 10000.0, fl,
+                                                   FAKE, FAKE, None)
+    assert g(s, 129) == ssa.SSA_ERR_SHAPE
+    assert g(s, -1) == ssa.SSA_ERR_SHAPE
+    assert g(s, 4, fl=ssa.SSA_ROPE) == ssa.SSA_ERR_UNSUPPORTED
+    assert g(s, 0) == ssa.SSA_OK
