@@ -16,9 +16,12 @@
 // relative output error near 3e-3.
 //
 // Rows of a workgroup are (position, head) pairs of one KV head, head fastest,
-// so the G query heads that share a KV head read each K/V tile once. Four
-// waves own 32 rows each; a 32-key tile of K (8 KB) and of V (8 KB) is staged
-// in LDS with direct-to-LDS loads, double-buffered. K is fetched straight into
+// so the G query heads that share a KV head read each K/V tile once. Eight
+// waves own 32 rows each (256 rows: every K/V tile staged in LDS serves 256
+// rows, which halves the cache traffic of 128-row blocks); a 32-key tile of K
+// (8 KB) and of V (8 KB) is staged in LDS with direct-to-LDS loads,
+// double-buffered. A 16-key step of W x V whose weights are all zero for a
+// wave's rows is skipped. K is fetched straight into
 // the A-fragment order of the MFMA; V would need a transpose, so a first pass
 // packs V once into B-fragment order in the workspace (zero past ctx_lens).
 // Long key ranges are split over S workgroups whose partial sums are added in
@@ -36,14 +39,16 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;         // four waves
-constexpr int kRowsPerBlock = 128;    // (position, head) rows per workgroup
+constexpr int kThreads = 256;         // the V packing and combine passes: four waves
+constexpr int kRowsPerBlock = 256;    // (position, head) rows per main-kernel workgroup
+constexpr int kMainWaves = kRowsPerBlock / 32;  // a wave owns 32 rows
+constexpr int kMainThreads = kMainWaves * kWave;
 constexpr int kSub = 32;              // keys per MFMA score block
 constexpr int kKeyTile = 64;          // keys per LDS tile: two score blocks
 constexpr int kFragBytes = 1024;      // one MFMA operand fragment: 64 lanes x 16 B
 constexpr int kTileBytes = 8 * kFragBytes;  // 32 keys x 128 dims x bf16 (one score block)
 constexpr int kMaxSplit = 16;
-constexpr int kTargetBlocks = 512;    // two resident workgroups per CU on 256 CUs
+constexpr int kTargetBlocks = 256;    // one resident 8-wave workgroup per CU on 256 CUs
 constexpr int kWaitVm0 = 0x0F70;      // s_waitcnt vmcnt(0)
 constexpr int kSlots = 2;
 // slot layout: K block 0, K block 1, V block 0, V block 1 (8 KB each)
@@ -145,14 +150,14 @@ struct PrefillGeom {
 // ---------------------------------------------------------------------------
 // Main kernel. Block = (b, kvh, query block qb, split sp).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
+__global__ __launch_bounds__(kMainThreads) void prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ ctx_lens, const uint8_t* __restrict__ k,
     const uint8_t* __restrict__ vp, PrefillGeom g, float scale, float c, float eps, int norm_q,
     float* __restrict__ out, float* __restrict__ part, float* __restrict__ pden) {
   // two tile slots: one being read, one filling
   __shared__ __attribute__((aligned(16))) uint8_t s_buf[kSlots][kSlotBytes];
-  __shared__ float s_den[4][32];
+  __shared__ float s_den[kMainWaves][32];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,12 +241,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   const uint8_t* vbase = vp + (size_t)bkv * g.ntiles * 2 * kTileBytes;
 
   // A 64-key tile is 32 fragments of 1 KB: K block 0 (k-steps 0-7), K block 1,
-  // then the packed V of blocks 0 and 1. Wave w issues fragments 8w .. 8w+7.
+  // then the packed V of blocks 0 and 1. Wave w issues fragments 4w .. 4w+3.
   const uint32_t lds0 = (uint32_t)(uintptr_t)&s_buf[0][0];
   auto issue = [&](int tile, int slot) {
+    constexpr int kFragsPerWave = 32 / kMainWaves;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int fi = wave * 8 + u;
+    for (int u = 0; u < kFragsPerWave; ++u) {
+      const int fi = wave * kFragsPerWave + u;
       const uint32_t lds = __builtin_amdgcn_readfirstlane(lds0 + slot * kSlotBytes + fi * kFragBytes);
       if (fi < 16) {
         // K: rows past the context repeat its last row (read, then masked);
@@ -266,11 +272,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
   auto qk = [&](int slot, int blk, f32x16& st) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) st[i] = 0.f;
+    // the block's 8 K fragments are read before the products: the chain of
+    // 16 dependent MFMAs then never waits on LDS
+    bf16x8 a[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) a[s] = frag(slot, blk * 8 + s);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8 a = frag(slot, blk * 8 + s);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qhi[s], st, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qlo[s], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qhi[s], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], qlo[s], st, 0, 0, 0);
     }
   };
 
@@ -289,8 +299,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
         const int i = 2 * p + e;
         float wv = relu_sq(st[i]);
         if (masked) wv = (key0 + 8 * (i / 4) + 4 * half + (i % 4) <= lim) ? wv : 0.f;
-        den += wv;
         w2[e] = wv;
+        // den takes w itself: hi + lo differs from w by about 2^-17 of w,
+        // far below the float32 rounding of a sum over tens of thousands of keys
+        den += wv;
       }
       split_pair(w2[0], w2[1], whi[p], wlo[p]);
     }
@@ -300,30 +312,58 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(
     w.l1 = as_bf16x8(u32x4{wlo[4], wlo[5], wlo[6], wlo[7]});
   };
 
-  auto pv = [&](int slot, int blk, const W& w) {
+  // W x V of one block; a k-step (16 keys) whose weights are all zero for the
+  // wave's rows is skipped (the order of the products into each acc[nb] stays
+  // h0, l0, h1, l1)
+  auto pv = [&](int slot, int blk, const W& w, bool live0, bool live1) {
+    if (live0) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const bf16x8 v0 = frag(slot, 16 + blk * 8 + 2 * nb);
-      const bf16x8 v1 = frag(slot, 16 + blk * 8 + 2 * nb + 1);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h0, v0, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l0, v0, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h1, v1, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l1, v1, acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8 v0 = frag(slot, 16 + blk * 8 + 2 * nb);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h0, v0, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l0, v0, acc[nb], 0, 0, 0);
+      }
+    }
+    if (live1) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const bf16x8 v1 = frag(slot, 16 + blk * 8 + 2 * nb + 1);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.h1, v1, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w.l1, v1, acc[nb], 0, 0, 0);
+      }
     }
   };
 
   // One 64-key tile: the second block's scores run on the matrix cores while
   // the first block's weights are formed, and the first block's W x V while
   // the second block's weights are formed.
+  // Which 16-key k-steps of a block have some positive score among the wave's
+  // 32 rows (st[i], i < 8: keys 0..15; i >= 8: keys 16..31). A k-step without
+  // one has all-zero weights and contributes nothing to W x V or to den.
+  auto live_steps = [&](const f32x16& st, bool& live0, bool& live1) {
+    const float m0 = fmaxf(fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3])),
+                           fmaxf(fmaxf(st[4], st[5]), fmaxf(st[6], st[7])));
+    const float m1 = fmaxf(fmaxf(fmaxf(st[8], st[9]), fmaxf(st[10], st[11])),
+                           fmaxf(fmaxf(st[12], st[13]), fmaxf(st[14], st[15])));
+    live0 = __builtin_amdgcn_ballot_w64(m0 > 0.f) != 0ull;
+    live1 = __builtin_amdgcn_ballot_w64(m1 > 0.f) != 0ull;
+  };
   auto tile_step = [&](int slot, int tile, bool masked) {
     f32x16 s0, s1;
     W w0, w1;
+    bool a0, a1, b0, b1;
     qk(slot, 0, s0);
     qk(slot, 1, s1);
-    weights(s0, tile * kKeyTile, masked, w0);
-    pv(slot, 0, w0);
-    weights(s1, tile * kKeyTile + kSub, masked, w1);
-    pv(slot, 1, w1);
+    live_steps(s0, a0, a1);
+    live_steps(s1, b0, b1);
+    if (a0 || a1) {
+      weights(s0, tile * kKeyTile, masked, w0);
+      pv(slot, 0, w0, a0, a1);
+    }
+    if (b0 || b1) {
+      weights(s1, tile * kKeyTile + kSub, masked, w1);
+      pv(slot, 1, w1, b0, b1);
+    }
   };
 
   // Double-buffered tiles; tiles [tb, tm) need no causal mask, [tm, te) do.
@@ -476,7 +516,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                      2 * g.ntiles, vp);
   float* part = g.S > 1 ? reinterpret_cast<float*>(ws + w.part) : nullptr;
   float* pden = g.S > 1 ? reinterpret_cast<float*>(ws + w.pden) : nullptr;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(units * g.S)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)(units * g.S)), dim3(kMainThreads), 0, stream,
                      static_cast<const uint16_t*>(a.q), a.q_pos0, a.ctx_lens,
                      static_cast<const uint8_t*>(a.k), reinterpret_cast<const uint8_t*>(vp), g,
                      a.scale, a.c, a.eps, (int)(a.flags & 1u), a.out, part, pden);
