@@ -515,9 +515,25 @@ __global__ __launch_bounds__(256) void decode_full_qprep(const float* __restrict
 // wave owns at least one tile). Every wave therefore streams the same number
 // of bytes (to within one tile) whatever the context lengths.
 
+// The split every kernel uses: W waves (the grid's, capped at T) over T tiles.
+struct Part {
+  int W, T;
+};
+__device__ __forceinline__ Part make_part(int W0, int T) {
+  Part p;
+  p.W = min(W0, T);
+  p.T = T;
+  return p;
+}
+
+// First tile of wave w (w = W gives T).
+__device__ __forceinline__ int part_start(int w, const Part& p) {
+  return (int)((int64_t)w * p.T / p.W);
+}
+
 // The wave whose range holds tile t.
-__device__ __forceinline__ int wave_of_tile(int t, int W, int T) {
-  return (int)(((int64_t)(t + 1) * W - 1) / T);
+__device__ __forceinline__ int wave_of_tile(int t, const Part& p) {
+  return (int)(((int64_t)(t + 1) * p.W - 1) / p.T);
 }
 
 __device__ __forceinline__ int live_keys(const int32_t* ctx_lens, int b, int max_ctx) {
@@ -590,9 +606,9 @@ constexpr int kFastRounds = 16;
 // First tile and tile count of the part of stream [s0, s1) that wave w of W
 // (over T tiles) takes: the candidate list of that (stream, wave) slot has
 // room for entries [first*64, (first + nt)*64).
-__device__ __forceinline__ void slot_tiles(int s0, int s1, int w, int W, int T, int* first,
+__device__ __forceinline__ void slot_tiles(int s0, int s1, int w, const Part& p, int* first,
                                            int* nt) {
-  const int t0 = (int)((int64_t)w * T / W), t1 = (int)((int64_t)(w + 1) * T / W);
+  const int t0 = part_start(w, p), t1 = part_start(w + 1, p);
   *first = max(s0, t0);
   *nt = min(s1, t1) - *first;
 }
@@ -628,7 +644,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   const int T = s_tpre[S];
   // With more waves than tiles only the first T waves work (one tile each),
   // so that every working wave owns at least one tile.
-  const int W = min((int)gridDim.x * kWaves, T);
+  const int nbl = gridDim.x;
+  const Part part = make_part(nbl * kWaves, T);
+  const int W = part.W;
   // XCD-aware numbering: work-group b runs on XCD b % 8 and, within it, the
   // work-groups fill the CUs in turn. Renumbering them so that the
   // work-groups sharing a CU, and neighbouring CUs, hold neighbouring tile
@@ -647,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   }
   const int w = lb * kWaves + wave;
   if (w >= W) return;
-  const int t0 = (int)((int64_t)w * T / W), t1 = (int)((int64_t)(w + 1) * T / W);
+  const int t0 = part_start(w, part), t1 = part_start(w + 1, part);
 
   struct Stream {
     int j, b, kvh, n, s0, s1;
@@ -715,7 +733,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   auto open_slot = [&](const Stream& st) __attribute__((always_inline)) {
     if constexpr (CAND) {
       int first, nt;
-      slot_tiles(st.s0, st.s1, w, W, T, &first, &nt);
+      slot_tiles(st.s0, st.s1, w, part, &first, &nt);
       lidx = cand_idx + (size_t)first * kTileKeys;
       lsc = cand_sc + (size_t)first * kTileKeys * G;
     }
@@ -1344,11 +1362,11 @@ __device__ void combine_row(
   const int kvh = h / G, jh = h - kvh * G;
   const int j = b * Hkv + kvh;
   const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
-  const int W = min(Wl, T);
+  const Part part = make_part(Wl, T);
   int p0 = 0, p1 = 0;
   if (s1 > s0) {
-    p0 = j + wave_of_tile(s0, W, T);
-    p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+    p0 = j + wave_of_tile(s0, part);
+    p1 = j + wave_of_tile(s1 - 1, part) + 1;
   }
   // den and the counts: one slot per thread
   float sd = 0.f;
@@ -1607,8 +1625,8 @@ __device__ __forceinline__ void select_from_cands(SelShared& sh,
     return;
   }
   const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
-  const int W = min(Wl, T);
-  const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+  const Part part = make_part(Wl, T);
+  const int p0 = j + wave_of_tile(s0, part), p1 = j + wave_of_tile(s1 - 1, part) + 1;
   const int np = p1 - p0;
   if (2 * np + 1 > kSegWords) {
     if (tid == 0) *flag = 1;
@@ -1628,7 +1646,7 @@ __device__ __forceinline__ void select_from_cands(SelShared& sh,
       offs[q] = (uint32_t)run;
       run += cand_cnt[p0 + q];
       int first, nt;
-      slot_tiles(s0, s1, p0 + q - j, W, T, &first, &nt);
+      slot_tiles(s0, s1, p0 + q - j, part, &first, &nt);
       base[q] = (uint32_t)(first * kTileKeys);
     }
     if (tid == 0) offs[np] = (uint32_t)total;
@@ -1738,8 +1756,8 @@ __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __rest
   const int k = min(k_top, pool);
   const int r0 = max(0, n - n_recent);
   if (k >= pool || n <= kCandAll || s1 <= s0) return false;
-  const int W = min(Wl, T);
-  const int p0 = j + wave_of_tile(s0, W, T), p1 = j + wave_of_tile(s1 - 1, W, T) + 1;
+  const Part part = make_part(Wl, T);
+  const int p0 = j + wave_of_tile(s0, part), p1 = j + wave_of_tile(s1 - 1, part) + 1;
   const int np = p1 - p0;
   if (np > kSelWaves * kFastRounds) return false;
   const int nr = ceil_div(max(0, np - wave), kSelWaves);  // this wave's rounds (uniform)
@@ -1753,7 +1771,7 @@ __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __rest
     // rounds load nothing)
     const int qv = min(wave + kSelWaves * (lane & (kFastRounds - 1)), np - 1);
     int fv, ntv;
-    slot_tiles(s0, s1, p0 + qv - j, W, T, &fv, &ntv);
+    slot_tiles(s0, s1, p0 + qv - j, part, &fv, &ntv);
     const int cntv = cand_cnt[p0 + qv];
     float sc[kFastRounds];
 #pragma unroll
@@ -1898,7 +1916,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
 // head) for the rescoring kernel.
 __global__ __launch_bounds__(256) void decode_full_decide(
     const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
-    const int* __restrict__ tile_pre, const int32_t* __restrict__ ctx_lens, int S, int W, int G,
+    const int* __restrict__ tile_pre, const int32_t* __restrict__ ctx_lens, int S, int Wl, int G,
     int Hq, int Hkv, int max_ctx, int k_top, int n_recent, int disjoint,
     int32_t* __restrict__ row_flag, int32_t* __restrict__ fmask) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -1907,8 +1925,10 @@ __global__ __launch_bounds__(256) void decode_full_decide(
   const int b = j / Hkv, kvh = j - b * Hkv;
   const int n = live_keys(ctx_lens, b, max_ctx);
   const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
-  const int p0 = s1 > s0 ? j + wave_of_tile(s0, W, T) : 0;
-  const int p1 = s1 > s0 ? j + wave_of_tile(s1 - 1, W, T) + 1 : 0;
+  // the main kernel's split (its wave count capped at the tile count)
+  const Part part = make_part(Wl, T);
+  const int p0 = s1 > s0 ? j + wave_of_tile(s0, part) : 0;
+  const int p1 = s1 > s0 ? j + wave_of_tile(s1 - 1, part) + 1 : 0;
   int E = 0, emax = 0;
   int nz[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   // two slots per lane in one round of loads (more slots loop)

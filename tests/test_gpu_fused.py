@@ -259,3 +259,30 @@ def test_context_lengths_clamped_to_max_ctx():
     assert_rows_close(out.cpu().numpy(), ref["out"], 2e-3, "clamped full layer")
     selection_vs_oracle(sub, ref["scores"], sel.cpu().numpy(), cnt.cpu().numpy(),
                         score_bound(sub, 1.0), range(2))
+
+
+def test_fused_contexts_far_below_host_bound():
+    """Every context far below max_ctx_len: the grid, sized from the host bound,
+    has more waves than there are tiles, so only the first T waves work, one
+    tile each. Every kernel after the main one must map tiles to the same
+    slots: fused equals two calls bit for bit, and both equal the oracle."""
+    wl = synth.make_workload("fused_small_ctx", seed=42, batch=3, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[100, 5000, 3], kv_capacity=16384, p=0.05)
+    cache = ssa.cache_from_workload(wl, DEV)
+    cache.max_ctx_len = 16384
+    q = torch.from_numpy(wl.q).to(DEV)
+    out, _, nnz, vrows, sel, cnt = two_calls(wl, cache, q, scale=1.0, c=1.0, eps=1e-6,
+                                             flags=ssa.SSA_NORM_Q, k_top=1024, n_recent=128,
+                                             sel_flags=0)
+    fout, fsel, fcnt, _, fnnz, fvrows = ssa.ssa_decode_full_select(q, cache, want_stats=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), fout.cpu().numpy().view(np.uint32))
+    assert np.array_equal(nnz.cpu().numpy(), fnnz.cpu().numpy())
+    assert np.array_equal(vrows.cpu().numpy(), fvrows.cpu().numpy())
+    assert np.array_equal(sel.cpu().numpy(), fsel.cpu().numpy())
+    assert np.array_equal(cnt.cpu().numpy(), fcnt.cpu().numpy())
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    from gpu_helpers import assert_rows_close
+    assert_rows_close(fout.cpu().numpy(), ref["out"], 2e-3, "full layer")
+    selection_vs_oracle(wl, ref["scores"], fsel.cpu().numpy(), fcnt.cpu().numpy(), score_bound(wl, 1.0),
+                        range(wl.batch))
