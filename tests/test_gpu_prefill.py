@@ -91,6 +91,23 @@ def test_prefill_all_scores_negative_c_zero_gives_zero():
     assert np.array_equal(got, np.zeros_like(got))
 
 
+def test_prefill_one_huge_key_value():
+    """One live key holds a value of 1e6: the keys that see it are dominated by it."""
+    pw = synth.prefill_chunk(seed=69, batch=1, n_query=40, ctx_lens=[3000], recipe="iid")
+    k = synth.bf16_bits_to_f32(pw.k)
+    k[0, 0, 1234, 5] = 1.0e6
+    pw.k = synth.to_bf16_bits(k)
+    check_all_rows(pw)
+
+
+@pytest.mark.parametrize("f", [1e-6, 1e4])
+def test_prefill_query_scale_far_from_one(f):
+    """Queries scaled by f and left unnormalised (flags 0): scores and weights far from 1."""
+    pw = synth.prefill_chunk(seed=70, batch=1, n_query=40, ctx_lens=[2000], recipe="iid")
+    pw.q = synth.to_bf16_bits(synth.bf16_bits_to_f32(pw.q) * f)
+    check_all_rows(pw, flags=0, scale=1.0)
+
+
 def test_prefill_empty_chunk():
     pw = synth.prefill_chunk(seed=67, batch=1, n_query=8, ctx_lens=[64], recipe="iid")
     cache = cache_of(pw)

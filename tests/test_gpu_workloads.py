@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DEV, TOL_BF16, assert_rows_close, check_decode_full, score_bound
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, assert_rows_close, check_decode_full, score_bound
 from oracle import ssa_oracle as O
 from long_context_decode_relu_amd import ssa, synth
 
@@ -99,3 +99,27 @@ def test_block_step_b32_full_size():
     for l in range(3):
         want = O.decode_sparse(sub.q_sparse[l], sub.k, sub.v, sels)
         assert_rows_close(outs[l].cpu().numpy()[seqs], want, TOL_BF16, f"block step sparse layer {l}")
+
+
+@pytest.mark.parametrize("which", ["tiny", "single"])
+def test_whole_step_through_fused_call(which):
+    """The 4096-key fp32 case (1 query head / 1 KV head, i.i.d., about half the weights zero)
+    and the 32768-key bf16 single sequence (16 / 2 heads, 95% sparse) at full size, through the
+    calls the benchmark times: ssa_decode_full_select, then ssa_decode_sparse. Full-layer rows,
+    the selection (tie band) and the sparse layer are compared with the oracle directly."""
+    wl = synth.tiny_decode() if which == "tiny" else synth.single_decode(n=32768)
+    tol = TOL_F32 if wl.kv_dtype == "f32" else TOL_BF16
+    cache = ssa.cache_from_workload(wl, DEV)
+    out, sel, cnt, _, nnz, vrows = ssa.ssa_decode_full_select(torch.from_numpy(wl.q).to(DEV), cache,
+                                                              want_stats=True)
+    sp = ssa.ssa_decode_sparse(torch.from_numpy(wl.q_sparse[0]).to(DEV), cache, sel, cnt)
+    torch.cuda.synchronize()
+    ref = O.decode_full(wl.q, wl.k, wl.v, wl.ctx_lens)
+    assert_rows_close(out.cpu().numpy(), ref["out"], tol, f"{which} full layer")
+    bounds = score_bound(wl, 1.0)
+    use, same = selection_vs_oracle(wl, ref["scores"], sel.cpu().numpy(), cnt.cpu().numpy(),
+                                    bounds, range(wl.batch))
+    assert same >= wl.n_q_heads - 1
+    sels = [[use[(b, h)] for h in range(wl.n_q_heads)] for b in range(wl.batch)]
+    want = O.decode_sparse(wl.q_sparse[0], wl.k, wl.v, sels)
+    assert_rows_close(sp.cpu().numpy(), want, tol, f"{which} sparse layer")
