@@ -22,10 +22,12 @@
 //   gather   one work-group (eight waves) per (stream, chunk of 256 union
 //            rows). Each wave finds its 32 rows from the segments' counts and
 //            offsets (a wave scan), copies their K rows HBM -> LDS by
-//            direct-to-LDS loads (16-byte pieces XOR-permuted so that a lane
-//            reads its own row without bank conflicts) and their V rows into
-//            registers (a lane holds two value dims of every row). Two lanes
-//            score a row against the G heads, half of the dims each; each wave
+//            direct-to-LDS loads (16-byte pieces XOR-permuted by row) and
+//            their V rows into registers (a lane holds two value dims of every
+//            row). The scores of the 32 rows against the G heads run on
+//            v_mfma_f32_32x32x16_bf16 (K rows as A fragments read from LDS,
+//            the queries as hi + lo bf16 B fragments; float32 caches score on
+//            the VALU, two lanes a row); each wave
 //            forms the softmax state of its rows per head (max, sum, weighted
 //            values, in base 2 with log2(e) folded into the query), and the
 //            eight waves' states are merged in wave order into the chunk's
@@ -53,10 +55,27 @@ constexpr int kUWaves = kUThreads / kWave;
 static_assert(kSegWords == kUThreads, "one bitmap word per thread");
 constexpr int kGWaves = 8;                        // gather work-group
 constexpr int kGThreads = kGWaves * kWave;
-constexpr int kWRows = kWave / 2;                 // rows per wave: two lanes per row
+constexpr int kWRows = kWave / 2;                 // rows per wave: two lanes per row (weights)
 constexpr int kChunk = kGWaves * kWRows;          // union rows per gather work-group
 constexpr int kKTileBf16 = kWRows * kHeadDim * 2; // one wave's bf16 K rows
 constexpr int kWaitVm0 = 0x0F70;                  // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;                // s_waitcnt lgkmcnt(0)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// (a, b) -> bf16 hi pair and lo pair with a ~= hi + lo to about 2^-17
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  bf16x2 h;
+  h[0] = (__bf16)a;
+  h[1] = (__bf16)b;
+  hi = __builtin_bit_cast(uint32_t, h);
+  bf16x2 l;
+  l[0] = (__bf16)(a - bf16_lo(hi));
+  l[1] = (__bf16)(b - bf16_hi(hi));
+  lo = __builtin_bit_cast(uint32_t, l);
+}
 constexpr int kMaxStride = kWave * kWave;         // two rounds of 64 probes
 
 // Numbers of entries below x0 and below x1 in list[0 .. cnt) (ascending;
@@ -318,66 +337,94 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     }
     if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-    // scores of this lane's row against the G heads: each of its two lanes
-    // takes half of the dims, then the halves are added
+    // scores of this lane's row against the G heads
     float t[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) t[h] = 0.f;
     float ss = 0.f;
-    if constexpr (FP8) {
-      const uint8_t* myrow = ktile + ri * kHeadDim;
-#pragma unroll 2
-      for (int i = 0; i < 4; ++i) {
-        const int pc = 4 * half + i;  // 16 dims per piece
-        const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((pc ^ (ri & 7)) << 4));
-        float xx[16];
+    if constexpr (BF16) {
+      // On the matrix cores: S[row][head] = sum_d K[row][d] Qs[head][d], A = the
+      // wave's K rows from LDS (lane l: row l % 32, dims 16 s + 8 (l / 32) ..
+      // +7 of k-step s), B = the scaled queries as hi + lo bf16 (lane l: head
+      // l % 32, zero past G); st[i] is then row 8 (i / 4) + 4 (l / 32) + i % 4
+      // against head l % 32. The scores go through this wave's weight slots in
+      // LDS (free until its weights are written) to the lanes of their rows.
+      const int ar = lane & 31, ah = lane >> 5;
+      f32x16 st;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], false);
-          const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], true);
-          xx[4 * e] = a[0]; xx[4 * e + 1] = a[1]; xx[4 * e + 2] = b[0]; xx[4 * e + 3] = b[1];
+      for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        u32x4 a;
+        if constexpr (FP8) {
+          // piece s8 (16 dims) of row ar sits in slot s8 ^ (ar & 7); this lane takes half ah
+          const uint2 raw = *reinterpret_cast<const uint2*>(ktile + ar * kHeadDim + ((s8 ^ (ar & 7)) << 4) + 8 * ah);
+          a[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false));
+          a[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true));
+          a[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false));
+          a[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true));
+        } else {
+          // piece 2 s8 + ah (8 dims) of row ar sits in slot (2 s8 + ah) ^ (ar & 15)
+          a = *reinterpret_cast<const u32x4*>(ktile + ar * (kHeadDim * 2) + (((2 * s8 + ah) ^ (ar & 15)) << 4));
         }
-        if constexpr (NORMK) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) ss = fmaf(xx[e], xx[e], ss);
+        uint32_t hv[4] = {0u, 0u, 0u, 0u}, lv[4] = {0u, 0u, 0u, 0u};
+        if (ar < G) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[ar][16 * s8 + 8 * ah]);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[ar][16 * s8 + 8 * ah + 4]);
+          split_pair(q0[0], q0[1], hv[0], lv[0]);
+          split_pair(q0[2], q0[3], hv[1], lv[1]);
+          split_pair(q1[0], q1[1], hv[2], lv[2]);
+          split_pair(q1[2], q1[3], hv[3], lv[3]);
         }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 qa = *reinterpret_cast<const f32x4*>(&s_q[h][16 * pc + 4 * q4]);
-            t[h] = fmaf(qa[0], xx[4 * q4], t[h]);
-            t[h] = fmaf(qa[1], xx[4 * q4 + 1], t[h]);
-            t[h] = fmaf(qa[2], xx[4 * q4 + 2], t[h]);
-            t[h] = fmaf(qa[3], xx[4 * q4 + 3], t[h]);
-          }
-        }
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(u32x4{hv[0], hv[1], hv[2], hv[3]}),
+                                                     st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(u32x4{lv[0], lv[1], lv[2], lv[3]}),
+                                                     st, 0, 0, 0);
       }
-    } else if constexpr (BF16) {
-      const uint8_t* myrow = ktile + ri * (kHeadDim * 2);
-#pragma unroll 2
-      for (int i = 0; i < 8; ++i) {
-        const int cc = 8 * half + i;
-        const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((cc ^ (ri & 15)) << 4));
-        float xx[8];
+      float* const sc = &s_p[wave][0][0];  // [head][row] here
+      if (ar < G) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { xx[2 * e] = bf16_lo(pcs[e]); xx[2 * e + 1] = bf16_hi(pcs[e]); }
-        if constexpr (NORMK) {
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(&sc[ar * kWRows + 8 * i4 + 4 * ah]) =
+              f32x4{st[4 * i4], st[4 * i4 + 1], st[4 * i4 + 2], st[4 * i4 + 3]};
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(xx[e], xx[e], ss);
-        }
+      for (int h = 0; h < G; ++h) t[h] = sc[h * kWRows + ri];
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();  // the weights overwrite these slots below
+      if constexpr (NORMK) {
+        // the key's sum of squares: each of its two lanes takes half of the dims
+        if constexpr (FP8) {
+          const uint8_t* myrow = ktile + ri * kHeadDim;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const f32x4 qa4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * cc]);
-          const f32x4 qb4 = *reinterpret_cast<const f32x4*>(&s_q[h][8 * cc + 4]);
-          t[h] = fmaf(qa4[0], xx[0], t[h]);
-          t[h] = fmaf(qa4[1], xx[1], t[h]);
-          t[h] = fmaf(qa4[2], xx[2], t[h]);
-          t[h] = fmaf(qa4[3], xx[3], t[h]);
-          t[h] = fmaf(qb4[0], xx[4], t[h]);
-          t[h] = fmaf(qb4[1], xx[5], t[h]);
-          t[h] = fmaf(qb4[2], xx[6], t[h]);
-          t[h] = fmaf(qb4[3], xx[7], t[h]);
+          for (int i = 0; i < 4; ++i) {
+            const int pc = 4 * half + i;
+            const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((pc ^ (ri & 7)) << 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const f32x2 x0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], false);
+              const f32x2 x1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pcs[e], true);
+              ss = fmaf(x0[0], x0[0], ss);
+              ss = fmaf(x0[1], x0[1], ss);
+              ss = fmaf(x1[0], x1[0], ss);
+              ss = fmaf(x1[1], x1[1], ss);
+            }
+          }
+        } else {
+          const uint8_t* myrow = ktile + ri * (kHeadDim * 2);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int cc = 8 * half + i;
+            const u32x4 pcs = *reinterpret_cast<const u32x4*>(myrow + ((cc ^ (ri & 15)) << 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x0 = bf16_lo(pcs[e]), x1 = bf16_hi(pcs[e]);
+              ss = fmaf(x0, x0, ss);
+              ss = fmaf(x1, x1, ss);
+            }
+          }
         }
       }
     } else {
@@ -393,12 +440,12 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
           t[h] = fmaf(qa4[0], xx[0], fmaf(qa4[1], xx[1], fmaf(qa4[2], xx[2], fmaf(qa4[3], xx[3], t[h]))));
         }
       }
-    }
-    // (lower half first, so both lanes of a row hold the same sum)
+      // (lower half first, so both lanes of a row hold the same sum)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float o = __shfl_xor(t[h], kWRows, kWave);
-      t[h] = half ? o + t[h] : t[h] + o;
+      for (int h = 0; h < G; ++h) {
+        const float o = __shfl_xor(t[h], kWRows, kWave);
+        t[h] = half ? o + t[h] : t[h] + o;
+      }
     }
     float kf = 1.f;
     if constexpr (NORMK) {
