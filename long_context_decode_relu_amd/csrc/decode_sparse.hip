@@ -29,7 +29,9 @@
 //            the queries as hi + lo bf16 B fragments; float32 caches score on
 //            the VALU, two lanes a row); each wave
 //            forms the softmax state of its rows per head (max, sum, weighted
-//            values, in base 2 with log2(e) folded into the query), and the
+//            values, in base 2 with log2(e) folded into the query; the
+//            weighted values on the matrix cores too when the rows are bf16 or
+//            8-bit and finite, V staged row-major in LDS), and the
 //            eight waves' states are merged in wave order into the chunk's
 //            partial.
 //   combine  merges the chunks of each (sequence, head) by log-sum-exp in
@@ -454,7 +456,9 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
       kf = 1.f / sqrtf(ss * (1.0f / kHeadDim) + eps);
     }
     // per head: the wave's maximum over its rows of the head, their weights
-    // relative to it and their sum (over the lower half's lanes)
+    // relative to it and their sum (over the lower half's lanes); the weights
+    // go to this wave's slots as [head][row]
+    float* const sp = &s_p[wave][0][0];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const bool on = (hb >> h) & 1;
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
       const float pr = on ? exp2f(th - mw) : 0.f;
       m_w[h] = mw;
       l_w[h] = wave_sum_dpp(half ? 0.f : pr);
-      if (!half) s_p[wave][ri][h] = pr;
+      if (!half) sp[h * kWRows + ri] = pr;  // [head][row]
     }
     // acc[h] (this lane's two dims) = sum over the wave's rows of p[r][h] v[r].
     // A row outside head h's selection never enters its sum: where a value
@@ -481,40 +485,118 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     const bool all_fin = __ballot(!fin) == 0;
     auto accumulate = [&](auto guarded) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rr = 0; rr < kWRows; ++rr) {
-        float v0, v1;
-        if constexpr (FP8) {
-          const f32x2 vf8 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vb[rr], false);
-          v0 = vf8[0];
-          v1 = vf8[1];
-        } else if constexpr (BF16) {
-          v0 = bf16_lo(vb[rr]);
-          v1 = bf16_hi(vb[rr]);
-        } else {
-          v0 = vf[rr][0];
-          v1 = vf[rr][1];
-        }
-        float pj[GP];
+      for (int r4 = 0; r4 < kWRows; r4 += 4) {
+        f32x4 p4[G];  // rows r4 .. r4+3 of each head
 #pragma unroll
-        for (int h = 0; h < GP; h += 4) {
-          const f32x4 pq = *reinterpret_cast<const f32x4*>(&s_p[wave][rr][h]);
+        for (int h = 0; h < G; ++h) p4[h] = *reinterpret_cast<const f32x4*>(&sp[h * kWRows + r4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pj[h + e] = pq[e];
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if constexpr (decltype(guarded)::value) {
-            acc[h][0] = pj[h] != 0.f ? fmaf(pj[h], v0, acc[h][0]) : acc[h][0];
-            acc[h][1] = pj[h] != 0.f ? fmaf(pj[h], v1, acc[h][1]) : acc[h][1];
+        for (int e = 0; e < 4; ++e) {
+          const int rr = r4 + e;
+          float v0, v1;
+          if constexpr (FP8) {
+            const f32x2 vf8 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vb[rr], false);
+            v0 = vf8[0];
+            v1 = vf8[1];
+          } else if constexpr (BF16) {
+            v0 = bf16_lo(vb[rr]);
+            v1 = bf16_hi(vb[rr]);
           } else {
-            acc[h][0] = fmaf(pj[h], v0, acc[h][0]);
-            acc[h][1] = fmaf(pj[h], v1, acc[h][1]);
+            v0 = vf[rr][0];
+            v1 = vf[rr][1];
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float pj = p4[h][e];
+            if constexpr (decltype(guarded)::value) {
+              acc[h][0] = pj != 0.f ? fmaf(pj, v0, acc[h][0]) : acc[h][0];
+              acc[h][1] = pj != 0.f ? fmaf(pj, v1, acc[h][1]) : acc[h][1];
+            } else {
+              acc[h][0] = fmaf(pj, v0, acc[h][0]);
+              acc[h][1] = fmaf(pj, v1, acc[h][1]);
+            }
           }
         }
       }
     };
-    if (all_fin) accumulate(std::false_type{});
-    else accumulate(std::true_type{});
+    // bf16 and 8-bit values with every value finite: on the matrix cores.
+    // C[h][d] = sum_row P[row][h] V[row][d] per 32-dim tile t: A = the weights
+    // as hi + lo bf16 (lane l: head l % 32, zero past G, rows 16 s + 8 (l / 32)
+    // .. +7 of k-step s), B = V (lane l: dim 32 t + l % 32, the same rows), so
+    // C[t][i] is head 8 (i / 4) + 4 (l / 32) + i % 4 at dim 32 t + l % 32. V is
+    // staged row-major in the wave's K tile (free once the scores are in; one
+    // conflict-free 4-byte store per row and lane) and read back 2 bytes at a
+    // time into B fragments; the products come back through the same slots as
+    // [head][dim].
+    auto accumulate_mfma = [&]() __attribute__((always_inline)) {
+      uint8_t* const vt = ktile;
+#pragma unroll
+      for (int rr = 0; rr < kWRows; ++rr) {
+        uint32_t x = vb[rr];
+        if constexpr (FP8)
+          x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)vb[rr], 1.0f, false));
+        *reinterpret_cast<uint32_t*>(vt + rr * (kHeadDim * 2) + 4 * lane) = x;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      const int ar = lane & 31, ah = lane >> 5;
+      const uint16_t* const v16 = reinterpret_cast<const uint16_t*>(vt);
+      f32x16 cacc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cacc[t][i] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        uint32_t hv[4] = {0u, 0u, 0u, 0u}, lv[4] = {0u, 0u, 0u, 0u};
+        if (ar < G) {
+          const f32x4 q0 = *reinterpret_cast<const f32x4*>(&sp[ar * kWRows + 16 * s2 + 8 * ah]);
+          const f32x4 q1 = *reinterpret_cast<const f32x4*>(&sp[ar * kWRows + 16 * s2 + 8 * ah + 4]);
+          split_pair(q0[0], q0[1], hv[0], lv[0]);
+          split_pair(q0[2], q0[3], hv[1], lv[1]);
+          split_pair(q1[0], q1[1], hv[2], lv[2]);
+          split_pair(q1[2], q1[3], hv[3], lv[3]);
+        }
+        const bf16x8 ah8 = as_bf16x8(u32x4{hv[0], hv[1], hv[2], hv[3]});
+        const bf16x8 al8 = as_bf16x8(u32x4{lv[0], lv[1], lv[2], lv[3]});
+        const int r0 = 16 * s2 + 8 * ah;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int d = 32 * t + ar;
+          u32x4 bv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bv[e] = (uint32_t)v16[(r0 + 2 * e) * kHeadDim + d] |
+                    ((uint32_t)v16[(r0 + 2 * e + 1) * kHeadDim + d] << 16);
+          cacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah8, as_bf16x8(bv), cacc[t], 0, 0, 0);
+          cacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al8, as_bf16x8(bv), cacc[t], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();  // V is read; its slots take the products
+      float* const ct = reinterpret_cast<float*>(vt);  // [head][dim]
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int h = 8 * (i / 4) + 4 * ah + (i % 4);
+          if (h < G) ct[h * kHeadDim + 32 * t + ar] = cacc[t][i];
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const f32x2 a2 = *reinterpret_cast<const f32x2*>(&ct[h * kHeadDim + 2 * lane]);
+        acc[h][0] = a2[0];
+        acc[h][1] = a2[1];
+      }
+    };
+    if constexpr (BF16) {
+      if (all_fin) accumulate_mfma();
+      else accumulate(std::true_type{});
+    } else {
+      if (all_fin) accumulate(std::false_type{});
+      else accumulate(std::true_type{});
+    }
   }
 
   // merge the waves' states in wave order into the chunk's partial
