@@ -71,6 +71,30 @@ def test_fp8_sparse_vs_oracle():
     assert_rows_close(out.cpu().numpy(), want, TOL_BF16, wl.name)
 
 
+@pytest.mark.parametrize("hq,hkv,flags", [(4, 4, O.SSA_NORM_Q), (8, 2, O.SSA_NORM_Q | O.SSA_NORM_K),
+                                           (16, 4, 0), (16, 2, O.SSA_NORM_Q)])
+def test_fp8_sparse_group_sizes_and_flags(hq, hkv, flags):
+    """8-bit rows through the sparse layer at group sizes 1, 4, 4 and 8, with and without
+    normalisation (rows widened exactly into the matrix-core fragments)."""
+    wl = fp8_workload(f"fp8_sp{hq // hkv}", 76, [4000, 777], hq=hq, hkv=hkv, p=0.1)
+    ref = O.decode_full(wl.q, wl.k, oracle_v(wl), wl.ctx_lens)
+    sels = O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
+    cache = ssa.cache_from_workload(wl, DEV)
+    idx = np.full((wl.batch, wl.n_q_heads, 1152), -1, dtype=np.int32)
+    cnt = np.zeros((wl.batch, wl.n_q_heads), dtype=np.int32)
+    for b in range(wl.batch):
+        for h in range(wl.n_q_heads):
+            s = np.asarray(sels[b][h], dtype=np.int32)
+            idx[b, h, :len(s)] = s
+            cnt[b, h] = len(s)
+    out = ssa.ssa_decode_sparse(torch.from_numpy(wl.q_sparse[0]).to(DEV), cache,
+                                torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV),
+                                flags=flags)
+    torch.cuda.synchronize()
+    want = O.decode_sparse(wl.q_sparse[0], wl.k, oracle_v(wl), sels, flags=flags)
+    assert_rows_close(out.cpu().numpy(), want, TOL_BF16, wl.name)
+
+
 def test_fp8_vskip_nan_poison():
     """Value rows that no head of the group needs hold the NaN code: the output
     does not change by a bit (they are never read)."""

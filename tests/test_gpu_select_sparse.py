@@ -181,6 +181,16 @@ def test_sparse_group_sizes(hq, hkv, dtype):
     check_sparse(wl, oracle_selection(wl))
 
 
+@pytest.mark.parametrize("hq,hkv,flags", [(2, 2, O.SSA_NORM_Q), (16, 4, O.SSA_NORM_Q | O.SSA_NORM_K),
+                                           (16, 2, 0)])
+def test_sparse_bf16_group_sizes_and_key_norm(hq, hkv, flags):
+    """bf16 rows at group sizes 1, 4 and 8 with and without normalisation: the gather's scores
+    and weighted values on the matrix cores."""
+    wl = synth.make_workload("spn", seed=35, batch=2, n_q_heads=hq, n_kv_heads=hkv,
+                             ctx_lens=[5000, 900], kv_dtype="bf16", recipe="planted", p=0.1)
+    check_sparse(wl, oracle_selection(wl), flags=flags)
+
+
 def test_sparse_short_context_is_full_softmax_and_empty():
     """n <= 1024: every key is selected; an empty selection returns 0."""
     wl = synth.make_workload("spshort", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
