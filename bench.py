@@ -211,8 +211,11 @@ def bench_leg(wl, *, n_sparse: int, steps: int, warmup: int = 3, rotate_bytes: i
                                                           n_recent=n_recent)
         if ev is not None:
             ev[1].record()
+        # the block's sparse layers share the selection: after the first, the
+        # row union already in the workspace is reused
         for l in range(n_sparse):
-            ssa.ssa_decode_sparse(qs[l], c, sel, cnt, out=outs[l], ws=ws_sp)
+            ssa.ssa_decode_sparse(qs[l], c, sel, cnt, out=outs[l], ws=ws_sp,
+                                  flags=ssa.SSA_NORM_Q | (ssa.SSA_SPARSE_REUSE_UNION if l else 0))
         if ev is not None:
             ev[2].record()
         return sel, cnt

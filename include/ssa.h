@@ -83,7 +83,8 @@ enum {
   SSA_NORM_K = 2,          /* RMS-normalise each key row on the fly (else keys are stored normalised) */
   SSA_SELECT_DISJOINT = 4, /* selection = recent window + top-k of the keys outside it */
   SSA_ROPE = 8,            /* window decode: rotate the query at its position (RoPE) */
-  SSA_ROPE_HALF = 16       /* RoPE pairs dims (i, i + D/2) instead of (2i, 2i + 1) */
+  SSA_ROPE_HALF = 16,      /* RoPE pairs dims (i, i + D/2) instead of (2i, 2i + 1) */
+  SSA_SPARSE_REUSE_UNION = 32 /* sparse layer: the workspace holds this selection's row union */
 };
 
 typedef struct {
@@ -179,7 +180,17 @@ ssa_status ssa_select_topk_recent(const ssa_shape* shape, const float* scores,
  *   t_j = scale * dot(q_hat, k[b,kvh,j]),  p = softmax(t) over S
  *   out[b,h] = sum_j p_j v[b,kvh,j]        (0 for an empty selection)
  * Rows shared by the heads of a KV group are read once. Indices outside
- * [0, ctx_lens[b]) are rejected in the kernel by skipping them. */
+ * [0, ctx_lens[b]) are rejected in the kernel by skipping them.
+ *
+ * The call first forms, per (b, kv head), the union of its heads' selected
+ * rows in ws. The sparse layers of one block reuse the full layer's cache and
+ * selection ("Three kinds of attention"), so every layer after the first may
+ * pass SSA_SPARSE_REUSE_UNION: the union pass is skipped and the union already
+ * in ws is used. The caller guarantees that ws (or, for
+ * ssa_decode_sparse_static, the library's array on this GPU) was last written
+ * by an ssa_decode_sparse call on the same stream with the same shape,
+ * ctx_lens, sel_idx, sel_count and sel_stride; otherwise the output is
+ * undefined (reads stay inside ws). */
 ssa_status ssa_decode_sparse(const ssa_shape* shape, const float* q, const void* k, const void* v,
                              const int32_t* ctx_lens, const int32_t* sel_idx,
                              const int32_t* sel_count, int32_t sel_stride, float scale, float eps,

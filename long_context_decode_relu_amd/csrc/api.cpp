@@ -91,7 +91,7 @@ ssa_status sparse_args(const ssa_shape* s, const float* q, const void* k, const 
   if (s->batch == 0) return SSA_OK;
   if (!q || !k || !v || !ctx_lens || !sel_idx || !sel_count || !out) return SSA_ERR_NULL;
   if (!finite(scale) || !finite(eps) || eps < 0.0f) return SSA_ERR_SHAPE;
-  if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K)) return SSA_ERR_UNSUPPORTED;
+  if (flags & ~(uint32_t)(SSA_NORM_Q | SSA_NORM_K | SSA_SPARSE_REUSE_UNION)) return SSA_ERR_UNSUPPORTED;
   a->B = s->batch;
   a->Hq = s->n_q_heads;
   a->Hkv = s->n_kv_heads;

@@ -722,7 +722,8 @@ void launch_t(const DecodeSparseArgs& a, const SpLayout& s, char* ws, hipStream_
   int2* urow = reinterpret_cast<int2*>(ws + s.urow);
   int32_t* ucnt = reinterpret_cast<int32_t*>(ws + s.ucnt);
   int32_t* uoff = reinterpret_cast<int32_t*>(ws + s.uoff);
-  if (s.nseg > 0)
+  // the union of an earlier call on the same selection may still be in ws
+  if (s.nseg > 0 && !(a.flags & SSA_SPARSE_REUSE_UNION))
     hipLaunchKernelGGL((sparse_union<G>), dim3(S * s.nseg), dim3(kUThreads), 0, stream, a.ctx_lens,
                        a.sel_idx, a.sel_count, a.sel_stride, a.Hq, a.Hkv, nlim, s.nseg, s.cap, urow,
                        ucnt, uoff);

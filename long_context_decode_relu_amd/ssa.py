@@ -36,6 +36,7 @@ SSA_NORM_K = 2
 SSA_SELECT_DISJOINT = 4
 SSA_ROPE = 8
 SSA_ROPE_HALF = 16
+SSA_SPARSE_REUSE_UNION = 32
 
 SSA_OP_DECODE_FULL = 0
 SSA_OP_SELECT = 1
@@ -290,6 +291,8 @@ def ssa_decode_sparse(q: torch.Tensor, cache: Cache, sel_idx: torch.Tensor, sel_
     stride = sel_idx.shape[2]
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(ws is not None or not (flags & SSA_SPARSE_REUSE_UNION),
+          "SSA_SPARSE_REUSE_UNION reuses the union in the workspace of an earlier call: pass that ws")
     if ws is None:
         ws = workspace(SSA_OP_DECODE_SPARSE, shp, stride, dev)
     st = lib().ssa_decode_sparse(ctypes.byref(shp), _ptr(q), _ptr(cache.k), _ptr(cache.v),

@@ -119,6 +119,9 @@ def test_sparse_and_prefill_reject():
                                FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_SHAPE
     assert L.ssa_decode_sparse(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, 1152, 0.1, 1e-6,
                                1, FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_NULL
+    for fl in (ssa.SSA_SELECT_DISJOINT, ssa.SSA_ROPE, 64):  # not sparse-layer flags
+        assert L.ssa_decode_sparse(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1152, 0.1,
+                                   1e-6, fl, FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_UNSUPPORTED
     assert L.ssa_prefill_full(ctypes.byref(shape(kv_dtype=ssa.SSA_F32)), FAKE, 16, FAKE, FAKE, FAKE,
                               FAKE, 1.0, 1.0, 1e-6, 1, FAKE, FAKE, 1 << 40, None) == ssa.SSA_ERR_UNSUPPORTED
     assert L.ssa_prefill_full(ctypes.byref(s), FAKE, -1, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 1e-6, 1,

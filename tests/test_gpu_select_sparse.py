@@ -191,6 +191,37 @@ def test_sparse_bf16_group_sizes_and_key_norm(hq, hkv, flags):
     check_sparse(wl, oracle_selection(wl), flags=flags)
 
 
+def test_sparse_layers_reuse_the_union():
+    """Three sparse layers on one selection (a block's full layer and its sparse layers): the
+    second and third pass SSA_SPARSE_REUSE_UNION with the first call's workspace and give the
+    same bits as calls that form the union again, through the workspace call and the static one."""
+    wl = synth.make_workload("reuse", seed=36, batch=3, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[70000, 1500, 9000], p=0.05, n_sparse_layers=3)
+    cache = ssa.cache_from_workload(wl, DEV)
+    sels = oracle_selection(wl)
+    sel, cnt = sel_tensors(sels, wl.batch, wl.n_q_heads, 1152)
+    qs = [torch.from_numpy(wl.q_sparse[l]).to(DEV) for l in range(3)]
+    fresh = [ssa.ssa_decode_sparse(qs[l], cache, sel, cnt).cpu().numpy() for l in range(3)]
+    ws = ssa.workspace(ssa.SSA_OP_DECODE_SPARSE, cache.shape(wl.n_q_heads), 1152, DEV)
+    reuse = []
+    for l in range(3):
+        fl = ssa.SSA_NORM_Q | (ssa.SSA_SPARSE_REUSE_UNION if l else 0)
+        reuse.append(ssa.ssa_decode_sparse(qs[l], cache, sel, cnt, flags=fl, ws=ws).cpu().numpy())
+    static = []
+    for l in range(3):
+        fl = ssa.SSA_NORM_Q | (ssa.SSA_SPARSE_REUSE_UNION if l else 0)
+        out = torch.empty((wl.batch, wl.n_q_heads, 128), dtype=torch.float32, device=DEV)
+        static.append(ssa.ssa_decode_sparse_static(qs[l], cache, sel, cnt, out, flags=fl).cpu().numpy())
+    torch.cuda.synchronize()
+    for l in range(3):
+        assert np.array_equal(reuse[l].view(np.uint32), fresh[l].view(np.uint32)), l
+        assert np.array_equal(static[l].view(np.uint32), fresh[l].view(np.uint32)), l
+        want = O.decode_sparse(wl.q_sparse[l], wl.k, wl.v, sels)
+        assert_rows_close(fresh[l], want, TOL_BF16, f"layer {l}")
+    with pytest.raises(ValueError):
+        ssa.ssa_decode_sparse(qs[1], cache, sel, cnt, flags=ssa.SSA_NORM_Q | ssa.SSA_SPARSE_REUSE_UNION)
+
+
 def test_sparse_short_context_is_full_softmax_and_empty():
     """n <= 1024: every key is selected; an empty selection returns 0."""
     wl = synth.make_workload("spshort", seed=34, batch=3, n_q_heads=16, n_kv_heads=2,
