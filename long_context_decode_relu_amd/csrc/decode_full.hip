@@ -593,8 +593,15 @@ __device__ __forceinline__ float head_rms_factor(const float* qrow, int lane, fl
 // then takes the keys of its stream's lists whose own score is positive.
 // Streams of at most kCandAll keys list every key instead, so that the exact
 // cut among the list always holds the top k. List position p holds the key
-// index at cand_idx[p] and the G scores at cand_sc[p*G ..].
+// index at cand_idx[p] and head h's score at cand_sc[h * cap + p], where cap
+// = S * ceil(max_ctx / 64) * 64 positions bounds every stream's tiles: a
+// row's selection then reads its own head's scores contiguously (one eighth
+// of the cache lines that interleaved scores would pull for G = 8).
 constexpr int kCandAll = 8192;
+// floats from one head's candidate scores to the next
+__device__ __forceinline__ size_t cand_plane(int S, int max_ctx) {
+  return (size_t)S * (size_t)ceil_div(max_ctx, kTileKeys) * kTileKeys;
+}
 // Entries a thread of a row's selection work-group gathers into registers:
 // rows whose lists hold more entries than kSelThreads * kGatherPer are
 // selected from rescored scores instead.
@@ -722,7 +729,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   int vrows = 0;
   int ccount = 0;              // entries listed in the current slot
   int32_t* lidx = nullptr;     // the current slot's list: key indices
-  float* lsc = nullptr;        //   and the group's scores, G per entry
+  float* lsc = nullptr;        //   and the first head's scores
+  const size_t sc_plane = CAND ? cand_plane(S, max_ctx) : 0;
   auto reset = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < G; ++h) { num[h][0] = num[h][1] = 0.f; den[h] = 0.f; nnz[h] = 0; }
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
       int first, nt;
       slot_tiles(st.s0, st.s1, w, part, &first, &nt);
       lidx = cand_idx + (size_t)first * kTileKeys;
-      lsc = cand_sc + (size_t)first * kTileKeys * G;
+      lsc = cand_sc + (size_t)first * kTileKeys;
     }
   };
   // Entry of this lane's key among the keys of mask m listed next in the
@@ -755,16 +763,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_full_kernel(
   // entry e of list (li, ls): key index and the group's scores sv
   auto list_store = [&](int32_t* li, float* ls, int e, int key, const float (&sv)[G]) {
     li[e] = key;
-    float* d = ls + (size_t)e * G;
-    if constexpr (G >= 4) {
 #pragma unroll
-      for (int p = 0; p < G / 4; ++p)
-        *reinterpret_cast<f32x4*>(d + 4 * p) = f32x4{sv[4 * p], sv[4 * p + 1], sv[4 * p + 2], sv[4 * p + 3]};
-    } else if constexpr (G == 2) {
-      *reinterpret_cast<f32x2*>(d) = f32x2{sv[0], sv[1]};
-    } else {
-      d[0] = sv[0];
-    }
+    for (int h = 0; h < G; ++h) ls[h * sc_plane + e] = sv[h];
   };
   auto flush = [&](const Stream& st) __attribute__((always_inline)) {
     const int64_t slot = (int64_t)st.j + w;
@@ -1600,12 +1600,12 @@ __device__ void cands_cut(SelShared& sh, const uint32_t (&key)[P], const int32_t
 
 // Selects row (b, h) into out[0..stride) and *count, or sets *flag. The
 // row's candidates are the entries of its stream's slot lists, in slot order
-// (ascending key index), whose score for head jh (cand_sc[p * qs] for
-// position p, with cand_sc pointing at the head's first score) is positive
+// (ascending key index), whose score for head jh (cand_sc[p] for position
+// p, with cand_sc pointing at the head's scores) is positive
 // (every entry when the stream lists all its keys), restricted to the pool.
 __device__ __forceinline__ void select_from_cands(SelShared& sh,
                                                   const int32_t* __restrict__ cand_idx,
-                                                  const float* __restrict__ cand_sc, int qs,
+                                                  const float* __restrict__ cand_sc,
                                                   const int32_t* __restrict__ cand_cnt,
                                                   const int* __restrict__ tile_pre, int S, int j,
                                                   int Wl, int n, int k_top, int n_recent,
@@ -1692,7 +1692,7 @@ __device__ __forceinline__ void select_from_cands(SelShared& sh,
       sc[u] = 0.f;
       idx[u] = 0;
       if (e0 + u < e1) {
-        sc[u] = cand_sc[at[u] * qs];
+        sc[u] = cand_sc[at[u]];
         idx[u] = cand_idx[at[u]];
       }
     }
@@ -1740,11 +1740,11 @@ __device__ __forceinline__ void select_from_cands(SelShared& sh,
 // those past the count are ignored). The selected entries are then written in
 // (slot, position) order, which is key order: ranks within a slot from a
 // ballot, the slots' places from one scan of their totals. Scores are read as
-// in select_from_cands (cand_sc[p * qs]). Returns false, having written
+// in select_from_cands (cand_sc[p]). Returns false, having written
 // nothing, when the row does not fit; select_from_cands then gives the same
 // selection from the same lists.
 __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __restrict__ cand_idx,
-                                            const float* __restrict__ cand_sc, int qs,
+                                            const float* __restrict__ cand_sc,
                                             const int32_t* __restrict__ cand_cnt, int T, int s0,
                                             int s1, int j, int Wl, int n, int k_top, int n_recent,
                                             int disjoint, int32_t* __restrict__ out, int stride,
@@ -1781,7 +1781,7 @@ __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __rest
       if (u < nr) {
         const size_t at = (size_t)__builtin_amdgcn_readlane(fv, u) * kTileKeys + lane;
         idx[u] = cand_idx[at];
-        sc[u] = cand_sc[at * qs];
+        sc[u] = cand_sc[at];
       }
     }
 #pragma unroll
@@ -1889,8 +1889,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   const int stride = k_top + n_recent;
   const int n = live_keys(ctx_lens, b, max_ctx);
   const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
-  const float* hsc = cand_sc + jh;  // the row's scores: every G-th float
-  const int qs = G;
+  const float* hsc = cand_sc + (size_t)jh * cand_plane(S, max_ctx);  // the row's scores
   int32_t* const o = sel_idx + (size_t)row * stride;
   if (row_flag[row]) {  // rescored: the exact selection from the row's scores
     select_row_exact(sh, rs + (size_t)row * max_ctx, n, k_top, n_recent, disjoint, o, stride,
@@ -1898,9 +1897,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
     return;
   }
   int32_t* const fail = sel_fail + row;
-  if (!select_fast(sh, cand_idx, hsc, qs, cand_cnt, T, s0, s1, j, Wl, n, k_top, n_recent, disjoint,
+  if (!select_fast(sh, cand_idx, hsc, cand_cnt, T, s0, s1, j, Wl, n, k_top, n_recent, disjoint,
                    o, stride, sel_count + row, fail))
-    select_from_cands(sh, cand_idx, hsc, qs, cand_cnt, tile_pre, S, j, Wl, n, k_top, n_recent,
+    select_from_cands(sh, cand_idx, hsc, cand_cnt, tile_pre, S, j, Wl, n, k_top, n_recent,
                       disjoint, o, stride, sel_count + row, fail);
   // the full-layer kernel flags every row these tests reject; should one be
   // rejected anyway its count is -1 (an empty selection), never stale
