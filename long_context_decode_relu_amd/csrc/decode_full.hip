@@ -1907,20 +1907,19 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine_select(
   if (threadIdx.x == 0 && *fail) sel_count[row] = -1;
 }
 
-// Rows whose candidate lists cannot decide their selection: one wave per
-// stream (sequence, KV head) decides which of its G rows the combine's list
+// Rows whose candidate lists cannot decide their selection: one wave decides
+// which of the G rows of stream j (sequence, KV head) the combine's list
 // selection would reject, by the tests that selection makes: fewer listed
 // keys with a positive score than k, or more list entries or slots than it
-// holds. It writes row_flag for the G rows and the stream's mask (one bit per
-// head) for the rescoring kernel.
-__global__ __launch_bounds__(256) void decode_full_decide(
-    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
-    const int* __restrict__ tile_pre, const int32_t* __restrict__ ctx_lens, int S, int Wl, int G,
-    int Hq, int Hkv, int max_ctx, int k_top, int n_recent, int disjoint,
-    int32_t* __restrict__ row_flag, int32_t* __restrict__ fmask) {
+// holds. Returns the stream's mask (bit h: row h rejected) on every lane and,
+// when row_flag is given, writes the G rows' flags.
+__device__ uint32_t decide_stream(int j, const int32_t* __restrict__ cand_cnt,
+                                  const int32_t* __restrict__ part_nnz,
+                                  const int* __restrict__ tile_pre,
+                                  const int32_t* __restrict__ ctx_lens, int S, int Wl, int G,
+                                  int Hq, int Hkv, int max_ctx, int k_top, int n_recent,
+                                  int disjoint, int32_t* __restrict__ row_flag) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= S) return;
   const int b = j / Hkv, kvh = j - b * Hkv;
   const int n = live_keys(ctx_lens, b, max_ctx);
   const int T = tile_pre[S], s0 = tile_pre[j], s1 = tile_pre[j + 1];
@@ -1980,34 +1979,39 @@ __global__ __launch_bounds__(256) void decode_full_decide(
     const int c = n <= kCandAll ? pool : wave_sum_i(nz[h]) - outside;
     const bool f = kk < pool && (too_big || c < kk);
     fm |= f ? 1u << h : 0u;
-    if (lane == 0) row_flag[b * Hq + kvh * G + h] = f ? 1 : 0;
+    if (row_flag && lane == 0) row_flag[b * Hq + kvh * G + h] = f ? 1 : 0;
   }
-  if (lane == 0) fmask[j] = (int32_t)fm;
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)fm);
 }
 
-// The flagged rows rescored. Every work-group reads the streams' masks,
-// keeps a bitmap of the streams with a flagged row in LDS, and takes its share
-// of the work items (flagged stream, slice of its 64-key tiles): each wave
-// copies its tiles into LDS as the full-layer kernel does and scores every key
-// exactly as it does (score_row: same widening, FMA order and query factors)
-// into the flagged rows' buffers of `max_ctx` floats. The combine then
-// selects those rows from the buffers. With nothing flagged every work-group
-// exits after one load.
+// The flagged rows rescored. The work items are (stream, slice of its 64-key
+// tiles), kFallbackSlices slices a stream; work-group w takes items w, w + W,
+// ... (W work-groups, at most kWaves items each). Each of its waves first
+// decides the stream of one item (decide_stream; the work-group holding a
+// stream's slice 0 writes its rows' flags), then the work-group rescores the
+// items whose stream has a flagged row: each wave copies its tiles into LDS
+// as the full-layer kernel does and scores every key exactly as it does
+// (score_row: same widening, FMA order and query factors) into the flagged
+// rows' buffers of `max_ctx` floats. The combine then selects those rows from
+// the buffers. With nothing flagged every work-group exits after its decide.
 constexpr int kFallbackBlocks = 256;
 constexpr int kFallbackSlices = 64;
+
+// Work-groups of the rescoring kernel for S streams: at least
+// kFallbackBlocks, and enough for at most kWaves items each.
+inline int rescore_blocks(int S) {
+  return std::max(kFallbackBlocks, ceil_div(S * kFallbackSlices, kWaves));
+}
 
 template <int G, bool BF16, bool NORMK, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_full_rescore(
     const float* __restrict__ q, const void* __restrict__ k, const int32_t* __restrict__ ctx_lens,
-    const int32_t* __restrict__ fmask, int S, int Hq, int Hkv, int Nmax, int max_ctx, float scale,
-    float eps, int normq, float* __restrict__ rs) {
+    const int32_t* __restrict__ cand_cnt, const int32_t* __restrict__ part_nnz,
+    const int* __restrict__ tile_pre, int S, int Wl, int Hq, int Hkv, int Nmax, int max_ctx,
+    int k_top, int n_recent, int disjoint, float scale, float eps, int normq,
+    int32_t* __restrict__ row_flag, float* __restrict__ rs) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[BF16 ? kWaves * kTileBytesBf16 : 16];
-  __shared__ int s_red[kWaves];
-  __shared__ int s_carry;
-  extern __shared__ uint32_t s_dyn[];  // bitmap of streams with a flagged row, then its word prefix
-  const int nw = ceil_div(S, 32);
-  uint32_t* const s_fw = s_dyn;
-  int* const s_fpre = reinterpret_cast<int*>(s_dyn + nw);
+  __shared__ uint32_t s_fm[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2016,53 +2020,27 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
   constexpr size_t kRowBytes = kHeadDim * (FP8 ? 1 : BF16 ? 2 : 4);
   const uint32_t f8off = fp8_tile_offset(lane);
   const TileOffsets toff(lane);
-  for (int i = tid; i < nw; i += kThreads) s_fw[i] = 0u;
-  __syncthreads();
-  int any = 0;
-  for (int j = tid; j < S; j += kThreads)
-    if (fmask[j]) {
-      atomicOr(&s_fw[j >> 5], 1u << (j & 31));
-      any = 1;
+  const int items = S * kFallbackSlices;
+  {
+    const int it = blockIdx.x + wave * gridDim.x;
+    uint32_t fm = 0u;
+    if (it < items) {
+      const int j = it / kFallbackSlices;
+      fm = decide_stream(j, cand_cnt, part_nnz, tile_pre, ctx_lens, S, Wl, G, Hq, Hkv, max_ctx,
+                         k_top, n_recent, disjoint, it % kFallbackSlices == 0 ? row_flag : nullptr);
     }
-  if (!__syncthreads_or(any)) return;  // nothing flagged
-  // exclusive prefix of the bitmap words' counts (block scan, kThreads at a time)
-  if (tid == 0) s_carry = 0;
-  for (int w0 = 0; w0 < nw; w0 += kThreads) {
-    __syncthreads();
-    const int i = w0 + tid;
-    const int c = i < nw ? __popc(s_fw[i]) : 0;
-    int incl = c;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += t;
-    }
-    if (lane == kWave - 1) s_red[wave] = incl;
-    __syncthreads();
-    int before = s_carry, total = s_carry;
-#pragma unroll
-    for (int x = 0; x < kWaves; ++x) {
-      before += x < wave ? s_red[x] : 0;
-      total += s_red[x];
-    }
-    if (i < nw) s_fpre[i] = before + incl - c;
-    __syncthreads();
-    if (tid == 0) s_carry = total;
+    if (lane == 0) s_fm[wave] = fm;
   }
   __syncthreads();
-  const int F = s_carry;  // streams with a flagged row
-  for (int it = blockIdx.x; it < F * kFallbackSlices; it += gridDim.x) {
-    const int f = it / kFallbackSlices, sl = it - f * kFallbackSlices;
-    // the f-th flagged stream: its bitmap word, then its bit within the word
-    int lo = 0, hi = nw - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_fpre[mid] <= f) lo = mid; else hi = mid - 1;
-    }
-    uint32_t x = s_fw[lo];
-    for (int r = f - s_fpre[lo]; r > 0; --r) x &= x - 1u;
-    const int j = __builtin_amdgcn_readfirstlane(lo * 32 + __builtin_ctz(x));
-    const uint32_t fm = (uint32_t)__builtin_amdgcn_readfirstlane(fmask[j]);
+  uint32_t any = 0u;
+#pragma unroll
+  for (int kk = 0; kk < kWaves; ++kk) any |= s_fm[kk];
+  if (__builtin_amdgcn_readfirstlane((int)any) == 0) return;  // nothing flagged here
+  for (int kk = 0; kk < kWaves; ++kk) {
+    const uint32_t fm = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_fm[kk]);
+    if (fm == 0u) continue;
+    const int it = blockIdx.x + kk * gridDim.x;
+    const int j = it / kFallbackSlices, sl = it - j * kFallbackSlices;
     const int b = j / Hkv, kvh = j - b * Hkv;
     const int row0 = b * Hq + kvh * G;  // the group's first row
     const int n = __builtin_amdgcn_readfirstlane(live_keys(ctx_lens, b, max_ctx));
@@ -2137,7 +2115,7 @@ __global__ __launch_bounds__(kThreads) void decode_full_rescore(
 struct WsLayout {
   size_t num, den, nnz, vrows, tile_pre, qhi, invc, total;
   // the fused selection: candidate lists and counts, row flags, rescored rows
-  size_t cand_idx, cand_sc, cand_cnt, flag, fail, fmask, rescored, total_sel;
+  size_t cand_idx, cand_sc, cand_cnt, flag, fail, rescored, total_sel;
 };
 
 WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
@@ -2161,7 +2139,6 @@ WsLayout ws_layout(int B, int Hq, int Hkv, int max_ctx) {
   l.cand_cnt = o; o += align_up(slots * sizeof(int32_t), 256);
   l.flag = o; o += align_up(rows * sizeof(int32_t), 256);
   l.fail = o; o += align_up(rows * sizeof(int32_t), 256);
-  l.fmask = o; o += align_up(S * sizeof(int32_t), 256);
   l.rescored = o; o += align_up(rows * (size_t)max_ctx * sizeof(float), 256);
   l.total_sel = o;
   return l;
@@ -2339,26 +2316,19 @@ hipError_t launch_decode_full_select(const DecodeFullSelectArgs& s, hipStream_t 
   const int disjoint = (s.sel_flags & SSA_SELECT_DISJOINT) ? 1 : 0;
   int grid = 0;
   // 1. filter inputs; 2. the full layer with its candidate lists; 3. per
-  // stream, the rows the lists cannot select flagged; 4. those rows rescored;
-  // 5. combine and selection, one work-group per row
+  // stream, the rows the lists cannot select flagged, and those rows
+  // rescored; 4. combine and selection, one work-group per row
   hipError_t e = launch_qprep(a, l, L, stream);
   if (e != hipSuccess) return e;
   e = launch_full<true>(a, L, stream, &grid);
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
   const int S = a.B * a.Hkv;
-  int32_t* fmask = reinterpret_cast<int32_t*>(ws + l.fmask);
-  hipLaunchKernelGGL(decode_full_decide, dim3(ceil_div(S, 4)), dim3(256), 0, stream, L.cand_cnt,
-                     L.nnz, L.tile_pre, a.ctx_lens, S, grid * kWaves, G, a.Hq, a.Hkv, a.max_ctx,
-                     s.k_top, s.n_recent, disjoint, row_flag, fmask);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // the rescoring kernel's LDS bitmap of streams and its word prefix
-  const size_t dyn = 2 * (size_t)ceil_div(S, 32) * sizeof(uint32_t);
   e = dispatch(G, kvt_of(a), a.flags & SSA_NORM_K, [&]<int g, bool bf16, bool nk, bool f8>() -> hipError_t {
-    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk, f8>), dim3(kFallbackBlocks), dim3(kThreads), dyn,
-                       stream, a.q, a.k, a.ctx_lens, fmask, S, a.Hq, a.Hkv, a.Nmax, a.max_ctx,
-                       a.scale, a.eps, L.normq, rescored);
+    hipLaunchKernelGGL((decode_full_rescore<g, bf16, nk, f8>), dim3(rescore_blocks(S)), dim3(kThreads), 0,
+                       stream, a.q, a.k, a.ctx_lens, L.cand_cnt, L.nnz, L.tile_pre, S, grid * kWaves,
+                       a.Hq, a.Hkv, a.Nmax, a.max_ctx, s.k_top, s.n_recent, disjoint, a.scale, a.eps,
+                       L.normq, row_flag, rescored);
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
