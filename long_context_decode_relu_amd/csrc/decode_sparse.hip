@@ -637,50 +637,76 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
 
 // out[b][h] = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c over the chunks
 // c of the stream, in chunk order (the maxima are in base-2 units); 0 for an
-// empty selection. The chunk maxima are staged in LDS so that the loads of all
-// chunks are in flight together.
-constexpr int kCmbChunk = 256;
+// empty selection. One round trip brings the chunk count, every chunk's
+// maximum and sum (chunk d + 128 i on thread d) and this thread's dimension
+// of the first kCmbPre chunks' weighted sums: slots past the count are read
+// (they lie inside the buffers) but not used. The weights 2^(m_c - M) go
+// through LDS to every thread.
+constexpr int kCmbChunk = 256;  // chunks per stream at most
+constexpr int kCmbPer = kCmbChunk / kHeadDim;
+constexpr int kCmbPre = 48;
+static_assert(8 * kMaxStride / kChunk <= kCmbChunk, "a stream's chunks fit the combine's LDS");
 
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
     const float* __restrict__ part_acc, const int32_t* __restrict__ nch, int Hq, int Hkv, int C,
     float* __restrict__ out) {
-  __shared__ float s_mm[kCmbChunk];
+  __shared__ float s_e[kCmbChunk];
   __shared__ float s_ll[kCmbChunk];
-  __shared__ float s_red[kHeadDim];
+  __shared__ float s_red[kHeadDim / kWave];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int lane = d & (kWave - 1), wave = d / kWave;
   const int G = Hq / Hkv;
   const int kvh = h / G, jh = h - kvh * G;
   const int j = b * Hkv + kvh;
-  const int pb = min(nch[j], C);
   const size_t s0 = (size_t)j * C;
-  // global maximum over the chunks
-  float M = -INFINITY;
-  for (int p = d; p < pb; p += kHeadDim) M = fmaxf(M, part_m[(s0 + p) * G + jh]);
-  s_red[d] = M;
-  __syncthreads();
-  for (int o = kHeadDim / 2; o > 0; o >>= 1) {
-    if (d < o) s_red[d] = fmaxf(s_red[d], s_red[d + o]);
-    __syncthreads();
+  const int nc = nch[j];
+  float mr[kCmbPer], lr[kCmbPer];
+#pragma unroll
+  for (int i = 0; i < kCmbPer; ++i) {
+    const int p = d + i * kHeadDim;
+    mr[i] = p < C ? part_m[(s0 + p) * G + jh] : -INFINITY;
+    lr[i] = p < C ? part_l[(s0 + p) * G + jh] : 0.f;
   }
+  float av[kCmbPre];
+#pragma unroll
+  for (int i = 0; i < kCmbPre; ++i)
+    av[i] = i < C ? part_acc[((s0 + i) * G + jh) * kHeadDim + d] : 0.f;
+  const int pb = min(nc, C);
+  // the maximum over the chunks that exist
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kCmbPer; ++i)
+    if (d + i * kHeadDim < pb) M = fmaxf(M, mr[i]);
+  M = wave_max_dpp(M);
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
   M = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kHeadDim / kWave; ++w) M = fmaxf(M, s_red[w]);
   float a = 0.f, ls = 0.f;
   if (M != -INFINITY) {
-    for (int c0 = 0; c0 < pb; c0 += kCmbChunk) {
-      const int cn = min(kCmbChunk, pb - c0);
-      __syncthreads();
-      for (int i = d; i < cn; i += kHeadDim) {
-        const float mp = part_m[(s0 + c0 + i) * G + jh];
-        s_mm[i] = mp == -INFINITY ? 0.f : exp2f(mp - M);
-        s_ll[i] = part_l[(s0 + c0 + i) * G + jh];
+#pragma unroll
+    for (int i = 0; i < kCmbPer; ++i) {
+      const int p = d + i * kHeadDim;
+      if (p < pb) {
+        s_e[p] = mr[i] == -INFINITY ? 0.f : exp2f(mr[i] - M);
+        s_ll[p] = lr[i];
       }
-      __syncthreads();
-#pragma unroll 8
-      for (int i = 0; i < cn; ++i) {
-        const float e = s_mm[i];
-        a = fmaf(e, part_acc[((s0 + c0 + i) * G + jh) * kHeadDim + d], a);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCmbPre; ++i) {
+      if (i < pb) {
+        const float e = s_e[i];
+        a = fmaf(e, av[i], a);
         ls = fmaf(e, s_ll[i], ls);
       }
+    }
+    for (int i = kCmbPre; i < pb; ++i) {
+      const float e = s_e[i];
+      a = fmaf(e, part_acc[((s0 + i) * G + jh) * kHeadDim + d], a);
+      ls = fmaf(e, s_ll[i], ls);
     }
   }
   out[((size_t)b * Hq + h) * kHeadDim + d] = ls > 0.f ? a / ls : 0.f;
