@@ -80,12 +80,14 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 }
 constexpr int kMaxStride = kWave * kWave;         // two rounds of 64 probes
 
-// Numbers of entries below x0 and below x1 in list[0 .. cnt) (ascending;
-// cnt <= 4096), by two rounds of 64 probes; every lane gets both.
-__device__ __forceinline__ int2 list_bounds(const int32_t* list, int cnt, int x0, int x1, int lane) {
+// Numbers of entries below x0 and below x1 in list[0 .. cnt) (ascending), by
+// two rounds of 64 probes, every lane getting both. The first round comes
+// loaded: v is the entry at position min(L, (lane + 1) * step) - 1 of the
+// list's row of L >= cnt slots (step = ceil(L / 64) <= 64), taken as INT_MAX
+// past cnt, so that those probes can be issued before cnt is known.
+__device__ __forceinline__ int2 list_bounds_from(const int32_t* list, int cnt, int step, int v,
+                                                 int x0, int x1, int lane) {
   if (cnt <= 0) return int2{0, 0};
-  const int step = ceil_div(cnt, kWave);  // <= 64
-  const int v = list[min(cnt, (lane + 1) * step) - 1];
   const int b0 = min(cnt, (int)__popcll(__ballot(v < x0)) * step);
   const int b1 = min(cnt, (int)__popcll(__ballot(v < x1)) * step);
   const int p0 = b0 + lane, p1 = b1 + lane;
@@ -110,6 +112,16 @@ __global__ __launch_bounds__(kUThreads) void sparse_union(
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const size_t hrow0 = (size_t)b * Hq + (size_t)kvh * G;
+  // the first round of probes into this wave's lists goes out with the
+  // counts: its positions depend only on the stride
+  const int pstep = ceil_div(stride, kWave);
+  const int ppos = min(stride, (lane + 1) * pstep) - 1;
+  int pv[HPW];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + i * kUWaves;
+    pv[i] = h < G ? sel_idx[(hrow0 + h) * stride + ppos] : 0;
+  }
   int cnt[HPW];
 #pragma unroll
   for (int i = 0; i < HPW; ++i) {
@@ -130,7 +142,8 @@ __global__ __launch_bounds__(kUThreads) void sparse_union(
     const int h = wave + i * kUWaves;
     if (h >= G) break;
     const int32_t* list = sel_idx + (hrow0 + h) * stride;
-    const int2 lh = list_bounds(list, cnt[i], c0, c1, lane);
+    const int2 lh = list_bounds_from(list, cnt[i], pstep, ppos < cnt[i] ? pv[i] : INT_MAX, c0, c1,
+                                     lane);
     // eight coalesced loads per lane in flight per round
     for (int p0 = lh.x; p0 < lh.y; p0 += 8 * kWave) {
       int xs[8];
@@ -828,7 +841,7 @@ size_t decode_sparse_ws_bytes(int B, int Hq, int Hkv, int max_ctx, int stride) {
 }
 
 hipError_t launch_decode_sparse(const DecodeSparseArgs& a, hipStream_t stream) {
-  if (a.sel_stride > kMaxStride) return hipErrorInvalidValue;
+  if (a.sel_stride < 1 || a.sel_stride > kMaxStride) return hipErrorInvalidValue;
   const int G = a.Hq / a.Hkv;
   const SpLayout s = sp_layout(a.B, a.Hq, a.Hkv, a.max_ctx, a.sel_stride);
   char* ws = static_cast<char*>(a.ws);
