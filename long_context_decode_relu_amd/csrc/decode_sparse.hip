@@ -78,24 +78,7 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   l[1] = (__bf16)(b - bf16_hi(hi));
   lo = __builtin_bit_cast(uint32_t, l);
 }
-constexpr int kMaxStride = kWave * kWave;         // two rounds of 64 probes
-
-// Numbers of entries below x0 and below x1 in list[0 .. cnt) (ascending), by
-// two rounds of 64 probes, every lane getting both. The first round comes
-// loaded: v is the entry at position min(L, (lane + 1) * step) - 1 of the
-// list's row of L >= cnt slots (step = ceil(L / 64) <= 64), taken as INT_MAX
-// past cnt, so that those probes can be issued before cnt is known.
-__device__ __forceinline__ int2 list_bounds_from(const int32_t* list, int cnt, int step, int v,
-                                                 int x0, int x1, int lane) {
-  if (cnt <= 0) return int2{0, 0};
-  const int b0 = min(cnt, (int)__popcll(__ballot(v < x0)) * step);
-  const int b1 = min(cnt, (int)__popcll(__ballot(v < x1)) * step);
-  const int p0 = b0 + lane, p1 = b1 + lane;
-  const bool in0 = lane < step && p0 < cnt && list[min(p0, cnt - 1)] < x0;
-  const bool in1 = lane < step && p1 < cnt && list[min(p1, cnt - 1)] < x1;
-  const int lo = b0 + (int)__popcll(__ballot(in0));
-  return int2{lo, max(lo, b1 + (int)__popcll(__ballot(in1)))};
-}
+constexpr int kMaxStride = kWave * kWave;         // 64 probes of at most 64 entries each
 
 template <int G>
 __global__ __launch_bounds__(kUThreads) void sparse_union(
@@ -135,28 +118,50 @@ __global__ __launch_bounds__(kUThreads) void sparse_union(
 #pragma unroll
   for (int h = 0; h < G; ++h) s_bm[h][tid] = 0u;
   __syncthreads();
-  // each wave marks its heads' entries in [c0, c1): with ascending lists they
-  // sit at positions [lo, hi) of the list; lo entries lie below the segment
+  // each wave marks its heads' entries in [c0, c1). With ascending lists the
+  // first probes bound the segment's start lo to [b0, b0 + step) and its end
+  // to below e1; positions [b0, e1) are then read (both heads' first rounds
+  // in flight together) and lo = b0 + the entries read that lie below c0.
+  int b0[HPW], e1[HPW];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int v = ppos < cnt[i] ? pv[i] : INT_MAX;
+    b0[i] = min(cnt[i], (int)__popcll(__ballot(v < c0)) * pstep);
+    e1[i] = min(cnt[i], (int)__popcll(__ballot(v < c1)) * pstep + pstep);
+  }
+  constexpr int kRound = 8;  // coalesced loads per lane in flight per head and round
+  int xs[HPW][kRound];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int32_t* list = sel_idx + (hrow0 + min(wave + i * kUWaves, G - 1)) * stride;
+#pragma unroll
+    for (int e = 0; e < kRound; ++e) {
+      const int p = b0[i] + e * kWave + lane;
+      xs[i][e] = p < e1[i] ? list[p] : INT_MAX;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < HPW; ++i) {
     const int h = wave + i * kUWaves;
     if (h >= G) break;
     const int32_t* list = sel_idx + (hrow0 + h) * stride;
-    const int2 lh = list_bounds_from(list, cnt[i], pstep, ppos < cnt[i] ? pv[i] : INT_MAX, c0, c1,
-                                     lane);
-    // eight coalesced loads per lane in flight per round
-    for (int p0 = lh.x; p0 < lh.y; p0 += 8 * kWave) {
-      int xs[8];
+    int below = 0;
+    for (int p0 = b0[i]; p0 < e1[i]; p0 += kRound * kWave) {
+      if (p0 != b0[i]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = p0 + e * kWave + lane;
-        xs[e] = p < lh.y ? list[p] : -1;
+        for (int e = 0; e < kRound; ++e) {
+          const int p = p0 + e * kWave + lane;
+          xs[i][e] = p < e1[i] ? list[p] : INT_MAX;
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (xs[e] >= c0 && xs[e] < c1) atomicOr(&s_bm[h][(xs[e] - c0) >> 5], 1u << (xs[e] & 31));
+      for (int e = 0; e < kRound; ++e) {
+        const int x = xs[i][e];
+        below += (int)__popcll(__ballot(x < c0));
+        if (x >= c0 && x < c1) atomicOr(&s_bm[h][(x - c0) >> 5], 1u << (x & 31));
+      }
     }
-    if (lane == 0) s_lo[h] = lh.x;
+    if (lane == 0) s_lo[h] = b0[i] + below;
   }
   __syncthreads();
   // union words (one per thread), their row counts and the exclusive prefix
