@@ -245,14 +245,25 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
   const int nsl = min(nseg, ceil_div(n, kSegKeys));
 
   // the queries in LDS, normalised and scaled by scale * log2(e) (the softmax
-  // runs in base 2: exp(t - m) = exp2(t2 - m2), t2 = t log2 e)
+  // runs in base 2: exp(t - m) = exp2(t2 - m2), t2 = t log2 e); for the matrix
+  // cores already split, once per work-group, into the hi + lo bf16 pairs of
+  // the B fragments: word l of head h's row holds the hi pair of dims 2l,
+  // 2l + 1 and word 64 + l its lo pair
+  uint32_t (*const s_qw)[kHeadDim] = reinterpret_cast<uint32_t (*)[kHeadDim]>(s_q);
   for (int h = wave; h < G; h += kGWaves) {
     const float q0 = q[(hrow0 + h) * kHeadDim + 2 * lane];
     const float q1 = q[(hrow0 + h) * kHeadDim + 2 * lane + 1];
     float f = scale * 1.4426950408889634f;
     if constexpr (NORMQ) f = f / sqrtf(wave_sum_dpp(q0 * q0 + q1 * q1) * (1.0f / kHeadDim) + eps);
-    s_q[h][2 * lane] = q0 * f;
-    s_q[h][2 * lane + 1] = q1 * f;
+    if constexpr (BF16) {
+      uint32_t hi, lo;
+      split_pair(q0 * f, q1 * f, hi, lo);
+      s_qw[h][lane] = hi;
+      s_qw[h][kHeadDim / 2 + lane] = lo;
+    } else {
+      s_q[h][2 * lane] = q0 * f;
+      s_q[h][2 * lane + 1] = q1 * f;
+    }
   }
 
   // The chunk's rows are union ranks [r0, r0 + kChunk) of the stream; row r
@@ -387,19 +398,13 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
           // piece 2 s8 + ah (8 dims) of row ar sits in slot (2 s8 + ah) ^ (ar & 15)
           a = *reinterpret_cast<const u32x4*>(ktile + ar * (kHeadDim * 2) + (((2 * s8 + ah) ^ (ar & 15)) << 4));
         }
-        uint32_t hv[4] = {0u, 0u, 0u, 0u}, lv[4] = {0u, 0u, 0u, 0u};
+        u32x4 hv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
         if (ar < G) {
-          const f32x4 q0 = *reinterpret_cast<const f32x4*>(&s_q[ar][16 * s8 + 8 * ah]);
-          const f32x4 q1 = *reinterpret_cast<const f32x4*>(&s_q[ar][16 * s8 + 8 * ah + 4]);
-          split_pair(q0[0], q0[1], hv[0], lv[0]);
-          split_pair(q0[2], q0[3], hv[1], lv[1]);
-          split_pair(q1[0], q1[1], hv[2], lv[2]);
-          split_pair(q1[2], q1[3], hv[3], lv[3]);
+          hv = *reinterpret_cast<const u32x4*>(&s_qw[ar][8 * s8 + 4 * ah]);
+          lv = *reinterpret_cast<const u32x4*>(&s_qw[ar][kHeadDim / 2 + 8 * s8 + 4 * ah]);
         }
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(u32x4{hv[0], hv[1], hv[2], hv[3]}),
-                                                     st, 0, 0, 0);
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(u32x4{lv[0], lv[1], lv[2], lv[3]}),
-                                                     st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(hv), st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(lv), st, 0, 0, 0);
       }
       float* const sc = &s_p[wave][0][0];  // [head][row] here
       if (ar < G) {
