@@ -309,6 +309,8 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
   // heads); a wave with no rows keeps an empty state
   const int nb = nrow - kWRows * wave;  // rows of this wave (uniform)
   float m_w[G], l_w[G], acc[G][2];
+  // matrix-core path: lane l's own head l % 32 (< G), its maximum and sum
+  float m_own = -INFINITY, l_own = 0.f;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_w[h] = -INFINITY;
@@ -368,7 +370,9 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     }
     if constexpr (BF16) __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-    // scores of this lane's row against the G heads
+    // scores of this lane's row against the G heads (the matrix cores leave
+    // them in st, one head per lane)
+    f32x16 st;
     float t[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) t[h] = 0.f;
@@ -381,7 +385,6 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
       // against head l % 32. The scores go through this wave's weight slots in
       // LDS (free until its weights are written) to the lanes of their rows.
       const int ar = lane & 31, ah = lane >> 5;
-      f32x16 st;
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[i] = 0.f;
 #pragma unroll
@@ -406,19 +409,6 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(hv), st, 0, 0, 0);
         st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(lv), st, 0, 0, 0);
       }
-      float* const sc = &s_p[wave][0][0];  // [head][row] here
-      if (ar < G) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4*>(&sc[ar * kWRows + 8 * i4 + 4 * ah]) =
-              f32x4{st[4 * i4], st[4 * i4 + 1], st[4 * i4 + 2], st[4 * i4 + 3]};
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int h = 0; h < G; ++h) t[h] = sc[h * kWRows + ri];
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_wave_barrier();  // the weights overwrite these slots below
       if constexpr (NORMK) {
         // the key's sum of squares: each of its two lanes takes half of the dims
         if constexpr (FP8) {
@@ -479,18 +469,68 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
       kf = 1.f / sqrtf(ss * (1.0f / kHeadDim) + eps);
     }
     // per head: the wave's maximum over its rows of the head, their weights
-    // relative to it and their sum (over the lower half's lanes); the weights
-    // go to this wave's slots as [head][row]
+    // relative to it and their sum; the weights go to this wave's slots as
+    // [head][row]
     float* const sp = &s_p[wave][0][0];
+    if constexpr (BF16) {
+      // in the scores' own layout: lane l holds head l % 32 against rows
+      // 8 (i / 4) + 4 (l / 32) + i % 4, i < 16, so a head's maximum and sum
+      // are 16 values in a lane and one exchange between its two lanes. Each
+      // row's head mask and key factor come through the wave's K tile, whose
+      // rows have been read.
+      const int ar = lane & 31, ah = lane >> 5;
+      float* const rowf = reinterpret_cast<float*>(ktile);  // [row]: factor, then mask
+      int* const rowm = reinterpret_cast<int*>(ktile) + kWRows;
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      if (!half) {
+        rowf[ri] = kf;
+        rowm[ri] = hb;
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_wave_barrier();
+      float th[16];
+      bool on[16];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bool on = (hb >> h) & 1;
-      const float th = on ? t[h] * kf : -INFINITY;
-      const float mw = wave_max_dpp(th);
-      const float pr = on ? exp2f(th - mw) : 0.f;
-      m_w[h] = mw;
-      l_w[h] = wave_sum_dpp(half ? 0.f : pr);
-      if (!half) sp[h * kWRows + ri] = pr;  // [head][row]
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&rowf[8 * i4 + 4 * ah]);
+        const int4 m4 = *reinterpret_cast<const int4*>(&rowm[8 * i4 + 4 * ah]);
+        const int mm[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          on[i] = ar < G && ((mm[e] >> ar) & 1);
+          th[i] = on[i] ? st[i] * k4[e] : -INFINITY;
+          mx = fmaxf(mx, th[i]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, kWRows, kWave));
+      float ls = 0.f;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 p4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          p4[e] = on[i] ? exp2f(th[i] - mx) : 0.f;
+          ls += p4[e];
+        }
+        if (ar < G) *reinterpret_cast<f32x4*>(&sp[ar * kWRows + 8 * i4 + 4 * ah]) = p4;
+      }
+      m_own = mx;
+      l_own = ls + __shfl_xor(ls, kWRows, kWave);
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bool on = (hb >> h) & 1;
+        const float th = on ? t[h] * kf : -INFINITY;
+        const float mw = wave_max_dpp(th);
+        const float pr = on ? exp2f(th - mw) : 0.f;
+        m_w[h] = mw;
+        l_w[h] = wave_sum_dpp(half ? 0.f : pr);
+        if (!half) sp[h * kWRows + ri] = pr;  // [head][row]
+      }
     }
     // acc[h] (this lane's two dims) = sum over the wave's rows of p[r][h] v[r].
     // A row outside head h's selection never enters its sum: where a value
@@ -628,10 +668,14 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     *reinterpret_cast<f32x2*>(&s_acc[(wave * G + h) * kHeadDim + 2 * lane]) = f32x2{acc[h][0], acc[h][1]};
-    if (lane == 0) {
+    if (!BF16 && lane == 0) {
       s_mm[wave][h] = m_w[h];
       s_ll[wave][h] = l_w[h];
     }
+  }
+  if (BF16 && lane < G) {
+    s_mm[wave][lane] = m_own;
+    s_ll[wave][lane] = l_own;
   }
   __syncthreads();
   const size_t slot = (size_t)j * C + c;
