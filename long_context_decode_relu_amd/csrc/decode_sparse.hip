@@ -537,13 +537,19 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     // row is not finite the products with zero weights are skipped (a wave
     // whose rows are all finite takes the plain loop)
     bool fin = true;
+    if constexpr (BF16) {
+      // a field is all ones exactly when adding one at its lowest bit carries
+      // into the bit above it (8-bit codes: the seven bits below the sign,
+      // S.1111.111 being the only non-finite code; bf16: the exponent), and
+      // no sum carries past its own half
+      uint32_t z = 0u;
 #pragma unroll
-    for (int rr = 0; rr < kWRows; ++rr) {
-      if constexpr (FP8)  // neither code is S.1111.111
-        fin = fin && (vb[rr] & 0x7fu) != 0x7fu && (vb[rr] & 0x7f00u) != 0x7f00u;
-      else if constexpr (BF16)  // exponent bits of neither bf16 all ones
-        fin = fin && (vb[rr] & 0x7f80u) != 0x7f80u && (vb[rr] & 0x7f800000u) != 0x7f800000u;
-      else fin = fin && isfinite(vf[rr][0]) && isfinite(vf[rr][1]);
+      for (int rr = 0; rr < kWRows; ++rr)
+        z |= FP8 ? (vb[rr] & 0x7f7fu) + 0x0101u : (vb[rr] & 0x7f807f80u) + 0x00800080u;
+      fin = (z & (FP8 ? 0x8080u : 0x80008000u)) == 0u;
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < kWRows; ++rr) fin = fin && isfinite(vf[rr][0]) && isfinite(vf[rr][1]);
     }
     const bool all_fin = __ballot(!fin) == 0;
     auto accumulate = [&](auto guarded) __attribute__((always_inline)) {

@@ -71,6 +71,37 @@ def test_fp8_sparse_vs_oracle():
     assert_rows_close(out.cpu().numpy(), want, TOL_BF16, wl.name)
 
 
+def test_fp8_sparse_nan_code_stays_in_its_head():
+    """A value row holding the NaN code (either sign), selected by one head of
+    its group only, makes that head's output NaN in those dims, as the
+    definition does, and leaves the group's other heads untouched: the gather
+    work-group holding it takes the guarded vector path, not the matrix cores."""
+    wl = fp8_workload("fp8_nan", 77, [6000])
+    ref = O.decode_full(wl.q, wl.k, oracle_v(wl), wl.ctx_lens)
+    sels = O.select_all(ref["scores"], wl.ctx_lens, 1024, 128)
+    used_by = np.zeros((8, 6000), dtype=bool)
+    for h in range(8):
+        used_by[h, sels[0][h]] = True
+    only = np.flatnonzero(used_by[0] & ~used_by[1:].any(axis=0))
+    assert len(only) >= 2
+    wl.v = wl.v.copy()
+    wl.v[0, 0, only[0], 9] = 0x7F
+    wl.v[0, 0, only[1], 120] = 0xFF
+    cache = ssa.cache_from_workload(wl, DEV)
+    idx = np.full((1, 16, 1152), -1, dtype=np.int32)
+    cnt = np.zeros((1, 16), dtype=np.int32)
+    for h in range(16):
+        idx[0, h, :len(sels[0][h])] = sels[0][h]
+        cnt[0, h] = len(sels[0][h])
+    out = ssa.ssa_decode_sparse(torch.from_numpy(wl.q_sparse[0]).to(DEV), cache,
+                                torch.from_numpy(idx).to(DEV),
+                                torch.from_numpy(cnt).to(DEV)).cpu().numpy()
+    want = O.decode_sparse(wl.q_sparse[0], wl.k, oracle_v(wl), sels)
+    assert np.array_equal(np.isfinite(out[0, 0]), np.isfinite(want[0, 0]))
+    assert np.isnan(want[0, 0, 9]) and np.isnan(want[0, 0, 120])
+    assert_rows_close(out[:, 1:], want[:, 1:], TOL_BF16, wl.name)
+
+
 @pytest.mark.parametrize("hq,hkv,flags", [(4, 4, O.SSA_NORM_Q), (8, 2, O.SSA_NORM_Q | O.SSA_NORM_K),
                                            (16, 4, 0), (16, 2, O.SSA_NORM_Q)])
 def test_fp8_sparse_group_sizes_and_flags(hq, hkv, flags):

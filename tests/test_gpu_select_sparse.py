@@ -252,6 +252,37 @@ def test_sparse_scale_flags_and_nan_poison():
     check_sparse(wl, sels, flags=O.SSA_NORM_Q | O.SSA_NORM_K)
 
 
+def test_sparse_nonfinite_value_rows_stay_in_their_heads():
+    """A value row with an infinite or NaN entry, selected by one head of its
+    group only, turns that head's output non-finite as the definition does and
+    leaves every other head of the group (which gives the row no weight, and
+    so never multiplies it) as it is: a gather work-group holding such a row
+    cannot take the matrix-core products, where a zero weight times it would
+    spread to every head."""
+    wl = synth.make_workload("spinf", seed=41, batch=1, n_q_heads=16, n_kv_heads=2,
+                             ctx_lens=[6000], recipe="planted", p=0.05)
+    sels = oracle_selection(wl)
+    used_by = np.zeros((8, 6000), dtype=bool)
+    for h in range(8):
+        used_by[h, sels[0][h]] = True
+    only = np.flatnonzero(used_by[0] & ~used_by[1:].any(axis=0))
+    assert len(only) >= 3
+    v = wl.v.copy()
+    v[0, 0, only[0], 5] = np.uint16(0x7F80)    # +inf
+    v[0, 0, only[1], 77] = np.uint16(0xFF80)   # -inf
+    v[0, 0, only[2], 100] = synth.BF16_NAN
+    qs = wl.q_sparse[0]
+    cache = ssa.cache_from_workload(wl, DEV)
+    cache.v = ssa.kv_tensor(v, DEV)
+    si, sc = sel_tensors(sels, 1, 16, 1152)
+    out = ssa.ssa_decode_sparse(torch.from_numpy(qs).to(DEV), cache, si, sc,
+                                flags=O.SSA_NORM_Q).cpu().numpy()
+    ref = O.decode_sparse(qs, wl.k, v, sels, flags=O.SSA_NORM_Q)
+    assert np.array_equal(np.isfinite(out[0, 0]), np.isfinite(ref[0, 0]))
+    assert not np.all(np.isfinite(ref[0, 0]))
+    assert_rows_close(out[:, 1:], ref[:, 1:], TOL_BF16, wl.name)
+
+
 def test_sparse_union_extremes():
     """Heads of a group select disjoint blocks (the union is the largest the
     stride allows, 8 * 1152 rows spread over several 64K-key planning passes),
