@@ -1446,8 +1446,8 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
 
 // Count, smallest and largest key of the candidates held in registers (the
 // first nr of P per thread; nr is uniform over the wave) over the work-group,
-// and whether `any` holds on some thread; clears the cut-bin counter. Two
-// barriers.
+// and whether `any` holds on some thread; clears the cut-bin counter and
+// ranks. Two barriers.
 template <int P>
 __device__ int cands_count_range(SelShared& sh, const uint32_t (&key)[P], const bool (&cnd)[P],
                                  int nr, bool any, uint32_t* kmin_out, uint32_t* kmax_out,
@@ -1477,6 +1477,7 @@ __device__ int cands_count_range(SelShared& sh, const uint32_t (&key)[P], const 
     sh.ckey[kSelWaves + wave] = kmax;
   }
   if (tid == 0) sh.ccount = 0;
+  if (tid < kWave) sh.crank[tid] = 0;
   __syncthreads();
   // the waves' figures: lane l < 16 reads wave l's, then a reduction over 16 lanes
   const int lw = lane & (kSelWaves - 1);
@@ -1520,8 +1521,10 @@ __device__ void cands_cut(SelShared& sh, const uint32_t (&key)[P], const int32_t
   bool done = false;
   while (true) {
     if (eq <= kWave) {
-      // the cut bin's keys to LDS, ranked by wave 0 (key descending, index
-      // ascending); the need-th is the last one selected
+      // the cut bin's keys to LDS and their ranks (key descending, index
+      // ascending; the keys are distinct pairs, so the ranks are 0 .. eq-1):
+      // wave w counts, for every key, those of keys 4w .. 4w+3 that come
+      // before it; then every wave finds the need-th, the last one selected
 #pragma unroll
       for (int u = 0; u < P; ++u) {
         if (u < nr && cnd[u] && in_bin(key[u], L, vstar)) {
@@ -1531,24 +1534,26 @@ __device__ void cands_cut(SelShared& sh, const uint32_t (&key)[P], const int32_t
         }
       }
       __syncthreads();
-      if (wave == 0) {
-        const bool has = lane < eq;
-        const uint32_t kl = has ? sh.ckey[lane] : 0u;
-        const int il = has ? sh.cidx[lane] : INT_MAX;
-        int rank = 0;
-        for (int q = 0; q < eq; ++q) {
-          const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, q);
-          const int iq = __builtin_amdgcn_readlane(il, q);
-          rank += (kq > kl || (kq == kl && iq < il)) ? 1 : 0;
-        }
-        if (has && rank == need - 1) {
-          sh.bcast[0] = (int)kl;
-          sh.bcast[1] = il;
+      static_assert(kSelWaves * 4 == kWave, "four keys a wave");
+      const bool has = lane < eq;
+      const uint32_t kl = has ? sh.ckey[lane] : 0u;
+      const int il = has ? sh.cidx[lane] : INT_MAX;
+      int before = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int qq = 4 * wave + e;
+        if (qq < eq) {
+          const uint32_t kq = sh.ckey[qq];
+          const int iq = sh.cidx[qq];
+          before += (kq > kl || (kq == kl && iq < il)) ? 1 : 0;
         }
       }
+      if (has && before > 0) atomicAdd(&sh.crank[lane], before);
       __syncthreads();
-      vstar = (uint32_t)__builtin_amdgcn_readfirstlane(sh.bcast[0]);
-      istar = __builtin_amdgcn_readfirstlane(sh.bcast[1]);
+      const int rank = has ? sh.crank[lane] : -1;
+      const int hl = __builtin_ctzll(__ballot(rank == need - 1));
+      vstar = (uint32_t)__builtin_amdgcn_readlane((int)kl, hl);
+      istar = __builtin_amdgcn_readlane(il, hl);
       done = true;
       break;
     }

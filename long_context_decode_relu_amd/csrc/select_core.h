@@ -28,6 +28,7 @@ struct SelShared {
   int32_t cidx[kCap];
   uint32_t bits[kSegWords];
   int32_t scan[kSelThreads];
+  int32_t crank[kWave];  // ranks of a cut bin of at most 64 keys
   int32_t ccount;
   int32_t bcast[4];
 };
