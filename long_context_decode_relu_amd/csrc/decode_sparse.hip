@@ -226,6 +226,8 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
   __shared__ __attribute__((aligned(16))) float s_p[kGWaves][kWRows][GP];
   __shared__ float s_mm[kGWaves][G];
   __shared__ float s_ll[kGWaves][G];
+  __shared__ float s_f[kGWaves][G];  // the merge's factor of each wave and head
+  __shared__ float s_ml[2][G];       // the chunk's maximum and sum per head
 
   // chunk-major order: the streams' first chunks, which always hold rows,
   // are dispatched before later chunks, which may hold none
@@ -684,26 +686,35 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     s_ll[wave][lane] = l_own;
   }
   __syncthreads();
+  // per head, once: the chunk's maximum over the waves, each wave's factor
+  // 2^(m_w - M) (0 for a wave without the head's rows, whose sums are then
+  // zero) and the chunk's sum
+  if (tid < G) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kGWaves; ++w) M = fmaxf(M, s_mm[w][tid]);
+    float ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGWaves; ++w) {
+      const float mp = s_mm[w][tid];
+      const float f = M == -INFINITY || mp == -INFINITY ? 0.f : exp2f(mp - M);
+      s_f[w][tid] = f;
+      ls = fmaf(f, s_ll[w][tid], ls);
+    }
+    s_ml[0][tid] = M;
+    s_ml[1][tid] = ls;
+  }
+  __syncthreads();
   const size_t slot = (size_t)j * C + c;
   for (int e = tid; e < G * kHeadDim; e += kGThreads) {
     const int h = e / kHeadDim, d = e - h * kHeadDim;
-    float M = -INFINITY;
+    float a = 0.f;
 #pragma unroll
-    for (int w = 0; w < kGWaves; ++w) M = fmaxf(M, s_mm[w][h]);
-    float a = 0.f, ls = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kGWaves; ++w) {
-        const float mp = s_mm[w][h];
-        const float f = mp == -INFINITY ? 0.f : exp2f(mp - M);
-        a = fmaf(f, s_acc[(w * G + h) * kHeadDim + d], a);
-        ls = fmaf(f, s_ll[w][h], ls);
-      }
-    }
+    for (int w = 0; w < kGWaves; ++w) a = fmaf(s_f[w][h], s_acc[(w * G + h) * kHeadDim + d], a);
     part_acc[(slot * G + h) * kHeadDim + d] = FP8 ? a * vsc[j] : a;
     if (d == 0) {
-      part_m[slot * G + h] = M;  // -inf: head h selects no row of the chunk
-      part_l[slot * G + h] = ls;
+      part_m[slot * G + h] = s_ml[0][h];  // -inf: head h selects no row of the chunk
+      part_l[slot * G + h] = s_ml[1][h];
     }
   }
 }
