@@ -37,11 +37,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
   return x;
 }
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
-  return x;
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
@@ -70,6 +65,30 @@ __device__ __forceinline__ float wave_max_dpp(float x) {
   const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16);
   const float r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Integer sum and maximum across the 64 lanes of a wave, with the same DPP
+// pattern (exact, so any order gives the same result); every lane of the
+// wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp_move_i<0xB1>(x);
+  x += dpp_move_i<0x4E>(x);
+  x += dpp_move_i<0x141>(x);
+  x += dpp_move_i<0x140>(x);
+  return (__builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16)) +
+         (__builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48));
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_move_i<0xB1>(x));
+  x = max(x, dpp_move_i<0x4E>(x));
+  x = max(x, dpp_move_i<0x141>(x));
+  x = max(x, dpp_move_i<0x140>(x));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // Order-preserving map of a float's bits to uint32 (larger float -> larger key).

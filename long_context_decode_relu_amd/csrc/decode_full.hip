@@ -1965,8 +1965,7 @@ __device__ uint32_t decide_stream(int j, const int32_t* __restrict__ cand_cnt,
     }
   }
   E = wave_sum_i(E);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, kWave));
+  emax = wave_max_i(emax);
   const int pool = disjoint ? max(0, n - n_recent) : n;
   const int kk = min(k_top, pool);
   // keys of the recent window are not in the pool of a disjoint selection
