@@ -1444,6 +1444,33 @@ __global__ __launch_bounds__(kCombineThreads) void decode_full_combine(
 // ---------------------------------------------------------------------------
 
 
+// Reductions over the 16 lanes of each row of a wave by DPP moves (every
+// lane active; each lane gets its row's result), and over the whole wave.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <class Op>
+__device__ __forceinline__ uint32_t row_reduce_u(uint32_t x, Op op) {
+  x = op(x, dpp_u<0xB1>(x));   // lane ^ 1
+  x = op(x, dpp_u<0x4E>(x));   // lane ^ 2
+  x = op(x, dpp_u<0x141>(x));  // the other quad of the half row
+  return op(x, dpp_u<0x140>(x));  // the other half of the row
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u(uint32_t x, Op op) {
+  x = row_reduce_u(x, op);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+struct MinU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct MaxU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? b : a; } };
+struct AddU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OrU { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+
 // Count, smallest and largest key of the candidates held in registers (the
 // first nr of P per thread; nr is uniform over the wave) over the work-group,
 // and whether `any` holds on some thread; clears the cut-bin counter and
@@ -1463,12 +1490,9 @@ __device__ int cands_count_range(SelShared& sh, const uint32_t (&key)[P], const 
       kmax = max(kmax, key[u]);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    local += __shfl_xor(local, off, kWave);
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-  }
+  local = (int)wave_reduce_u((uint32_t)local, AddU{});
+  kmin = wave_reduce_u(kmin, MinU{});
+  kmax = wave_reduce_u(kmax, MaxU{});
   const bool wany = __ballot(any) != 0;
   if (lane == 0) {
     sh.scan[wave] = local;
@@ -1484,13 +1508,11 @@ __device__ int cands_count_range(SelShared& sh, const uint32_t (&key)[P], const 
   int c = sh.scan[lw], a = sh.scan[kSelWaves + lw];
   kmin = sh.ckey[lw];
   kmax = sh.ckey[kSelWaves + lw];
-#pragma unroll
-  for (int off = kSelWaves / 2; off >= 1; off >>= 1) {
-    c += __shfl_xor(c, off, kWave);
-    a |= __shfl_xor(a, off, kWave);
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-  }
+  static_assert(kSelWaves == 16, "one figure per lane of a DPP row");
+  c = (int)row_reduce_u((uint32_t)c, AddU{});
+  a = (int)row_reduce_u((uint32_t)a, OrU{});
+  kmin = row_reduce_u(kmin, MinU{});
+  kmax = row_reduce_u(kmax, MaxU{});
   __syncthreads();  // sh.scan and sh.ckey are reused by the caller
   // the same on every lane: scalar from here on
   *kmin_out = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmin);
