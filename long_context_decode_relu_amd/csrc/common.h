@@ -91,6 +91,20 @@ __device__ __forceinline__ int wave_max_i(int x) {
              max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
+// Inclusive integer scan over the 64 lanes of a wave by DPP moves (every lane
+// active): shifts by 1, 2, 4 and 8 within each row of 16 lanes (lanes below
+// the shift add zero), then lane 15's total into row 1 and row 3 and lane
+// 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_scan_incl_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 // Order-preserving map of a float's bits to uint32 (larger float -> larger key).
 // -0.0 is mapped like +0.0 so that the two compare equal.
 __device__ __forceinline__ uint32_t ordered_key(float x) {

@@ -551,12 +551,7 @@ __device__ void tile_prefix(const int32_t* ctx_lens, int S, int Hkv, int max_ctx
     const int i = i0 + r;
     if (i < S) local += ceil_div(live_keys(ctx_lens, i / Hkv, max_ctx), kTileKeys);
   }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_scan_incl_i(local);
   int run = incl - local;
   for (int r = 0; r < per; ++r) {
     const int i = i0 + r;
@@ -1857,12 +1852,7 @@ __device__ __forceinline__ bool select_fast(SelShared& sh, const int32_t* __rest
       v[i] = q < np ? sh.bits[q] : 0u;
       local += v[i];
     }
-    uint32_t incl = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_up((int)incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
+    const uint32_t incl = (uint32_t)wave_scan_incl_i((int)local);
     uint32_t run = incl - local;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {

@@ -174,12 +174,7 @@ __global__ __launch_bounds__(kUThreads) void sparse_union(
     x |= hw[h];
   }
   const int pc = __popc(x);
-  int incl = pc;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_scan_incl_i(pc);
   if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int before = 0, total = 0, off = 0;
@@ -280,13 +275,7 @@ __global__ __launch_bounds__(kGThreads) void sparse_gather(
     int u = g0 == 0 ? ua : (g < nsl ? ucnt[(size_t)j * nseg + g] : 0);
     const int o = g0 == 0 ? oa : (g < nsl ? uoff[(size_t)j * nseg + g] : 0);
     u = g < nsl ? u : 0;
-    int incl = u;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += t;
-    }
-    incl += carry;
+    const int incl = wave_scan_incl_i(u) + carry;
     const int tot = __shfl(incl, kWave - 1, kWave);
     // segments of this round whose inclusive prefix is <= r (every lane runs
     // the shuffles; rows past this round's total take nothing from it)

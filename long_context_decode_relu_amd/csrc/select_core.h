@@ -153,12 +153,7 @@ __device__ int cut_bin(const uint32_t* hist, int nb, int need, SelShared& sh, in
     const int b = nb - 1 - (tid * per + i);
     if (b >= 0) local += (int)hist[b];
   }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
+  const int incl = wave_scan_incl_i(local);
   if (lane == kWave - 1) sh.scan[wave] = incl;
   __syncthreads();
   int before = 0;
