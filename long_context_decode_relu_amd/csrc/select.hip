@@ -89,12 +89,7 @@ __device__ uint32_t sample_threshold(const float* s, int pool, int k, uint32_t* 
       int c[4], sum = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) { c[e] = (int)hist[255 - 4 * lane - e]; sum += c[e]; }
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int t = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += t;
-      }
+      const int incl = wave_scan_incl_i(sum);
       const int before = incl - sum;
       if (before < need && incl >= need) {
         int run2 = before;

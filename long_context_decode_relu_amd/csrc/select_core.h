@@ -76,22 +76,12 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool act)
 // the 16 wave totals are then scanned by one wave (two barriers in all).
 __device__ int block_scan_excl(int x, int32_t* scratch, int* total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  int incl = x;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
+  const int incl = wave_scan_incl_i(x);
   if (lane == kWave - 1) scratch[wave] = incl;
   __syncthreads();
   if (wave == 0) {
     const int wt = lane < kSelWaves ? scratch[lane] : 0;
-    int wi = wt;
-#pragma unroll
-    for (int off = 1; off < kSelWaves; off <<= 1) {
-      const int t = __shfl_up(wi, off, kWave);
-      if (lane >= off) wi += t;
-    }
+    const int wi = wave_scan_incl_i(wt);
     if (lane < kSelWaves) scratch[kSelWaves + lane] = wi - wt;  // exclusive wave offsets
     if (lane == kSelWaves - 1) scratch[2 * kSelWaves] = wi;
   }
